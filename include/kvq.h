@@ -1,0 +1,220 @@
+/*
+ * kvq.h -- C ABI of libkvq: quantize-on-write and split-K paged decode
+ * attention over an INT8, FP8 (OCP E4M3) or INT4 KV cache, for AMD MI355X
+ * (gfx950).
+ *
+ * Method (from three web pages on KV-cache quantization):
+ *   [yunthe]  "KV Cache量化压缩技术与vLLM推理引擎显存优化实战"
+ *   [oh-bug]  "KV Cache Quantization 生产实战：用低精度缓存降低长上下文推理显存"
+ *   [intelli] "大模型KV Cache显存优化与量化技术实践"
+ *
+ *  - Symmetric quantization: scale = max|x| / 127, q = clamp(round(x/scale),
+ *    -128, 127)  ([intelli] §3.1 对称量化算法; [yunthe] section
+ *    "KV Cache量化策略：INT8与FP8精度对比与选择").  Division is one IEEE fp32
+ *    division, rounding is half-to-even.  FP8 uses scale = max|x| / 448 and
+ *    round-to-nearest-even into E4M3 after clamping to +-448.
+ *  - Granularity of the scale: tensor, head, channel or token ([oh-bug]
+ *    section "量化不是简单'截断精度'"); dynamic per-token scales are computed
+ *    on write ([intelli] §3.2 动态量化策略), static ones are inputs.
+ *  - Paged cache of 16-token blocks, dequantized inside the attention kernel
+ *    ([yunthe] section "PagedAttention与KV Cache量化协同工作原理").
+ *  - INT4 KIVI-style cache: K per channel, V per token, group 64, two codes
+ *    per byte, the newest tokens kept in fp16 (residual 128) ([oh-bug]
+ *    sections "Key 和 Value 的分布不一定相同" and "Transformers：适合实验和
+ *    小规模验证").
+ *  - Decode attention softmax(q K^T * softmax_scale) V over every cached token
+ *    ([intelli] §6 Q1; [oh-bug] section "为什么长上下文更需要 KV Cache
+ *    Quantization").
+ *
+ * Conventions for every entry point:
+ *  - All buffers are caller-owned DEVICE pointers except the kvq_layout and
+ *    kvq_cache structs themselves, which are host memory read during the call
+ *    only.  The library allocates, frees and synchronises nothing; it keeps no
+ *    state between calls and may be called from several host threads.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Kernels run
+ *    asynchronously on it, in call order.
+ *  - Arguments are validated on the host before any launch; on error a
+ *    negative kvq_status is returned and nothing is enqueued.  A failed launch
+ *    returns KVQ_ERR_HIP (the HIP error state is cleared before launching).
+ *  - Device pointers must be 16-byte aligned; fp16 data is IEEE binary16
+ *    passed as uint16_t; fp32 is IEEE binary32.
+ *  - Host integers (batch, total_new, max_new_per_seq, max_seq_len) size the
+ *    grids, because seq_lens lives on the device; they must bound the device
+ *    values (max over b of seq_lens[b] <= max_seq_len, new tokens per
+ *    sequence <= max_new_per_seq).  Violating a bound is undefined.
+ *  - Non-finite K/V inputs give unspecified codes.
+ *
+ * One kvq_cache describes ONE layer.  Shapes below use
+ *   NB = num_blocks, H = num_kv_heads, Hq = num_q_heads, D = head_dim = 128,
+ *   BS = block_size = 16, R = residual_len, G = group_size = 64,
+ *   RING = R + G (fp16 ring slots per sequence and head, INT4 only).
+ * Token t of batch row b lives in physical block block_tables[b*MBS + t/16],
+ * slot t % 16 (MBS = max_blocks_per_seq).
+ *
+ * ---- INT8 / FP8 code layout: uint8 [NB][H][2048] for each of K and V ------
+ * One (block, head) chunk holds 16 tokens x 128 channels.  Byte offset of
+ * (slot s, channel c) inside the chunk:
+ *   K: 1024*((c>>4)&1) + 256*(c>>5) + 16*s + (c&15)
+ *   V: 1024*(c>>6) + 256*(s>>2) + 16*(c&15) + 4*((c>>4)&3) + (s&3)
+ * INT8 codes are two's complement; FP8 codes are OCP E4M3 (0x7F/0xFF never
+ * written).  The orders put each lane's matrix-core operand in one 16-byte
+ * run so the decode kernel loads tiles straight into registers.
+ *
+ * ---- INT8 / FP8 scales (fp32), by granularity, for each of K and V ---------
+ *   KVQ_PER_TENSOR : [1]            (input)
+ *   KVQ_PER_HEAD   : [H]            (input)
+ *   KVQ_PER_CHANNEL: [H][128]       (input)
+ *   KVQ_PER_TOKEN  : [NB][H][16]    (written by kvq_write, max|x|/127 or /448)
+ * A zero scale quantizes every value to code 0.
+ *
+ * ---- INT4 (KIVI) layout ------------------------------------------------------
+ * The first nq(S) = max(0, floor((S-R)/G))*G tokens of a sequence are INT4;
+ * tokens nq(S) .. S-1 (R to R+G-1 of them once S >= R) stay fp16 in a ring.
+ *   k_codes : uint8 [NB][H][1024]; (slot s, channel c) at byte
+ *             256*(c>>5) + 16*s + ((c&31)>>1), low nibble for even c.
+ *   v_codes : uint8 [NB][H][1024]; with j = c>>4, u = (c&15) + 16*(s>>2),
+ *             w = j>>1, e = s&3, nibble p = 2*(j&1) + (e>>1) + 4*(e&1):
+ *             byte 16*u + 4*w + (p>>1), low nibble when p is even.
+ *   Codes are two's-complement nibbles in [-8, 7].
+ *   k_scales: fp32 [NB][H][32]; the block at logical index j of a sequence
+ *             holds the per-channel scales (max over the group's 64 tokens
+ *             of |K| / 7) of channels 32*(j%4) .. 32*(j%4)+31 of group j/4.
+ *   v_scales: fp32 [NB][H][16][2]; per token, channels 0..63 and 64..127
+ *             (max over the 64 channels of |V| / 7).
+ *   k_resid : fp16 [ring_rows][H][RING][128]; token t at slot t % RING.
+ *   v_resid : fp16 [ring_rows][H][RING/4][128][4]; token t at slot
+ *             s = t % RING is element [s>>2][c][s&3].
+ * Both granularity fields must be KVQ_PER_CHANNEL (K) and KVQ_PER_TOKEN (V).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* null pointer, bad enum, bad count            */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim != 128, g > 16 */
+  KVQ_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned      */
+  KVQ_ERR_WORKSPACE = -4,   /* decode workspace too small or misaligned     */
+  KVQ_ERR_CAPACITY = -5,    /* a length exceeds max_blocks_per_seq * 16      */
+  KVQ_ERR_HIP = -6          /* a kernel launch failed                       */
+} kvq_status;
+
+typedef enum kvq_dtype {
+  KVQ_INT8 = 1,     /* 1 byte per value, symmetric, divisor 127             */
+  KVQ_FP8_E4M3 = 2, /* 1 byte per value, OCP E4M3, divisor 448              */
+  KVQ_INT4 = 3      /* 0.5 byte per value, KIVI grouping, divisor 7         */
+} kvq_dtype;
+
+typedef enum kvq_granularity {
+  KVQ_PER_TENSOR = 0,
+  KVQ_PER_HEAD = 1,
+  KVQ_PER_CHANNEL = 2,
+  KVQ_PER_TOKEN = 3
+} kvq_granularity;
+
+/* Shape and quantization scheme of one layer's cache (host struct). */
+typedef struct kvq_layout {
+  uint32_t struct_size;       /* sizeof(kvq_layout)                          */
+  int32_t dtype;              /* kvq_dtype                                   */
+  int32_t k_gran;             /* kvq_granularity of K scales                 */
+  int32_t v_gran;             /* kvq_granularity of V scales                 */
+  int32_t group_size;         /* INT4: must be 64; ignored otherwise         */
+  int32_t residual_len;       /* INT4: multiple of 64, >= 64; else ignored   */
+  int32_t block_size;         /* must be 16                                  */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads              */
+  int32_t num_kv_heads;       /* H; Hq / H must be 1..16                     */
+  int32_t head_dim;           /* must be 128                                 */
+  int32_t num_blocks;         /* NB, physical blocks in the pool             */
+  int32_t max_blocks_per_seq; /* MBS, row length of block_tables             */
+  int32_t split_tokens;       /* decode partition length in tokens; 0 picks
+                                 one from the grid size.  Multiple of 16
+                                 (INT4: of 64).                              */
+} kvq_layout;
+
+/* Device buffers of one layer's cache (host struct of device pointers). */
+typedef struct kvq_cache {
+  void *k_codes;      /* see the layout notes above                          */
+  void *v_codes;
+  float *k_scales;
+  float *v_scales;
+  uint16_t *k_resid;  /* INT4 only (else may be NULL)                        */
+  uint16_t *v_resid;  /* INT4 only (else may be NULL)                        */
+  int32_t ring_rows;  /* INT4: rows of the fp16 rings (>= batch)             */
+} kvq_cache;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kvq_status_str(kvq_status status);
+
+/* Host-only check of a layout, cache and call size, exactly the checks the
+ * entry points run before launching.  Makes no HIP call.
+ * batch == 0 is valid (the entry points then do nothing). */
+kvq_status kvq_validate(const kvq_layout *layout, const kvq_cache *cache,
+                        int32_t batch, int32_t max_seq_len);
+
+/* Bytes of decode workspace for (layout, batch, max_seq_len); 0 if the
+ * layout is invalid.  The workspace holds split-K partials (m, l, o per
+ * partition and query head) and one int32 arrival counter per (b, KV head).
+ * The counters must be zero before the first kvq_paged_decode call that
+ * uses the buffer (e.g. zero-fill at allocation); every completed call
+ * leaves them at zero again. */
+size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
+                                  int32_t max_seq_len);
+
+/* Quantize-on-write: append new K/V tokens to the cache.
+ *   k_new, v_new : fp16 [total_new][H][128], the new tokens of all rows
+ *                  packed in row order.
+ *   cu_new       : int32 [batch+1], row b's tokens are k_new[cu_new[b] ..
+ *                  cu_new[b+1]-1]; cu_new[0] == 0, cu_new[batch] ==
+ *                  total_new.
+ *   block_tables : int32 [batch][MBS], physical block of each logical block.
+ *   seq_lens     : int32 [batch], lengths AFTER this write; the new tokens
+ *                  of row b take positions seq_lens[b]-n_b .. seq_lens[b]-1.
+ *   max_new_per_seq: host bound on n_b.
+ * INT8/FP8: writes codes (and per-token scales when the granularity is
+ * KVQ_PER_TOKEN) into the block slots.  Static scales are read from the
+ * cache's scale arrays.
+ * INT4: first quantizes every 64-token group that leaves the fp16 window
+ * (from the ring or straight from k_new/v_new) into INT4 blocks with its
+ * scales, then stores the remaining new tokens in the ring (two launches,
+ * in that order, so a ring slot is read before it is reused).
+ * Sequences must be extended in order; positions already written are
+ * overwritten with the same values when rewritten. */
+kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
+                     const uint16_t *k_new, const uint16_t *v_new,
+                     const int32_t *cu_new, const int32_t *block_tables,
+                     const int32_t *seq_lens, int32_t batch,
+                     int32_t total_new, int32_t max_new_per_seq,
+                     void *stream);
+
+/* Decode attention over the quantized paged cache, one query per row:
+ *   out[b][hq][:] = sum_t softmax_t(s_t) * v_hat[t],
+ *   s_t = softmax_scale * dot(q[b][hq], k_hat[t]),  t < seq_lens[b],
+ * with KV head hq / (Hq/H), k_hat/v_hat the dequantized values (code*scale,
+ * or fp16 for INT4 residual tokens).
+ *   q        : fp16 [batch][Hq][128]
+ *   out      : fp32 [batch][Hq][128]; rows with seq_lens[b] == 0 get zeros.
+ *   workspace: device buffer of at least kvq_decode_workspace_bytes(layout,
+ *              batch, max_seq_len) bytes, 256-byte aligned.  Calls that
+ *              share a workspace must not overlap in time.
+ * One kernel launch: split-K over token partitions; the last partition of
+ * each (row, KV head) to finish merges the partials (log-sum-exp) in a
+ * fixed order, so results are bitwise reproducible. */
+kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
+                            const uint16_t *q, const int32_t *block_tables,
+                            const int32_t *seq_lens, int32_t batch,
+                            int32_t max_seq_len, float softmax_scale,
+                            float *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

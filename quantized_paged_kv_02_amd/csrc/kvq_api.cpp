@@ -1,0 +1,247 @@
+// Host side of libkvq: argument validation, partition sizing and kernel
+// dispatch for the C ABI declared in include/kvq.h.  Everything here runs on
+// the host before any launch; the library keeps no state.
+#include "kvq.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kvq_args.h"
+
+namespace {
+
+constexpr int kBlock = 16;
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 64;
+// Aim for this many partition wavefronts per decode launch when the layout
+// does not fix the partition length (256 CUs x 8 resident wavefronts).
+constexpr long kTargetWaves = 2048;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int kivi_len(int s, int residual) {
+  const int n = s - residual;
+  return n > 0 ? (n / kGroup) * kGroup : 0;
+}
+
+kvq_status check_layout(const kvq_layout *L) {
+  if (!L) return KVQ_ERR_INVALID_ARG;
+  if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
+  if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4)
+    return KVQ_ERR_INVALID_ARG;
+  if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
+  if (L->v_gran < KVQ_PER_TENSOR || L->v_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
+  if (L->num_kv_heads < 1 || L->num_q_heads < 1) return KVQ_ERR_INVALID_ARG;
+  if (L->num_q_heads % L->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (L->num_blocks < 1 || L->max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (L->split_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (L->head_dim != kHeadDim || L->block_size != kBlock) return KVQ_ERR_UNSUPPORTED;
+  if (L->num_q_heads / L->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  if (L->dtype == KVQ_INT4) {
+    if (L->k_gran != KVQ_PER_CHANNEL || L->v_gran != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
+    if (L->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
+    if (L->residual_len < kGroup || L->residual_len % kGroup != 0) return KVQ_ERR_UNSUPPORTED;
+    if (L->split_tokens % kGroup != 0) return KVQ_ERR_INVALID_ARG;
+  } else if (L->split_tokens % kBlock != 0) {
+    return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_layout *L, const kvq_cache *C, int32_t batch) {
+  if (!C) return KVQ_ERR_INVALID_ARG;
+  if (!C->k_codes || !C->v_codes || !C->k_scales || !C->v_scales) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(C->k_codes) || !aligned16(C->v_codes) || !aligned16(C->k_scales) ||
+      !aligned16(C->v_scales))
+    return KVQ_ERR_ALIGNMENT;
+  if (L->dtype == KVQ_INT4) {
+    if (!C->k_resid || !C->v_resid) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(C->k_resid) || !aligned16(C->v_resid)) return KVQ_ERR_ALIGNMENT;
+    if (C->ring_rows < batch) return KVQ_ERR_CAPACITY;
+  }
+  return KVQ_OK;
+}
+
+// Partition plan for a decode launch.
+struct Plan {
+  int part_blocks;  // blocks per main partition
+  int num_parts;    // main partitions in the grid
+  int slots;        // partial slots per (row, query head)
+};
+
+Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
+  Plan p{};
+  const bool int4 = L->dtype == KVQ_INT4;
+  const int blocks = int4 ? kivi_len(max_seq_len, L->residual_len) / kBlock
+                          : (max_seq_len + kBlock - 1) / kBlock;
+  const int unit = int4 ? 4 : 1;  // INT4 partitions hold whole groups
+  int pb;
+  if (L->split_tokens > 0) {
+    pb = L->split_tokens / kBlock;
+  } else {
+    const long units = (long)batch * L->num_kv_heads;
+    long want = (units * blocks + kTargetWaves - 1) / kTargetWaves;
+    if (want < 8) want = 8;
+    pb = (int)((want + unit - 1) / unit * unit);
+  }
+  if (pb < unit) pb = unit;
+  p.part_blocks = pb;
+  p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 0;
+  if (!int4 && p.num_parts == 0) p.num_parts = 1;  // rows of length 0 still write zeros
+  p.slots = p.num_parts + (int4 ? 1 : 0);
+  return p;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WorkspaceLayout {
+  size_t cnt_off, m_off, l_off, o_off, total;
+};
+
+WorkspaceLayout workspace_layout(const kvq_layout *L, int32_t batch, const Plan &p) {
+  WorkspaceLayout w{};
+  const size_t rows = (size_t)batch * L->num_q_heads * p.slots;
+  w.cnt_off = 0;
+  w.m_off = round_up((size_t)batch * L->num_kv_heads * sizeof(int32_t), 256);
+  w.l_off = w.m_off + round_up(rows * sizeof(float), 256);
+  w.o_off = w.l_off + round_up(rows * sizeof(float), 256);
+  w.total = w.o_off + round_up(rows * kHeadDim * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG: invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: configuration not supported";
+    case KVQ_ERR_ALIGNMENT: return "KVQ_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: workspace too small or misaligned";
+    case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY: length exceeds the block table";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: kernel launch failed";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+kvq_status kvq_validate(const kvq_layout *layout, const kvq_cache *cache, int32_t batch,
+                        int32_t max_seq_len) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return KVQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)layout->max_blocks_per_seq * kBlock) return KVQ_ERR_CAPACITY;
+  return check_cache(layout, cache, batch);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
+                                  int32_t max_seq_len) {
+  if (check_layout(layout) != KVQ_OK || batch < 0 || max_seq_len < 0) return 0;
+  const Plan p = make_plan(layout, batch, max_seq_len);
+  return workspace_layout(layout, batch, p).total;
+}
+
+kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uint16_t *k_new,
+                     const uint16_t *v_new, const int32_t *cu_new,
+                     const int32_t *block_tables, const int32_t *seq_lens, int32_t batch,
+                     int32_t total_new, int32_t max_new_per_seq, void *stream) {
+  kvq_status st = kvq_validate(layout, cache, batch, 0);
+  if (st != KVQ_OK) return st;
+  if (total_new < 0 || max_new_per_seq < 0) return KVQ_ERR_INVALID_ARG;
+  if ((int64_t)max_new_per_seq > (int64_t)layout->max_blocks_per_seq * kBlock)
+    return KVQ_ERR_CAPACITY;
+  if (batch == 0 || total_new == 0 || max_new_per_seq == 0) return KVQ_OK;
+  if (!k_new || !v_new || !cu_new || !block_tables || !seq_lens) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cu_new) ||
+      !aligned16(block_tables) || !aligned16(seq_lens))
+    return KVQ_ERR_ALIGNMENT;
+
+  kvq::WriteArgs a{};
+  a.k_codes = static_cast<uint8_t *>(cache->k_codes);
+  a.v_codes = static_cast<uint8_t *>(cache->v_codes);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
+  a.k_resid = cache->k_resid;
+  a.v_resid = cache->v_resid;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_new = cu_new;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.max_blocks_per_seq = layout->max_blocks_per_seq;
+  a.k_gran = layout->k_gran;
+  a.v_gran = layout->v_gran;
+  a.residual = layout->residual_len;
+  a.ring = layout->residual_len + kGroup;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e;
+  if (layout->dtype == KVQ_INT4) {
+    // groups leaving the window: at most ceil(n/64) + 1 per row
+    const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup + 1;
+    e = kvq::launch_write_int4(a, batch, max_new_per_seq, max_groups, s);
+  } else {
+    e = kvq::launch_write_q8(a, layout->dtype, batch, max_new_per_seq, s);
+  }
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
+                            const uint16_t *q, const int32_t *block_tables,
+                            const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                            float softmax_scale, float *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  kvq_status st = kvq_validate(layout, cache, batch, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !block_tables || !seq_lens || !out) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(block_tables) || !aligned16(seq_lens) || !aligned16(out))
+    return KVQ_ERR_ALIGNMENT;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return KVQ_ERR_INVALID_ARG;
+  const Plan p = make_plan(layout, batch, max_seq_len);
+  const WorkspaceLayout w = workspace_layout(layout, batch, p);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < w.total)
+    return KVQ_ERR_WORKSPACE;
+
+  char *ws = static_cast<char *>(workspace);
+  kvq::DecodeArgs a{};
+  a.k_codes = static_cast<const uint8_t *>(cache->k_codes);
+  a.v_codes = static_cast<const uint8_t *>(cache->v_codes);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
+  a.k_resid = cache->k_resid;
+  a.v_resid = cache->v_resid;
+  a.q = q;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.ws_cnt = reinterpret_cast<int32_t *>(ws + w.cnt_off);
+  a.ws_m = reinterpret_cast<float *>(ws + w.m_off);
+  a.ws_l = reinterpret_cast<float *>(ws + w.l_off);
+  a.ws_o = reinterpret_cast<float *>(ws + w.o_off);
+  a.num_q_heads = layout->num_q_heads;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.group = layout->num_q_heads / layout->num_kv_heads;
+  a.max_blocks_per_seq = layout->max_blocks_per_seq;
+  a.part_blocks = p.part_blocks;
+  a.num_parts = p.num_parts;
+  a.slots = p.slots;
+  a.residual = layout->residual_len;
+  a.ring = layout->residual_len + kGroup;
+  a.k_head_stride = layout->k_gran == KVQ_PER_HEAD ? 1 : 0;
+  a.v_head_stride = layout->v_gran == KVQ_PER_HEAD ? 1 : 0;
+  a.qk_scale = softmax_scale * 1.4426950408889634f;
+
+  (void)hipGetLastError();
+  const hipError_t e = kvq::launch_decode(a, layout->dtype, kvq::decode_scale_kind(layout->k_gran),
+                                          kvq::decode_scale_kind(layout->v_gran), batch,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Kernel argument blocks and launch entry points shared by the host API
+// (kvq_api.cpp) and the kernel files.  Internal to libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct WriteArgs {
+  uint8_t *k_codes;
+  uint8_t *v_codes;
+  float *k_scales;
+  float *v_scales;
+  uint16_t *k_resid;
+  uint16_t *v_resid;
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  const int32_t *cu_new;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t k_gran;        // kvq_granularity
+  int32_t v_gran;
+  int32_t ring;          // INT4: residual_len + group
+  int32_t residual;      // INT4: residual_len
+};
+
+struct DecodeArgs {
+  const uint8_t *k_codes;
+  const uint8_t *v_codes;
+  const float *k_scales;
+  const float *v_scales;
+  const uint16_t *k_resid;
+  const uint16_t *v_resid;
+  const uint16_t *q;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  float *out;
+  float *ws_o;      // [B][Hq][slots][128]
+  float *ws_m;      // [B][Hq][slots]
+  float *ws_l;      // [B][Hq][slots]
+  int32_t *ws_cnt;  // [B][H]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;            // Hq / H
+  int32_t max_blocks_per_seq;
+  int32_t part_blocks;      // blocks per main partition
+  int32_t num_parts;        // main partitions in the grid
+  int32_t slots;            // partial slots per (b, hq): num_parts (+1 INT4)
+  int32_t ring;             // INT4 ring slots
+  int32_t residual;         // INT4 residual length
+  int32_t k_head_stride;    // 0 for a per-tensor K scale, 1 per head
+  int32_t v_head_stride;
+  float qk_scale;           // softmax_scale * log2(e)
+};
+
+// Kernel-side scale kinds for the decode templates.
+int decode_scale_kind(int granularity);
+
+hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch,
+                           int max_new, hipStream_t stream);
+hipError_t launch_write_int4(const WriteArgs &a, int batch, int max_new,
+                             int max_flush_groups, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind,
+                         int v_kind, int batch, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,130 @@
+// Device-side helpers shared by the libkvq kernels (gfx950 only).
+//
+// Vector types for matrix-core operands, exact code -> fp16 conversions and
+// wavefront reductions.  Conversions are written so that every code becomes
+// the exact fp16 value of the integer (or E4M3 number) it encodes; scales are
+// never applied per element here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 16;
+constexpr int kGroup = 64;        // INT4 group (tokens for K, channels for V)
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3 };
+// Granularity as the decode kernel sees it: a scale that is uniform over a
+// (row, KV head) (per-tensor or per-head), per channel, or per token.
+enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
+
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) {
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) {
+  return __builtin_bit_cast(f16x2, v);
+}
+// Two fp32 -> packed fp16 pair, rounding toward zero (v_cvt_pkrtz_f16_f32).
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// --- INT8: 4 two's-complement codes in a dword -> 4 exact fp16 -------------
+// Bias each byte to code+128 (xor 0x80), splice it under the fp16 exponent of
+// 1024 (0x64 high byte: 1024 + u exactly) and subtract 1152.
+__device__ __forceinline__ f16x4 int8x4_to_f16(uint32_t x) {
+  const uint32_t u = x ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(f16)-1152.0f, (f16)-1152.0f};
+  const f16x2 a = as_f16x2(lo) + bias;
+  const f16x2 b = as_f16x2(hi) + bias;
+  return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// --- FP8 E4M3: 4 codes in a dword -> 4 exact fp16 (hardware OCP convert) ---
+__device__ __forceinline__ f16x4 fp8x4_to_f16(uint32_t x) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// --- INT4: 8 nibbles in a dword -> 4 fp16 pairs (nibble s, nibble s+4) ------
+// Bias each nibble to code+8 (xor 0x8), splice it under 1024 and subtract
+// 1032.  pair s holds nibbles s (low half) and s+4 (high half).
+__device__ __forceinline__ void int4x8_to_f16_pairs(uint32_t x, uint32_t out[4]) {
+  const uint32_t u = x ^ 0x88888888u;
+  const f16x2 bias = {(f16)-1032.0f, (f16)-1032.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t p = ((u >> (4 * s)) & 0x000F000Fu) | 0x64006400u;
+    out[s] = as_u32(as_f16x2(p) + bias);
+  }
+}
+
+__device__ __forceinline__ f16x8 pairs_to_f16x8(const uint32_t p[4]) {
+  const f16x2 a = as_f16x2(p[0]), b = as_f16x2(p[1]), c = as_f16x2(p[2]),
+              d = as_f16x2(p[3]);
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// --- cross-lane helpers (wave64) --------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+// max over the four lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float max_over_quads(float v) {
+  v = fmaxf(v, shfl_xor(v, 16));
+  v = fmaxf(v, shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_quads(float v) {
+  v += shfl_xor(v, 16);
+  v += shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// --- matrix cores -----------------------------------------------------------
+// D(16x16) += A(16x32) * B(32x16): lane l supplies row l%16 of A and column
+// l%16 of B for k-slots 8*(l/16) .. +7; D row 4*(l/16)+i, column l%16 is
+// element i of the result.
+__device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// D(16x16) += A(16x16) * B(16x16) with k-slots 4*(l/16) .. +3 per lane.
+__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global load (one dwordx4 per lane).
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ f32x4 ld16f(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+
+__device__ __forceinline__ int kivi_quantized_len(int s, int residual) {
+  const int n = s - residual;
+  return n > 0 ? (n / kGroup) * kGroup : 0;
+}
+
+}  // namespace kvq

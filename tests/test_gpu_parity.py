@@ -1,0 +1,101 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Codes and scales must match bit for bit; attention outputs within
+atol 2e-3 + rtol 1e-2 of the oracle's fp64 attention over the same
+dequantized values.  Sizes here span several blocks, partitions and a
+ragged tail; the full-size workloads are in test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+
+from quantized_paged_kv_02_amd import inputs
+from tests.gpu_harness import check_rows, run_case
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+def _small(dtype, kg, vg, hq=8, hkv=2, table="identity", **kw):
+    return inputs.scaled_down(W["tiny"], name=f"small-{dtype}-{kg}-{vg}-{hq}-{hkv}",
+                              batch=3, num_q_heads=hq, num_kv_heads=hkv, dtype=dtype,
+                              k_gran=kg, v_gran=vg, table=table, **kw)
+
+
+def test_tiny_workload_whole():
+    w = W["tiny"]
+    res = run_case(w, inputs.seq_lens(w), decode_twice=True)
+    err = check_rows(res)
+    assert np.array_equal(res.out, res.out2), "decode is not bitwise reproducible"
+    assert res.pools["ws_counters_zero"]
+    print(f"tiny: max abs err {err:.2e}")
+
+
+GRANS = ["tensor", "head", "channel", "token"]
+
+
+@pytest.mark.parametrize("dtype", ["int8", "fp8"])
+@pytest.mark.parametrize("kg", GRANS)
+@pytest.mark.parametrize("vg", GRANS)
+def test_granularities(dtype, kg, vg):
+    w = _small(dtype, kg, vg)
+    res = run_case(w, [1, 37, 300], split_tokens=64)
+    check_rows(res)
+    assert res.pools["ws_counters_zero"]
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1), (16, 2), (32, 2), (12, 3)])
+def test_group_sizes(hq, hkv):
+    w = _small("int8", "token", "token", hq=hq, hkv=hkv)
+    check_rows(run_case(w, [16, 33, 129], split_tokens=32))
+
+
+@pytest.mark.parametrize("split", [0, 16, 64, 256, 4096])
+def test_partition_sweep_fp8_shuffled(split):
+    w = _small("fp8", "head", "head", table="shuffled")
+    res = run_case(w, [15, 17, 700], split_tokens=split)
+    check_rows(res)
+
+
+def test_identity_vs_shuffled_tables_bitwise():
+    wi = _small("int8", "token", "token", table="identity")
+    ws = _small("int8", "token", "token", table="shuffled")
+    a = run_case(wi, [100, 257, 31], split_tokens=64)
+    b = run_case(ws, [100, 257, 31], split_tokens=64)
+    assert not np.array_equal(a.table, b.table)
+    assert np.array_equal(a.out, b.out)
+
+
+def test_empty_rows_and_single_token():
+    w = _small("int8", "token", "token")
+    res = run_case(w, [0, 1, 0])
+    assert np.all(res.out[0] == 0) and np.all(res.out[2] == 0)
+    check_rows(res, rows=[1])
+
+
+@pytest.mark.parametrize("lens,split", [([100, 192, 777], 64), ([1, 128, 129], 0),
+                                        ([191, 192, 193], 128), ([640, 64, 2000], 256)])
+def test_int4_kivi(lens, split):
+    w = _small("int4", "channel", "token", channel_outliers=(8, 10.0, "k"))
+    res = run_case(w, lens, split_tokens=split, decode_twice=True)
+    check_rows(res)
+    assert np.array_equal(res.out, res.out2)
+
+
+@pytest.mark.parametrize("chunks", [2, 3, 7])
+def test_int4_chunked_writes(chunks):
+    # groups flushed from a mix of ring tokens and new tokens, ring slots reused
+    w = _small("int4", "channel", "token", channel_outliers=(8, 10.0, "k"))
+    check_rows(run_case(w, [300, 1000, 450], chunks=chunks, split_tokens=64))
+
+
+def test_int4_residual_64_shuffled():
+    w = _small("int4", "channel", "token", residual_len=64, table="shuffled")
+    check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))
+
+
+@pytest.mark.parametrize("chunks", [2, 5])
+def test_int8_chunked_writes(chunks):
+    w = _small("int8", "token", "channel")
+    check_rows(run_case(w, [300, 1000, 17], chunks=chunks, split_tokens=128))
