@@ -1,0 +1,350 @@
+"""Decode-step benchmark of libkvq on one MI355X.
+
+One step = for every layer: quantize-on-write of each row's new token
+(kvq_write) and split-K paged decode attention over the whole cache
+(kvq_paged_decode).  The cache is prefilled once, untimed; every step
+rewrites the same position with the same token, so all steps do identical
+work.  The step is captured once into a HIP graph and replayed (``--eager``
+launches it from Python instead).
+
+Prints ONE JSON line: KV read GB/s of the step (algorithmic decode bytes /
+step time) as ``value``, decode tokens/s, the decode kernel's roofline
+figures (per-launch algorithmic bytes / its HIP-event-timed launch
+duration) and the CPU oracle's rate on a bounded sample of the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
+                    [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from quantized_paged_kv_02_amd import inputs, metrics  # noqa: E402
+
+METRIC = ("quantized paged-decode KV read GB/s (% of HBM peak) + decode tokens/s, 1 GPU")
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = "llama2-7b"
+DECODE_KERNEL = "kvq_paged_decode_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_paged_kv_02_amd", "csrc", f)
+                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of (layer, row) units
+# ---------------------------------------------------------------------------
+
+def _cpu_unit(args):
+    """Quantize one (layer, row) cache with the oracle (untimed), then time
+    the oracle's decode step for it: quantize the new token (INT4: the
+    64-token group that leaves the fp16 window), dequantize the row's cache
+    and run fp64 attention for all query heads.  Returns seconds."""
+    name, layer, row, seq = args
+    from threadpoolctl import threadpool_limits
+    import torch
+    torch.set_num_threads(1)
+    import oracle
+    w = inputs.WORKLOADS[name]
+    k, v = inputs.gen_kv(w, layer, row, seq, "cpu", 0)
+    k = k.numpy()
+    v = v.numpy()
+    q = inputs.gen_q(w, layer, "cpu", 0)[row].numpy().astype(np.float64)
+    scale = 1.0 / math.sqrt(inputs.HEAD_DIM)
+    with threadpool_limits(limits=1):
+        if w.dtype == "int4":
+            full = oracle.kivi_quantize(k, v, residual=w.residual_len)
+            nq_old = oracle.kivi_quantized_len(seq - 1, w.residual_len)
+            t0 = time.perf_counter()
+            for g0 in range(nq_old, full["nq"], 64):
+                for h in range(w.num_kv_heads):
+                    oracle.kivi_quantize_k_group(k[g0:g0 + 64, h])
+                    oracle.kivi_quantize_v_tokens(v[g0:g0 + 64, h])
+            k_hat, v_hat = oracle.kivi_dequantize(full)
+            oracle.decode_attention(q, k_hat, v_hat, scale)
+            return time.perf_counter() - t0
+        if w.k_gran == "token":
+            kc, ks = oracle.quantize_per_token(k, w.dtype)
+            vc, vs = oracle.quantize_per_token(v, w.dtype)
+            t0 = time.perf_counter()
+            oracle.quantize_per_token(k[seq - 1:], w.dtype)
+            oracle.quantize_per_token(v[seq - 1:], w.dtype)
+            k_hat = oracle.dequantize(kc, ks[..., None], w.dtype)
+            v_hat = oracle.dequantize(vc, vs[..., None], w.dtype)
+        else:
+            sk = inputs.calibrated_scales([torch.from_numpy(k[:seq - 1])], w.k_gran,
+                                          w.num_kv_heads)
+            sv = inputs.calibrated_scales([torch.from_numpy(v[:seq - 1])], w.v_gran,
+                                          w.num_kv_heads)
+            kc = oracle.quantize_static(k, sk, w.k_gran, w.dtype)
+            vc = oracle.quantize_static(v, sv, w.v_gran, w.dtype)
+            shp = (1, 1, 1) if w.k_gran == "tensor" else (1, -1, 1)
+            t0 = time.perf_counter()
+            oracle.quantize_static(k[seq - 1:], sk, w.k_gran, w.dtype)
+            oracle.quantize_static(v[seq - 1:], sv, w.v_gran, w.dtype)
+            k_hat = oracle.dequantize(kc, sk.reshape(shp), w.dtype)
+            v_hat = oracle.dequantize(vc, sv.reshape(shp), w.dtype)
+        oracle.decode_attention(q, k_hat, v_hat, scale)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, lens, workers: int, units_per_worker: int = 2):
+    """Time the oracle over a bounded sample of (layer, row) units on
+    ``workers`` host processes (one BLAS thread each)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    all_units = [(w.name, layer, row, int(lens[row]))
+                 for layer in range(w.layers) for row in range(w.batch)]
+    unit_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [int(max(lens))],
+                                      w.num_q_heads, w.num_kv_heads, w.residual_len)
+    if unit_bytes > (64 << 20):       # long rows: one unit per process keeps it bounded
+        units_per_worker = 1
+    n = min(len(all_units), workers * units_per_worker)
+    units = all_units[:n]
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        secs = list(ex.map(_cpu_unit, units))
+    sample_bytes = sum(metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [u[3]],
+                                            w.num_q_heads, w.num_kv_heads, w.residual_len)
+                       for u in units)
+    # units ran concurrently on `workers` processes
+    wall = sum(secs) / min(workers, n)
+    gbs = sample_bytes / wall / 1e9
+    step_s = sum(secs) / n * w.layers * w.batch / min(workers, n)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": min(workers, n), "kind": "oracle",
+            "tokens_per_s": round(w.batch / step_s, 4),
+            "sample": (f"{n} of {len(all_units)} (layer, row) units of {w.name}; each: "
+                       f"quantize the new token, dequantize the row's cache, fp64 attention "
+                       f"(numpy oracle, 1 BLAS thread per process, {min(workers, n)} processes); "
+                       f"{sum(secs):.1f} s of CPU work; K/V drawn on the CPU by the same "
+                       f"recipe")}
+
+
+# ---------------------------------------------------------------------------
+# GPU setup
+# ---------------------------------------------------------------------------
+
+class Bench:
+    def __init__(self, w: inputs.Workload, device="cuda"):
+        import torch
+        from quantized_paged_kv_02_amd import kvq
+        self.torch, self.kvq, self.w = torch, kvq, w
+        lens = inputs.seq_lens(w)
+        self.lens = lens
+        table, nb = inputs.block_tables(w, lens)
+        self.table = torch.as_tensor(table, device=device)
+        self.lens_t = torch.as_tensor(lens, device=device)
+        self.max_len = int(lens.max())
+        self.layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads,
+                                      w.num_kv_heads, nb, table.shape[1], 0, w.residual_len)
+        b = w.batch
+        self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)
+        self.caches, self.k_new, self.v_new, self.q, self.out = [], [], [], [], []
+        for layer in range(w.layers):
+            kk, vv = [], []
+            for r in range(b):
+                k, v = inputs.gen_kv(w, layer, r, int(lens[r]), device, 0)
+                kk.append(k)
+                vv.append(v)
+            pre_k = [k[:-1] for k in kk]
+            pre_v = [v[:-1] for v in vv]
+            k_static = v_static = None
+            if w.dtype != "int4" and w.k_gran in ("tensor", "head"):
+                k_static = inputs.calibrated_scales(pre_k, w.k_gran, w.num_kv_heads)
+            if w.dtype != "int4" and w.v_gran in ("tensor", "head"):
+                v_static = inputs.calibrated_scales(pre_v, w.v_gran, w.num_kv_heads)
+            cache = kvq.alloc_cache(self.layout, ring_rows=b, device=device,
+                                    k_static=k_static, v_static=v_static)
+            n = (lens - 1).astype(np.int32)
+            cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32),
+                                 device=device)
+            kvq.write(cache, torch.cat(pre_k).contiguous(), torch.cat(pre_v).contiguous(), cu,
+                      self.table, torch.as_tensor(n, device=device), int(n.max()))
+            self.caches.append(cache)
+            self.k_new.append(torch.cat([k[-1:] for k in kk]).contiguous())
+            self.v_new.append(torch.cat([v[-1:] for v in vv]).contiguous())
+            self.q.append(inputs.gen_q(w, layer, device, 0))
+            self.out.append(torch.empty((b, w.num_q_heads, 128), dtype=torch.float32,
+                                        device=device))
+            del kk, vv, pre_k, pre_v
+        self.ws = kvq.alloc_workspace(self.layout, b, self.max_len, device)
+        self.scale = 1.0 / math.sqrt(128)
+        torch.cuda.synchronize()
+
+    def step(self, events=None, write=True):
+        kvq = self.kvq
+        for layer in range(self.w.layers):
+            if write:
+                kvq.write(self.caches[layer], self.k_new[layer], self.v_new[layer],
+                          self.ones_cu, self.table, self.lens_t, 1)
+            if events is not None:
+                events[layer][0].record()
+            kvq.paged_decode(self.caches[layer], self.q[layer], self.table, self.lens_t,
+                             self.max_len, self.scale, self.out[layer], self.ws)
+            if events is not None:
+                events[layer][1].record()
+
+
+def run(args):
+    import torch
+    w = inputs.WORKLOADS[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched: the oracle runs in fresh worker processes
+        cpu = cpu_baseline(w, inputs.seq_lens(w), workers=args.cpu_workers)
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    bench = Bench(w)
+    b = w.batch
+    L = w.layers
+    layer_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, bench.lens,
+                                       w.num_q_heads, w.num_kv_heads, w.residual_len)
+    step_bytes = layer_bytes * L
+
+    # eager reference pass, then the graph
+    bench.step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in bench.out]
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            bench.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            bench.step()
+        torch.cuda.synchronize()
+
+    def one():
+        if graph is not None:
+            graph.replay()
+        else:
+            bench.step()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    for o, r in zip(bench.out, ref):
+        if not torch.equal(o, r):
+            raise SystemExit("replayed step output differs from the eager step")
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        one()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    # Decode-kernel launch durations: HIP event pairs around each decode
+    # launch on the stream it runs on.  A spin kernel keeps the stream busy
+    # while all launches and events are queued, so each pair brackets one
+    # kernel and no host launch latency.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(L)]
+    durs = []
+    for _ in range(max(1, args.kernel_samples)):
+        torch.cuda._sleep(int(2e7))
+        bench.step(events, write=False)
+        torch.cuda.synchronize()
+        durs += [e0.elapsed_time(e1) for e0, e1 in events]
+    kernel_timing = "HIP event pairs around each decode launch, queued behind a spin kernel"
+    kern_ms = float(np.mean(durs))
+    achieved = layer_bytes / (kern_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        ent = t.get(w.name)
+        if ent and t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = ent.get("bytes_per_launch")
+
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "tokens_per_s": round(b / (ms * 1e-3), 2),
+        "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "config": {
+            "workload": w.name, "description": w.description, "layers": L, "batch": b,
+            "seq_len": int(w.max_seq) if not isinstance(w.seq, tuple) else list(w.seq),
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "kv_dtype": w.dtype, "k_granularity": w.k_gran, "v_granularity": w.v_gran,
+            "block_tables": w.table, "step": "per layer: kvq_write of 1 token/row + "
+            "kvq_paged_decode", "launch": "hip graph" if graph is not None else "eager",
+            "algorithmic_bytes_per_step": step_bytes,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": DECODE_KERNEL, "bytes_per_launch": layer_bytes,
+            "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs),
+            "timing": kernel_timing,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--eager", action="store_true", help="launch from Python, no HIP graph")
+    ap.add_argument("--kernel-samples", type=int, default=10,
+                    help="extra synchronised replays for the per-launch timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
+              "path has no multi-GPU mode in this library", file=sys.stderr)
+        raise SystemExit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        raise SystemExit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

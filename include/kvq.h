@@ -159,11 +159,10 @@ kvq_status kvq_validate(const kvq_layout *layout, const kvq_cache *cache,
                         int32_t batch, int32_t max_seq_len);
 
 /* Bytes of decode workspace for (layout, batch, max_seq_len); 0 if the
- * layout is invalid.  The workspace holds split-K partials (m, l, o per
- * partition and query head) and one int32 arrival counter per (b, KV head).
- * The counters must be zero before the first kvq_paged_decode call that
- * uses the buffer (e.g. zero-fill at allocation); every completed call
- * leaves them at zero again. */
+ * layout is invalid or if the launch needs none (a single partition per
+ * row).  The workspace holds the split-K partials (running max, softmax sum
+ * and unnormalised output per partition and query head); its contents need
+ * no initialisation and are dead after the call. */
 size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
                                   int32_t max_seq_len);
 
@@ -201,11 +200,13 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
  *   q        : fp16 [batch][Hq][128]
  *   out      : fp32 [batch][Hq][128]; rows with seq_lens[b] == 0 get zeros.
  *   workspace: device buffer of at least kvq_decode_workspace_bytes(layout,
- *              batch, max_seq_len) bytes, 256-byte aligned.  Calls that
- *              share a workspace must not overlap in time.
- * One kernel launch: split-K over token partitions; the last partition of
- * each (row, KV head) to finish merges the partials (log-sum-exp) in a
- * fixed order, so results are bitwise reproducible. */
+ *              batch, max_seq_len) bytes, 256-byte aligned (may be NULL when
+ *              that size is 0).  Calls that share a workspace must not
+ *              overlap in time (on one stream they never do).
+ * Split-K: one launch computes partials per token partition (four
+ * wavefronts per partition, merged in LDS), a second launch merges the
+ * partitions of each (row, query head) by log-sum-exp in a fixed order, so
+ * results are bitwise reproducible. */
 kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
                             const uint16_t *q, const int32_t *block_tables,
                             const int32_t *seq_lens, int32_t batch,

@@ -13,9 +13,9 @@ namespace {
 constexpr int kBlock = 16;
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 64;
-// Aim for this many partition wavefronts per decode launch when the layout
-// does not fix the partition length (256 CUs x 8 resident wavefronts).
-constexpr long kTargetWaves = 2048;
+// Aim for this many partition workgroups (four wavefronts each) per decode
+// launch when the layout does not fix the partition length: 256 CUs x 4.
+constexpr long kTargetWorkgroups = 1024;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -74,17 +74,19 @@ Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
   const bool int4 = L->dtype == KVQ_INT4;
   const int blocks = int4 ? kivi_len(max_seq_len, L->residual_len) / kBlock
                           : (max_seq_len + kBlock - 1) / kBlock;
-  const int unit = int4 ? 4 : 1;  // INT4 partitions hold whole groups
+  // a workgroup's four waves take units of 2 blocks (INT8/FP8) or one
+  // 64-token group (INT4) in turn; automatic partitions give each wave
+  // whole units
+  const int quantum = int4 ? 16 : 8;
   int pb;
   if (L->split_tokens > 0) {
     pb = L->split_tokens / kBlock;
   } else {
     const long units = (long)batch * L->num_kv_heads;
-    long want = (units * blocks + kTargetWaves - 1) / kTargetWaves;
-    if (want < 8) want = 8;
-    pb = (int)((want + unit - 1) / unit * unit);
+    const long want = (units * blocks + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    pb = (int)((want + quantum - 1) / quantum * quantum);
+    if (pb < quantum) pb = quantum;
   }
-  if (pb < unit) pb = unit;
   p.part_blocks = pb;
   p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 0;
   if (!int4 && p.num_parts == 0) p.num_parts = 1;  // rows of length 0 still write zeros
@@ -95,14 +97,16 @@ Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t cnt_off, m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, total;
 };
 
+// Partials of every (row, query head, partition slot); none when the plan
+// has a single slot (the decode kernel then writes the output directly).
 WorkspaceLayout workspace_layout(const kvq_layout *L, int32_t batch, const Plan &p) {
   WorkspaceLayout w{};
+  if (p.slots <= 1) return w;
   const size_t rows = (size_t)batch * L->num_q_heads * p.slots;
-  w.cnt_off = 0;
-  w.m_off = round_up((size_t)batch * L->num_kv_heads * sizeof(int32_t), 256);
+  w.m_off = 0;
   w.l_off = w.m_off + round_up(rows * sizeof(float), 256);
   w.o_off = w.l_off + round_up(rows * sizeof(float), 256);
   w.total = w.o_off + round_up(rows * kHeadDim * sizeof(float), 256);
@@ -204,8 +208,8 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
     return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(layout, batch, max_seq_len);
   const WorkspaceLayout w = workspace_layout(layout, batch, p);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < w.total)
+  if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+                      workspace_bytes < w.total))
     return KVQ_ERR_WORKSPACE;
 
   char *ws = static_cast<char *>(workspace);
@@ -220,10 +224,10 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.ws_cnt = reinterpret_cast<int32_t *>(ws + w.cnt_off);
   a.ws_m = reinterpret_cast<float *>(ws + w.m_off);
   a.ws_l = reinterpret_cast<float *>(ws + w.l_off);
   a.ws_o = reinterpret_cast<float *>(ws + w.o_off);
+  a.batch = batch;
   a.num_q_heads = layout->num_q_heads;
   a.num_kv_heads = layout->num_kv_heads;
   a.group = layout->num_q_heads / layout->num_kv_heads;

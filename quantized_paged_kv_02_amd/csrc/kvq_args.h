@@ -39,17 +39,18 @@ struct DecodeArgs {
   const int32_t *block_tables;
   const int32_t *seq_lens;
   float *out;
-  float *ws_o;      // [B][Hq][slots][128]
-  float *ws_m;      // [B][Hq][slots]
-  float *ws_l;      // [B][Hq][slots]
-  int32_t *ws_cnt;  // [B][H]
+  float *ws_o;      // [B][Hq][slots][128] unnormalised partial outputs
+  float *ws_m;      // [B][Hq][slots] partial running max (log2 domain)
+  float *ws_l;      // [B][Hq][slots] partial softmax sums
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;            // Hq / H
   int32_t max_blocks_per_seq;
   int32_t part_blocks;      // blocks per main partition
   int32_t num_parts;        // main partitions in the grid
-  int32_t slots;            // partial slots per (b, hq): num_parts (+1 INT4)
+  int32_t slots;            // partial slots per (b, hq): num_parts (+1 INT4);
+                            // 1 = the decode kernel writes out directly
   int32_t ring;             // INT4 ring slots
   int32_t residual;         // INT4 residual length
   int32_t k_head_stride;    // 0 for a per-tensor K scale, 1 per head

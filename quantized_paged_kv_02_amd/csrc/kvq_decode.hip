@@ -10,44 +10,73 @@
 // Quantization 生产实战", section "为什么长上下文更需要 KV Cache Quantization":
 // each decode step streams the whole history, so the kernel is bound by HBM).
 //
-// Work decomposition: one wavefront (workgroup of 64) per (partition p, KV
-// head h, row b).  A partition is `part_blocks` consecutive 16-token blocks
-// (INT4: whole 64-token groups); INT4 adds one partition for the fp16
-// residual ring.  Each wavefront keeps an online softmax (running max m in
-// the log2 domain, running sum l, unnormalised output o) for the g query
-// heads that share h, writes it as a partial, and the last partition of
-// (b, h) to arrive merges all partials in partition order (log-sum-exp) and
-// writes out.  Rows with a single partition write out directly.
+// Work decomposition.  A workgroup of four wavefronts handles one partition
+// p of one (row b, KV head h): `part_blocks` consecutive 16-token blocks
+// (INT4: whole 64-token groups).  INT4 adds one workgroup per (b, h) for the
+// fp16 residual ring.  The workgroup stages the partition's physical block
+// ids in LDS; wave w takes units w, w+4, w+8, ... (a unit is a pair of
+// blocks for INT8/FP8, a 64-token group for INT4) and keeps an online
+// softmax (running max m in the log2 domain, running sum l, unnormalised
+// output o) for the g query heads that share h.  The four wave states are
+// merged in LDS; the result is the final output when the launch has a
+// single partition per row, else one partial (m, l, o) per (b, hq, p) that
+// kvq_partition_reduce merges (log-sum-exp, fixed order) in a second
+// launch.  Stream order is the only synchronisation between the two: no
+// atomics, no cross-workgroup fences.
+//
+// Pipelining: unit loads are issued unconditionally one unit ahead of the
+// compute (the loop is unrolled by two and the last unit is peeled), so the
+// compiler waits only for the unit about to be used while the next one is
+// in flight.
 //
 // Matrix cores: scores S^T[token][head] = K[token][:] . Q^T[:][head] use
-// v_mfma_f32_16x16x32_f16 (16 tokens x 16 head slots, g of them live); the
-// value product O^T[channel][head] = V^T[channel][token] . P^T[token][head]
-// uses v_mfma_f32_16x16x16_f16.  Both leave lane (head n = l%16, quad
-// qd = l/16) owning tokens 4qd..4qd+3 of head n (scores) and channels
-// 16j+4qd..+3 of head n (output), so softmax state, rescaling and the V-scale
-// folding are lane-local.  The cache layout (kvq.h) gives every lane its
-// operand bytes as one 16-byte run, loaded straight into registers.
+// v_mfma_f32_16x16x32_f16 per 16-token block (16 head slots, g of them
+// live).  The value product O^T[channel][head] = V^T[channel][token] .
+// P^T[token][head] uses v_mfma_f32_16x16x32_f16 over a pair of blocks: lane
+// (n = l%16, qd = l/16) holds scores of tokens 4qd..4qd+3 of both blocks,
+// which are exactly its eight k-slots of P^T, and the cache layout gives it
+// the matching eight V codes of channel 16j + n.  Output lane layout: o[j]
+// element i is channel 16j + 4qd + i of head n.
 //
 // Scales are factored out of the contraction: per-token K scales multiply
-// the 16 scores, uniform K scales fold into one multiplier, per-channel K
+// the scores, uniform K scales fold into one multiplier, per-channel K
 // scales (and INT4 group scales) fold into q, kept exact as an fp16 hi/lo
 // pair; per-token V scales fold into p, uniform and per-channel V scales are
-// applied to o once per partition.
+// applied to o once per wave.
 #include "kvq_args.h"
 #include "kvq_device.h"
 
 namespace kvq {
 namespace {
 
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kIdChunk = 256;  // block ids staged in LDS per pass
 constexpr float kNegInf = -__builtin_inff();
 // The running max is only moved when a score exceeds it by more than this
 // (log2 units), so p <= 2^8 and rescaling of o is rare.
 constexpr float kRescaleSlack = 8.0f;
 
 struct Softmax {
-  float m;       // running max (log2 domain), same on the 4 lanes of a head
-  float l;       // this lane's share of the running sum
-  f32x4 o[8];    // o^T rows 16j + 4qd + i for head n
+  float m;     // running max (log2 domain), same on the 4 lanes of a head
+  float l;     // this lane's share of the running sum
+  f32x4 o[8];  // o^T rows 16j + 4qd + i for head n
+};
+
+// Workgroup LDS: block ids and per-wave INT4 scale staging while streaming,
+// then the four wave states for the merge.
+struct StreamLds {
+  int ids[kIdChunk];
+  float scl[kWaves][256];  // INT4: K scales [128 channels], V scales [64 tok][2]
+};
+struct MergeLds {
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float o[kWaves][16][kHeadDim];
+};
+union SharedLds {
+  StreamLds s;
+  MergeLds g;
 };
 
 __device__ __forceinline__ void softmax_init(Softmax &st) {
@@ -57,10 +86,12 @@ __device__ __forceinline__ void softmax_init(Softmax &st) {
   for (int j = 0; j < 8; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Fold one tile of 16 scores (4 per lane, log2 domain, masked = -inf) into
-// the running state; returns p (relative to the updated max).
-__device__ __forceinline__ f32x4 softmax_update(Softmax &st, f32x4 sc) {
-  float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+// Fold the scores of two blocks (4 tokens each per lane, log2 domain,
+// masked = -inf) into the running state; returns p relative to the new max.
+__device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, const f32x4 &s1,
+                                               f32x4 &p0, f32x4 &p1) {
+  float bm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
   bm = max_over_quads(bm);
   const bool need = bm > st.m + kRescaleSlack;
   if (__any(need)) {
@@ -71,37 +102,27 @@ __device__ __forceinline__ f32x4 softmax_update(Softmax &st, f32x4 sc) {
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
     st.m = mn;
   }
-  f32x4 p;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - st.m);
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  return p;
+  for (int r = 0; r < 4; ++r) {
+    p0[r] = __builtin_amdgcn_exp2f(s0[r] - st.m);
+    p1[r] = __builtin_amdgcn_exp2f(s1[r] - st.m);
+  }
+  st.l += ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
 }
 
-__device__ __forceinline__ f16x4 to_f16x4(f32x4 v) {
-  const f16x2 a = as_f16x2(pack_rtz(v[0], v[1]));
-  const f16x2 b = as_f16x2(pack_rtz(v[2], v[3]));
-  return f16x4{a.x, a.y, b.x, b.y};
+// P^T operand of the value product: tokens 4qd..4qd+3 of block 0, then of
+// block 1, rounded to nearest even fp16 (no bias against the fp32 sum).
+__device__ __forceinline__ f16x8 p_operand(const f32x4 &p0, const f32x4 &p1) {
+  return f16x8{(f16)p0[0], (f16)p0[1], (f16)p0[2], (f16)p0[3],
+               (f16)p1[0], (f16)p1[1], (f16)p1[2], (f16)p1[3]};
 }
 
-// Split fp32 x into hi + lo fp16 parts (hi rounded toward zero, lo the
-// rounded remainder): |x - hi - lo| <= 2^-22 |x|.
-__device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi,
-                                            uint32_t &lo) {
-  hi = pack_rtz(x0, x1);
-  const f16x2 h = as_f16x2(hi);
-  const float r0 = x0 - (float)h.x;
-  const float r1 = x1 - (float)h.y;
-  lo = pack_rtz(r0, r1);
+__device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-__device__ __forceinline__ f16x8 u4_to_f16x8(u32x4 v) {
-  return __builtin_bit_cast(f16x8, v);
-}
-
-__device__ __forceinline__ f16x4 u2_to_f16x4(u32x2 v) {
-  return __builtin_bit_cast(f16x4, v);
-}
+__device__ __forceinline__ f16x8 u4_to_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f16x4 u2_to_f16x4(u32x2 v) { return __builtin_bit_cast(f16x4, v); }
 
 template <int DT>
 __device__ __forceinline__ f16x4 codes4_to_f16(uint32_t w) {
@@ -117,309 +138,145 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int n) {
   return n >= 4 ? w : (n <= 0 ? 0u : (w & ((1u << (8 * n)) - 1u)));
 }
 
-// Physical block ids of a partition, read 64 at a time into one vector
-// register and handed out with readlane (uniform index), so the tile loads
-// never wait on a dependent block-table load.
-struct BlockIds {
-  const int32_t *bt;
-  int end, base, vec;
-  // requires begin < stop; lanes past the end re-read the last entry
-  __device__ BlockIds(const int32_t *table, int begin, int stop, int lane)
-      : bt(table), end(stop), base(begin) {
-    vec = table[min(begin + lane, stop - 1)];
+// q' = x rounded toward zero to fp16 (hi) plus the fp16 remainder (lo):
+// |x - hi - lo| <= 2^-22 |x|.
+__device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_rtz(x0, x1);
+  const f16x2 hh = as_f16x2(hi);
+  lo = pack_rtz(x0 - (float)hh.x, x1 - (float)hh.y);
+}
+
+// Stage physical block ids [c0, c1) of a row in LDS (whole workgroup).
+__device__ __forceinline__ void stage_ids(SharedLds &sh, const int32_t *bt, int c0, int c1,
+                                          int tid) {
+  __syncthreads();
+  for (int i = tid; i < c1 - c0; i += kThreads) sh.s.ids[i] = bt[c0 + i];
+  __syncthreads();
+}
+
+// Run `cnt` units through a one-ahead software pipeline.  load(T&, k)
+// issues unit k's loads, compute(T&, k) consumes them.
+template <typename T, typename Load, typename Compute>
+__device__ __forceinline__ void pipeline(int cnt, Load &&load, Compute &&compute) {
+  if (cnt <= 0) return;
+  T a, b;
+  load(a, 0);
+  int k = 0;
+  for (; k + 2 < cnt; k += 2) {
+    load(b, k + 1);
+    compute(a, k);
+    load(a, k + 2);
+    compute(b, k + 1);
   }
-  __device__ __forceinline__ int get(int jb, int lane) {
-    if (jb - base >= 64) {
-      base = jb;
-      vec = bt[min(base + lane, end - 1)];
-    }
-    return __builtin_amdgcn_readlane(vec, jb - base);
+  if (k + 1 < cnt) {
+    load(b, k + 1);
+    compute(a, k);
+    compute(b, k + 1);
+  } else {
+    compute(a, k);
   }
-};
+}
 
 // ---------------------------------------------------------------------------
-// INT8 / FP8 block tile
+// INT8 / FP8: a unit is a pair of 16-token blocks
 // ---------------------------------------------------------------------------
-struct Tile8 {
-  u32x4 k0, k1;   // K bytes: channels 32qd+0..15 / +16..31 of token l%16
-  u32x4 v0, v1;   // V bytes: 4 tokens x channels 16j + l%16, j = 0..3 / 4..7
-  f32x4 ks, vs;   // per-token scales of tokens 4qd..4qd+3
+struct Pair8 {
+  u32x4 k[2][2];  // block u: K bytes of channels 32qd+0..15 / +16..31, token l%16
+  u32x4 v[2][2];  // block u: V bytes, 4 tokens x channels 16j + l%16 (j 0..3 / 4..7)
+  f32x4 ks[2];    // per-token K scales of tokens 4qd..4qd+3
+  f32x4 vs[2];
 };
 
 template <int KS, int VS>
-__device__ __forceinline__ void load_tile8(Tile8 &t, const DecodeArgs &a, int phys,
+__device__ __forceinline__ void load_pair8(Pair8 &t, const DecodeArgs &a, int ph0, int ph1,
                                            int h, int lane, int qd) {
-  const size_t chunk = (size_t)phys * a.num_kv_heads + h;
-  const uint8_t *kc = a.k_codes + chunk * 2048 + 16 * lane;
-  const uint8_t *vc = a.v_codes + chunk * 2048 + 16 * lane;
-  t.k0 = ld16(kc);
-  t.k1 = ld16(kc + 1024);
-  t.v0 = ld16(vc);
-  t.v1 = ld16(vc + 1024);
-  if constexpr (KS == kToken) t.ks = ld16f(a.k_scales + chunk * kBlock + 4 * qd);
-  if constexpr (VS == kToken) t.vs = ld16f(a.v_scales + chunk * kBlock + 4 * qd);
+  const int ph[2] = {ph0, ph1};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const size_t chunk = (size_t)ph[u] * a.num_kv_heads + h;
+    const uint8_t *kc = a.k_codes + chunk * 2048 + 16 * lane;
+    const uint8_t *vc = a.v_codes + chunk * 2048 + 16 * lane;
+    t.k[u][0] = ld16(kc);
+    t.k[u][1] = ld16(kc + 1024);
+    t.v[u][0] = ld16(vc);
+    t.v[u][1] = ld16(vc + 1024);
+    if constexpr (KS == kToken) t.ks[u] = ld16f(a.k_scales + chunk * kBlock + 4 * qd);
+    if constexpr (VS == kToken) t.vs[u] = ld16f(a.v_scales + chunk * kBlock + 4 * qd);
+  }
 }
 
-template <int DT, int KS, int VS, bool TAIL>
-__device__ __forceinline__ void compute_tile8(Softmax &st, const Tile8 &t,
-                                              const f16x8 (&bq)[4],
-                                              const f16x8 (&bq_lo)[4], float kmul,
-                                              int tok0, int seq_len, int qd) {
-  // scores: MFMA j covers channels 32qd + 8j .. +7 (j = 2i + jj uses dwords
-  // 2jj, 2jj+1 of load i)
+// Scores of one block: 4 x v_mfma_f32_16x16x32_f16 over channels 32qd+8j..+7.
+template <int DT, int KS>
+__device__ __forceinline__ f32x4 block_scores8(const u32x4 (&k)[2], const f16x8 (&bq)[4],
+                                               const f16x8 (&bq_lo)[4]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const u32x4 &src = (j < 2) ? t.k0 : t.k1;
+    const u32x4 &src = k[j >> 1];
     const int jj = j & 1;
-    const f16x4 a0 = codes4_to_f16<DT>(src[2 * jj]);
-    const f16x4 a1 = codes4_to_f16<DT>(src[2 * jj + 1]);
-    const f16x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const f16x8 av = cat(codes4_to_f16<DT>(src[2 * jj]), codes4_to_f16<DT>(src[2 * jj + 1]));
     s = mfma32(av, bq[j], s);
     if constexpr (KS == kChannel) s = mfma32(av, bq_lo[j], s);
   }
-  f32x4 sc;
+  return s;
+}
+
+// valid: tokens of the pair that are attended (TAIL only), 1..32.
+template <int DT, int KS, int VS, bool TAIL>
+__device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8 (&bq)[4],
+                                              const f16x8 (&bq_lo)[4], float kmul, int valid,
+                                              int qd) {
+  f32x4 s[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float v = s[r];
-    if constexpr (KS == kToken) v *= t.ks[r] * kmul;
-    else if constexpr (KS == kUniform) v *= kmul;
-    if (TAIL && tok0 + 4 * qd + r >= seq_len) v = kNegInf;
-    sc[r] = v;
+  for (int u = 0; u < 2; ++u) {
+    s[u] = block_scores8<DT, KS>(t.k[u], bq, bq_lo);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = s[u][r];
+      if constexpr (KS == kToken) v *= t.ks[u][r] * kmul;
+      else v *= kmul;
+      if (TAIL && 16 * u + 4 * qd + r >= valid) v = kNegInf;
+      s[u][r] = v;
+    }
   }
-  f32x4 p = softmax_update(st, sc);
+  f32x4 p0, p1;
+  softmax_update(st, s[0], s[1], p0, p1);
   if constexpr (VS == kToken) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] *= t.vs[r];
-      if (TAIL && tok0 + 4 * qd + r >= seq_len) p[r] = 0.0f;
+      p0[r] *= t.vs[0][r];
+      p1[r] *= t.vs[1][r];
+      if (TAIL && 4 * qd + r >= valid) p0[r] = 0.0f;
+      if (TAIL && 16 + 4 * qd + r >= valid) p1[r] = 0.0f;
     }
   }
-  const f16x4 pb = to_f16x4(p);
-  int valid = 4;
-  if (TAIL) valid = seq_len - (tok0 + 4 * qd);
+  const f16x8 pb = p_operand(p0, p1);
+  if (TAIL) {
+    // zero the codes of unattended tokens (their bytes may be stale or NaN)
+    const int v0 = valid - 4 * qd, v1 = valid - 16 - 4 * qd;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t w = (j < 4) ? t.v0[j] : t.v1[j - 4];
-    if (TAIL) w = keep_bytes(w, valid);
-    st.o[j] = mfma16(codes4_to_f16<DT>(w), pb, st.o[j]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// INT4 group tile (4 blocks = 64 tokens)
-// ---------------------------------------------------------------------------
-struct Tile4 {
-  u32x4 k[4];      // per block: channels 32qd..32qd+31 of token l%16 (nibbles)
-  u32x4 v[4];      // per block: 4 tokens x 8 channels (nibbles)
-  f32x4 vs[4][2];  // per block: V scales of tokens 4qd..4qd+3, both groups
-  f32x4 ks[8];     // K scales of channels 32qd .. 32qd+31 for the group
-};
-
-__device__ __forceinline__ void load_tile4(Tile4 &t, const DecodeArgs &a,
-                                           const int (&phys)[4], int h, int lane,
-                                           int qd) {
-  const int H = a.num_kv_heads;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const size_t chunk = (size_t)phys[u] * H + h;
-    t.k[u] = ld16(a.k_codes + chunk * 1024 + 16 * lane);
-    t.v[u] = ld16(a.v_codes + chunk * 1024 + 16 * lane);
-    const float *vsp = a.v_scales + (chunk * kBlock + 4 * qd) * 2;
-    t.vs[u][0] = ld16f(vsp);
-    t.vs[u][1] = ld16f(vsp + 4);
-  }
-  // block u of the group holds the scales of channels 32u..32u+31
-  const int pq = qd == 0 ? phys[0] : qd == 1 ? phys[1] : qd == 2 ? phys[2] : phys[3];
-  const float *ksp = a.k_scales + ((size_t)pq * H + h) * 32;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) t.ks[m] = ld16f(ksp + 4 * m);
-}
-
-// k-slot order produced by int4x8_to_f16_pairs: (0,4,1,5,2,6,3,7)
-__device__ __forceinline__ int int4_kslot(int e) { return (e >> 1) + 4 * (e & 1); }
-
-__device__ __forceinline__ void compute_tile4(Softmax &st, const Tile4 &t,
-                                              const float (&qf)[32], int qd) {
-  // q' = q * scale_c * qk_scale for this lane's 32 channels, as hi/lo fp16
-  f16x8 bhi[4], blo[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const int k0 = int4_kslot(2 * e2), k1 = int4_kslot(2 * e2 + 1);
-      const int c0 = 8 * j + k0, c1 = 8 * j + k1;
-      const float x0 = qf[c0] * t.ks[c0 >> 2][c0 & 3];
-      const float x1 = qf[c1] * t.ks[c1 >> 2][c1 & 3];
-      split_hi_lo(x0, x1, hi[e2], lo[e2]);
-    }
-    bhi[j] = pairs_to_f16x8(hi);
-    blo[j] = pairs_to_f16x8(lo);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t pr[4];
-      int4x8_to_f16_pairs(t.k[u][j], pr);
-      const f16x8 av = pairs_to_f16x8(pr);
-      s = mfma32(av, bhi[j], s);
-      s = mfma32(av, blo[j], s);
-    }
-    const f32x4 p = softmax_update(st, s);
-    f32x4 p0, p1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p0[r] = p[r] * t.vs[u][r >> 1][2 * (r & 1)];
-      p1[r] = p[r] * t.vs[u][r >> 1][2 * (r & 1) + 1];
-    }
-    const f16x4 pb0 = to_f16x4(p0), pb1 = to_f16x4(p1);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t pr[4];
-      int4x8_to_f16_pairs(t.v[u][w], pr);
-      const f16x2 a0 = as_f16x2(pr[0]), a1 = as_f16x2(pr[1]);
-      const f16x2 b0 = as_f16x2(pr[2]), b1 = as_f16x2(pr[3]);
-      const f16x4 va = {a0.x, a0.y, a1.x, a1.y};
-      const f16x4 vb = {b0.x, b0.y, b1.x, b1.y};
-      const f16x4 &pb = (w < 2) ? pb0 : pb1;
-      st.o[2 * w] = mfma16(va, pb, st.o[2 * w]);
-      st.o[2 * w + 1] = mfma16(vb, pb, st.o[2 * w + 1]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// fp16 residual ring tile (INT4 caches)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void compute_ring_tile(Softmax &st, const DecodeArgs &a,
-                                                  const uint16_t *kr, const uint16_t *vr,
-                                                  const f16x8 (&bq)[4], int slot0,
-                                                  int tok0, int seq_len, int n, int qd) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4 kv = ld16(kr + (size_t)(slot0 + n) * kHeadDim + 32 * qd + 8 * j);
-    s = mfma32(u4_to_f16x8(kv), bq[j], s);
-  }
-  const int valid = seq_len - (tok0 + 4 * qd);
-  f32x4 sc;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sc[r] = r < valid ? s[r] * a.qk_scale : kNegInf;
-  f32x4 p = softmax_update(st, sc);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = r < valid ? p[r] : 0.0f;
-  const f16x4 pb = to_f16x4(p);
-  const uint16_t *vq = vr + ((size_t)(slot0 / 4 + qd) * kHeadDim + n) * 4;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x2 w = *reinterpret_cast<const u32x2 *>(vq + 16 * j * 4);
-    if (valid < 4) {
-      // zero the halves of tokens past the end (the ring may hold stale data)
-      if (valid <= 0) w = u32x2{0u, 0u};
-      else if (valid == 1) w = u32x2{w[0] & 0xFFFFu, 0u};
-      else if (valid == 2) w = u32x2{w[0], 0u};
-      else w = u32x2{w[0], w[1] & 0xFFFFu};
-    }
-    st.o[j] = mfma16(u2_to_f16x4(w), pb, st.o[j]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// epilogue: partial write + last-arrival merge
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_out(float *dst, const f32x4 (&o)[8], float inv,
-                                          int qd) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    *reinterpret_cast<f32x4 *>(dst + 16 * j + 4 * qd) = o[j] * inv;
-  }
-}
-
-__device__ void finish(const DecodeArgs &a, Softmax &st, int b, int h, int p,
-                       int n_main, bool has_ring, int lane) {
-  const int n = lane & 15, qd = lane >> 4;
-  const bool live = n < a.group;
-  const int hq = h * a.group + n;
-  const float lsum = sum_over_quads(st.l);
-  const int total = n_main + (has_ring ? 1 : 0);
-  float *out = a.out + ((size_t)b * a.num_q_heads + hq) * kHeadDim;
-  if (total == 1) {
-    if (live) store_out(out, st.o, 1.0f / lsum, qd);
-    return;
-  }
-  const size_t row = (size_t)b * a.num_q_heads + hq;
-  if (live) {
-    const size_t idx = row * a.slots + p;
-    store_out(a.ws_o + idx * kHeadDim, st.o, 1.0f, qd);
-    if (qd == 0) {
-      a.ws_m[idx] = st.m;
-      a.ws_l[idx] = lsum;
-    }
-  }
-  __threadfence();
-  int prev = 0;
-  if (lane == 0) {
-    prev = __hip_atomic_fetch_add(a.ws_cnt + (size_t)b * a.num_kv_heads + h, 1,
-                                  __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  prev = __shfl(prev, 0, 64);
-  if (prev != total - 1) return;
-  __threadfence();
-  if (live) {
-    const size_t base = row * a.slots;
-    float big = kNegInf;
-    for (int pp = 0; pp < total; ++pp) {
-      const int slot = pp < n_main ? pp : a.num_parts;
-      big = fmaxf(big, a.ws_m[base + slot]);
-    }
-    float lt = 0.0f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int pp = 0; pp < total; ++pp) {
-      const int slot = pp < n_main ? pp : a.num_parts;
-      const float w = __builtin_amdgcn_exp2f(a.ws_m[base + slot] - big);
-      lt += w * a.ws_l[base + slot];
-      const float *src = a.ws_o + (base + slot) * kHeadDim;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[j] += w * *reinterpret_cast<const f32x4 *>(src + 16 * j + 4 * qd);
+      for (int w = 0; w < 4; ++w) {
+        t.v[0][i][w] = keep_bytes(t.v[0][i][w], v0);
+        t.v[1][i][w] = keep_bytes(t.v[1][i][w], v1);
       }
-    }
-    store_out(out, acc, 1.0f / lt, qd);
   }
-  if (lane == 0) {
-    __hip_atomic_store(a.ws_cnt + (size_t)b * a.num_kv_heads + h, 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f16x8 av = cat(codes4_to_f16<DT>(t.v[0][j >> 2][j & 3]),
+                         codes4_to_f16<DT>(t.v[1][j >> 2][j & 3]));
+    st.o[j] = mfma32(av, pb, st.o[j]);
   }
 }
 
-// per-channel / uniform V scale applied to o before it leaves the wavefront
-template <int VS>
-__device__ __forceinline__ void apply_v_scale(Softmax &st, const DecodeArgs &a, int h,
-                                              int qd) {
-  if constexpr (VS == kUniform) {
-    const float s = a.v_scales[h * a.v_head_stride];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] *= s;
-  } else if constexpr (VS == kChannel) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const f32x4 s = ld16f(a.v_scales + h * kHeadDim + 16 * j + 4 * qd);
-      st.o[j] *= s;
-    }
-  }
-}
-
-// Load this lane's 32 query channels 32qd .. 32qd+31 (as 4 x 8 fp16).
-__device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int b, int h,
-                                       int hq, bool live, int qd) {
-  // lanes past the group read the group's first head and discard it
-  const int hq_safe = live ? hq : h * a.group;
-  const uint16_t *qp = a.q + ((size_t)b * a.num_q_heads + hq_safe) * kHeadDim + 32 * qd;
+// Query operand of the score product for this lane's channels 32qd..32qd+31
+// (as 4 x 8 fp16), zero for the 16 - g padding columns.
+__device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int b, int h, int n,
+                                       int qd) {
+  const bool live = n < a.group;
+  const int hq = h * a.group + (live ? n : 0);
+  const uint16_t *qp = a.q + ((size_t)b * a.num_q_heads + hq) * kHeadDim + 32 * qd;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const u32x4 v = ld16(qp + 8 * j);
@@ -428,169 +285,436 @@ __device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int 
 }
 
 template <int DT, int KS, int VS>
-__global__ __launch_bounds__(64) void kvq_paged_decode_kernel(DecodeArgs a) {
+__device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h, int p,
+                          int seq_len, int wave, int lane, int tid) {
+  const int n = lane & 15, qd = lane >> 4;
+  u32x4 qr[4];
+  load_q(qr, a, b, h, n, qd);
+  f16x8 bq[4], bq_lo[4];
+  float kmul = a.qk_scale;
+  if constexpr (KS == kChannel) {
+    const float *ksc = a.k_scales + h * kHeadDim + 32 * qd;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 hv = u4_to_f16x8(qr[j]);
+      const f32x4 s0 = ld16f(ksc + 8 * j), s1 = ld16f(ksc + 8 * j + 4);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e = 2 * e2;
+        const float x0 = (float)hv[e] * a.qk_scale * (e < 4 ? s0[e] : s1[e - 4]);
+        const float x1 = (float)hv[e + 1] * a.qk_scale * (e + 1 < 4 ? s0[e + 1] : s1[e - 3]);
+        split_hi_lo(x0, x1, hi[e2], lo[e2]);
+      }
+      bq[j] = pairs_to_f16x8(hi);
+      bq_lo[j] = pairs_to_f16x8(lo);
+    }
+    kmul = 1.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bq[j] = u4_to_f16x8(qr[j]);
+      bq_lo[j] = bq[j];
+    }
+    if constexpr (KS == kUniform) kmul *= a.k_scales[h * a.k_head_stride];
+  }
+
+  const int n_blocks = (seq_len + kBlock - 1) / kBlock;
+  const int blk0 = p * a.part_blocks;
+  const int blk1 = min(n_blocks, blk0 + a.part_blocks);
+  const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
+    const int c1 = min(blk1, c0 + kIdChunk);
+    stage_ids(sh, bt, c0, c1, tid);
+    const int npairs = (c1 - c0 + 1) / 2;
+    // the last pair is masked when it holds the row's partial block or only
+    // one block of the chunk
+    const int end_tok = min(seq_len, c1 * kBlock);
+    const bool last_masked = (c0 + 2 * npairs) * kBlock > end_tok;
+    const int nfull = npairs - (last_masked ? 1 : 0);
+    const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
+    auto load = [&](Pair8 &t, int k) {
+      const int j0 = 2 * (wave + kWaves * k);
+      load_pair8<KS, VS>(t, a, sh.s.ids[j0], sh.s.ids[j0 + 1], h, lane, qd);
+    };
+    auto compute = [&](Pair8 &t, int) {
+      compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
+    };
+    pipeline<Pair8>(cnt, load, compute);
+    if (last_masked && wave == nfull % kWaves) {
+      const int j0 = 2 * nfull;
+      const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
+      const int ph0 = sh.s.ids[j0];
+      const int ph1 = c0 + j0 + 1 < c1 ? sh.s.ids[j0 + 1] : ph0;
+      Pair8 t;
+      load_pair8<KS, VS>(t, a, ph0, ph1, h, lane, qd);
+      compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid, qd);
+    }
+  }
+  // uniform and per-channel V scales multiply o once
+  if constexpr (VS == kUniform) {
+    const float s = a.v_scales[h * a.v_head_stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= s;
+  } else if constexpr (VS == kChannel) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= ld16f(a.v_scales + h * kHeadDim + 16 * j + 4 * qd);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// INT4 KIVI: a unit is a 64-token group (4 blocks)
+// ---------------------------------------------------------------------------
+struct Group4 {
+  u32x4 k[4];   // block u: nibbles of channels 32qd..32qd+31, token l%16
+  u32x4 v[4];   // block u: nibbles of 4 tokens x 8 channel tiles
+  float ks[2];  // K scales of channels 2l, 2l+1 (held by block l/16)
+  float vs[2];  // V scales (channel groups 0, 1) of token l of the group
+};
+
+__device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
+                                            int h, int lane) {
+  const int H = a.num_kv_heads;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t chunk = (size_t)ph[u] * H + h;
+    t.k[u] = ld16(a.k_codes + chunk * 1024 + 16 * lane);
+    t.v[u] = ld16(a.v_codes + chunk * 1024 + 16 * lane);
+  }
+  const int mine = lane >> 4;
+  const int pm = mine == 0 ? ph[0] : mine == 1 ? ph[1] : mine == 2 ? ph[2] : ph[3];
+  const size_t chunk = (size_t)pm * H + h;
+  const float2 ks = *reinterpret_cast<const float2 *>(a.k_scales + chunk * 32 + 2 * (lane & 15));
+  const float2 vs =
+      *reinterpret_cast<const float2 *>(a.v_scales + (chunk * kBlock + (lane & 15)) * 2);
+  t.ks[0] = ks.x;
+  t.ks[1] = ks.y;
+  t.vs[0] = vs.x;
+  t.vs[1] = vs.y;
+}
+
+// Join block b0's and block b1's nibbles of channel tile j (dword j>>1 of
+// each, tile A = bytes 0/2, tile B = bytes 1/3) into one dword whose eight
+// nibbles convert to tokens 4qd..4qd+3 of b0 then of b1.
+__device__ __forceinline__ uint32_t pair_tile(uint32_t w0, uint32_t w1, int odd) {
+  return __builtin_amdgcn_perm(w1, w0, odd ? 0x07030501u : 0x06020400u);
+}
+
+// 8 nibbles -> 8 exact fp16, k-slot order (0,4,1,5,2,6,3,7) of the nibbles.
+__device__ __forceinline__ f16x8 int4x8_to_f16(uint32_t x) {
+  uint32_t pr[4];
+  int4x8_to_f16_pairs(x, pr);
+  return pairs_to_f16x8(pr);
+}
+
+// k-slot order produced by int4x8_to_f16 (nibble index of slot e)
+__device__ __forceinline__ int int4_kslot(int e) { return (e >> 1) + 4 * (e & 1); }
+
+__device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t,
+                                               const u32x4 (&qr)[4], float *scl, float qk_scale,
+                                               int lane, int qd) {
+  // stage the group's scales in this wave's LDS slot (in-order within a wave)
+  *reinterpret_cast<float2 *>(scl + 2 * lane) = float2{t.ks[0], t.ks[1]};
+  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0], t.vs[1]};
+  // q' = q * s_c for channels 32qd..32qd+31 as fp16 hi + lo, in the k-slot
+  // order of the nibble conversion
+  f16x8 bhi[4], blo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x8 qh = u4_to_f16x8(qr[j]);
+    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(scl + 32 * qd + 8 * j);
+    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(scl + 32 * qd + 8 * j + 4);
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int c0 = int4_kslot(2 * e2), c1 = int4_kslot(2 * e2 + 1);
+      const float x0 = (float)qh[c0] * (c0 < 4 ? s0[c0] : s1[c0 - 4]);
+      const float x1 = (float)qh[c1] * (c1 < 4 ? s0[c1] : s1[c1 - 4]);
+      split_hi_lo(x0, x1, hi[e2], lo[e2]);
+    }
+    bhi[j] = pairs_to_f16x8(hi);
+    blo[j] = pairs_to_f16x8(lo);
+  }
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {
+    f32x4 s[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = 2 * pr + uu;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 av = int4x8_to_f16(t.k[u][j]);
+        acc = mfma32(av, bhi[j], acc);
+        acc = mfma32(av, blo[j], acc);
+      }
+      s[uu] = acc * qk_scale;
+    }
+    f32x4 p0, p1;
+    softmax_update(st, s[0], s[1], p0, p1);
+    // per-token V scales (channel groups 0 and 1) of tokens 4qd..4qd+3
+    const float *vsp = scl + 128 + 2 * (32 * pr + 4 * qd);
+    const f32x4 va0 = *reinterpret_cast<const f32x4 *>(vsp);        // tokens 0,1 of b0
+    const f32x4 va1 = *reinterpret_cast<const f32x4 *>(vsp + 4);    // tokens 2,3 of b0
+    const f32x4 vb0 = *reinterpret_cast<const f32x4 *>(vsp + 32);   // tokens 0,1 of b1
+    const f32x4 vb1 = *reinterpret_cast<const f32x4 *>(vsp + 36);   // tokens 2,3 of b1
+    const f32x4 g0a = {va0[0], va0[2], va1[0], va1[2]}, g1a = {va0[1], va0[3], va1[1], va1[3]};
+    const f32x4 g0b = {vb0[0], vb0[2], vb1[0], vb1[2]}, g1b = {vb0[1], vb0[3], vb1[1], vb1[3]};
+    const f16x8 pb0 = p_operand(p0 * g0a, p1 * g0b);
+    const f16x8 pb1 = p_operand(p0 * g1a, p1 * g1b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = pair_tile(t.v[2 * pr][j >> 1], t.v[2 * pr + 1][j >> 1], j & 1);
+      st.o[j] = mfma32(int4x8_to_f16(w), j < 4 ? pb0 : pb1, st.o[j]);
+    }
+  }
+}
+
+__device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
+                            int p, int seq_len, int wave, int lane, int tid) {
+  const int n = lane & 15, qd = lane >> 4;
+  u32x4 qr[4];
+  load_q(qr, a, b, h, n, qd);
+  // the INT4 layout's k-slot order is applied to q' inside compute_group4
+  const int nq = kivi_quantized_len(seq_len, a.residual);
+  const int n_blocks = nq / kBlock;
+  const int blk0 = p * a.part_blocks;
+  const int blk1 = min(n_blocks, blk0 + a.part_blocks);
+  const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  float *scl = sh.s.scl[wave];
+  for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
+    const int c1 = min(blk1, c0 + kIdChunk);
+    stage_ids(sh, bt, c0, c1, tid);
+    const int ngroups = (c1 - c0) / 4;
+    const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    auto load = [&](Group4 &t, int k) {
+      const int j0 = 4 * (wave + kWaves * k);
+      const int ph[4] = {sh.s.ids[j0], sh.s.ids[j0 + 1], sh.s.ids[j0 + 2], sh.s.ids[j0 + 3]};
+      load_group4(t, a, ph, h, lane);
+    };
+    auto compute = [&](Group4 &t, int) {
+      compute_group4(st, t, qr, scl, a.qk_scale, lane, qd);
+    };
+    pipeline<Group4>(cnt, load, compute);
+  }
+}
+
+// fp16 residual ring of an INT4 cache: tokens nq .. seq_len-1, two 16-token
+// tiles per step (wave w takes tile pairs w, w+4, ...).
+__device__ void stream_ring(Softmax &st, const DecodeArgs &a, int b, int h, int seq_len,
+                            int wave, int lane) {
+  const int n = lane & 15, qd = lane >> 4;
+  u32x4 qr[4];
+  load_q(qr, a, b, h, n, qd);
+  f16x8 bq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bq[j] = u4_to_f16x8(qr[j]);
+  const int nq = kivi_quantized_len(seq_len, a.residual);
+  const size_t row = (size_t)b * a.num_kv_heads + h;
+  const uint16_t *kr = a.k_resid + row * a.ring * kHeadDim;
+  const uint16_t *vr = a.v_resid + row * (a.ring / 4) * kHeadDim * 4;
+  for (int t0 = nq + 32 * wave; t0 < seq_len; t0 += 32 * kWaves) {
+    f32x4 s[2];
+    u32x2 vw[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // ring slots of one 16-token tile are contiguous: nq and the ring
+      // length are multiples of 16
+      const int tok = t0 + 16 * u;
+      const int slot0 = tok % a.ring;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 kv = ld16(kr + (size_t)(slot0 + n) * kHeadDim + 32 * qd + 8 * j);
+        acc = mfma32(u4_to_f16x8(kv), bq[j], acc);
+      }
+      const int valid = seq_len - (tok + 4 * qd);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[u][r] = r < valid ? acc[r] * a.qk_scale : kNegInf;
+      const uint16_t *vq = vr + ((size_t)(slot0 / 4 + qd) * kHeadDim + n) * 4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x2 w = *reinterpret_cast<const u32x2 *>(vq + 16 * j * 4);
+        // zero the halves of tokens past the end (the ring may hold stale data)
+        if (valid <= 0) w = u32x2{0u, 0u};
+        else if (valid == 1) w = u32x2{w[0] & 0xFFFFu, 0u};
+        else if (valid == 2) w = u32x2{w[0], 0u};
+        else if (valid == 3) w = u32x2{w[0], w[1] & 0xFFFFu};
+        vw[u][j] = w;
+      }
+    }
+    f32x4 p0, p1;
+    softmax_update(st, s[0], s[1], p0, p1);
+    const f16x8 pb = p_operand(p0, p1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      st.o[j] = mfma32(cat(u2_to_f16x4(vw[0][j]), u2_to_f16x4(vw[1][j])), pb, st.o[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// workgroup merge and partial / output store
+// ---------------------------------------------------------------------------
+__device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st, int b, int h,
+                                int slot, bool direct, int wave, int lane, int tid) {
+  const int n = lane & 15, qd = lane >> 4;
+  const float lsum = sum_over_quads(st.l);
+  __syncthreads();  // streaming LDS is dead from here on
+  if (qd == 0) {
+    sh.g.m[wave][n] = st.m;
+    sh.g.l[wave][n] = lsum;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<f32x4 *>(&sh.g.o[wave][n][16 * j + 4 * qd]) = st.o[j];
+  __syncthreads();
+  // thread -> (head slot hn, channels 8*c8 .. 8*c8+7)
+  const int hn = tid >> 4, c8 = tid & 15;
+  if (hn >= a.group) return;
+  float big = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) big = fmaxf(big, sh.g.m[w][hn]);
+  float lt = 0.0f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = sh.g.m[w][hn];
+    // a wave that saw no token has m = -inf and contributes nothing
+    const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - big);
+    lt += f * sh.g.l[w][hn];
+    acc0 += f * *reinterpret_cast<const f32x4 *>(&sh.g.o[w][hn][8 * c8]);
+    acc1 += f * *reinterpret_cast<const f32x4 *>(&sh.g.o[w][hn][8 * c8 + 4]);
+  }
+  const size_t row = (size_t)b * a.num_q_heads + h * a.group + hn;
+  if (direct) {
+    const float inv = 1.0f / lt;
+    float *out = a.out + row * kHeadDim + 8 * c8;
+    *reinterpret_cast<f32x4 *>(out) = acc0 * inv;
+    *reinterpret_cast<f32x4 *>(out + 4) = acc1 * inv;
+  } else {
+    const size_t idx = row * a.slots + slot;
+    float *o = a.ws_o + idx * kHeadDim + 8 * c8;
+    *reinterpret_cast<f32x4 *>(o) = acc0;
+    *reinterpret_cast<f32x4 *>(o + 4) = acc1;
+    if (c8 == 0) {
+      a.ws_m[idx] = big;
+      a.ws_l[idx] = lt;
+    }
+  }
+}
+
+template <int DT, int KS, int VS>
+__global__ __launch_bounds__(kThreads) void kvq_paged_decode_kernel(DecodeArgs a) {
+  __shared__ SharedLds sh;
   const int p = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int n = lane & 15, qd = lane >> 4;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int seq_len = a.seq_lens[b];
-  const bool live = n < a.group;
-  const int hq = h * a.group + n;
+  const bool direct = a.slots == 1;
 
   if (seq_len <= 0) {
-    if (p == 0 && live) {
-      float *out = a.out + ((size_t)b * a.num_q_heads + hq) * kHeadDim;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4 *>(out + 16 * j + 4 * qd) = z;
+    // rows of length 0: zeros (written here only when no reduce follows)
+    if (direct && p == 0) {
+      const int hn = tid >> 4, c8 = tid & 15;
+      if (hn < a.group) {
+        float *out = a.out + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(out) = z;
+        *reinterpret_cast<f32x4 *>(out + 4) = z;
+      }
     }
     return;
   }
 
-  int n_blocks, nq = 0;
-  bool has_ring = false;
-  if constexpr (DT == kInt4) {
-    nq = kivi_quantized_len(seq_len, a.residual);
-    n_blocks = nq / kBlock;
-    has_ring = seq_len > nq;
-  } else {
-    n_blocks = (seq_len + kBlock - 1) / kBlock;
-  }
-  const int n_main = (n_blocks + a.part_blocks - 1) / a.part_blocks;
-  const bool ring_part = (DT == kInt4) && p == a.num_parts;
-  if (!ring_part && p >= n_main) return;
-  if (ring_part && !has_ring) return;
-
-  u32x4 qr[4];
-  load_q(qr, a, b, h, hq, live, qd);
-
   Softmax st;
   softmax_init(st);
-  const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-
   if constexpr (DT == kInt4) {
-    if (ring_part) {
-      f16x8 bq[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bq[j] = u4_to_f16x8(qr[j]);
-      const size_t row = (size_t)b * a.num_kv_heads + h;
-      const uint16_t *kr = a.k_resid + row * a.ring * kHeadDim;
-      const uint16_t *vr = a.v_resid + row * (a.ring / 4) * kHeadDim * 4;
-      for (int t0 = nq; t0 < seq_len; t0 += kBlock) {
-        compute_ring_tile(st, a, kr, vr, bq, t0 % a.ring, t0, seq_len, n, qd);
-      }
+    const int nq = kivi_quantized_len(seq_len, a.residual);
+    const int n_main = (nq / kBlock + a.part_blocks - 1) / a.part_blocks;
+    if (p == a.num_parts) {
+      if (seq_len <= nq) return;  // no residual tokens (cannot happen once S >= 1)
+      stream_ring(st, a, b, h, seq_len, wave, lane);
     } else {
-      // q * qk_scale in fp32 for the lane's 32 channels (natural order)
-      float qf[32];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 hv = u4_to_f16x8(qr[j]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[8 * j + e] = (float)hv[e] * a.qk_scale;
-      }
-      const int g0 = (p * a.part_blocks) / 4;
-      const int g1 = min(n_blocks, (p + 1) * a.part_blocks) / 4;
-      BlockIds ids(bt, 4 * g0, 4 * g1, lane);
-      Tile4 cur, nxt;
-      int ph[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ph[u] = ids.get(4 * g0 + u, lane);
-      load_tile4(cur, a, ph, h, lane, qd);
-      for (int gi = g0; gi < g1; gi += 2) {
-        if (gi + 1 < g1) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ph[u] = ids.get(4 * (gi + 1) + u, lane);
-          load_tile4(nxt, a, ph, h, lane, qd);
-        }
-        compute_tile4(st, cur, qf, qd);
-        if (gi + 1 >= g1) break;
-        if (gi + 2 < g1) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ph[u] = ids.get(4 * (gi + 2) + u, lane);
-          load_tile4(cur, a, ph, h, lane, qd);
-        }
-        compute_tile4(st, nxt, qf, qd);
-      }
+      if (p >= n_main) return;
+      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
     }
   } else {
-    // INT8 / FP8 paged blocks
-    f16x8 bq[4], bq_lo[4];
-    float kmul = a.qk_scale;
-    if constexpr (KS == kChannel) {
-      const float *ksc = a.k_scales + h * kHeadDim + 32 * qd;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 hv = u4_to_f16x8(qr[j]);
-        const f32x4 s0 = ld16f(ksc + 8 * j), s1 = ld16f(ksc + 8 * j + 4);
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e = 2 * e2;
-          const float x0 = (float)hv[e] * a.qk_scale * (e < 4 ? s0[e] : s1[e - 4]);
-          const float x1 = (float)hv[e + 1] * a.qk_scale * (e + 1 < 4 ? s0[e + 1] : s1[e - 3]);
-          split_hi_lo(x0, x1, hi[e2], lo[e2]);
-        }
-        bq[j] = pairs_to_f16x8(hi);
-        bq_lo[j] = pairs_to_f16x8(lo);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bq[j] = u4_to_f16x8(qr[j]);
-        bq_lo[j] = bq[j];
-      }
-      if constexpr (KS == kUniform) kmul *= a.k_scales[h * a.k_head_stride];
-    }
-    const int blk0 = p * a.part_blocks;
-    const int blk1 = min(n_blocks, blk0 + a.part_blocks);
-    const int last = n_blocks - 1;
-    const bool partial_last = (seq_len % kBlock) != 0;
-    BlockIds ids(bt, blk0, blk1, lane);
-    Tile8 cur, nxt;
-    load_tile8<KS, VS>(cur, a, ids.get(blk0, lane), h, lane, qd);
-    for (int jb = blk0; jb < blk1; jb += 2) {
-      if (jb + 1 < blk1) load_tile8<KS, VS>(nxt, a, ids.get(jb + 1, lane), h, lane, qd);
-      if (jb == last && partial_last) {
-        compute_tile8<DT, KS, VS, true>(st, cur, bq, bq_lo, kmul, jb * kBlock, seq_len, qd);
-      } else {
-        compute_tile8<DT, KS, VS, false>(st, cur, bq, bq_lo, kmul, jb * kBlock, seq_len, qd);
-      }
-      if (jb + 1 >= blk1) break;
-      if (jb + 2 < blk1) load_tile8<KS, VS>(cur, a, ids.get(jb + 2, lane), h, lane, qd);
-      if (jb + 1 == last && partial_last) {
-        compute_tile8<DT, KS, VS, true>(st, nxt, bq, bq_lo, kmul, (jb + 1) * kBlock, seq_len, qd);
-      } else {
-        compute_tile8<DT, KS, VS, false>(st, nxt, bq, bq_lo, kmul, (jb + 1) * kBlock, seq_len, qd);
-      }
-    }
-    apply_v_scale<VS>(st, a, h, qd);
+    const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
+    if (p >= n_main) return;
+    stream_q8<DT, KS, VS>(st, a, sh, b, h, p, seq_len, wave, lane, tid);
   }
-  finish(a, st, b, h, ring_part ? a.num_parts : p, n_main, has_ring, lane);
+  merge_and_store(a, sh, st, b, h, p, direct, wave, lane, tid);
+}
+
+// Log-sum-exp merge of the partition partials of each (row, query head):
+// M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p, in
+// partition order.  A partition past the row's length (or a ring partition
+// of a row without residual tokens) wrote nothing and is skipped by index.
+// One thread per 4 channels: 32 threads per (row, query head).
+__global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a, int is_int4) {
+  const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, hq) row
+  const int c4 = threadIdx.x & 31;
+  const int b = gid / a.num_q_heads;
+  if (b >= a.batch) return;
+  const int seq_len = a.seq_lens[b];
+  float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
+  if (seq_len <= 0) {
+    *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  int n_main, has_ring = 0;
+  if (is_int4) {
+    const int nq = kivi_quantized_len(seq_len, a.residual);
+    n_main = (nq / kBlock + a.part_blocks - 1) / a.part_blocks;
+    has_ring = seq_len > nq ? 1 : 0;
+  } else {
+    n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
+  }
+  const int total = n_main + has_ring;
+  const size_t base = (size_t)gid * a.slots;
+  float big = kNegInf;
+  for (int pp = 0; pp < total; ++pp) {
+    const int slot = pp < n_main ? pp : a.num_parts;
+    big = fmaxf(big, a.ws_m[base + slot]);
+  }
+  float lt = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int pp = 0; pp < total; ++pp) {
+    const int slot = pp < n_main ? pp : a.num_parts;
+    const float w = __builtin_amdgcn_exp2f(a.ws_m[base + slot] - big);
+    lt += w * a.ws_l[base + slot];
+    acc += w * *reinterpret_cast<const f32x4 *>(a.ws_o + (base + slot) * kHeadDim + 4 * c4);
+  }
+  *reinterpret_cast<f32x4 *>(out) = acc * (1.0f / lt);
 }
 
 template <int DT, int KS>
-hipError_t launch_v(const DecodeArgs &a, int v_kind, dim3 grid, hipStream_t s) {
+void launch_v(const DecodeArgs &a, int v_kind, dim3 grid, hipStream_t s) {
   switch (v_kind) {
     case kUniform:
-      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kUniform>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kUniform>), grid, dim3(kThreads), 0, s,
+                         a);
       break;
     case kChannel:
-      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kChannel>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kChannel>), grid, dim3(kThreads), 0, s,
+                         a);
       break;
     default:
-      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kToken>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((kvq_paged_decode_kernel<DT, KS, kToken>), grid, dim3(kThreads), 0, s,
+                         a);
       break;
   }
-  return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_k(const DecodeArgs &a, int k_kind, int v_kind, dim3 grid, hipStream_t s) {
+void launch_k(const DecodeArgs &a, int k_kind, int v_kind, dim3 grid, hipStream_t s) {
   switch (k_kind) {
-    case kUniform: return launch_v<DT, kUniform>(a, v_kind, grid, s);
-    case kChannel: return launch_v<DT, kChannel>(a, v_kind, grid, s);
-    default: return launch_v<DT, kToken>(a, v_kind, grid, s);
+    case kUniform: launch_v<DT, kUniform>(a, v_kind, grid, s); break;
+    case kChannel: launch_v<DT, kChannel>(a, v_kind, grid, s); break;
+    default: launch_v<DT, kToken>(a, v_kind, grid, s); break;
   }
 }
 
@@ -608,12 +732,19 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   const int parts = a.num_parts + (dtype == kInt4 ? 1 : 0);
   const dim3 grid(parts, a.num_kv_heads, batch);
   if (dtype == kInt4) {
-    hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken>), grid, dim3(64), 0,
-                       stream, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken>), grid,
+                       dim3(kThreads), 0, stream, a);
+  } else if (dtype == kFp8) {
+    launch_k<kFp8>(a, k_kind, v_kind, grid, stream);
+  } else {
+    launch_k<kInt8>(a, k_kind, v_kind, grid, stream);
   }
-  if (dtype == kFp8) return launch_k<kFp8>(a, k_kind, v_kind, grid, stream);
-  return launch_k<kInt8>(a, k_kind, v_kind, grid, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.slots == 1) return e;
+  const int rows = batch * a.num_q_heads;
+  hipLaunchKernelGGL(kvq_partition_reduce_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, a,
+                     dtype == kInt4 ? 1 : 0);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

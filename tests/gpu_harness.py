@@ -136,7 +136,6 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     if cache.k_resid is not None:
         pools["k_resid"] = cache.k_resid.cpu().numpy()
         pools["v_resid"] = cache.v_resid.cpu().numpy()
-    pools["ws_counters_zero"] = bool((ws[:4 * b * w.num_kv_heads].view(torch.int32) == 0).all())
     res = CaseResult(w, lens, table, [k.cpu().numpy() for k in ks], [v.cpu().numpy() for v in vs],
                      q.cpu().numpy(), out.cpu().numpy(), pools, k_static, v_static, scale)
     if decode_twice:

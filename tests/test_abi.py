@@ -115,8 +115,14 @@ def test_workspace_bytes():
     # explicit partitions: 4 rows x 8 q heads x ceil(256/64) slots of (m, l, o[128])
     lay64 = _layout(split_tokens=64)
     rows = 4 * 8 * 4
-    want = 256 + 2 * ((rows * 4 + 255) // 256 * 256) + rows * 512
+    want = 2 * ((rows * 4 + 255) // 256 * 256) + rows * 512
     assert kvq.decode_workspace_bytes(lay64, 4, 256) == want
+    # one partition per row: the decode kernel writes the output directly
+    assert kvq.decode_workspace_bytes(_layout(split_tokens=256), 4, 256) == 0
+    # INT4 always has a residual partition beside the INT4 ones
+    lay4 = _layout(dtype=3, k_gran=2, v_gran=3, split_tokens=64)
+    assert kvq.decode_workspace_bytes(lay4, 2, 100) == 0          # residual only
+    assert kvq.decode_workspace_bytes(lay4, 2, 128 + 64 + 64) > 0
 
 
 def _decode(lay, cache, q=FAKE, bt=FAKE, sl=FAKE, batch=2, max_len=100, scale=0.1,
@@ -134,8 +140,10 @@ def test_entry_points_reject_before_launch():
     lay, c = _layout(), _cache()
     assert _decode(lay, c, q=None) == INV
     assert _decode(lay, c, out=FAKE + 8) == ALN
-    assert _decode(lay, c, ws=FAKE + 16) == WS
-    assert _decode(lay, c, ws_bytes=16) == WS
+    split = _layout(split_tokens=16)              # 7 partitions: partials needed
+    assert _decode(split, c, ws=FAKE + 16) == WS
+    assert _decode(split, c, ws_bytes=16) == WS
+    assert _decode(split, c, ws=None) == WS
     assert _decode(lay, c, scale=float("nan")) == INV
     assert _decode(lay, c, max_len=10 ** 6) == CAP
     assert _decode(lay, c, batch=0) == OK            # nothing to do, nothing launched
