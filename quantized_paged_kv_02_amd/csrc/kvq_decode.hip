@@ -146,6 +146,10 @@ __device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, ui
   lo = pack_rtz(x0 - (float)hh.x, x1 - (float)hh.y);
 }
 
+// A wave-uniform value (a block id read from LDS) moved to a scalar register,
+// so tile addresses are a scalar base plus one shared per-lane offset.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Stage physical block ids [c0, c1) of a row in LDS (whole workgroup).
 __device__ __forceinline__ void stage_ids(SharedLds &sh, const int32_t *bt, int c0, int c1,
                                           int tid) {
@@ -335,7 +339,7 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
     auto load = [&](Pair8 &t, int k) {
       const int j0 = 2 * (wave + kWaves * k);
-      load_pair8<KS, VS>(t, a, sh.s.ids[j0], sh.s.ids[j0 + 1], h, lane, qd);
+      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd);
     };
     auto compute = [&](Pair8 &t, int) {
       compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
@@ -344,8 +348,8 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     if (last_masked && wave == nfull % kWaves) {
       const int j0 = 2 * nfull;
       const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
-      const int ph0 = sh.s.ids[j0];
-      const int ph1 = c0 + j0 + 1 < c1 ? sh.s.ids[j0 + 1] : ph0;
+      const int ph0 = uniform(sh.s.ids[j0]);
+      const int ph1 = c0 + j0 + 1 < c1 ? uniform(sh.s.ids[j0 + 1]) : ph0;
       Pair8 t;
       load_pair8<KS, VS>(t, a, ph0, ph1, h, lane, qd);
       compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid, qd);
@@ -489,7 +493,8 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     auto load = [&](Group4 &t, int k) {
       const int j0 = 4 * (wave + kWaves * k);
-      const int ph[4] = {sh.s.ids[j0], sh.s.ids[j0 + 1], sh.s.ids[j0 + 2], sh.s.ids[j0 + 3]};
+      const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
+                         uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
       load_group4(t, a, ph, h, lane);
     };
     auto compute = [&](Group4 &t, int) {
@@ -605,7 +610,7 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
 }
 
 template <int DT, int KS, int VS>
-__global__ __launch_bounds__(kThreads) void kvq_paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void kvq_paged_decode_kernel(DecodeArgs a) {
   __shared__ SharedLds sh;
   const int p = blockIdx.x;
   const int h = blockIdx.y;

@@ -61,16 +61,24 @@ __device__ __forceinline__ f16x4 fp8x4_to_f16(uint32_t x) {
 }
 
 // --- INT4: 8 nibbles in a dword -> 4 fp16 pairs (nibble s, nibble s+4) ------
-// Bias each nibble to code+8 (xor 0x8), splice it under 1024 and subtract
-// 1032.  pair s holds nibbles s (low half) and s+4 (high half).
+// Bitwise select m ? (x ^ c) : c, one v_bitop3_b32: under the mask it biases
+// the nibble to code+8 (xor of its top bit, carried in c); elsewhere it
+// writes the fp16 exponent of 1024.  Low nibbles become 1024 + code + 8
+// (subtract 1032); nibbles in the upper half of a byte become
+// 1024 + 16 (code + 8) (times 1/16, minus 72).  All steps are exact.
+__device__ __forceinline__ uint32_t bsel(uint32_t x, uint32_t m, uint32_t c) {
+  return ((x ^ c) & m) | (c & ~m);
+}
+
 __device__ __forceinline__ void int4x8_to_f16_pairs(uint32_t x, uint32_t out[4]) {
-  const uint32_t u = x ^ 0x88888888u;
-  const f16x2 bias = {(f16)-1032.0f, (f16)-1032.0f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t p = ((u >> (4 * s)) & 0x000F000Fu) | 0x64006400u;
-    out[s] = as_u32(as_f16x2(p) + bias);
-  }
+  const f16x2 sub = {(f16)-1032.0f, (f16)-1032.0f};
+  const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 sub_hi = {(f16)-72.0f, (f16)-72.0f};
+  const uint32_t y = x >> 8;
+  out[0] = as_u32(as_f16x2(bsel(x, 0x000F000Fu, 0x64086408u)) + sub);
+  out[1] = as_u32(as_f16x2(bsel(x, 0x00F000F0u, 0x64806480u)) * sixteenth + sub_hi);
+  out[2] = as_u32(as_f16x2(bsel(y, 0x000F000Fu, 0x64086408u)) + sub);
+  out[3] = as_u32(as_f16x2(bsel(y, 0x00F000F0u, 0x64806480u)) * sixteenth + sub_hi);
 }
 
 __device__ __forceinline__ f16x8 pairs_to_f16x8(const uint32_t p[4]) {
@@ -84,16 +92,25 @@ __device__ __forceinline__ float shfl_xor(float v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
-// max over the four lanes l, l^16, l^32, l^48
+// Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 row
+// swaps (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows and
+// 32-lane halves between two registers; passing the value twice yields the
+// value and its partner).
 __device__ __forceinline__ float max_over_quads(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  v = fmaxf(v, shfl_xor(v, 32));
-  return v;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 __device__ __forceinline__ float sum_over_quads(float v) {
-  v += shfl_xor(v, 16);
-  v += shfl_xor(v, 32);
-  return v;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
