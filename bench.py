@@ -276,6 +276,28 @@ def run(args):
         durs += [e0.elapsed_time(e1) for e0, e1 in events]
     kernel_timing = "HIP event pairs around each decode launch, queued behind a spin kernel"
     kern_ms = float(np.mean(durs))
+
+    copy_probe = None
+    if args.copy_probe_mib > 0:
+        # a plain device-to-device copy of known size: the yardstick that
+        # converts profiler byte counters into bytes
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0.record()
+        for _ in range(3):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / 3
+        copy_probe = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(cms, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
     achieved = layer_bytes / (kern_ms * 1e-3) / 1e9
 
     traffic = None
@@ -320,6 +342,8 @@ def run(args):
         },
         "cpu_baseline": cpu,
     }
+    if copy_probe is not None:
+        result["copy_probe"] = copy_probe
     print(json.dumps(result), flush=True)
 
 
@@ -334,6 +358,8 @@ def main():
     ap.add_argument("--kernel-samples", type=int, default=10,
                     help="extra synchronised replays for the per-launch timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also time a device copy of this many MiB (profiler yardstick)")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
     args = ap.parse_args()
     if args.gpus != 1:

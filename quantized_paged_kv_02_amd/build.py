@@ -41,28 +41,31 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvq)")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source and link ``libkvq.so``; returns its path."""
+def build_library(verbose: bool = False, out: str = LIB_PATH, defines=(),
+                  objdir: str | None = None) -> str:
+    """Compile every source and link ``libkvq.so`` (or ``out``); ``defines``
+    are extra ``-D`` flags.  Returns the library path."""
     hipcc = hipcc_path()
-    objdir = os.path.join(PKG_DIR, "_build")
+    objdir = objdir or os.path.join(PKG_DIR, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+        cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC,
+               *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -13,9 +13,15 @@ namespace {
 constexpr int kBlock = 16;
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 64;
-// Aim for this many partition workgroups (four wavefronts each) per decode
-// launch when the layout does not fix the partition length: 256 CUs x 4.
-constexpr long kTargetWorkgroups = 1024;
+// Partition sizing: decode workgroups (four wavefronts) resident at once
+// on a 256-CU MI355X -- two per CU for INT4, three for INT8/FP8 (the
+// register budgets of the kernels) -- and the fixed cost of a workgroup
+// (first-load latency, LDS merge, partial store) in blocks of streaming.
+constexpr long kCUs = 256;
+constexpr long kResidentInt4 = 2 * kCUs;
+constexpr long kResidentQ8 = 3 * kCUs;
+constexpr long kWgOverheadInt4 = 16;
+constexpr long kWgOverheadQ8 = 8;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -82,15 +88,30 @@ Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
   if (L->split_tokens > 0) {
     pb = L->split_tokens / kBlock;
   } else {
+    // Pick the partition length that minimises (dispatch rounds) x (blocks
+    // per workgroup + fixed cost): a launch whose last round is nearly
+    // empty wastes a whole workgroup time.
     const long units = (long)batch * L->num_kv_heads;
-    const long want = (units * blocks + kTargetWorkgroups - 1) / kTargetWorkgroups;
-    pb = (int)((want + quantum - 1) / quantum * quantum);
-    if (pb < quantum) pb = quantum;
+    const long resident = int4 ? kResidentInt4 : kResidentQ8;
+    const long overhead = int4 ? kWgOverheadInt4 : kWgOverheadQ8;
+    const long top = blocks > quantum ? blocks : quantum;
+    long best_t = -1;
+    pb = quantum;
+    for (long c = quantum; c <= top + quantum - 1; c += quantum) {
+      const long parts = (blocks + c - 1) / c;
+      if (parts > 4096) continue;
+      const long rounds = (units * (parts > 0 ? parts : 1) + resident - 1) / resident;
+      const long t = rounds * (c + overhead);
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        pb = (int)c;
+      }
+    }
   }
+  if (pb < (int4 ? 4 : 1)) pb = int4 ? 4 : 1;
   p.part_blocks = pb;
-  p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 0;
-  if (!int4 && p.num_parts == 0) p.num_parts = 1;  // rows of length 0 still write zeros
-  p.slots = p.num_parts + (int4 ? 1 : 0);
+  p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 1;  // >= 1: empty rows, INT4 rings
+  p.slots = p.num_parts;
   return p;
 }
 

@@ -49,7 +49,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t part_blocks;      // blocks per main partition
   int32_t num_parts;        // main partitions in the grid
-  int32_t slots;            // partial slots per (b, hq): num_parts (+1 INT4);
+  int32_t slots;            // partial slots per (b, hq) = num_parts;
                             // 1 = the decode kernel writes out directly
   int32_t ring;             // INT4 ring slots
   int32_t residual;         // INT4 residual length

@@ -12,8 +12,8 @@
 //
 // Work decomposition.  A workgroup of four wavefronts handles one partition
 // p of one (row b, KV head h): `part_blocks` consecutive 16-token blocks
-// (INT4: whole 64-token groups).  INT4 adds one workgroup per (b, h) for the
-// fp16 residual ring.  The workgroup stages the partition's physical block
+// (INT4: whole 64-token groups; the row's last partition also takes the fp16
+// residual ring).  The workgroup stages the partition's physical block
 // ids in LDS; wave w takes units w, w+4, w+8, ... (a unit is a pair of
 // blocks for INT8/FP8, a 64-token group for INT4) and keeps an online
 // softmax (running max m in the log2 domain, running sum l, unnormalised
@@ -49,7 +49,21 @@
 namespace kvq {
 namespace {
 
+// Tuning knobs (compile-time): software pipeline depth of the INT4 and
+// INT8/FP8 streams (2 = one unit ahead, 3 = two units ahead) and the
+// workgroups per CU the register allocation is bounded for.
+#ifndef KVQ_INT4_DEPTH
+#define KVQ_INT4_DEPTH 2
+#endif
+#ifndef KVQ_Q8_DEPTH
+#define KVQ_Q8_DEPTH 2
+#endif
+#ifndef KVQ_WG_PER_CU
+#define KVQ_WG_PER_CU 2
+#endif
+
 constexpr int kWaves = 4;
+constexpr int kQRow = 128 + 8;  // LDS row of a staged query (fp16)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kIdChunk = 256;  // block ids staged in LDS per pass
 constexpr float kNegInf = -__builtin_inff();
@@ -67,12 +81,18 @@ struct Softmax {
 // then the four wave states for the merge.
 struct StreamLds {
   int ids[kIdChunk];
-  float scl[kWaves][256];  // INT4: K scales [128 channels], V scales [64 tok][2]
+  float scl[kWaves][256];   // INT4: K scales [128 channels], V scales [64 tok][2]
+  // INT4: the group's queries, zero past the group; rows padded by 16 bytes
+  // so the 16 head rows of one read start in different banks
+  f16 q[16][kQRow];
 };
+// o rows padded by 4 floats so the 16 head rows of one store or load fall
+// in different banks
+constexpr int kMergeRow = kHeadDim + 4;
 struct MergeLds {
   float m[kWaves][16];
   float l[kWaves][16];
-  float o[kWaves][16][kHeadDim];
+  float o[kWaves][16][kMergeRow];
 };
 union SharedLds {
   StreamLds s;
@@ -108,6 +128,33 @@ __device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, con
     p1[r] = __builtin_amdgcn_exp2f(s1[r] - st.m);
   }
   st.l += ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+}
+
+// The same for four blocks at once (one max and one rescale decision).
+__device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4],
+                                                f32x4 (&p)[4]) {
+  float bm = kNegInf;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    bm = fmaxf(bm, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
+  bm = max_over_quads(bm);
+  const bool need = bm > st.m + kRescaleSlack;
+  if (__any(need)) {
+    const float mn = need ? bm : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
+    st.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    st.m = mn;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[u][r] = __builtin_amdgcn_exp2f(s[u][r] - st.m);
+    sum += (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
+  }
+  st.l += sum;
 }
 
 // P^T operand of the value product: tokens 4qd..4qd+3 of block 0, then of
@@ -158,26 +205,63 @@ __device__ __forceinline__ void stage_ids(SharedLds &sh, const int32_t *bt, int 
   __syncthreads();
 }
 
+// The scheduler may not move instructions across a pipeline stage boundary:
+// otherwise it sinks the next unit's loads below the current unit's first
+// use, and the wait for the current unit then also waits for the next one.
+__device__ __forceinline__ void stage_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Run `cnt` units through a one-ahead software pipeline.  load(T&, k)
 // issues unit k's loads, compute(T&, k) consumes them.
 template <typename T, typename Load, typename Compute>
 __device__ __forceinline__ void pipeline(int cnt, Load &&load, Compute &&compute) {
   if (cnt <= 0) return;
-  T a, b;
+  T a(0), b(1);
   load(a, 0);
   int k = 0;
   for (; k + 2 < cnt; k += 2) {
     load(b, k + 1);
+    stage_fence();
     compute(a, k);
+    stage_fence();
     load(a, k + 2);
+    stage_fence();
     compute(b, k + 1);
+    stage_fence();
   }
   if (k + 1 < cnt) {
     load(b, k + 1);
+    stage_fence();
     compute(a, k);
+    stage_fence();
     compute(b, k + 1);
   } else {
     compute(a, k);
+  }
+}
+
+// Three-buffer version: units k+1 and k+2 are in flight while unit k is
+// consumed.  Every step issues the same loads; load(T&, k, live) with
+// live == false must issue them without memory traffic (zero-size buffer
+// resources), so the compiler's wait counts are the same on every path.
+template <typename T, typename Load, typename Compute>
+__device__ __forceinline__ void pipeline3(int cnt, Load &&load, Compute &&compute) {
+  if (cnt <= 0) return;
+  T a(0), b(1), c(2);
+  load(a, 0, true);
+  load(b, 1, 1 < cnt);
+  for (int k = 0; k < cnt; k += 3) {
+    load(c, k + 2, k + 2 < cnt);
+    stage_fence();
+    compute(a, k);
+    stage_fence();
+    load(a, k + 3, k + 3 < cnt);
+    stage_fence();
+    if (k + 1 < cnt) compute(b, k + 1);
+    stage_fence();
+    load(b, k + 4, k + 4 < cnt);
+    stage_fence();
+    if (k + 2 < cnt) compute(c, k + 2);
+    stage_fence();
   }
 }
 
@@ -189,23 +273,28 @@ struct Pair8 {
   u32x4 v[2][2];  // block u: V bytes, 4 tokens x channels 16j + l%16 (j 0..3 / 4..7)
   f32x4 ks[2];    // per-token K scales of tokens 4qd..4qd+3
   f32x4 vs[2];
+  __device__ explicit Pair8(int = 0) {}
 };
 
+// live == false issues the same loads through zero-size resources.
 template <int KS, int VS>
 __device__ __forceinline__ void load_pair8(Pair8 &t, const DecodeArgs &a, int ph0, int ph1,
-                                           int h, int lane, int qd) {
+                                           int h, int lane, int qd, bool live = true) {
   const int ph[2] = {ph0, ph1};
+  const uint32_t cb = live ? 2048u : 0u, sb = live ? 64u : 0u;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t chunk = (size_t)ph[u] * a.num_kv_heads + h;
-    const uint8_t *kc = a.k_codes + chunk * 2048 + 16 * lane;
-    const uint8_t *vc = a.v_codes + chunk * 2048 + 16 * lane;
-    t.k[u][0] = ld16(kc);
-    t.k[u][1] = ld16(kc + 1024);
-    t.v[u][0] = ld16(vc);
-    t.v[u][1] = ld16(vc + 1024);
-    if constexpr (KS == kToken) t.ks[u] = ld16f(a.k_scales + chunk * kBlock + 4 * qd);
-    if constexpr (VS == kToken) t.vs[u] = ld16f(a.v_scales + chunk * kBlock + 4 * qd);
+    const rsrc_t kr = make_rsrc(a.k_codes + chunk * 2048, cb);
+    const rsrc_t vr = make_rsrc(a.v_codes + chunk * 2048, cb);
+    t.k[u][0] = bld16(kr, 16 * lane);
+    t.k[u][1] = bld16(kr, 16 * lane + 1024);
+    t.v[u][0] = bld16(vr, 16 * lane);
+    t.v[u][1] = bld16(vr, 16 * lane + 1024);
+    if constexpr (KS == kToken)
+      t.ks[u] = bld16f(make_rsrc(a.k_scales + chunk * kBlock, sb), 16 * qd);
+    if constexpr (VS == kToken)
+      t.vs[u] = bld16f(make_rsrc(a.v_scales + chunk * kBlock, sb), 16 * qd);
   }
 }
 
@@ -337,14 +426,19 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const bool last_masked = (c0 + 2 * npairs) * kBlock > end_tok;
     const int nfull = npairs - (last_masked ? 1 : 0);
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Pair8 &t, int k) {
-      const int j0 = 2 * (wave + kWaves * k);
-      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd);
+    auto load = [&](Pair8 &t, int k, bool live) {
+      const int j0 = live ? 2 * (wave + kWaves * k) : 0;
+      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd,
+                         live);
     };
     auto compute = [&](Pair8 &t, int) {
       compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
     };
-    pipeline<Pair8>(cnt, load, compute);
+#if KVQ_Q8_DEPTH == 3
+    pipeline3<Pair8>(cnt, load, compute);
+#else
+    pipeline<Pair8>(cnt, [&](Pair8 &t, int k) { load(t, k, true); }, compute);
+#endif
     if (last_masked && wave == nfull % kWaves) {
       const int j0 = 2 * nfull;
       const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
@@ -374,19 +468,24 @@ struct Group4 {
   u32x4 v[4];   // block u: nibbles of 4 tokens x 8 channel tiles
   float ks[2];  // K scales of channels 2l, 2l+1 (held by block l/16)
   float vs[2];  // V scales (channel groups 0, 1) of token l of the group
+  __device__ explicit Group4(int = 0) {}
 };
 
+// live == false: the loads are issued through zero-size resources (codes)
+// or at the partition's first group (scales) and their values are unused.
+// pm: physical block of this lane's scale row (block lane/16 of the group).
+// live == false: the code loads go through zero-size resources and the
+// scale loads re-read the first group; their values are unused.
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
-                                            int h, int lane) {
+                                            int pm, int h, int lane, bool live) {
   const int H = a.num_kv_heads;
+  const uint32_t bytes = live ? 1024u : 0u;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t chunk = (size_t)ph[u] * H + h;
-    t.k[u] = ld16(a.k_codes + chunk * 1024 + 16 * lane);
-    t.v[u] = ld16(a.v_codes + chunk * 1024 + 16 * lane);
+    t.k[u] = bld16(make_rsrc(a.k_codes + chunk * 1024, bytes), 16 * lane);
+    t.v[u] = bld16(make_rsrc(a.v_codes + chunk * 1024, bytes), 16 * lane);
   }
-  const int mine = lane >> 4;
-  const int pm = mine == 0 ? ph[0] : mine == 1 ? ph[1] : mine == 2 ? ph[2] : ph[3];
   const size_t chunk = (size_t)pm * H + h;
   const float2 ks = *reinterpret_cast<const float2 *>(a.k_scales + chunk * 32 + 2 * (lane & 15));
   const float2 vs =
@@ -414,18 +513,21 @@ __device__ __forceinline__ f16x8 int4x8_to_f16(uint32_t x) {
 // k-slot order produced by int4x8_to_f16 (nibble index of slot e)
 __device__ __forceinline__ int int4_kslot(int e) { return (e >> 1) + 4 * (e & 1); }
 
-__device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t,
-                                               const u32x4 (&qr)[4], float *scl, float qk_scale,
-                                               int lane, int qd) {
+__device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, const f16 *qs,
+                                               float *scl, float qk_scale, int lane, int n,
+                                               int qd) {
   // stage the group's scales in this wave's LDS slot (in-order within a wave)
   *reinterpret_cast<float2 *>(scl + 2 * lane) = float2{t.ks[0], t.ks[1]};
   *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0], t.vs[1]};
-  // q' = q * s_c for channels 32qd..32qd+31 as fp16 hi + lo, in the k-slot
-  // order of the nibble conversion
-  f16x8 bhi[4], blo[4];
+  // Scores, channel chunk by chunk: q' = q * s_c for channels 32qd+8j..+7
+  // as fp16 hi + lo in the k-slot order of the nibble conversion, applied
+  // to the chunk of all four blocks.
+  f32x4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f16x8 qh = u4_to_f16x8(qr[j]);
+    const f16x8 qh = *reinterpret_cast<const f16x8 *>(qs + n * kQRow + 32 * qd + 8 * j);
     const f32x4 s0 = *reinterpret_cast<const f32x4 *>(scl + 32 * qd + 8 * j);
     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(scl + 32 * qd + 8 * j + 4);
     uint32_t hi[4], lo[4];
@@ -436,26 +538,21 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t,
       const float x1 = (float)qh[c1] * (c1 < 4 ? s0[c1] : s1[c1 - 4]);
       split_hi_lo(x0, x1, hi[e2], lo[e2]);
     }
-    bhi[j] = pairs_to_f16x8(hi);
-    blo[j] = pairs_to_f16x8(lo);
+    const f16x8 bhi = pairs_to_f16x8(hi), blo = pairs_to_f16x8(lo);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f16x8 av = int4x8_to_f16(t.k[u][j]);
+      acc[u] = mfma32(av, bhi, acc[u]);
+      acc[u] = mfma32(av, blo, acc[u]);
+    }
   }
+  f32x4 pg[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] *= qk_scale;
+  softmax_update4(st, acc, pg);
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
-    f32x4 s[2];
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      const int u = 2 * pr + uu;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 av = int4x8_to_f16(t.k[u][j]);
-        acc = mfma32(av, bhi[j], acc);
-        acc = mfma32(av, blo[j], acc);
-      }
-      s[uu] = acc * qk_scale;
-    }
-    f32x4 p0, p1;
-    softmax_update(st, s[0], s[1], p0, p1);
+    const f32x4 &p0 = pg[2 * pr], &p1 = pg[2 * pr + 1];
     // per-token V scales (channel groups 0 and 1) of tokens 4qd..4qd+3
     const float *vsp = scl + 128 + 2 * (32 * pr + 4 * qd);
     const f32x4 va0 = *reinterpret_cast<const f32x4 *>(vsp);        // tokens 0,1 of b0
@@ -477,9 +574,15 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t,
 __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
                             int p, int seq_len, int wave, int lane, int tid) {
   const int n = lane & 15, qd = lane >> 4;
-  u32x4 qr[4];
-  load_q(qr, a, b, h, n, qd);
-  // the INT4 layout's k-slot order is applied to q' inside compute_group4
+  // the group's queries (fp16, zero rows past the group) stay in LDS and are
+  // re-read per channel chunk, which keeps them out of the register budget
+  {
+    const int hn = tid >> 4, c8 = tid & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (hn < a.group)
+      v = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
+    *reinterpret_cast<u32x4 *>(&sh.s.q[hn][8 * c8]) = v;
+  }
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -491,16 +594,23 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
     stage_ids(sh, bt, c0, c1, tid);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4 &t, int k) {
-      const int j0 = 4 * (wave + kWaves * k);
+    auto load = [&](Group4 &t, int k, bool live) {
+      const int j0 = live ? 4 * (wave + kWaves * k) : 0;
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
-      load_group4(t, a, ph, h, lane);
+      // a per-lane LDS read: selecting among ph[] per lane would become a
+      // private-array access, whose scratch load joins the in-order vmcnt
+      // queue and makes every group wait for all loads in flight
+      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
     };
     auto compute = [&](Group4 &t, int) {
-      compute_group4(st, t, qr, scl, a.qk_scale, lane, qd);
+      compute_group4(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
     };
-    pipeline<Group4>(cnt, load, compute);
+#if KVQ_INT4_DEPTH == 3
+    pipeline3<Group4>(cnt, load, compute);
+#else
+    pipeline<Group4>(cnt, [&](Group4 &t, int k) { load(t, k, true); }, compute);
+#endif
   }
 }
 
@@ -610,13 +720,13 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
 }
 
 template <int DT, int KS, int VS>
-__global__ __launch_bounds__(kThreads, 2) void kvq_paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, KVQ_WG_PER_CU) void kvq_paged_decode_kernel(DecodeArgs a) {
   __shared__ SharedLds sh;
   const int p = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seq_len = a.seq_lens[b];
   const bool direct = a.slots == 1;
 
@@ -637,15 +747,13 @@ __global__ __launch_bounds__(kThreads, 2) void kvq_paged_decode_kernel(DecodeArg
   Softmax st;
   softmax_init(st);
   if constexpr (DT == kInt4) {
+    // the fp16 residual tokens ride with the row's last partition, so a
+    // launch has no short extra workgroups to leave a ragged last round
     const int nq = kivi_quantized_len(seq_len, a.residual);
-    const int n_main = (nq / kBlock + a.part_blocks - 1) / a.part_blocks;
-    if (p == a.num_parts) {
-      if (seq_len <= nq) return;  // no residual tokens (cannot happen once S >= 1)
-      stream_ring(st, a, b, h, seq_len, wave, lane);
-    } else {
-      if (p >= n_main) return;
-      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
-    }
+    const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
+    if (p >= n_main) return;
+    stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+    if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
   } else {
     const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
     if (p >= n_main) return;
@@ -656,10 +764,12 @@ __global__ __launch_bounds__(kThreads, 2) void kvq_paged_decode_kernel(DecodeArg
 
 // Log-sum-exp merge of the partition partials of each (row, query head):
 // M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p, in
-// partition order.  A partition past the row's length (or a ring partition
-// of a row without residual tokens) wrote nothing and is skipped by index.
-// One thread per 4 channels: 32 threads per (row, query head).
+// partition order.  Partitions past the row's length wrote nothing and are
+// not read.  One thread per 4 channels, 32 threads per (row, query head);
+// partials are read eight at a time (clamped indices, zero weights past the
+// end) so their loads are in flight together.
 __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a, int is_int4) {
+  constexpr int kUnroll = 8;
   const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, hq) row
   const int c4 = threadIdx.x & 31;
   const int b = gid / a.num_q_heads;
@@ -670,28 +780,40 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
     *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  int n_main, has_ring = 0;
+  int total;
   if (is_int4) {
     const int nq = kivi_quantized_len(seq_len, a.residual);
-    n_main = (nq / kBlock + a.part_blocks - 1) / a.part_blocks;
-    has_ring = seq_len > nq ? 1 : 0;
+    total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
   } else {
-    n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
+    total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
   }
-  const int total = n_main + has_ring;
   const size_t base = (size_t)gid * a.slots;
   float big = kNegInf;
-  for (int pp = 0; pp < total; ++pp) {
-    const int slot = pp < n_main ? pp : a.num_parts;
-    big = fmaxf(big, a.ws_m[base + slot]);
+  for (int p0 = 0; p0 < total; p0 += kUnroll) {
+    float mv[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) mv[i] = a.ws_m[base + min(p0 + i, total - 1)];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) big = fmaxf(big, mv[i]);
   }
   float lt = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int pp = 0; pp < total; ++pp) {
-    const int slot = pp < n_main ? pp : a.num_parts;
-    const float w = __builtin_amdgcn_exp2f(a.ws_m[base + slot] - big);
-    lt += w * a.ws_l[base + slot];
-    acc += w * *reinterpret_cast<const f32x4 *>(a.ws_o + (base + slot) * kHeadDim + 4 * c4);
+  for (int p0 = 0; p0 < total; p0 += kUnroll) {
+    float mv[kUnroll], lv[kUnroll];
+    f32x4 ov[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const size_t slot = base + min(p0 + i, total - 1);
+      mv[i] = a.ws_m[slot];
+      lv[i] = a.ws_l[slot];
+      ov[i] = *reinterpret_cast<const f32x4 *>(a.ws_o + slot * kHeadDim + 4 * c4);
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const float w = p0 + i < total ? __builtin_amdgcn_exp2f(mv[i] - big) : 0.0f;
+      lt += w * lv[i];
+      acc += w * ov[i];
+    }
   }
   *reinterpret_cast<f32x4 *>(out) = acc * (1.0f / lt);
 }
@@ -734,8 +856,7 @@ int decode_scale_kind(int granularity) {
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind, int batch,
                          hipStream_t stream) {
-  const int parts = a.num_parts + (dtype == kInt4 ? 1 : 0);
-  const dim3 grid(parts, a.num_kv_heads, batch);
+  const dim3 grid(a.num_parts, a.num_kv_heads, batch);
   if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken>), grid,
                        dim3(kThreads), 0, stream, a);

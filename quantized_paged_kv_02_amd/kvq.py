@@ -67,12 +67,12 @@ class KvqError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m quantized_paged_kv_02_amd.build` (there is no fallback)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.kvq_status_str.restype = ctypes.c_char_p
     lib.kvq_status_str.argtypes = [I32]
