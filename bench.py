@@ -20,7 +20,6 @@ workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -34,22 +33,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from quantized_paged_kv_02_amd import inputs, metrics  # noqa: E402
+from quantized_paged_kv_02_amd.profile_summary import kernel_source_hash  # noqa: E402
 
 METRIC = ("quantized paged-decode KV read GB/s (% of HBM peak) + decode tokens/s, 1 GPU")
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 DEFAULT_WORKLOAD = "llama2-7b"
-DECODE_KERNEL = "kvq_paged_decode_kernel"
+DECODE_KERNEL = ("kvq_paged_decode launch: kvq_paged_decode_kernel + "
+                 "kvq_partition_reduce_kernel (the reduce is skipped when one partition "
+                 "covers every row)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "quantized_paged_kv_02_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h")]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -109,34 +101,39 @@ def _cpu_unit(args):
         return time.perf_counter() - t0
 
 
-def cpu_baseline(w, lens, workers: int, units_per_worker: int = 2):
+def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
     """Time the oracle over a bounded sample of (layer, row) units on
-    ``workers`` host processes (one BLAS thread each)."""
+    ``workers`` host processes (one BLAS thread each): one unit per process
+    first, then as many more as fit in about ``target_cpu_s`` seconds of
+    CPU work (never more than the whole step)."""
     import concurrent.futures as cf
     import multiprocessing as mp
     all_units = [(w.name, layer, row, int(lens[row]))
                  for layer in range(w.layers) for row in range(w.batch)]
-    unit_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [int(max(lens))],
-                                      w.num_q_heads, w.num_kv_heads, w.residual_len)
-    if unit_bytes > (64 << 20):       # long rows: one unit per process keeps it bounded
-        units_per_worker = 1
-    n = min(len(all_units), workers * units_per_worker)
-    units = all_units[:n]
     ctx = mp.get_context("spawn")
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
-        secs = list(ex.map(_cpu_unit, units))
+        first = all_units[:min(workers, len(all_units))]
+        secs = list(ex.map(_cpu_unit, first))
+        per_unit = sum(secs) / len(secs)
+        more = int(max(0.0, target_cpu_s - sum(secs)) / max(per_unit, 1e-6))
+        rest = all_units[len(first):len(first) + more]
+        if rest:
+            secs += list(ex.map(_cpu_unit, rest))
+    units = all_units[:len(secs)]
+    n = len(units)
+    cores = min(workers, n)
     sample_bytes = sum(metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [u[3]],
                                             w.num_q_heads, w.num_kv_heads, w.residual_len)
                        for u in units)
-    # units ran concurrently on `workers` processes
-    wall = sum(secs) / min(workers, n)
+    # units ran concurrently on `cores` processes
+    wall = sum(secs) / cores
     gbs = sample_bytes / wall / 1e9
-    step_s = sum(secs) / n * w.layers * w.batch / min(workers, n)
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": min(workers, n), "kind": "oracle",
+    step_s = sum(secs) / n * w.layers * w.batch / cores
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "tokens_per_s": round(w.batch / step_s, 4),
             "sample": (f"{n} of {len(all_units)} (layer, row) units of {w.name}; each: "
                        f"quantize the new token, dequantize the row's cache, fp64 attention "
-                       f"(numpy oracle, 1 BLAS thread per process, {min(workers, n)} processes); "
+                       f"(numpy oracle, 1 BLAS thread per process, {cores} processes); "
                        f"{sum(secs):.1f} s of CPU work; K/V drawn on the CPU by the same "
                        f"recipe")}
 

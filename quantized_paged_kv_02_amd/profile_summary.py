@@ -1,0 +1,146 @@
+"""Summaries of rocprofv3 output for the decode kernels (host tooling).
+
+Two commands:
+
+  python -m quantized_paged_kv_02_amd.profile_summary stats <dir> --command CMD --out FILE
+      Kernel durations from a ``rocprofv3 --kernel-trace --stats
+      --output-format csv`` run (the ``*_kernel_trace.csv`` under <dir>):
+      calls, mean, median, min and max per kernel, written as markdown.
+
+  python -m quantized_paged_kv_02_amd.profile_summary traffic <fetch_dir> <write_dir>
+        --workload NAME --command-fetch CMD --command-write CMD --out FILE
+      HBM bytes per decode launch from two ``rocprofv3 --pmc FETCH_SIZE``
+      and ``--pmc WRITE_SIZE`` runs of ``bench.py --copy-probe-mib M``.
+      Both counters are in KiB; each is scaled by what it reads for the
+      plain device copy of known size in the same run (copyBuffer
+      dispatches of the probe's grid), so the figure is in bytes.  The
+      decode launch is the decode kernel plus the partition reduce kernel.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_paged_kv_02_amd", "csrc", f)
+                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h")]
+
+
+def kernel_source_hash() -> str:
+    """Hash of the decode kernel sources; traffic figures are valid only for
+    the sources they were measured on."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(directory: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def stats(directory: str, command: str, out: str) -> None:
+    rows = list(csv.DictReader(open(_find(directory, "kernel_trace.csv"))))
+    per = {}
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per.setdefault(r["Kernel_Name"], []).append(d)
+    lines = ["# rocprofv3 kernel trace summary", "",
+             f"Command: `{command}`", "",
+             "Durations in microseconds (per dispatch).", "",
+             "| kernel | calls | mean | median | min | max | total ms |",
+             "|---|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{_short(name)}` | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{sum(v) / 1000:.3f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def _counter(directory: str, counter: str):
+    rows = list(csv.DictReader(open(_find(directory, "counter_collection.csv"))))
+    return [r for r in rows if r["Counter_Name"] == counter]
+
+
+def _per_launch(rows, copy_bytes_kib: float):
+    # calibration: the largest copyBuffer dispatches are the probe copies
+    copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    probe = max(copies)
+    probe_rows = [c for c in copies if c > 0.9 * probe]
+    factor = copy_bytes_kib / statistics.median(probe_rows)
+    dec = [float(r["Counter_Value"]) for r in rows if "paged_decode" in r["Kernel_Name"]]
+    red = [float(r["Counter_Value"]) for r in rows if "partition_reduce" in r["Kernel_Name"]]
+    kib = statistics.median(dec) + (statistics.median(red) if red else 0.0)
+    return kib * 1024 * factor, factor, len(dec)
+
+
+def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fetch: str,
+            cmd_write: str, out: str) -> None:
+    copy_kib = copy_mib * 1024.0
+    rd, rf, n_rd = _per_launch(_counter(fetch_dir, "FETCH_SIZE"), copy_kib)
+    wr, wf, n_wr = _per_launch(_counter(write_dir, "WRITE_SIZE"), copy_kib)
+    data = {}
+    if os.path.exists(out):
+        data = json.load(open(out))
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        data = {}
+    data["kernel_source_hash"] = kernel_source_hash()
+    data["note"] = ("HBM bytes per kvq_paged_decode launch (decode kernel + partition reduce), "
+                    "median over dispatches; FETCH_SIZE and WRITE_SIZE (KiB) scaled by what "
+                    "they read for a device copy of known size in the same run")
+    data[workload] = {
+        "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
+        "fetch_scale": round(rf, 4), "write_scale": round(wf, 4),
+        "dispatches": [n_rd, n_wr], "command_fetch": cmd_fetch, "command_write": cmd_write,
+    }
+    with open(out, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(f"wrote {out}: {workload} read {rd / 1e6:.2f} MB write {wr / 1e6:.2f} MB per launch "
+          f"(scales {rf:.3f} / {wf:.3f})")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        stats(a.dir, a.command, a.out)
+    else:
+        traffic(a.fetch_dir, a.write_dir, a.workload, a.copy_mib, a.command_fetch,
+                a.command_write, a.out)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
