@@ -356,12 +356,15 @@ def kivi_dequantize(kv, group=KIVI_GROUP):
     """K_hat, V_hat [S, Hkv, D] fp64 from :func:`kivi_quantize` output: INT4
     tokens as code * scale, residual tokens as their fp16 values."""
     nq = kv["nq"]
-    kc = kv["k_codes"].astype(np.float64)
-    ks = np.repeat(kv["k_scales"].astype(np.float64), group, axis=0)
-    k_hat_q = kc * ks
-    vc = kv["v_codes"].astype(np.float64)
-    vs = np.repeat(kv["v_scales"].astype(np.float64), group, axis=2)
-    v_hat_q = vc * vs
+    hkv, d = kv["k_codes"].shape[1], kv["k_codes"].shape[2]
+    # K: token t of group t // group uses that group's per-channel scales
+    kc = kv["k_codes"].astype(np.float64).reshape(nq // group, group, hkv, d)
+    ks = kv["k_scales"].astype(np.float64)[:, None, :, :]
+    k_hat_q = (kc * ks).reshape(nq, hkv, d)
+    # V: channel c of a token uses the token's scale of channel group c // group
+    vc = kv["v_codes"].astype(np.float64).reshape(nq, hkv, d // group, group)
+    vs = kv["v_scales"].astype(np.float64)[..., None]
+    v_hat_q = (vc * vs).reshape(nq, hkv, d)
     k_hat = np.concatenate([k_hat_q, kv["k_resid"].astype(np.float64)], axis=0)
     v_hat = np.concatenate([v_hat_q, kv["v_resid"].astype(np.float64)], axis=0)
     assert k_hat.shape[0] == nq + kv["k_resid"].shape[0]
