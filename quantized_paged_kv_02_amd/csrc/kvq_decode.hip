@@ -61,11 +61,25 @@ namespace {
 #ifndef KVQ_WG_PER_CU
 #define KVQ_WG_PER_CU 2
 #endif
+#ifndef KVQ_BRANCHLESS_RESCALE
+#define KVQ_BRANCHLESS_RESCALE 0
+#endif
+// INT4 values: convert nibbles without removing the fp16 exponent bias and
+// cancel the bias with one extra matrix-core product per channel tile and
+// block pair (moves work from the vector ALUs to the matrix cores).
+#ifndef KVQ_INT4_VBIAS
+#define KVQ_INT4_VBIAS 1
+#endif
 
 constexpr int kWaves = 4;
 constexpr int kQRow = 128 + 8;  // LDS row of a staged query (fp16)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kIdChunk = 256;  // block ids staged in LDS per pass
+// Block ids staged in LDS per pass (a small first pass lets streaming start
+// sooner; measured better than staging whole partitions at once).
+#ifndef KVQ_ID_CHUNK
+#define KVQ_ID_CHUNK 256
+#endif
+constexpr int kIdChunk = KVQ_ID_CHUNK;
 constexpr float kNegInf = -__builtin_inff();
 // The running max is only moved when a score exceeds it by more than this
 // (log2 units), so p <= 2^8 and rescaling of o is rare.
@@ -138,6 +152,19 @@ __device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4]
   for (int u = 0; u < 4; ++u)
     bm = fmaxf(bm, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
   bm = max_over_quads(bm);
+#if KVQ_BRANCHLESS_RESCALE
+  {
+    // one straight-line block per group: always rescale (alpha = 1 when the
+    // max did not move by more than the slack)
+    const bool need = bm > st.m + kRescaleSlack;
+    const float mn = need ? bm : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
+    st.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    st.m = mn;
+  }
+#else
   const bool need = bm > st.m + kRescaleSlack;
   if (__any(need)) {
     const float mn = need ? bm : st.m;
@@ -147,6 +174,7 @@ __device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4]
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
     st.m = mn;
   }
+#endif
   float sum = 0.0f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -510,6 +538,16 @@ __device__ __forceinline__ f16x8 int4x8_to_f16(uint32_t x) {
   return pairs_to_f16x8(pr);
 }
 
+// 8 nibbles -> 8 fp16 still carrying the exponent bias of the
+// bitwise-select trick: k-slots 0,1,4,5 hold 1032 + code, k-slots 2,3,6,7
+// hold 1152 + 16 code (nibbles in the upper half of a byte).  Exact.
+[[maybe_unused]] __device__ __forceinline__ f16x8 int4x8_to_f16_biased(uint32_t x) {
+  const uint32_t y = x >> 8;
+  const uint32_t r[4] = {bsel(x, 0x000F000Fu, 0x64086408u), bsel(x, 0x00F000F0u, 0x64806480u),
+                         bsel(y, 0x000F000Fu, 0x64086408u), bsel(y, 0x00F000F0u, 0x64806480u)};
+  return pairs_to_f16x8(r);
+}
+
 // k-slot order produced by int4x8_to_f16 (nibble index of slot e)
 __device__ __forceinline__ int int4_kslot(int e) { return (e >> 1) + 4 * (e & 1); }
 
@@ -518,7 +556,14 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
                                                int qd) {
   // stage the group's scales in this wave's LDS slot (in-order within a wave)
   *reinterpret_cast<float2 *>(scl + 2 * lane) = float2{t.ks[0], t.ks[1]};
+#if KVQ_INT4_VBIAS
+  // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code:
+  // their weights carry 1/16 (exact)
+  const float vsf = (lane & 2) ? 0.0625f : 1.0f;
+  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0] * vsf, t.vs[1] * vsf};
+#else
   *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0], t.vs[1]};
+#endif
   // Scores, channel chunk by chunk: q' = q * s_c for channels 32qd+8j..+7
   // as fp16 hi + lo in the k-slot order of the nibble conversion, applied
   // to the chunk of all four blocks.
@@ -539,12 +584,16 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
       split_hi_lo(x0, x1, hi[e2], lo[e2]);
     }
     const f16x8 bhi = pairs_to_f16x8(hi), blo = pairs_to_f16x8(lo);
+    // all hi products, then all lo products: an accumulator's two updates
+    // are four matrix instructions apart
+    f16x8 av[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const f16x8 av = int4x8_to_f16(t.k[u][j]);
-      acc[u] = mfma32(av, bhi, acc[u]);
-      acc[u] = mfma32(av, blo, acc[u]);
+      av[u] = int4x8_to_f16(t.k[u][j]);
+      acc[u] = mfma32(av[u], bhi, acc[u]);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = mfma32(av[u], blo, acc[u]);
   }
   f32x4 pg[4];
 #pragma unroll
@@ -563,11 +612,27 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     const f32x4 g0b = {vb0[0], vb0[2], vb1[0], vb1[2]}, g1b = {vb0[1], vb0[3], vb1[1], vb1[3]};
     const f16x8 pb0 = p_operand(p0 * g0a, p1 * g0b);
     const f16x8 pb1 = p_operand(p0 * g1a, p1 * g1b);
+#if KVQ_INT4_VBIAS
+    // every row of the bias operand is the per-k-slot bias of the biased
+    // conversion (1032 for slots 0,1,4,5; 1152 for 2,3,6,7), negated
+    const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
+    const f16x8 abias = {b0, b0, b1, b1, b0, b0, b1, b1};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = pair_tile(t.v[2 * pr][j >> 1], t.v[2 * pr + 1][j >> 1], j & 1);
+      st.o[j] = mfma32(int4x8_to_f16_biased(w), j < 4 ? pb0 : pb1, st.o[j]);
+    }
+    // bias cancellation after all eight tiles (each o[j] update is eight
+    // matrix instructions after the previous one)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
+#else
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w = pair_tile(t.v[2 * pr][j >> 1], t.v[2 * pr + 1][j >> 1], j & 1);
       st.o[j] = mfma32(int4x8_to_f16(w), j < 4 ? pb0 : pb1, st.o[j]);
     }
+#endif
   }
 }
 
