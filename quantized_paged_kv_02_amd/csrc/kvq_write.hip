@@ -124,16 +124,22 @@ __device__ __forceinline__ int kivi_len(int s, int residual) {
   return kivi_quantized_len(s, residual);
 }
 
-// Gather one token's 128 fp16 values of K and V for the flush: from the ring
-// when the token was already cached, else from the call's new tokens.
-__global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
-  __shared__ f16 kx[kGroup][kHeadDim];
-  __shared__ f16 vx[kGroup][kHeadDim];
-  __shared__ float ksc[kHeadDim];
-  __shared__ float vsc[kGroup][2];
+// Flush of one 64-token group leaving the fp16 window, for one (row, KV
+// head) and one of K or V: 256 threads.  The group's fp16 values are
+// gathered into LDS (from the ring for tokens already cached, else from the
+// call's new tokens), the scales are reduced across threads, and every
+// thread then quantizes exactly the 32 nibbles of one 16-byte unit of the
+// block layout and writes it with one store.
+constexpr int kFlushRow = kHeadDim + 8;  // padded LDS row (fp16)
+
+__device__ void int4_flush(const WriteArgs &a, int bx) {
+  __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
+  __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
+  __shared__ float sc[kHeadDim];        // K: [128] channel scales; V: [64][2] token scales
   __shared__ int phys_s[4];
 
-  const int gs = blockIdx.x;
+  const int gs = bx >> 1;
+  const bool is_v = (bx & 1) != 0;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -148,104 +154,146 @@ __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
   if (t0 >= nq_new) return;
 
   const size_t ring_row = (size_t)b * H + h;
-  // gather: 64 tokens x 64 channel pairs = 4096 pairs, 16 per thread
-  for (int e = tid; e < kGroup * (kHeadDim / 2); e += 256) {
-    const int tt = e >> 6;
-    const int c = (e & 63) * 2;
-    const int t = t0 + tt;
-    uint32_t kp, vp;
-    if (t < s_old) {
-      const int slot = t % a.ring;
-      kp = *reinterpret_cast<const uint32_t *>(
-          a.k_resid + (ring_row * a.ring + slot) * kHeadDim + c);
-      const uint16_t *vb = a.v_resid +
-                           ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim + c) * 4 +
-                           (slot & 3);
-      vp = (uint32_t)vb[0] | ((uint32_t)vb[4] << 16);
-    } else {
-      const size_t src = ((size_t)(c_begin + t - s_old) * H + h) * kHeadDim + c;
-      kp = *reinterpret_cast<const uint32_t *>(a.k_new + src);
-      vp = *reinterpret_cast<const uint32_t *>(a.v_new + src);
+  const uint16_t *fresh = is_v ? a.v_new : a.k_new;
+  if (!is_v) {
+    // K: 16-byte units (token, 8 channels); ring rows are contiguous
+    for (int e = tid; e < kGroup * 16; e += 256) {
+      const int tt = e >> 4, c8 = (e & 15) * 8;
+      const int t = t0 + tt;
+      const uint16_t *src =
+          t < s_old ? a.k_resid + (ring_row * a.ring + t % a.ring) * kHeadDim + c8
+                    : fresh + ((size_t)(c_begin + t - s_old) * H + h) * kHeadDim + c8;
+      *reinterpret_cast<u32x4 *>(&x[tt][c8]) = ld16(src);
     }
-    *reinterpret_cast<uint32_t *>(&kx[tt][c]) = kp;
-    *reinterpret_cast<uint32_t *>(&vx[tt][c]) = vp;
+  } else {
+    // V: the ring is token-minor in quads ([slot/4][channel][slot%4]); a
+    // 16-byte unit is 2 channels x 4 tokens of one quad
+    for (int e = tid; e < (kGroup / 4) * (kHeadDim / 2); e += 256) {
+      const int q = e >> 6, cp = e & 63;
+      const int tq = t0 + 4 * q;
+      if (tq + 3 < s_old) {
+        const int slot = tq % a.ring;  // multiple of 4: the quad is contiguous
+        const u32x4 w = ld16(a.v_resid + ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim +
+                                          2 * cp) * 4);
+        // w = [c0 t0..t3][c1 t0..t3] as fp16 pairs
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+          const uint32_t hi = (i & 1) ? (w[2 + (i >> 1)] >> 16) : (w[2 + (i >> 1)] & 0xFFFFu);
+          *reinterpret_cast<uint32_t *>(&x[4 * q + i][2 * cp]) = lo | (hi << 16);
+        }
+      } else {
+        for (int i = 0; i < 4; ++i) {
+          const int t = tq + i;
+          uint32_t pr;
+          if (t < s_old) {
+            const int slot = t % a.ring;
+            const uint16_t *vb = a.v_resid +
+                                 ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim + 2 * cp) * 4 +
+                                 (slot & 3);
+            pr = (uint32_t)vb[0] | ((uint32_t)vb[4] << 16);
+          } else {
+            pr = *reinterpret_cast<const uint32_t *>(
+                fresh + ((size_t)(c_begin + t - s_old) * H + h) * kHeadDim + 2 * cp);
+          }
+          *reinterpret_cast<uint32_t *>(&x[4 * q + i][2 * cp]) = pr;
+        }
+      }
+    }
   }
   if (tid < 4) {
     phys_s[tid] = a.block_tables[(size_t)b * a.max_blocks_per_seq + t0 / kBlock + tid];
   }
   __syncthreads();
 
-  if (tid < kHeadDim) {
-    // K: per-channel scale over the group's 64 tokens
-    float amax = 0.0f;
-    for (int tt = 0; tt < kGroup; ++tt) amax = fmaxf(amax, fabsf((float)kx[tt][tid]));
-    ksc[tid] = amax / 7.0f;
-  } else {
-    // V: per-token scale over each 64-channel group
-    const int tt = (tid - kHeadDim) >> 1;
-    const int grp = tid & 1;
-    float amax = 0.0f;
-    for (int c = 0; c < kGroup; ++c) amax = fmaxf(amax, fabsf((float)vx[tt][grp * kGroup + c]));
-    vsc[tt][grp] = amax / 7.0f;
-  }
-  __syncthreads();
-
-  // scales to the pool
-  if (tid < kHeadDim) {
-    const int ub = tid >> 5;  // block of the group that holds this channel's scale
-    a.k_scales[((size_t)phys_s[ub] * H + h) * 32 + (tid & 31)] = ksc[tid];
-  } else {
-    const int tt = (tid - kHeadDim) >> 1;
-    const int grp = tid & 1;
-    a.v_scales[(((size_t)phys_s[tt >> 4] * H + h) * kBlock + (tt & 15)) * 2 + grp] =
-        vsc[tt][grp];
-  }
-
-  // K codes: 1024 dwords, 8 channels of one token each
-  for (int di = tid; di < 1024; di += 256) {
-    const int tt = di >> 4;
-    const int d0 = (di & 15) * 8;
-    uint32_t word = 0;
+  if (!is_v) {
+    // K scales: max over the group's 64 tokens of |K[:, c]| / 7
+    {
+      const int cp = tid & 63, qq = tid >> 6;
+      float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const f16x2 v = *reinterpret_cast<const f16x2 *>(&x[16 * qq + i][2 * cp]);
+        m0 = fmaxf(m0, fabsf((float)v.x));
+        m1 = fmaxf(m1, fabsf((float)v.y));
+      }
+      part[qq][2 * cp] = m0;
+      part[qq][2 * cp + 1] = m1;
+    }
+    __syncthreads();
+    if (tid < kHeadDim) {
+      const float amax = fmaxf(fmaxf(part[0][tid], part[1][tid]), fmaxf(part[2][tid], part[3][tid]));
+      sc[tid] = amax / 7.0f;
+      a.k_scales[((size_t)phys_s[tid >> 5] * H + h) * 32 + (tid & 31)] = amax / 7.0f;
+    }
+    __syncthreads();
+    // one unit: channels 32cb .. 32cb+31 of token tt, nibble e of dword d is
+    // channel 32cb + 8d + e
+    const int tt = tid >> 2, cb = tid & 3;
+    u32x4 out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t q = quant_int((float)kx[tt][d0 + e], ksc[d0 + e], -8.0f, 7.0f) & 0xFu;
-      word |= q << (4 * e);
+    for (int d = 0; d < 4; ++d) {
+      const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t q = quant_int((float)v[e], sc[32 * cb + 8 * d + e], -8.0f, 7.0f) & 0xFu;
+        word |= q << (4 * e);
+      }
+      out[d] = word;
     }
     uint8_t *chunk = a.k_codes + ((size_t)phys_s[tt >> 4] * H + h) * 1024;
-    *reinterpret_cast<uint32_t *>(chunk + 256 * (d0 >> 5) + 16 * (tt & 15) +
-                                  ((d0 & 31) >> 1)) = word;
-  }
-  // V codes: per block 64 units x 4 dwords; a dword holds channels
-  // A = 32w + m and B = 32w + 16 + m for the unit's four tokens.
-  for (int di = tid; di < 1024; di += 256) {
-    const int ub = di >> 8;          // block within the group
-    const int u = (di >> 2) & 63;    // 16-byte unit
-    const int w = di & 3;            // dword within the unit
-    const int m = u & 15;
-    const int qd = u >> 4;
-    const int ca = 32 * w + m;
-    const int cb = ca + 16;
-    uint32_t word = 0;
+    *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
+  } else {
+    // V scales: per token, max over each 64-channel half of |V| / 7
+    {
+      const int tt = tid >> 2, qq = tid & 3;
+      float m = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * qq + 8 * d]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      if ((qq & 1) == 0) {
+        const float s = m / 7.0f;
+        sc[2 * tt + (qq >> 1)] = s;
+        a.v_scales[(((size_t)phys_s[tt >> 4] * H + h) * kBlock + (tt & 15)) * 2 + (qq >> 1)] = s;
+      }
+    }
+    __syncthreads();
+    // one unit u of block ub: channels 16j + m (j = 0..7) of the quad's four
+    // tokens; dword w holds tiles 2w and 2w+1, token e of tile j at nibble
+    // 2(j&1) + (e>>1) + 4(e&1)
+    const int ub = tid >> 6, u = tid & 63;
+    const int m = u & 15, quad = u >> 4;
+    u32x4 out = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int tt = ub * kBlock + 4 * qd + e;
-      const uint32_t qa = quant_int((float)vx[tt][ca], vsc[tt][ca >> 6], -8.0f, 7.0f) & 0xFu;
-      const uint32_t qb = quant_int((float)vx[tt][cb], vsc[tt][cb >> 6], -8.0f, 7.0f) & 0xFu;
-      const int pa = (e >> 1) + 4 * (e & 1);
-      word |= qa << (4 * pa);
-      word |= qb << (4 * (pa + 2));
+      const int tt = 16 * ub + 4 * quad + e;
+      const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = 16 * j + m;
+        const uint32_t q =
+            quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
+        const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
+        out[j >> 1] |= q << (4 * p);
+      }
     }
     uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * 1024;
-    *reinterpret_cast<uint32_t *>(chunk + 16 * u + 4 * w) = word;
+    *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;
   }
 }
 
+__global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
+  int4_flush(a, blockIdx.x);
+}
+
 // Append the new tokens that stay fp16 to the ring.
-__global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
-  const int i = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x;
+// Store new token i of row b, head h in the fp16 ring (first wave of the
+// workgroup) unless it is already part of a quantized group.
+__device__ __forceinline__ void append_token(const WriteArgs &a, int i, int h, int b, int lane) {
   const int H = a.num_kv_heads;
   const int c_begin = a.cu_new[b];
   const int n_new = a.cu_new[b + 1] - c_begin;
@@ -266,6 +314,22 @@ __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
   vb[4] = (uint16_t)(vp >> 16);
 }
 
+__global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
+  append_token(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+}
+
+// Flush and append in one launch: workgroups x < 2*groups flush, the rest
+// append.  Only for calls that add at most one token per row: the appended
+// token is then fewer than R + G positions after any token the flush reads
+// from the ring, so its ring slot is never one of them.
+__global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a, int groups) {
+  if ((int)blockIdx.x < 2 * groups) {
+    int4_flush(a, blockIdx.x);
+  } else if (threadIdx.x < 64) {
+    append_token(a, blockIdx.x - 2 * groups, blockIdx.y, blockIdx.z, threadIdx.x);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new,
@@ -281,8 +345,14 @@ hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new
 
 hipError_t launch_write_int4(const WriteArgs &a, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream) {
+  if (max_new == 1 && max_flush_groups > 0) {
+    hipLaunchKernelGGL(kvq_int4_flush_append_kernel,
+                       dim3(2 * max_flush_groups + 1, a.num_kv_heads, batch), dim3(256), 0,
+                       stream, a, max_flush_groups);
+    return hipGetLastError();
+  }
   if (max_flush_groups > 0) {
-    hipLaunchKernelGGL(kvq_int4_flush_kernel, dim3(max_flush_groups, a.num_kv_heads, batch),
+    hipLaunchKernelGGL(kvq_int4_flush_kernel, dim3(2 * max_flush_groups, a.num_kv_heads, batch),
                        dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
