@@ -73,6 +73,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kQRow = 128 + 8;  // LDS row of a staged query (fp16)
+constexpr int kQbRow = 64 + 4;  // LDS row of q' (dwords of fp16 pairs)
 constexpr int kThreads = 64 * kWaves;
 // Block ids staged in LDS per pass (a small first pass lets streaming start
 // sooner; measured better than staging whole partitions at once).
@@ -99,6 +100,10 @@ struct StreamLds {
   // INT4: the group's queries, zero past the group; rows padded by 16 bytes
   // so the 16 head rows of one read start in different banks
   f16 q[16][kQRow];
+  // INT4 with a query group of at most 4: per wave, q' = q * s_c of the
+  // four heads as fp16 hi and lo rows (channels in the k-slot order of the
+  // nibble conversion) and a zero row for the padding columns
+  uint32_t qb[kWaves][2][5][kQbRow];
 };
 // o rows padded by 4 floats so the 16 head rows of one store or load fall
 // in different banks
@@ -494,7 +499,7 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
 struct Group4 {
   u32x4 k[4];   // block u: nibbles of channels 32qd..32qd+31, token l%16
   u32x4 v[4];   // block u: nibbles of 4 tokens x 8 channel tiles
-  float ks[2];  // K scales of channels 2l, 2l+1 (held by block l/16)
+  float ks[2];  // K scales of channels 8(l/4) + l%4 and + 4 (block l/16)
   float vs[2];  // V scales (channel groups 0, 1) of token l of the group
   __device__ explicit Group4(int = 0) {}
 };
@@ -515,11 +520,13 @@ __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, cons
     t.v[u] = bld16(make_rsrc(a.v_codes + chunk * 1024, bytes), 16 * lane);
   }
   const size_t chunk = (size_t)pm * H + h;
-  const float2 ks = *reinterpret_cast<const float2 *>(a.k_scales + chunk * 32 + 2 * (lane & 15));
+  // channels 8(lane/4) + lane%4 and that + 4 (positions 2(lane%4), +1 of
+  // k-slot chunk lane/4), held by block lane/16 of the group
+  const float *ksp = a.k_scales + chunk * 32 + 8 * ((lane >> 2) & 3) + (lane & 3);
   const float2 vs =
       *reinterpret_cast<const float2 *>(a.v_scales + (chunk * kBlock + (lane & 15)) * 2);
-  t.ks[0] = ks.x;
-  t.ks[1] = ks.y;
+  t.ks[0] = ksp[0];
+  t.ks[1] = ksp[4];
   t.vs[0] = vs.x;
   t.vs[1] = vs.y;
 }
@@ -555,7 +562,11 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
                                                float *scl, float qk_scale, int lane, int n,
                                                int qd) {
   // stage the group's scales in this wave's LDS slot (in-order within a wave)
-  *reinterpret_cast<float2 *>(scl + 2 * lane) = float2{t.ks[0], t.ks[1]};
+  {
+    const int c0 = 8 * (lane >> 2) + (lane & 3);
+    scl[c0] = t.ks[0];
+    scl[c0 + 4] = t.ks[1];
+  }
 #if KVQ_INT4_VBIAS
   // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code:
   // their weights carry 1/16 (exact)
@@ -679,6 +690,191 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// INT4 with a query group of at most 4: compact score layout.  The score
+// product fills only four of its sixteen columns, so after it the four
+// blocks' score tiles are packed into one: lane (n, qd) then holds tokens
+// 4qd..4qd+3 of block n/4 for head n%4, and the softmax runs on four values
+// per lane instead of sixteen.  q' = q * s_c is formed once per lane for two
+// channels of the four heads and shared through LDS.
+// ---------------------------------------------------------------------------
+
+// Scores of four blocks (one per register set) packed into the compact layout.
+__device__ __forceinline__ f32x4 pack_scores(const f32x4 (&acc)[4]) {
+  f32x4 s = acc[0];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = dpp_f32<kRowShr + 4, 0x2>(s[i], acc[1][i]);
+    s[i] = dpp_f32<kRowShr + 8, 0x4>(s[i], acc[2][i]);
+    s[i] = dpp_f32<kRowShr + 12, 0x8>(s[i], acc[3][i]);
+  }
+  return s;
+}
+
+// Online softmax on compact scores.  The running max moves only when some
+// score exceeds it by more than the slack; only then is the head-wide max
+// taken (over the four banks and the four row groups).
+__device__ __forceinline__ void softmax_update_c(Softmax &st, const f32x4 &s, f32x4 &p) {
+  const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  if (__any(lm > st.m + kRescaleSlack)) {
+    const float bm = max_over_quads(bank_max(lm));
+    const bool need = bm > st.m + kRescaleSlack;
+    const float mn = need ? bm : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
+    st.l *= alpha;
+    // o column n belongs to head n; for n < 4 that is this lane's head
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    st.m = mn;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - st.m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
+}
+
+// P^T operand of block pair pr (blocks 2pr, 2pr+1) for lanes n < 4 from
+// the compact p dwords d[0] (tokens 0,1) and d[1] (tokens 2,3).
+template <int PR>
+__device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
+  const u32x4 w = {dpp_u32<kRowShl + 8 * PR>(0u, d[0]), dpp_u32<kRowShl + 8 * PR>(0u, d[1]),
+                   dpp_u32<kRowShl + 8 * PR + 4>(0u, d[0]),
+                   dpp_u32<kRowShl + 8 * PR + 4>(0u, d[1])};
+  return u4_to_f16x8(w);
+}
+
+template <int PR>
+__device__ __forceinline__ void value_pair_c(Softmax &st, const Group4 &t, const f16x8 &pb0,
+                                             const f16x8 &pb1) {
+#if KVQ_INT4_VBIAS
+  const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
+  const f16x8 abias = {b0, b0, b1, b1, b0, b0, b1, b1};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = pair_tile(t.v[2 * PR][j >> 1], t.v[2 * PR + 1][j >> 1], j & 1);
+    st.o[j] = mfma32(int4x8_to_f16_biased(w), j < 4 ? pb0 : pb1, st.o[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
+#else
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = pair_tile(t.v[2 * PR][j >> 1], t.v[2 * PR + 1][j >> 1], j & 1);
+    st.o[j] = mfma32(int4x8_to_f16(w), j < 4 ? pb0 : pb1, st.o[j]);
+  }
+#endif
+}
+
+// qv[hh]: this lane's query values of head hh at channels c0 = 8(lane/4) +
+// lane%4 and c0 + 4; qb: this wave's q' rows; qrd: dword offset of this
+// lane's operand row (head n, or the zero row) and row group.
+__device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
+                                                const float (&qv)[4][2], uint32_t *qb, int qrd,
+                                                float *scl, float qk_scale, int lane, int n,
+                                                int qd) {
+#if KVQ_INT4_VBIAS
+  const float vsf = (lane & 2) ? 0.0625f : 1.0f;
+#else
+  const float vsf = 1.0f;
+#endif
+  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0] * vsf, t.vs[1] * vsf};
+  // q' of this lane's two channels for the four heads (dword `lane` of each row)
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    uint32_t hi, lo;
+    split_hi_lo(qv[hh][0] * t.ks[0], qv[hh][1] * t.ks[1], hi, lo);
+    qb[hh * kQbRow + lane] = hi;
+    qb[(5 + hh) * kQbRow + lane] = lo;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x8 bhi = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qrd + 4 * j));
+    const f16x8 blo = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + 5 * kQbRow + qrd + 4 * j));
+    f16x8 av[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = int4x8_to_f16(t.k[u][j]);
+      acc[u] = mfma32(av[u], bhi, acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = mfma32(av[u], blo, acc[u]);
+  }
+  f32x4 s = pack_scores(acc);
+  s *= qk_scale;
+  f32x4 p;
+  softmax_update_c(st, s, p);
+  // V scales of this lane's tokens 4qd..4qd+3 of block n/4 (channel groups 0, 1)
+  const float *vsp = scl + 128 + 2 * (16 * (n >> 2) + 4 * qd);
+  const f32x4 va0 = *reinterpret_cast<const f32x4 *>(vsp);
+  const f32x4 va1 = *reinterpret_cast<const f32x4 *>(vsp + 4);
+  const uint32_t d0[2] = {pack_rne(p[0] * va0[0], p[1] * va0[2]),
+                          pack_rne(p[2] * va1[0], p[3] * va1[2])};
+  const uint32_t d1[2] = {pack_rne(p[0] * va0[1], p[1] * va0[3]),
+                          pack_rne(p[2] * va1[1], p[3] * va1[3])};
+  value_pair_c<0>(st, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
+  value_pair_c<1>(st, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
+}
+
+__device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
+                             int p, int seq_len, int wave, int lane, int tid) {
+  const int n = lane & 15, qd = lane >> 4;
+  {
+    const int hn = tid >> 4, c8 = tid & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (hn < a.group)
+      v = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
+    *reinterpret_cast<u32x4 *>(&sh.s.q[hn][8 * c8]) = v;
+  }
+  uint32_t *qb = &sh.s.qb[wave][0][0][0];
+  qb[4 * kQbRow + lane] = 0u;
+  qb[9 * kQbRow + lane] = 0u;
+  __syncthreads();
+  float qv[4][2];
+  {
+    const int c0 = 8 * (lane >> 2) + (lane & 3);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      qv[hh][0] = (float)sh.s.q[hh][c0];
+      qv[hh][1] = (float)sh.s.q[hh][c0 + 4];
+    }
+  }
+  const int qrd = (n < 4 ? n : 4) * kQbRow + 16 * qd;
+  const int nq = kivi_quantized_len(seq_len, a.residual);
+  const int n_blocks = nq / kBlock;
+  const int blk0 = p * a.part_blocks;
+  const int blk1 = min(n_blocks, blk0 + a.part_blocks);
+  const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  float *scl = sh.s.scl[wave];
+  for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
+    const int c1 = min(blk1, c0 + kIdChunk);
+    stage_ids(sh, bt, c0, c1, tid);
+    const int ngroups = (c1 - c0) / 4;
+    const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    auto load = [&](Group4 &t, int k, bool live) {
+      const int j0 = live ? 4 * (wave + kWaves * k) : 0;
+      const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
+                         uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
+      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
+    };
+    auto compute = [&](Group4 &t, int) {
+      compute_group4c(st, t, qv, qb, qrd, scl, a.qk_scale, lane, n, qd);
+    };
+#if KVQ_INT4_DEPTH == 3
+    pipeline3<Group4>(cnt, load, compute);
+#else
+    pipeline<Group4>(cnt, [&](Group4 &t, int k) { load(t, k, true); }, compute);
+#endif
+  }
+  // back to one head per lane (n < 4): this lane's share of head n's sum
+  st.l = bank_sum(st.l);
+}
+
 // fp16 residual ring of an INT4 cache: tokens nq .. seq_len-1, two 16-token
 // tiles per step (wave w takes tile pairs w, w+4, ...).
 __device__ void stream_ring(Softmax &st, const DecodeArgs &a, int b, int h, int seq_len,
@@ -784,7 +980,8 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
   }
 }
 
-template <int DT, int KS, int VS>
+// G4: INT4 cache with a query group of at most 4 (compact score layout).
+template <int DT, int KS, int VS, bool G4 = false>
 __global__ __launch_bounds__(kThreads, KVQ_WG_PER_CU) void kvq_paged_decode_kernel(DecodeArgs a) {
   __shared__ SharedLds sh;
   const int p = blockIdx.x;
@@ -817,7 +1014,11 @@ __global__ __launch_bounds__(kThreads, KVQ_WG_PER_CU) void kvq_paged_decode_kern
     const int nq = kivi_quantized_len(seq_len, a.residual);
     const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
     if (p >= n_main) return;
-    stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+    if constexpr (G4) {
+      stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+    } else {
+      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+    }
     if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
   } else {
     const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
@@ -922,7 +1123,10 @@ int decode_scale_kind(int granularity) {
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind, int batch,
                          hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, batch);
-  if (dtype == kInt4) {
+  if (dtype == kInt4 && a.group <= 4) {
+    hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken, true>), grid,
+                       dim3(kThreads), 0, stream, a);
+  } else if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken>), grid,
                        dim3(kThreads), 0, stream, a);
   } else if (dtype == kFp8) {

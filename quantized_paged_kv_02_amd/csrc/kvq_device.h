@@ -113,6 +113,36 @@ __device__ __forceinline__ float sum_over_quads(float v) {
   return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
+// DPP moves within 16-lane rows.  Row shift left by k: lane i reads lane
+// i + k; right: lane i reads lane i - k; rotate right: lane i reads lane
+// (i - k) mod 16.  Lanes whose source falls outside the row read zero.
+// Bank b of a row is its lanes 4b .. 4b+3; lanes outside `bank_mask` keep
+// `old`.
+constexpr int kRowShl = 0x100, kRowShr = 0x110, kRowRor = 0x120;
+template <int Ctrl, int BankMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+  if constexpr ((Ctrl & 0xF) == 0) {
+    return src;  // shift by zero
+  } else {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, Ctrl, 0xF, BankMask, true);
+  }
+}
+template <int Ctrl, int BankMask = 0xF>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __builtin_bit_cast(
+      float, dpp_u32<Ctrl, BankMask>(__builtin_bit_cast(uint32_t, old), __builtin_bit_cast(uint32_t, src)));
+}
+// max / sum over the four banks of a row (lanes i, i^4, i^8, i^12 share the
+// result)
+__device__ __forceinline__ float bank_max(float v) {
+  v = fmaxf(v, dpp_f32<kRowRor + 4>(0.0f, v));
+  return fmaxf(v, dpp_f32<kRowRor + 8>(0.0f, v));
+}
+__device__ __forceinline__ float bank_sum(float v) {
+  v += dpp_f32<kRowRor + 4>(0.0f, v);
+  return v + dpp_f32<kRowRor + 8>(0.0f, v);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
