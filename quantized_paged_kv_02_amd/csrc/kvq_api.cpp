@@ -14,12 +14,10 @@ constexpr int kBlock = 16;
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 64;
 // Partition sizing: decode workgroups (four wavefronts) resident at once
-// on a 256-CU MI355X -- two per CU for INT4, three for INT8/FP8 (the
-// register budgets of the kernels) -- and the fixed cost of a workgroup
-// (first-load latency, LDS merge, partial store) in blocks of streaming.
+// on a 256-CU MI355X (kvq::decode_wg_per_cu per CU, the register budgets
+// of the kernels) and the fixed cost of a workgroup (first-load latency,
+// LDS merge, partial store) in blocks of streaming.
 constexpr long kCUs = 256;
-constexpr long kResidentInt4 = 2 * kCUs;
-constexpr long kResidentQ8 = 3 * kCUs;
 constexpr long kWgOverheadInt4 = 16;
 constexpr long kWgOverheadQ8 = 8;
 
@@ -92,7 +90,9 @@ Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
     // per workgroup + fixed cost): a launch whose last round is nearly
     // empty wastes a whole workgroup time.
     const long units = (long)batch * L->num_kv_heads;
-    const long resident = int4 ? kResidentInt4 : kResidentQ8;
+    const long resident =
+        kCUs * kvq::decode_wg_per_cu(L->dtype, kvq::decode_scale_kind(L->k_gran),
+                                     kvq::decode_scale_kind(L->v_gran));
     const long overhead = int4 ? kWgOverheadInt4 : kWgOverheadQ8;
     const long top = blocks > quantum ? blocks : quantum;
     long best_t = -1;

@@ -8,6 +8,19 @@
 
 namespace kvq {
 
+enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3 };  // kvq_dtype values
+// Granularity as the decode kernel sees it: a scale that is uniform over a
+// (row, KV head) (per-tensor or per-head), per channel, or per token.
+enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
+
+// Decode workgroups (four wavefronts) guaranteed resident per CU for a cache
+// dtype and K / V scale kinds: the kernel's register bound and the partition
+// plan's round size.  INT4 and FP8 with per-token V and non-uniform K scales
+// need the larger per-wave register budget of two per CU.
+constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
+  return dtype == kInt4 ? 2 : (dtype == kFp8 && v_kind == kToken && k_kind != kUniform) ? 2 : 3;
+}
+
 struct WriteArgs {
   uint8_t *k_codes;
   uint8_t *v_codes;

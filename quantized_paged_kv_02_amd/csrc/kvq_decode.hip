@@ -58,9 +58,6 @@ namespace {
 #ifndef KVQ_Q8_DEPTH
 #define KVQ_Q8_DEPTH 2
 #endif
-#ifndef KVQ_WG_PER_CU
-#define KVQ_WG_PER_CU 2
-#endif
 #ifndef KVQ_BRANCHLESS_RESCALE
 #define KVQ_BRANCHLESS_RESCALE 0
 #endif
@@ -230,11 +227,17 @@ __device__ __forceinline__ void split_hi_lo(float x0, float x1, uint32_t &hi, ui
 // so tile addresses are a scalar base plus one shared per-lane offset.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Stage physical block ids [c0, c1) of a row in LDS (whole workgroup).
+// Stage physical block ids [c0, c1) of a row in LDS (whole workgroup).  The
+// partition's first chunk arrives prefetched (`pre`, one id per thread).
+static_assert(kIdChunk == kThreads, "one prefetched block id per thread");
 __device__ __forceinline__ void stage_ids(SharedLds &sh, const int32_t *bt, int c0, int c1,
-                                          int tid) {
+                                          int tid, int pre, bool use_pre) {
   __syncthreads();
-  for (int i = tid; i < c1 - c0; i += kThreads) sh.s.ids[i] = bt[c0 + i];
+  if (use_pre) {
+    if (tid < c1 - c0) sh.s.ids[tid] = pre;
+  } else if (tid < c1 - c0) {
+    sh.s.ids[tid] = bt[c0 + tid];
+  }
   __syncthreads();
 }
 
@@ -412,7 +415,7 @@ __device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int 
 
 template <int DT, int KS, int VS>
 __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h, int p,
-                          int seq_len, int wave, int lane, int tid) {
+                          int seq_len, int wave, int lane, int tid, int pre_id) {
   const int n = lane & 15, qd = lane >> 4;
   u32x4 qr[4];
   load_q(qr, a, b, h, n, qd);
@@ -451,7 +454,7 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
   const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
   for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
     const int c1 = min(blk1, c0 + kIdChunk);
-    stage_ids(sh, bt, c0, c1, tid);
+    stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int npairs = (c1 - c0 + 1) / 2;
     // the last pair is masked when it holds the row's partial block or only
     // one block of the chunk
@@ -648,17 +651,12 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
 }
 
 __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
-                            int p, int seq_len, int wave, int lane, int tid) {
+                            int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
+                            int pre_id) {
   const int n = lane & 15, qd = lane >> 4;
   // the group's queries (fp16, zero rows past the group) stay in LDS and are
   // re-read per channel chunk, which keeps them out of the register budget
-  {
-    const int hn = tid >> 4, c8 = tid & 15;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hn < a.group)
-      v = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
-    *reinterpret_cast<u32x4 *>(&sh.s.q[hn][8 * c8]) = v;
-  }
+  *reinterpret_cast<u32x4 *>(&sh.s.q[tid >> 4][8 * (tid & 15)]) = qrow;
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -667,7 +665,7 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
   float *scl = sh.s.scl[wave];
   for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
     const int c1 = min(blk1, c0 + kIdChunk);
-    stage_ids(sh, bt, c0, c1, tid);
+    stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     auto load = [&](Group4 &t, int k, bool live) {
@@ -691,22 +689,27 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
 }
 
 // ---------------------------------------------------------------------------
-// INT4 with a query group of at most 4: compact score layout.  The score
-// product fills only four of its sixteen columns, so after it the four
-// blocks' score tiles are packed into one: lane (n, qd) then holds tokens
+// INT4 with a query group of at most 4: compact score layout.  Four heads
+// fill only four of the score product's sixteen columns, so each product
+// carries the hi and the lo part of q' in two column banks, and the four
+// blocks' scores end in one register set: lane (n, qd) holds tokens
 // 4qd..4qd+3 of block n/4 for head n%4, and the softmax runs on four values
 // per lane instead of sixteen.  q' = q * s_c is formed once per lane for two
 // channels of the four heads and shared through LDS.
 // ---------------------------------------------------------------------------
 
-// Scores of four blocks (one per register set) packed into the compact layout.
-__device__ __forceinline__ f32x4 pack_scores(const f32x4 (&acc)[4]) {
-  f32x4 s = acc[0];
+// Score tiles with hi and lo in separate columns: tile u writes head h's
+// hi product to column 4u + h and its lo product to column 4(u^1) + h, so
+// tiles 0, 2 share one accumulator (banks hi0 lo0 hi2 lo2) and tiles 1, 3
+// the other (lo1 hi1 lo3 hi3).  Adding each bank's partner bank gives the
+// compact scores.
+__device__ __forceinline__ f32x4 combine_scores(const f32x4 &ae, const f32x4 &ao, bool odd_bank) {
+  f32x4 s;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[i] = dpp_f32<kRowShr + 4, 0x2>(s[i], acc[1][i]);
-    s[i] = dpp_f32<kRowShr + 8, 0x4>(s[i], acc[2][i]);
-    s[i] = dpp_f32<kRowShr + 12, 0x8>(s[i], acc[3][i]);
+    const float e = ae[i] + dpp_f32<kRowShl + 4>(0.0f, ae[i]);
+    const float o = ao[i] + dpp_f32<kRowShr + 4>(0.0f, ao[i]);
+    s[i] = odd_bank ? o : e;
   }
   return s;
 }
@@ -769,12 +772,13 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4 &t, const
 }
 
 // qv[hh]: this lane's query values of head hh at channels c0 = 8(lane/4) +
-// lane%4 and c0 + 4; qb: this wave's q' rows; qrd: dword offset of this
-// lane's operand row (head n, or the zero row) and row group.
+// lane%4 and c0 + 4; qb: this wave's q' rows; qro[u]: dword offset of this
+// lane's operand row for block u (hi row of head n%4 in bank u, lo row in
+// bank u^1, else the zero row) and row group.
 __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
-                                                const float (&qv)[4][2], uint32_t *qb, int qrd,
-                                                float *scl, float qk_scale, int lane, int n,
-                                                int qd) {
+                                                const float (&qv)[4][2], uint32_t *qb,
+                                                const int (&qro)[4], float *scl, float qk_scale,
+                                                int lane, int n, int qd) {
 #if KVQ_INT4_VBIAS
   const float vsf = (lane & 2) ? 0.0625f : 1.0f;
 #else
@@ -789,23 +793,21 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
     qb[hh * kQbRow + lane] = hi;
     qb[(5 + hh) * kQbRow + lane] = lo;
   }
-  f32x4 acc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ae = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f16x8 bhi = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qrd + 4 * j));
-    const f16x8 blo = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + 5 * kQbRow + qrd + 4 * j));
-    f16x8 av[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      av[u] = int4x8_to_f16(t.k[u][j]);
-      acc[u] = mfma32(av[u], bhi, acc[u]);
+      const f16x8 bq = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qro[u] + 4 * j));
+      const f16x8 av = int4x8_to_f16(t.k[u][j]);
+      if (u & 1) {
+        ao = mfma32(av, bq, ao);
+      } else {
+        ae = mfma32(av, bq, ae);
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = mfma32(av[u], blo, acc[u]);
   }
-  f32x4 s = pack_scores(acc);
+  f32x4 s = combine_scores(ae, ao, (n & 4) != 0);
   s *= qk_scale;
   f32x4 p;
   softmax_update_c(st, s, p);
@@ -822,15 +824,10 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
 }
 
 __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
-                             int p, int seq_len, int wave, int lane, int tid) {
+                             int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
+                             int pre_id) {
   const int n = lane & 15, qd = lane >> 4;
-  {
-    const int hn = tid >> 4, c8 = tid & 15;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (hn < a.group)
-      v = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
-    *reinterpret_cast<u32x4 *>(&sh.s.q[hn][8 * c8]) = v;
-  }
+  *reinterpret_cast<u32x4 *>(&sh.s.q[tid >> 4][8 * (tid & 15)]) = qrow;
   uint32_t *qb = &sh.s.qb[wave][0][0][0];
   qb[4 * kQbRow + lane] = 0u;
   qb[9 * kQbRow + lane] = 0u;
@@ -844,7 +841,13 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
       qv[hh][1] = (float)sh.s.q[hh][c0 + 4];
     }
   }
-  const int qrd = (n < 4 ? n : 4) * kQbRow + 16 * qd;
+  int qro[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int bank = n >> 2;
+    const int row = bank == u ? (n & 3) : (bank == (u ^ 1) ? 5 + (n & 3) : 4);
+    qro[u] = row * kQbRow + 16 * qd;
+  }
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -853,7 +856,7 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   float *scl = sh.s.scl[wave];
   for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
     const int c1 = min(blk1, c0 + kIdChunk);
-    stage_ids(sh, bt, c0, c1, tid);
+    stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     auto load = [&](Group4 &t, int k, bool live) {
@@ -863,7 +866,7 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
       load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
     };
     auto compute = [&](Group4 &t, int) {
-      compute_group4c(st, t, qv, qb, qrd, scl, a.qk_scale, lane, n, qd);
+      compute_group4c(st, t, qv, qb, qro, scl, a.qk_scale, lane, n, qd);
     };
 #if KVQ_INT4_DEPTH == 3
     pipeline3<Group4>(cnt, load, compute);
@@ -981,14 +984,27 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
 }
 
 // G4: INT4 cache with a query group of at most 4 (compact score layout).
-template <int DT, int KS, int VS, bool G4 = false>
-__global__ __launch_bounds__(kThreads, KVQ_WG_PER_CU) void kvq_paged_decode_kernel(DecodeArgs a) {
-  __shared__ SharedLds sh;
+template <int DT, int KS, int VS, bool G4>
+__device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
   const int p = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Loads that do not need the row length are issued before it arrives: the
+  // partition's first block ids (within the table row; ids past the row's
+  // blocks are never used) and, for INT4, the query group (one 16-byte unit
+  // per thread, zero past the group).
+  const int blk0 = p * a.part_blocks;
+  const int pre_id = blk0 + tid < a.max_blocks_per_seq
+                         ? a.block_tables[(size_t)b * a.max_blocks_per_seq + blk0 + tid]
+                         : 0;
+  u32x4 qrow = {0u, 0u, 0u, 0u};
+  if constexpr (DT == kInt4) {
+    const int hn = tid >> 4, c8 = tid & 15;
+    if (hn < a.group)
+      qrow = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
+  }
   const int seq_len = a.seq_lens[b];
   const bool direct = a.slots == 1;
 
@@ -1015,70 +1031,92 @@ __global__ __launch_bounds__(kThreads, KVQ_WG_PER_CU) void kvq_paged_decode_kern
     const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
     if (p >= n_main) return;
     if constexpr (G4) {
-      stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+      stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
-      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     }
     if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
   } else {
     const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
     if (p >= n_main) return;
-    stream_q8<DT, KS, VS>(st, a, sh, b, h, p, seq_len, wave, lane, tid);
+    stream_q8<DT, KS, VS>(st, a, sh, b, h, p, seq_len, wave, lane, tid, pre_id);
   }
   merge_and_store(a, sh, st, b, h, p, direct, wave, lane, tid);
 }
 
+// INT8 / FP8 and INT4 caches get separate kernels so that each is held to
+// the register budget of its own occupancy.
+template <int DT, int KS, int VS>
+__global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, KS, VS)) void kvq_paged_decode_kernel(
+    DecodeArgs a) {
+  __shared__ SharedLds sh;
+  decode_workgroup<DT, KS, VS, false>(a, sh);
+}
+
+template <bool G4>
+__global__ __launch_bounds__(kThreads, decode_wg_per_cu(kInt4, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
+    DecodeArgs a) {
+  __shared__ SharedLds sh;
+  decode_workgroup<kInt4, kChannel, kToken, G4>(a, sh);
+}
+
 // Log-sum-exp merge of the partition partials of each (row, query head):
 // M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p, in
-// partition order.  Partitions past the row's length wrote nothing and are
-// not read.  One thread per 4 channels, 32 threads per (row, query head);
-// partials are read eight at a time (clamped indices, zero weights past the
-// end) so their loads are in flight together.
+// partition order.  One thread per 4 channels, 32 threads per (row, query
+// head).  Partials are read eight at a time with indices clamped to the
+// workspace's slots, so the first eight are in flight together with the
+// row length; slots at or past the row's partition count (never written by
+// this launch, possibly stale or uninitialised) are excluded by selects.
+// More than eight partitions merge chunk by chunk with a running max.
 __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a, int is_int4) {
   constexpr int kUnroll = 8;
   const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, hq) row
   const int c4 = threadIdx.x & 31;
   const int b = gid / a.num_q_heads;
   if (b >= a.batch) return;
-  const int seq_len = a.seq_lens[b];
-  float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
-  if (seq_len <= 0) {
-    *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  int total;
-  if (is_int4) {
-    const int nq = kivi_quantized_len(seq_len, a.residual);
-    total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
-  } else {
-    total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
-  }
   const size_t base = (size_t)gid * a.slots;
-  float big = kNegInf;
-  for (int p0 = 0; p0 < total; p0 += kUnroll) {
-    float mv[kUnroll];
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i) mv[i] = a.ws_m[base + min(p0 + i, total - 1)];
-#pragma unroll
-    for (int i = 0; i < kUnroll; ++i) big = fmaxf(big, mv[i]);
-  }
-  float lt = 0.0f;
+  float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
+  float big = kNegInf, lt = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int total = kUnroll;  // known once the row length has arrived
   for (int p0 = 0; p0 < total; p0 += kUnroll) {
     float mv[kUnroll], lv[kUnroll];
     f32x4 ov[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const size_t slot = base + min(p0 + i, total - 1);
+      const size_t slot = base + min(p0 + i, a.slots - 1);
       mv[i] = a.ws_m[slot];
       lv[i] = a.ws_l[slot];
       ov[i] = *reinterpret_cast<const f32x4 *>(a.ws_o + slot * kHeadDim + 4 * c4);
     }
+    if (p0 == 0) {
+      const int seq_len = a.seq_lens[b];
+      if (seq_len <= 0) {
+        *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+      }
+      if (is_int4) {
+        const int nq = kivi_quantized_len(seq_len, a.residual);
+        total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
+      } else {
+        total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
+      }
+    }
+    float cm = big;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) cm = p0 + i < total ? fmaxf(cm, mv[i]) : cm;
+    // rescale what earlier chunks summed (factor 1 for the first chunk)
+    const float r = big == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(big - cm);
+    lt *= r;
+    acc *= r;
+    big = cm;
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const float w = p0 + i < total ? __builtin_amdgcn_exp2f(mv[i] - big) : 0.0f;
-      lt += w * lv[i];
-      acc += w * ov[i];
+      if (p0 + i < total) {
+        const float w = __builtin_amdgcn_exp2f(mv[i] - big);
+        lt += w * lv[i];
+        acc += w * ov[i];
+      }
     }
   }
   *reinterpret_cast<f32x4 *>(out) = acc * (1.0f / lt);
@@ -1124,11 +1162,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
                          hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, batch);
   if (dtype == kInt4 && a.group <= 4) {
-    hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken, true>), grid,
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   } else if (dtype == kInt4) {
-    hipLaunchKernelGGL((kvq_paged_decode_kernel<kInt4, kChannel, kToken>), grid,
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   } else if (dtype == kFp8) {
     launch_k<kFp8>(a, k_kind, v_kind, grid, stream);
   } else {

@@ -24,11 +24,6 @@ constexpr int kBlock = 16;
 constexpr int kGroup = 64;        // INT4 group (tokens for K, channels for V)
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3 };
-// Granularity as the decode kernel sees it: a scale that is uniform over a
-// (row, KV head) (per-tensor or per-head), per channel, or per token.
-enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
-
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) {
   return __builtin_bit_cast(uint32_t, v);
 }

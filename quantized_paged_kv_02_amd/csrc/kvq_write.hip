@@ -52,48 +52,41 @@ __device__ __forceinline__ float fp8_prescale(float x, float s) {
   return fminf(fmaxf(y, -448.0f), 448.0f);
 }
 
-// Quantize one tensor (K or V) of one (token, KV head) and store its codes
-// (and its scale for per-token granularity).
-template <int DT, bool IS_V>
-__device__ __forceinline__ void write_vector(const uint16_t *src, uint8_t *chunk,
-                                             float *scales, int gran, int h,
-                                             int slot, size_t token_scale_index) {
-  const int lane = threadIdx.x;
-  const uint32_t raw = reinterpret_cast<const uint32_t *>(src)[lane];
+// Codes of channels 2 lane, 2 lane + 1 of one tensor (K or V) of one
+// (token, KV head), and the token's scale.
+struct CodePair {
+  uint32_t q0, q1;
+  float scale;
+};
+
+// Scale of channels c0, c0 + 1 for the static granularities.
+__device__ __forceinline__ float2 static_scales(const float *scales, int gran, int h, int c0) {
+  if (gran == kPerTensor) return float2{scales[0], scales[0]};
+  if (gran == kPerHead) return float2{scales[h], scales[h]};
+  return float2{scales[h * kHeadDim + c0], scales[h * kHeadDim + c0 + 1]};
+}
+
+template <int DT>
+__device__ __forceinline__ CodePair quantize_pair(uint32_t raw, int gran, float2 st) {
   const float x0 = half_bits_to_float(raw & 0xFFFFu);
   const float x1 = half_bits_to_float(raw >> 16);
-  const int c0 = 2 * lane;
-  float s0, s1;
+  float s0 = st.x, s1 = st.y;
   if (gran == kPerToken) {
     const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
     s0 = s1 = amax / (DT == kFp8 ? 448.0f : 127.0f);
-    if (lane == 0) scales[token_scale_index] = s0;
-  } else if (gran == kPerTensor) {
-    s0 = s1 = scales[0];
-  } else if (gran == kPerHead) {
-    s0 = s1 = scales[h];
-  } else {
-    s0 = scales[h * kHeadDim + c0];
-    s1 = scales[h * kHeadDim + c0 + 1];
   }
-  uint32_t q0, q1;
+  CodePair r;
+  r.scale = s0;
   if (DT == kFp8) {
     const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
         fp8_prescale(x0, s0), fp8_prescale(x1, s1), 0, false);
-    q0 = pk & 0xFFu;
-    q1 = (pk >> 8) & 0xFFu;
+    r.q0 = pk & 0xFFu;
+    r.q1 = (pk >> 8) & 0xFFu;
   } else {
-    q0 = quant_int(x0, s0, -128.0f, 127.0f) & 0xFFu;
-    q1 = quant_int(x1, s1, -128.0f, 127.0f) & 0xFFu;
+    r.q0 = quant_int(x0, s0, -128.0f, 127.0f) & 0xFFu;
+    r.q1 = quant_int(x1, s1, -128.0f, 127.0f) & 0xFFu;
   }
-  if (!IS_V) {
-    // channels c0 and c0+1 are adjacent bytes of one 16-byte run
-    *reinterpret_cast<uint16_t *>(chunk + k8_offset(slot, c0)) =
-        (uint16_t)(q0 | (q1 << 8));
-  } else {
-    chunk[v8_offset(slot, c0)] = (uint8_t)q0;
-    chunk[v8_offset(slot, c0 + 1)] = (uint8_t)q1;
-  }
+  return r;
 }
 
 template <int DT>
@@ -101,19 +94,37 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
+  const int lane = threadIdx.x;
   const int c_begin = a.cu_new[b];
   const int n_new = a.cu_new[b + 1] - c_begin;
   if (i >= n_new) return;
   const int pos = a.seq_lens[b] - n_new + i;
+  const int c0 = 2 * lane;
+  // every load first (block id, both input vectors, static scales): the
+  // code stores below are byte stores, which may alias any of them
+  const size_t src = ((size_t)(c_begin + i) * a.num_kv_heads + h) * kHeadDim;
+  const uint32_t rk = reinterpret_cast<const uint32_t *>(a.k_new + src)[lane];
+  const uint32_t rv = reinterpret_cast<const uint32_t *>(a.v_new + src)[lane];
   const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kBlock];
+  float2 sk = {0.f, 0.f}, sv = {0.f, 0.f};
+  if (a.k_gran != kPerToken) sk = static_scales(a.k_scales, a.k_gran, h, c0);
+  if (a.v_gran != kPerToken) sv = static_scales(a.v_scales, a.v_gran, h, c0);
+  const CodePair qk = quantize_pair<DT>(rk, a.k_gran, sk);
+  const CodePair qv = quantize_pair<DT>(rv, a.v_gran, sv);
+
   const int slot = pos % kBlock;
   const size_t chunk = (size_t)phys * a.num_kv_heads + h;
-  const size_t src = ((size_t)(c_begin + i) * a.num_kv_heads + h) * kHeadDim;
-  const size_t tsi = chunk * kBlock + slot;
-  write_vector<DT, false>(a.k_new + src, a.k_codes + chunk * 2048, a.k_scales,
-                          a.k_gran, h, slot, tsi);
-  write_vector<DT, true>(a.v_new + src, a.v_codes + chunk * 2048, a.v_scales,
-                         a.v_gran, h, slot, tsi);
+  uint8_t *kc = a.k_codes + chunk * 2048;
+  uint8_t *vc = a.v_codes + chunk * 2048;
+  // K: channels c0 and c0+1 are adjacent bytes of one 16-byte run
+  *reinterpret_cast<uint16_t *>(kc + k8_offset(slot, c0)) = (uint16_t)(qk.q0 | (qk.q1 << 8));
+  vc[v8_offset(slot, c0)] = (uint8_t)qv.q0;
+  vc[v8_offset(slot, c0 + 1)] = (uint8_t)qv.q1;
+  if (lane == 0) {
+    const size_t tsi = chunk * kBlock + slot;
+    if (a.k_gran == kPerToken) a.k_scales[tsi] = qk.scale;
+    if (a.v_gran == kPerToken) a.v_scales[tsi] = qv.scale;
+  }
 }
 
 // ---------------------------------------------------------------------------
