@@ -189,9 +189,18 @@ class Bench:
         self.scale = 1.0 / math.sqrt(128)
         torch.cuda.synchronize()
 
-    def step(self, events=None, write=True):
+    def step(self, events=None, write=True, fused=True):
+        """One decode step over all layers: append each row's new token and
+        decode.  fused: one kvq_write_decode call per layer, else kvq_write
+        then kvq_paged_decode.  events (with write=False) bracket each
+        kvq_paged_decode launch."""
         kvq = self.kvq
         for layer in range(self.w.layers):
+            if write and fused and events is None:
+                kvq.write_decode(self.caches[layer], self.k_new[layer], self.v_new[layer],
+                                 self.q[layer], self.table, self.lens_t, self.max_len,
+                                 self.scale, self.out[layer], self.ws)
+                continue
             if write:
                 kvq.write(self.caches[layer], self.k_new[layer], self.v_new[layer],
                           self.ones_cu, self.table, self.lens_t, 1)
@@ -220,7 +229,8 @@ def run(args):
     step_bytes = layer_bytes * L
 
     # eager reference pass, then the graph
-    bench.step()
+    fused = not args.separate
+    bench.step(fused=fused)
     torch.cuda.synchronize()
     ref = [o.clone() for o in bench.out]
     graph = None
@@ -228,19 +238,19 @@ def run(args):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            bench.step()
+            bench.step(fused=fused)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            bench.step()
+            bench.step(fused=fused)
         torch.cuda.synchronize()
 
     def one():
         if graph is not None:
             graph.replay()
         else:
-            bench.step()
+            bench.step(fused=fused)
 
     for _ in range(args.warmup):
         one()
@@ -326,8 +336,10 @@ def run(args):
             "seq_len": int(w.max_seq) if not isinstance(w.seq, tuple) else list(w.seq),
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "kv_dtype": w.dtype, "k_granularity": w.k_gran, "v_granularity": w.v_gran,
-            "block_tables": w.table, "step": "per layer: kvq_write of 1 token/row + "
-            "kvq_paged_decode", "launch": "hip graph" if graph is not None else "eager",
+            "block_tables": w.table,
+            "step": ("per layer: kvq_write of 1 token/row + kvq_paged_decode" if args.separate
+                     else "per layer: kvq_write_decode (1 token/row appended, then decoded)"),
+            "launch": "hip graph" if graph is not None else "eager",
             "algorithmic_bytes_per_step": step_bytes,
         },
         "roofline": {
@@ -352,6 +364,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--eager", action="store_true", help="launch from Python, no HIP graph")
+    ap.add_argument("--separate", action="store_true",
+                    help="step with kvq_write + kvq_paged_decode instead of kvq_write_decode")
     ap.add_argument("--kernel-samples", type=int, default=10,
                     help="extra synchronised replays for the per-launch timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -214,6 +214,31 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
                             float *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* One decode step: quantize-on-write of ONE new token per row followed by
+ * decode attention over the updated cache (the per-step append then read of
+ * [yunthe] section "PagedAttention与KV Cache量化协同工作原理").  Same cache
+ * contents and the same out, bit for bit, as kvq_write with one token per
+ * row followed by kvq_paged_decode with these arguments.
+ *   k_new, v_new : fp16 [batch][H][128]; entry b is row b's new token, at
+ *                  position seq_lens[b]-1 (seq_lens count it).  Rows with
+ *                  seq_lens[b] == 0 take no token and their entry is unread.
+ *   q, block_tables, seq_lens, max_seq_len, softmax_scale, out, workspace,
+ *   workspace_bytes: as for kvq_paged_decode.
+ * INT8/FP8: a single launch (plus the partition merge when the launch is
+ * split): the workgroup that streams a row's last partition quantizes and
+ * stores the row's token (codes and per-token scales) before streaming.
+ * INT4: the kvq_write launches, then the decode launches.
+ * Errors: as for kvq_paged_decode; additionally KVQ_ERR_INVALID_ARG when
+ * k_new or v_new is NULL (batch > 0) and KVQ_ERR_ALIGNMENT when either is
+ * not 16-byte aligned.  Nothing is enqueued on error. */
+kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
+                            const uint16_t *k_new, const uint16_t *v_new,
+                            const uint16_t *q, const int32_t *block_tables,
+                            const int32_t *seq_lens, int32_t batch,
+                            int32_t max_seq_len, float softmax_scale,
+                            float *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

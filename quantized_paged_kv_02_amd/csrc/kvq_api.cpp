@@ -214,11 +214,14 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
-                            const uint16_t *q, const int32_t *block_tables,
-                            const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
-                            float softmax_scale, float *out, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+// Host checks and kernel arguments of a decode launch; KVQ_OK with
+// *launch == false when there is nothing to do (batch == 0).
+static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
+                               const uint16_t *q, const int32_t *block_tables,
+                               const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                               float softmax_scale, float *out, void *workspace,
+                               size_t workspace_bytes, kvq::DecodeArgs *a, bool *launch) {
+  *launch = false;
   kvq_status st = kvq_validate(layout, cache, batch, max_seq_len);
   if (st != KVQ_OK) return st;
   if (batch == 0) return KVQ_OK;
@@ -234,39 +237,99 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
     return KVQ_ERR_WORKSPACE;
 
   char *ws = static_cast<char *>(workspace);
-  kvq::DecodeArgs a{};
-  a.k_codes = static_cast<const uint8_t *>(cache->k_codes);
-  a.v_codes = static_cast<const uint8_t *>(cache->v_codes);
-  a.k_scales = cache->k_scales;
-  a.v_scales = cache->v_scales;
-  a.k_resid = cache->k_resid;
-  a.v_resid = cache->v_resid;
-  a.q = q;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.ws_m = reinterpret_cast<float *>(ws + w.m_off);
-  a.ws_l = reinterpret_cast<float *>(ws + w.l_off);
-  a.ws_o = reinterpret_cast<float *>(ws + w.o_off);
-  a.batch = batch;
-  a.num_q_heads = layout->num_q_heads;
-  a.num_kv_heads = layout->num_kv_heads;
-  a.group = layout->num_q_heads / layout->num_kv_heads;
-  a.max_blocks_per_seq = layout->max_blocks_per_seq;
-  a.part_blocks = p.part_blocks;
-  a.num_parts = p.num_parts;
-  a.slots = p.slots;
-  a.residual = layout->residual_len;
-  a.ring = layout->residual_len + kGroup;
-  a.k_head_stride = layout->k_gran == KVQ_PER_HEAD ? 1 : 0;
-  a.v_head_stride = layout->v_gran == KVQ_PER_HEAD ? 1 : 0;
-  a.qk_scale = softmax_scale * 1.4426950408889634f;
+  *a = kvq::DecodeArgs{};
+  a->k_codes = static_cast<const uint8_t *>(cache->k_codes);
+  a->v_codes = static_cast<const uint8_t *>(cache->v_codes);
+  a->k_scales = cache->k_scales;
+  a->v_scales = cache->v_scales;
+  a->k_resid = cache->k_resid;
+  a->v_resid = cache->v_resid;
+  a->q = q;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->out = out;
+  a->ws_m = reinterpret_cast<float *>(ws + w.m_off);
+  a->ws_l = reinterpret_cast<float *>(ws + w.l_off);
+  a->ws_o = reinterpret_cast<float *>(ws + w.o_off);
+  a->batch = batch;
+  a->num_q_heads = layout->num_q_heads;
+  a->num_kv_heads = layout->num_kv_heads;
+  a->group = layout->num_q_heads / layout->num_kv_heads;
+  a->max_blocks_per_seq = layout->max_blocks_per_seq;
+  a->part_blocks = p.part_blocks;
+  a->num_parts = p.num_parts;
+  a->slots = p.slots;
+  a->residual = layout->residual_len;
+  a->ring = layout->residual_len + kGroup;
+  a->k_head_stride = layout->k_gran == KVQ_PER_HEAD ? 1 : 0;
+  a->v_head_stride = layout->v_gran == KVQ_PER_HEAD ? 1 : 0;
+  a->qk_scale = softmax_scale * 1.4426950408889634f;
+  *launch = true;
+  return KVQ_OK;
+}
 
+static kvq_status decode_launch(const kvq_layout *layout, const kvq::DecodeArgs &a,
+                                int32_t batch, void *stream) {
   (void)hipGetLastError();
   const hipError_t e = kvq::launch_decode(a, layout->dtype, kvq::decode_scale_kind(layout->k_gran),
                                           kvq::decode_scale_kind(layout->v_gran), batch,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
+                            const uint16_t *q, const int32_t *block_tables,
+                            const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                            float softmax_scale, float *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  kvq::DecodeArgs a;
+  bool launch;
+  const kvq_status st = decode_setup(layout, cache, q, block_tables, seq_lens, batch, max_seq_len,
+                                     softmax_scale, out, workspace, workspace_bytes, &a, &launch);
+  if (st != KVQ_OK || !launch) return st;
+  return decode_launch(layout, a, batch, stream);
+}
+
+kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
+                            const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                            const int32_t *block_tables, const int32_t *seq_lens, int32_t batch,
+                            int32_t max_seq_len, float softmax_scale, float *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  kvq::DecodeArgs a;
+  bool launch;
+  const kvq_status st = decode_setup(layout, cache, q, block_tables, seq_lens, batch, max_seq_len,
+                                     softmax_scale, out, workspace, workspace_bytes, &a, &launch);
+  if (st != KVQ_OK || !launch) return st;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+  if (layout->dtype != KVQ_INT4) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    return decode_launch(layout, a, batch, stream);
+  }
+  // INT4: the write launches (one token per row, no cu_new), then decode
+  kvq::WriteArgs w{};
+  w.k_codes = static_cast<uint8_t *>(cache->k_codes);
+  w.v_codes = static_cast<uint8_t *>(cache->v_codes);
+  w.k_scales = cache->k_scales;
+  w.v_scales = cache->v_scales;
+  w.k_resid = cache->k_resid;
+  w.v_resid = cache->v_resid;
+  w.k_new = k_new;
+  w.v_new = v_new;
+  w.cu_new = nullptr;
+  w.block_tables = block_tables;
+  w.seq_lens = seq_lens;
+  w.num_kv_heads = layout->num_kv_heads;
+  w.max_blocks_per_seq = layout->max_blocks_per_seq;
+  w.k_gran = layout->k_gran;
+  w.v_gran = layout->v_gran;
+  w.residual = layout->residual_len;
+  w.ring = layout->residual_len + kGroup;
+  (void)hipGetLastError();
+  const hipError_t e = kvq::launch_write_int4(w, batch, 1, 2, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  return decode_launch(layout, a, batch, stream);
 }
 
 }  // extern "C"

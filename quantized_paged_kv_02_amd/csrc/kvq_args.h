@@ -51,6 +51,11 @@ struct DecodeArgs {
   const uint16_t *q;
   const int32_t *block_tables;
   const int32_t *seq_lens;
+  // Fused append (INT8/FP8): row b's new token, fp16 [B][H][128] at position
+  // seq_lens[b] - 1, quantized and stored (codes, per-token scales) by the
+  // workgroup that streams the row's last partition.  Null: no append.
+  const uint16_t *k_new;
+  const uint16_t *v_new;
   float *out;
   float *ws_o;      // [B][Hq][slots][128] unnormalised partial outputs
   float *ws_m;      // [B][Hq][slots] partial running max (log2 domain)

@@ -45,6 +45,7 @@
 // applied to o once per wave.
 #include "kvq_args.h"
 #include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -983,6 +984,41 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
   }
 }
 
+// Fused append of row b's new token for KV head h (INT8/FP8): wave 0
+// quantizes and stores K, wave 1 V, exactly as the write kernel does.
+template <int DT, int KS, int VS>
+__device__ __forceinline__ void append_token_q8(const DecodeArgs &a, int b, int h, int seq_len,
+                                                int wave, int lane) {
+  if (wave >= 2) return;
+  const bool is_v = wave == 1;
+  const int kind = is_v ? VS : KS;
+  const int H = a.num_kv_heads;
+  const int pos = seq_len - 1;
+  const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kBlock];
+  const int slot = pos % kBlock;
+  const size_t chunk = (size_t)phys * H + h;
+  const uint16_t *src = (is_v ? a.v_new : a.k_new) + ((size_t)b * H + h) * kHeadDim;
+  const uint32_t raw = reinterpret_cast<const uint32_t *>(src)[lane];
+  // the cache arrays are the caller's writable buffers (const in DecodeArgs
+  // because streaming only reads them)
+  float *scales = const_cast<float *>(is_v ? a.v_scales : a.k_scales);
+  float2 st = {0.f, 0.f};
+  if (kind == kUniform) {
+    const float s = scales[h * (is_v ? a.v_head_stride : a.k_head_stride)];
+    st = float2{s, s};
+  } else if (kind == kChannel) {
+    st = float2{scales[h * kHeadDim + 2 * lane], scales[h * kHeadDim + 2 * lane + 1]};
+  }
+  const CodePair q = quantize_pair<DT>(raw, kind == kToken ? kPerToken : kPerTensor, st);
+  uint8_t *codes = const_cast<uint8_t *>(is_v ? a.v_codes : a.k_codes) + chunk * 2048;
+  if (is_v) {
+    store_v_codes(codes, slot, lane, q);
+  } else {
+    store_k_codes(codes, slot, lane, q);
+  }
+  if (kind == kToken && lane == 0) scales[chunk * kBlock + slot] = q.scale;
+}
+
 // G4: INT4 cache with a query group of at most 4 (compact score layout).
 template <int DT, int KS, int VS, bool G4>
 __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
@@ -1039,6 +1075,13 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
   } else {
     const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
     if (p >= n_main) return;
+    if (a.k_new != nullptr && p == n_main - 1) {
+      // this workgroup streams the row's last block: store the new token
+      // first, complete (every counter drained) before any wave reads it
+      append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     stream_q8<DT, KS, VS>(st, a, sh, b, h, p, seq_len, wave, lane, tid, pre_id);
   }
   merge_and_store(a, sh, st, b, h, p, direct, wave, lane, tid);

@@ -1,0 +1,94 @@
+// INT8 / FP8 quantize-on-write of one token vector, shared by the write
+// kernel and the decode kernel's fused append.  Symmetric rule from
+// [intelli] "大模型KV Cache显存优化与量化技术实践" §3.1 对称量化算法 and
+// [yunthe] "KV Cache量化压缩技术与vLLM推理引擎显存优化实战", section
+// "KV Cache量化策略：INT8与FP8精度对比与选择": scale = max|x| / 127 (448 for
+// E4M3), code = clamp(round(x / scale)); dynamic per-token scales follow
+// [intelli] §3.2 动态量化策略.  fp32 division is the correctly rounded IEEE
+// one (the library is built without fast-math); rounding is rintf
+// (half-to-even).
+#pragma once
+
+#include "kvq_args.h"
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr int kPerTensor = 0, kPerHead = 1, kPerToken = 3;
+
+// Byte offset of (slot s, channel c) inside an INT8/FP8 (block, head) chunk.
+__device__ __forceinline__ int k8_offset(int s, int c) {
+  return 1024 * ((c >> 4) & 1) + 256 * (c >> 5) + 16 * s + (c & 15);
+}
+__device__ __forceinline__ int v8_offset(int s, int c) {
+  return 1024 * (c >> 6) + 256 * (s >> 2) + 16 * (c & 15) + 4 * ((c >> 4) & 3) +
+         (s & 3);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float hi) {
+  if (s == 0.0f) return 0u;
+  float y = rintf(x / s);
+  y = fminf(fmaxf(y, lo), hi);
+  return (uint32_t)(int)y;
+}
+
+__device__ __forceinline__ float fp8_prescale(float x, float s) {
+  if (s == 0.0f) return 0.0f;
+  const float y = x / s;
+  return fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
+// Codes of channels 2 lane, 2 lane + 1 of one tensor (K or V) of one
+// (token, KV head), and the token's scale.
+struct CodePair {
+  uint32_t q0, q1;
+  float scale;
+};
+
+// Scale of channels c0, c0 + 1 for the static granularities.
+__device__ __forceinline__ float2 static_scales(const float *scales, int gran, int h, int c0) {
+  if (gran == kPerTensor) return float2{scales[0], scales[0]};
+  if (gran == kPerHead) return float2{scales[h], scales[h]};
+  return float2{scales[h * kHeadDim + c0], scales[h * kHeadDim + c0 + 1]};
+}
+
+template <int DT>
+__device__ __forceinline__ CodePair quantize_pair(uint32_t raw, int gran, float2 st) {
+  const float x0 = half_bits_to_float(raw & 0xFFFFu);
+  const float x1 = half_bits_to_float(raw >> 16);
+  float s0 = st.x, s1 = st.y;
+  if (gran == kPerToken) {
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    s0 = s1 = amax / (DT == kFp8 ? 448.0f : 127.0f);
+  }
+  CodePair r;
+  r.scale = s0;
+  if (DT == kFp8) {
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+        fp8_prescale(x0, s0), fp8_prescale(x1, s1), 0, false);
+    r.q0 = pk & 0xFFu;
+    r.q1 = (pk >> 8) & 0xFFu;
+  } else {
+    r.q0 = quant_int(x0, s0, -128.0f, 127.0f) & 0xFFu;
+    r.q1 = quant_int(x1, s1, -128.0f, 127.0f) & 0xFFu;
+  }
+  return r;
+}
+
+// Store codes of channels 2 lane, 2 lane + 1 at `slot` of a (block, head)
+// chunk.  K: the two channels are adjacent bytes of one 16-byte run.
+__device__ __forceinline__ void store_k_codes(uint8_t *chunk, int slot, int lane,
+                                              const CodePair &q) {
+  *reinterpret_cast<uint16_t *>(chunk + k8_offset(slot, 2 * lane)) = (uint16_t)(q.q0 | (q.q1 << 8));
+}
+__device__ __forceinline__ void store_v_codes(uint8_t *chunk, int slot, int lane,
+                                              const CodePair &q) {
+  chunk[v8_offset(slot, 2 * lane)] = (uint8_t)q.q0;
+  chunk[v8_offset(slot, 2 * lane + 1)] = (uint8_t)q.q1;
+}
+
+}  // namespace kvq

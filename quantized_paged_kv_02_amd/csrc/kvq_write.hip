@@ -1,15 +1,8 @@
 // Quantize-on-write kernels.
 //
 // INT8 / FP8: one wavefront per (new token, KV head) quantizes the token's K
-// and V vectors (128 values each, two per lane) and scatters the codes into
-// the block slot given by the block table.  Symmetric rule from
-// [intelli] "大模型KV Cache显存优化与量化技术实践" §3.1 对称量化算法 and
-// [yunthe] "KV Cache量化压缩技术与vLLM推理引擎显存优化实战", section
-// "KV Cache量化策略：INT8与FP8精度对比与选择": scale = max|x| / 127 (448 for
-// E4M3), code = clamp(round(x / scale)).  Dynamic per-token scales follow
-// [intelli] §3.2 动态量化策略.  fp32 division is the correctly rounded IEEE
-// one (the library is built without fast-math); rounding is rintf
-// (half-to-even).
+// and V vectors (128 values each, two per lane; the rule is in kvq_quant.h)
+// and scatters the codes into the block slot given by the block table.
 //
 // INT4 (KIVI-style, [oh-bug] "KV Cache Quantization 生产实战", sections
 // "Key 和 Value 的分布不一定相同" and "Transformers：适合实验和小规模验证"):
@@ -20,73 +13,22 @@
 // to the fp16 ring.
 #include "kvq_args.h"
 #include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kPerTensor = 0, kPerHead = 1, kPerToken = 3;
-
-// Byte offset of (slot s, channel c) inside an INT8/FP8 (block, head) chunk.
-__device__ __forceinline__ int k8_offset(int s, int c) {
-  return 1024 * ((c >> 4) & 1) + 256 * (c >> 5) + 16 * s + (c & 15);
-}
-__device__ __forceinline__ int v8_offset(int s, int c) {
-  return 1024 * (c >> 6) + 256 * (s >> 2) + 16 * (c & 15) + 4 * ((c >> 4) & 3) +
-         (s & 3);
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-  return (float)__builtin_bit_cast(f16, (uint16_t)h);
-}
-
-__device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float hi) {
-  if (s == 0.0f) return 0u;
-  float y = rintf(x / s);
-  y = fminf(fmaxf(y, lo), hi);
-  return (uint32_t)(int)y;
-}
-
-__device__ __forceinline__ float fp8_prescale(float x, float s) {
-  if (s == 0.0f) return 0.0f;
-  const float y = x / s;
-  return fminf(fmaxf(y, -448.0f), 448.0f);
-}
-
-// Codes of channels 2 lane, 2 lane + 1 of one tensor (K or V) of one
-// (token, KV head), and the token's scale.
-struct CodePair {
-  uint32_t q0, q1;
-  float scale;
-};
-
-// Scale of channels c0, c0 + 1 for the static granularities.
-__device__ __forceinline__ float2 static_scales(const float *scales, int gran, int h, int c0) {
-  if (gran == kPerTensor) return float2{scales[0], scales[0]};
-  if (gran == kPerHead) return float2{scales[h], scales[h]};
-  return float2{scales[h * kHeadDim + c0], scales[h * kHeadDim + c0 + 1]};
-}
-
-template <int DT>
-__device__ __forceinline__ CodePair quantize_pair(uint32_t raw, int gran, float2 st) {
-  const float x0 = half_bits_to_float(raw & 0xFFFFu);
-  const float x1 = half_bits_to_float(raw >> 16);
-  float s0 = st.x, s1 = st.y;
-  if (gran == kPerToken) {
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    s0 = s1 = amax / (DT == kFp8 ? 448.0f : 127.0f);
-  }
-  CodePair r;
-  r.scale = s0;
-  if (DT == kFp8) {
-    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-        fp8_prescale(x0, s0), fp8_prescale(x1, s1), 0, false);
-    r.q0 = pk & 0xFFu;
-    r.q1 = (pk >> 8) & 0xFFu;
+// New tokens of row b: entries [c_begin, c_begin + n_new) of k_new / v_new.
+// Without cu_new every row owns entry b and holds one new token unless the
+// row is empty.
+__device__ __forceinline__ void new_tokens(const WriteArgs &a, int b, int &c_begin, int &n_new) {
+  if (a.cu_new != nullptr) {
+    c_begin = a.cu_new[b];
+    n_new = a.cu_new[b + 1] - c_begin;
   } else {
-    r.q0 = quant_int(x0, s0, -128.0f, 127.0f) & 0xFFu;
-    r.q1 = quant_int(x1, s1, -128.0f, 127.0f) & 0xFFu;
+    c_begin = b;
+    n_new = a.seq_lens[b] > 0 ? 1 : 0;
   }
-  return r;
 }
 
 template <int DT>
@@ -95,8 +37,8 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x;
-  const int c_begin = a.cu_new[b];
-  const int n_new = a.cu_new[b + 1] - c_begin;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
   if (i >= n_new) return;
   const int pos = a.seq_lens[b] - n_new + i;
   const int c0 = 2 * lane;
@@ -116,10 +58,8 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
   const size_t chunk = (size_t)phys * a.num_kv_heads + h;
   uint8_t *kc = a.k_codes + chunk * 2048;
   uint8_t *vc = a.v_codes + chunk * 2048;
-  // K: channels c0 and c0+1 are adjacent bytes of one 16-byte run
-  *reinterpret_cast<uint16_t *>(kc + k8_offset(slot, c0)) = (uint16_t)(qk.q0 | (qk.q1 << 8));
-  vc[v8_offset(slot, c0)] = (uint8_t)qv.q0;
-  vc[v8_offset(slot, c0 + 1)] = (uint8_t)qv.q1;
+  store_k_codes(kc, slot, lane, qk);
+  store_v_codes(vc, slot, lane, qv);
   if (lane == 0) {
     const size_t tsi = chunk * kBlock + slot;
     if (a.k_gran == kPerToken) a.k_scales[tsi] = qk.scale;
@@ -155,8 +95,8 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int H = a.num_kv_heads;
-  const int c_begin = a.cu_new[b];
-  const int n_new = a.cu_new[b + 1] - c_begin;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
   const int s_new = a.seq_lens[b];
   const int s_old = s_new - n_new;
   const int nq_old = kivi_len(s_old, a.residual);
@@ -306,8 +246,8 @@ __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
 // workgroup) unless it is already part of a quantized group.
 __device__ __forceinline__ void append_token(const WriteArgs &a, int i, int h, int b, int lane) {
   const int H = a.num_kv_heads;
-  const int c_begin = a.cu_new[b];
-  const int n_new = a.cu_new[b + 1] - c_begin;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
   if (i >= n_new) return;
   const int s_new = a.seq_lens[b];
   const int pos = s_new - n_new + i;

@@ -28,7 +28,7 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -5: "KVQ_ERR_CAPACITY", -6: "KVQ_ERR_HIP"}
 
 EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
-            "kvq_write", "kvq_paged_decode")
+            "kvq_write", "kvq_paged_decode", "kvq_write_decode")
 
 
 class Layout(ctypes.Structure):
@@ -86,6 +86,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_paged_decode.restype = I32
     lib.kvq_paged_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P,
                                      I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_write_decode.restype = I32
+    lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
+                                     P, I32, I32, ctypes.c_float, P, P, SZ, P]
     return lib
 
 
@@ -216,3 +219,17 @@ def paged_decode(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
                               _stream_handle(stream))
     if st != 0:
         raise KvqError(st, "kvq_paged_decode")
+
+
+def write_decode(cache: KVCache, k_new, v_new, q, block_tables, seq_lens, max_seq_len: int,
+                 softmax_scale: float, out, workspace, stream=None) -> None:
+    """kvq_write_decode: append one token per row, then decode (see kvq.h)."""
+    batch = block_tables.shape[0]
+    c = cache.struct()
+    st = LIB.kvq_write_decode(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(k_new),
+                              _ptr(v_new), _ptr(q), _ptr(block_tables), _ptr(seq_lens), batch,
+                              max_seq_len, float(softmax_scale), _ptr(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(),
+                              _stream_handle(stream))
+    if st != 0:
+        raise KvqError(st, "kvq_write_decode")

@@ -67,9 +67,11 @@ def fill_garbage(cache):
 
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
-             table=None, garbage=True, decode_twice=False, device="cuda"):
+             table=None, garbage=True, decode_twice=False, fused=False, device="cuda"):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
-    calls, then one decode token) and run one decode step."""
+    calls, then one decode token) and run one decode step.  ``fused``: the
+    decode token is written by kvq_write_decode together with the decode
+    step instead of by kvq_write before kvq_paged_decode."""
     from quantized_paged_kv_02_amd import kvq
     lens = np.asarray(lens, np.int32)
     b = len(lens)
@@ -113,7 +115,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         kvq.write(cache, kn, vn, cu, table_t, sl, int(n.max()))
     # decode token (rows with S >= 1)
     n = (lens >= 1).astype(np.int32)
-    if n.sum():
+    if n.sum() and not fused:
         kn = torch.cat([ks[r][lens[r] - 1:lens[r]] for r in range(b) if lens[r] >= 1]).contiguous()
         vn = torch.cat([vs[r][lens[r] - 1:lens[r]] for r in range(b) if lens[r] >= 1]).contiguous()
         cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32), device=device)
@@ -125,7 +127,17 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     ws = kvq.alloc_workspace(layout, b, max_len, device)
     scale = 1.0 / math.sqrt(128)
     lens_t = torch.as_tensor(lens, device=device)
-    kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, out, ws)
+    if fused:
+        # entry r is row r's decode token; rows of length 0 keep zeros (unread)
+        kn = torch.zeros((b, w.num_kv_heads, 128), dtype=torch.float16, device=device)
+        vn = torch.zeros_like(kn)
+        for r in range(b):
+            if lens[r] >= 1:
+                kn[r] = ks[r][lens[r] - 1]
+                vn[r] = vs[r][lens[r] - 1]
+        kvq.write_decode(cache, kn, vn, q, table_t, lens_t, max_len, scale, out, ws)
+    else:
+        kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, out, ws)
     out2 = None
     if decode_twice:
         out2 = torch.full_like(out, float("nan"))

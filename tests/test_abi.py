@@ -136,6 +136,32 @@ def _write(lay, cache, kn=FAKE, vn=FAKE, cu=FAKE, bt=FAKE, sl=FAKE, batch=2, tot
                              total, max_new, None)
 
 
+def _write_decode(lay, cache, kn=FAKE, vn=FAKE, q=FAKE, bt=FAKE, sl=FAKE, batch=2, max_len=100,
+                  scale=0.1, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return kvq.LIB.kvq_write_decode(ctypes.byref(lay), ctypes.byref(cache), kn, vn, q, bt, sl,
+                                    batch, max_len, scale, out, ws, ws_bytes, None)
+
+
+def test_write_decode_rejects_before_launch():
+    lay, c = _layout(), _cache()
+    assert _write_decode(lay, c, kn=None) == INV
+    assert _write_decode(lay, c, vn=None) == INV
+    assert _write_decode(lay, c, kn=FAKE + 8) == ALN
+    assert _write_decode(lay, c, q=None) == INV
+    assert _write_decode(lay, c, out=FAKE + 4) == ALN
+    assert _write_decode(lay, c, scale=float("inf")) == INV
+    assert _write_decode(lay, c, max_len=10 ** 6) == CAP
+    split = _layout(split_tokens=16)
+    assert _write_decode(split, c, ws_bytes=16) == WS
+    assert _write_decode(lay, c, batch=0) == OK            # nothing to do, nothing launched
+    assert _write_decode(lay, c, batch=0, kn=None) == OK
+    lay4 = _layout(dtype=3, k_gran=2, v_gran=3, residual_len=128, group_size=64)
+    c4 = _cache(int4=True)
+    assert kvq.validate(lay4, c4, 2, 100) == OK
+    assert _write_decode(lay4, c4, vn=None) == INV
+    assert _write_decode(lay4, c4, kn=FAKE + 2) == ALN
+
+
 def test_entry_points_reject_before_launch():
     lay, c = _layout(), _cache()
     assert _decode(lay, c, q=None) == INV

@@ -1,0 +1,68 @@
+"""GPU parity of kvq_write_decode (one decode step: append one token per
+row, then decode).
+
+Each case runs the same inputs twice, once with kvq_write followed by
+kvq_paged_decode and once with kvq_write_decode, and requires:
+  * the cache contents (codes, scales, INT4 ring) and the outputs of the two
+    runs to be equal bit for bit;
+  * the fused run to pass the oracle checks (codes and scales bit-exact,
+    attention within atol 2e-3 + rtol 1e-2 of the oracle's fp64 attention).
+Lengths cover empty rows, a single token, a token that opens a new block,
+block boundaries and several partitions.
+"""
+
+import numpy as np
+import pytest
+
+from quantized_paged_kv_02_amd import inputs
+from tests.gpu_harness import check_rows, run_case
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+# (dtype, K granularity, V granularity, table): one case per decode kernel
+# family, including the FP8 variant held to two workgroups per CU
+CASES = [
+    ("int8", "token", "token", "identity"),
+    ("int8", "channel", "head", "shuffled"),
+    ("fp8", "tensor", "tensor", "identity"),
+    ("fp8", "head", "head", "shuffled"),
+    ("fp8", "channel", "token", "identity"),
+    ("int4", "channel", "token", "shuffled"),
+]
+
+LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2]]
+
+
+def _w(dtype, kg, vg, table):
+    extra = {"channel_outliers": (8, 10.0, "k")} if dtype == "int4" else {}
+    return inputs.scaled_down(W["tiny"], name=f"wd-{dtype}-{kg}-{vg}", batch=4,
+                              num_q_heads=8, num_kv_heads=2, dtype=dtype, k_gran=kg,
+                              v_gran=vg, table=table, **extra)
+
+
+def _same_pools(a, b):
+    for name in a.pools:
+        x, y = a.pools[name], b.pools[name]
+        if x.dtype.kind == "f":   # compare bits (NaN poison in unwritten slots)
+            x, y = x.view(np.uint32 if x.itemsize == 4 else np.uint16), \
+                y.view(np.uint32 if y.itemsize == 4 else np.uint16)
+        assert np.array_equal(x, y), f"cache array {name} differs"
+
+
+@pytest.mark.parametrize("dtype,kg,vg,table", CASES)
+@pytest.mark.parametrize("lens", LENS)
+@pytest.mark.parametrize("split", [0, 64])
+def test_write_decode_matches_separate_calls(dtype, kg, vg, table, lens, split):
+    w = _w(dtype, kg, vg, table)
+    sep = run_case(w, lens, split_tokens=split, seed=3)
+    fus = run_case(w, lens, split_tokens=split, seed=3, fused=True)
+    _same_pools(sep, fus)
+    assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), \
+        "fused output differs from kvq_write + kvq_paged_decode"
+    # oracle rows: the non-empty ones (empty rows must give zeros)
+    check_rows(fus, rows=[r for r, s in enumerate(lens) if s > 0])
+    for r, s in enumerate(lens):
+        if s == 0:
+            assert np.all(fus.out[r] == 0)
