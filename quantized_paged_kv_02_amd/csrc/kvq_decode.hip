@@ -100,8 +100,8 @@ struct StreamLds {
   f16 q[16][kQRow];
   // INT4 with a query group of at most 4: per wave, q' = q * s_c of the
   // four heads as fp16 hi and lo rows (channels in the k-slot order of the
-  // nibble conversion) and a zero row for the padding columns
-  uint32_t qb[kWaves][2][5][kQbRow];
+  // key conversion)
+  uint32_t qb[kWaves][2][4][kQbRow];
 };
 // o rows padded by 4 floats so the 16 head rows of one store or load fall
 // in different banks
@@ -318,7 +318,8 @@ template <int KS, int VS>
 __device__ __forceinline__ void load_pair8(Pair8 &t, const DecodeArgs &a, int ph0, int ph1,
                                            int h, int lane, int qd, bool live = true) {
   const int ph[2] = {ph0, ph1};
-  const uint32_t cb = live ? 2048u : 0u, sb = live ? 64u : 0u;
+  // wave-uniform by construction (see load_group4)
+  const uint32_t cb = (uint32_t)uniform(live ? 2048 : 0), sb = (uint32_t)uniform(live ? 64 : 0);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t chunk = (size_t)ph[u] * a.num_kv_heads + h;
@@ -500,10 +501,34 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
 // ---------------------------------------------------------------------------
 // INT4 KIVI: a unit is a 64-token group (4 blocks)
 // ---------------------------------------------------------------------------
+// Key nibbles -> 8 fp16 with offsets, in six operations: the low nibble of
+// each byte, biased to code + 8, is the OCP E4M3 byte 0000nnnn = (code + 8)
+// / 512 exactly (subnormal below 8), which the hardware conversion with
+// scale 512 turns into code + 8; high nibbles take the exponent splice
+// (1152 + 16 code).  Slot e holds nibble kperm(e) = 0, 2, 1, 5, 4, 6, 3, 7;
+// slots 2, 3, 6, 7 are the high nibbles.  The offsets (8 per low slot, 1152
+// per high slot) add a per-(head, group) constant to every score of the
+// group, removed after the product.
+__device__ __forceinline__ f16x8 int4x8_to_f16_koff(uint32_t x) {
+  const uint32_t lo = bsel(x, 0x0F0F0F0Fu, 0x08080808u);
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // nibbles 0, 2
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // nibbles 4, 6
+  const f16x2 b = as_f16x2(bsel(x, 0x00F000F0u, 0x64806480u));                  // nibbles 1, 5
+  const f16x2 d = as_f16x2(bsel(x >> 8, 0x00F000F0u, 0x64806480u));             // nibbles 3, 7
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// The two channels (within a k-slot chunk of 8) of lane l's slot pair
+// 2(l%4), 2(l%4)+1 in the offset conversion's order: (0,2) (1,5) (4,6) (3,7).
+__device__ __forceinline__ int2 koff_pair(int lane) {
+  const int i = lane & 3;
+  return int2{(0x3410 >> (4 * i)) & 0xF, (0x7652 >> (4 * i)) & 0xF};
+}
+
 struct Group4 {
   u32x4 k[4];   // block u: nibbles of channels 32qd..32qd+31, token l%16
   u32x4 v[4];   // block u: nibbles of 4 tokens x 8 channel tiles
-  float ks[2];  // K scales of channels 8(l/4) + l%4 and + 4 (block l/16)
+  float ks[2];  // K scales of channels 8(l/4) + koff_pair(l) (block l/16)
   float vs[2];  // V scales (channel groups 0, 1) of token l of the group
   __device__ explicit Group4(int = 0) {}
 };
@@ -516,7 +541,9 @@ struct Group4 {
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
                                             int pm, int h, int lane, bool live) {
   const int H = a.num_kv_heads;
-  const uint32_t bytes = live ? 1024u : 0u;
+  // wave-uniform by construction; said explicitly so the resource stays in
+  // scalar registers (a per-lane size would make every load a lane loop)
+  const uint32_t bytes = (uint32_t)uniform(live ? 1024 : 0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t chunk = (size_t)ph[u] * H + h;
@@ -524,13 +551,13 @@ __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, cons
     t.v[u] = bld16(make_rsrc(a.v_codes + chunk * 1024, bytes), 16 * lane);
   }
   const size_t chunk = (size_t)pm * H + h;
-  // channels 8(lane/4) + lane%4 and that + 4 (positions 2(lane%4), +1 of
-  // k-slot chunk lane/4), held by block lane/16 of the group
-  const float *ksp = a.k_scales + chunk * 32 + 8 * ((lane >> 2) & 3) + (lane & 3);
+  // channels koff_pair(lane) of k-slot chunk lane/4, held by block lane/16
+  const int2 ko = koff_pair(lane);
+  const float *ksp = a.k_scales + chunk * 32 + 8 * ((lane >> 2) & 3);
   const float2 vs =
       *reinterpret_cast<const float2 *>(a.v_scales + (chunk * kBlock + (lane & 15)) * 2);
-  t.ks[0] = ksp[0];
-  t.ks[1] = ksp[4];
+  t.ks[0] = ksp[ko.x];
+  t.ks[1] = ksp[ko.y];
   t.vs[0] = vs.x;
   t.vs[1] = vs.y;
 }
@@ -567,9 +594,9 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
                                                int qd) {
   // stage the group's scales in this wave's LDS slot (in-order within a wave)
   {
-    const int c0 = 8 * (lane >> 2) + (lane & 3);
-    scl[c0] = t.ks[0];
-    scl[c0 + 4] = t.ks[1];
+    const int2 ko = koff_pair(lane);
+    scl[8 * (lane >> 2) + ko.x] = t.ks[0];
+    scl[8 * (lane >> 2) + ko.y] = t.ks[1];
   }
 #if KVQ_INT4_VBIAS
   // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code:
@@ -699,20 +726,31 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
 // channels of the four heads and shared through LDS.
 // ---------------------------------------------------------------------------
 
-// Score tiles with hi and lo in separate columns: tile u writes head h's
-// hi product to column 4u + h and its lo product to column 4(u^1) + h, so
-// tiles 0, 2 share one accumulator (banks hi0 lo0 hi2 lo2) and tiles 1, 3
-// the other (lo1 hi1 lo3 hi3).  Adding each bank's partner bank gives the
-// compact scores.
-__device__ __forceinline__ f32x4 combine_scores(const f32x4 &ae, const f32x4 &ao, bool odd_bank) {
+// One score operand serves all four blocks: column 4b + h carries head h's
+// hi part of q' in the even banks b and its lo part in the odd banks, so
+// block u's product holds hi and lo of head h in banks (0, 1) and again in
+// (2, 3).  Adding each even bank's odd neighbour gives the score in banks 0
+// and 2; moving block u's score into bank u packs the four blocks into one
+// register set (lane (n, qd) = block n/4, head n%4, tokens 4qd..4qd+3).
+constexpr int kQuadIdentity = 0xE4;  // DPP quad_perm [0, 1, 2, 3]
+__device__ __forceinline__ float hi_plus_lo(float x) {
+  return x + dpp_f32<kRowShl + 4>(0.0f, x);  // even banks: bank + next bank
+}
+__device__ __forceinline__ f32x4 pack_scores(const f32x4 (&acc)[4]) {
   f32x4 s;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float e = ae[i] + dpp_f32<kRowShl + 4>(0.0f, ae[i]);
-    const float o = ao[i] + dpp_f32<kRowShr + 4>(0.0f, ao[i]);
-    s[i] = odd_bank ? o : e;
+    float c = hi_plus_lo(acc[0][i]);                                    // bank 0
+    c = dpp_f32<kQuadIdentity, 0x4>(c, hi_plus_lo(acc[2][i]));          // bank 2
+    c = dpp_f32<kRowShr + 4, 0x2>(c, hi_plus_lo(acc[1][i]));            // bank 1 <- 0
+    s[i] = dpp_f32<kRowShr + 4, 0x8>(c, hi_plus_lo(acc[3][i]));         // bank 3 <- 2
   }
   return s;
+}
+// A value valid in banks 0 and 2 (hi + lo of a column product) in every bank.
+__device__ __forceinline__ float all_banks(float x) {
+  const float c = hi_plus_lo(x);
+  return dpp_f32<kRowShr + 4, 0xA>(c, c);
 }
 
 // Online softmax on compact scores.  The running max moves only when some
@@ -772,14 +810,14 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4 &t, const
 #endif
 }
 
-// qv[hh]: this lane's query values of head hh at channels c0 = 8(lane/4) +
-// lane%4 and c0 + 4; qb: this wave's q' rows; qro[u]: dword offset of this
-// lane's operand row for block u (hi row of head n%4 in bank u, lo row in
-// bank u^1, else the zero row) and row group.
+// qv[hh]: this lane's query values of head hh at channels 8(lane/4) +
+// koff_pair(lane), times 1/16 for the high-nibble slots; qb: this wave's q'
+// rows; qrd: dword offset of this lane's score-operand row (hi row of head
+// n%4 in even banks, lo row in odd banks) and row group.
 __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
-                                                const float (&qv)[4][2], uint32_t *qb,
-                                                const int (&qro)[4], float *scl, float qk_scale,
-                                                int lane, int n, int qd) {
+                                                const float (&qv)[4][2], uint32_t *qb, int qrd,
+                                                float *scl, float qk_scale, int lane, int n,
+                                                int qd) {
 #if KVQ_INT4_VBIAS
   const float vsf = (lane & 2) ? 0.0625f : 1.0f;
 #else
@@ -792,24 +830,29 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
     uint32_t hi, lo;
     split_hi_lo(qv[hh][0] * t.ks[0], qv[hh][1] * t.ks[1], hi, lo);
     qb[hh * kQbRow + lane] = hi;
-    qb[(5 + hh) * kQbRow + lane] = lo;
+    qb[(4 + hh) * kQbRow + lane] = lo;
   }
-  f32x4 ae = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+  // every row of the offset operand is the conversion's per-slot offset
+  const f16 o_lo = (f16)8.0f, o_hi = (f16)1152.0f;
+  const f16x8 aoff = {o_lo, o_lo, o_hi, o_hi, o_lo, o_lo, o_hi, o_hi};
+  f16x8 bq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bq[j] = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qrd + 4 * j));
+  f32x4 acc[4], ac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f16x8 bq = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qro[u] + 4 * j));
-      const f16x8 av = int4x8_to_f16(t.k[u][j]);
-      if (u & 1) {
-        ao = mfma32(av, bq, ao);
-      } else {
-        ae = mfma32(av, bq, ae);
-      }
-    }
+    for (int u = 0; u < 4; ++u) acc[u] = mfma32(int4x8_to_f16_koff(t.k[u][j]), bq[j], acc[u]);
+    ac = mfma32(aoff, bq[j], ac);
   }
-  f32x4 s = combine_scores(ae, ao, (n & 4) != 0);
-  s *= qk_scale;
+  // every row of ac holds the offsets' products with head n%4's hi / lo
+  const float off = all_banks(ac[0]);
+  f32x4 s = pack_scores(acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
   softmax_update_c(st, s, p);
   // V scales of this lane's tokens 4qd..4qd+3 of block n/4 (channel groups 0, 1)
@@ -830,25 +873,20 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   const int n = lane & 15, qd = lane >> 4;
   *reinterpret_cast<u32x4 *>(&sh.s.q[tid >> 4][8 * (tid & 15)]) = qrow;
   uint32_t *qb = &sh.s.qb[wave][0][0][0];
-  qb[4 * kQbRow + lane] = 0u;
-  qb[9 * kQbRow + lane] = 0u;
   __syncthreads();
   float qv[4][2];
   {
-    const int c0 = 8 * (lane >> 2) + (lane & 3);
+    const int2 ko = koff_pair(lane);
+    const int c = 8 * (lane >> 2);
+    // high-nibble slots (odd lanes) carry 16 x code: their q' is taken / 16
+    const float f = (lane & 1) ? 0.0625f : 1.0f;
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
-      qv[hh][0] = (float)sh.s.q[hh][c0];
-      qv[hh][1] = (float)sh.s.q[hh][c0 + 4];
+      qv[hh][0] = (float)sh.s.q[hh][c + ko.x] * f;
+      qv[hh][1] = (float)sh.s.q[hh][c + ko.y] * f;
     }
   }
-  int qro[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int bank = n >> 2;
-    const int row = bank == u ? (n & 3) : (bank == (u ^ 1) ? 5 + (n & 3) : 4);
-    qro[u] = row * kQbRow + 16 * qd;
-  }
+  const int qrd = ((n & 4) ? 4 + (n & 3) : (n & 3)) * kQbRow + 16 * qd;
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -867,7 +905,7 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
       load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
     };
     auto compute = [&](Group4 &t, int) {
-      compute_group4c(st, t, qv, qb, qro, scl, a.qk_scale, lane, n, qd);
+      compute_group4c(st, t, qv, qb, qrd, scl, a.qk_scale, lane, n, qd);
     };
 #if KVQ_INT4_DEPTH == 3
     pipeline3<Group4>(cnt, load, compute);

@@ -67,7 +67,8 @@ def fill_garbage(cache):
 
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
-             table=None, garbage=True, decode_twice=False, fused=False, device="cuda"):
+             table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
+             device="cuda"):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
@@ -142,6 +143,12 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     if decode_twice:
         out2 = torch.full_like(out, float("nan"))
         kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, out2, ws)
+    # further launches on the same workspace (`repeats` of them)
+    rep_outs = []
+    for _ in range(repeats):
+        o = torch.full_like(out, float("nan"))
+        kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, o, ws)
+        rep_outs.append(o)
     torch.cuda.synchronize()
     pools = {name: getattr(cache, name).cpu().numpy()
              for name in ("k_codes", "v_codes", "k_scales", "v_scales")}
@@ -152,6 +159,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
                      q.cpu().numpy(), out.cpu().numpy(), pools, k_static, v_static, scale)
     if decode_twice:
         res.out2 = out2.cpu().numpy()
+    res.repeat_outs = [o.cpu().numpy() for o in rep_outs]
     return res
 
 

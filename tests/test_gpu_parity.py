@@ -97,3 +97,15 @@ def test_int4_residual_64_shuffled():
 def test_int8_chunked_writes(chunks):
     w = _small("int8", "token", "channel")
     check_rows(run_case(w, [300, 1000, 17], chunks=chunks, split_tokens=128))
+
+
+@pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("int4", "channel", "token")])
+def test_repeated_split_launches_on_one_workspace(dtype, kg, vg):
+    # many partitions per row; launches that reuse one workspace (partials
+    # left by the previous launch) must agree bit for bit
+    w = _small(dtype, kg, vg, table="shuffled")
+    res = run_case(w, [1000, 64, 0, 777], split_tokens=64, repeats=6)
+    for o in res.repeat_outs:
+        assert np.array_equal(o.view(np.uint32), res.out.view(np.uint32))
+    check_rows(res, rows=[0, 1, 3])
+    assert np.all(res.out[2] == 0)
