@@ -533,11 +533,9 @@ struct Group4 {
   __device__ explicit Group4(int = 0) {}
 };
 
-// live == false: the loads are issued through zero-size resources (codes)
-// or at the partition's first group (scales) and their values are unused.
-// pm: physical block of this lane's scale row (block lane/16 of the group).
-// live == false: the code loads go through zero-size resources and the
-// scale loads re-read the first group; their values are unused.
+// pm: physical block of this lane's K-scale row (block lane/16 of the
+// group).  live == false: the code loads go through zero-size resources and
+// the scale loads re-read the first group; their values are unused.
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
                                             int pm, int h, int lane, bool live) {
   const int H = a.num_kv_heads;
@@ -560,6 +558,37 @@ __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, cons
   t.ks[1] = ksp[ko.y];
   t.vs[0] = vs.x;
   t.vs[1] = vs.y;
+}
+
+// The group as the compact path reads it: K scales as above, and the V
+// scales of this lane's tokens 4qd..4qd+3 of block (l%16)/4 straight from
+// the scale rows (channel groups 0, 1 interleaved: tokens 0, 1 then 2, 3).
+struct Group4C {
+  u32x4 k[4];
+  u32x4 v[4];
+  float ks[2];
+  f32x4 vsa, vsb;
+  __device__ explicit Group4C(int = 0) {}
+};
+
+// pm as for load_group4; pv: physical block (l%16)/4 of the group.
+__device__ __forceinline__ void load_group4c(Group4C &t, const DecodeArgs &a, const int (&ph)[4],
+                                             int pm, int pv, int h, int lane, bool live) {
+  const int H = a.num_kv_heads;
+  const uint32_t bytes = (uint32_t)uniform(live ? 1024 : 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t chunk = (size_t)ph[u] * H + h;
+    t.k[u] = bld16(make_rsrc(a.k_codes + chunk * 1024, bytes), 16 * lane);
+    t.v[u] = bld16(make_rsrc(a.v_codes + chunk * 1024, bytes), 16 * lane);
+  }
+  const int2 ko = koff_pair(lane);
+  const float *ksp = a.k_scales + ((size_t)pm * H + h) * 32 + 8 * ((lane >> 2) & 3);
+  t.ks[0] = ksp[ko.x];
+  t.ks[1] = ksp[ko.y];
+  const float *vsp = a.v_scales + ((size_t)pv * H + h) * (kBlock * 2) + 8 * (lane >> 4);
+  t.vsa = ld16f(vsp);
+  t.vsb = ld16f(vsp + 4);
 }
 
 // Join block b0's and block b1's nibbles of channel tile j (dword j>>1 of
@@ -789,7 +818,7 @@ __device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
 }
 
 template <int PR>
-__device__ __forceinline__ void value_pair_c(Softmax &st, const Group4 &t, const f16x8 &pb0,
+__device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, const f16x8 &pb0,
                                              const f16x8 &pb1) {
 #if KVQ_INT4_VBIAS
   const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
@@ -814,16 +843,9 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4 &t, const
 // koff_pair(lane), times 1/16 for the high-nibble slots; qb: this wave's q'
 // rows; qrd: dword offset of this lane's score-operand row (hi row of head
 // n%4 in even banks, lo row in odd banks) and row group.
-__device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
+__device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
                                                 const float (&qv)[4][2], uint32_t *qb, int qrd,
-                                                float *scl, float qk_scale, int lane, int n,
-                                                int qd) {
-#if KVQ_INT4_VBIAS
-  const float vsf = (lane & 2) ? 0.0625f : 1.0f;
-#else
-  const float vsf = 1.0f;
-#endif
-  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0] * vsf, t.vs[1] * vsf};
+                                                float qk_scale, int lane, int n) {
   // q' of this lane's two channels for the four heads (dword `lane` of each row)
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
@@ -855,14 +877,17 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4 &t,
   for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
   softmax_update_c(st, s, p);
-  // V scales of this lane's tokens 4qd..4qd+3 of block n/4 (channel groups 0, 1)
-  const float *vsp = scl + 128 + 2 * (16 * (n >> 2) + 4 * qd);
-  const f32x4 va0 = *reinterpret_cast<const f32x4 *>(vsp);
-  const f32x4 va1 = *reinterpret_cast<const f32x4 *>(vsp + 4);
-  const uint32_t d0[2] = {pack_rne(p[0] * va0[0], p[1] * va0[2]),
-                          pack_rne(p[2] * va1[0], p[3] * va1[2])};
-  const uint32_t d1[2] = {pack_rne(p[0] * va0[1], p[1] * va0[3]),
-                          pack_rne(p[2] * va1[1], p[3] * va1[3])};
+  // weights times the V scales of this lane's tokens (channel groups 0, 1)
+#if KVQ_INT4_VBIAS
+  // tokens 2, 3 of every 4 meet value codes stored as 1152 + 16 code
+  const float p2 = p[2] * 0.0625f, p3 = p[3] * 0.0625f;
+#else
+  const float p2 = p[2], p3 = p[3];
+#endif
+  const uint32_t d0[2] = {pack_rne(p[0] * t.vsa[0], p[1] * t.vsa[2]),
+                          pack_rne(p2 * t.vsb[0], p3 * t.vsb[2])};
+  const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
+                          pack_rne(p2 * t.vsb[1], p3 * t.vsb[3])};
   value_pair_c<0>(st, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
   value_pair_c<1>(st, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
 }
@@ -892,25 +917,24 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   const int blk0 = p * a.part_blocks;
   const int blk1 = min(n_blocks, blk0 + a.part_blocks);
   const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  float *scl = sh.s.scl[wave];
   for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
     const int c1 = min(blk1, c0 + kIdChunk);
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4 &t, int k, bool live) {
+    auto load = [&](Group4C &t, int k, bool live) {
       const int j0 = live ? 4 * (wave + kWaves * k) : 0;
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
-      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
+      load_group4c(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane, live);
     };
-    auto compute = [&](Group4 &t, int) {
-      compute_group4c(st, t, qv, qb, qrd, scl, a.qk_scale, lane, n, qd);
+    auto compute = [&](Group4C &t, int) {
+      compute_group4c(st, t, qv, qb, qrd, a.qk_scale, lane, n);
     };
 #if KVQ_INT4_DEPTH == 3
-    pipeline3<Group4>(cnt, load, compute);
+    pipeline3<Group4C>(cnt, load, compute);
 #else
-    pipeline<Group4>(cnt, [&](Group4 &t, int k) { load(t, k, true); }, compute);
+    pipeline<Group4C>(cnt, [&](Group4C &t, int k) { load(t, k, true); }, compute);
 #endif
   }
   // back to one head per lane (n < 4): this lane's share of head n's sum
