@@ -912,6 +912,13 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
     }
   }
   const int qrd = ((n & 4) ? 4 + (n & 3) : (n & 3)) * kQbRow + 16 * qd;
+  // from one head per lane (lanes n < 4, as the window left it) to the
+  // compact layout: every bank takes head n%4's running max, the sum stays
+  // in bank 0 (the banks' shares are added back at the end)
+  st.m = dpp_f32<kRowShr + 4, 0x2>(st.m, st.m);
+  st.m = dpp_f32<kRowShr + 8, 0x4>(st.m, st.m);
+  st.m = dpp_f32<kRowShr + 12, 0x8>(st.m, st.m);
+  st.l = n < 4 ? st.l : 0.0f;
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -1129,11 +1136,14 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
     if (p >= n_main) return;
     if constexpr (G4) {
+      // the window first: its loads and arithmetic overlap the start of the
+      // INT4 stream instead of trailing it with nothing else in flight
+      if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
       stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
       stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
     }
-    if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
   } else {
     const int n_main = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
     if (p >= n_main) return;
