@@ -50,35 +50,13 @@
 namespace kvq {
 namespace {
 
-// Tuning knobs (compile-time): software pipeline depth of the INT4 and
-// INT8/FP8 streams (2 = one unit ahead, 3 = two units ahead) and the
-// workgroups per CU the register allocation is bounded for.
-#ifndef KVQ_INT4_DEPTH
-#define KVQ_INT4_DEPTH 2
-#endif
-#ifndef KVQ_Q8_DEPTH
-#define KVQ_Q8_DEPTH 2
-#endif
-#ifndef KVQ_BRANCHLESS_RESCALE
-#define KVQ_BRANCHLESS_RESCALE 0
-#endif
-// INT4 values: convert nibbles without removing the fp16 exponent bias and
-// cancel the bias with one extra matrix-core product per channel tile and
-// block pair (moves work from the vector ALUs to the matrix cores).
-#ifndef KVQ_INT4_VBIAS
-#define KVQ_INT4_VBIAS 1
-#endif
-
 constexpr int kWaves = 4;
 constexpr int kQRow = 128 + 8;  // LDS row of a staged query (fp16)
 constexpr int kQbRow = 64 + 4;  // LDS row of q' (dwords of fp16 pairs)
 constexpr int kThreads = 64 * kWaves;
-// Block ids staged in LDS per pass (a small first pass lets streaming start
-// sooner; measured better than staging whole partitions at once).
-#ifndef KVQ_ID_CHUNK
-#define KVQ_ID_CHUNK 256
-#endif
-constexpr int kIdChunk = KVQ_ID_CHUNK;
+// Block ids staged in LDS per pass (one id per thread; 512-id passes
+// measured no faster).
+constexpr int kIdChunk = kThreads;
 constexpr float kNegInf = -__builtin_inff();
 // The running max is only moved when a score exceeds it by more than this
 // (log2 units), so p <= 2^8 and rescaling of o is rare.
@@ -155,19 +133,6 @@ __device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4]
   for (int u = 0; u < 4; ++u)
     bm = fmaxf(bm, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
   bm = max_over_quads(bm);
-#if KVQ_BRANCHLESS_RESCALE
-  {
-    // one straight-line block per group: always rescale (alpha = 1 when the
-    // max did not move by more than the slack)
-    const bool need = bm > st.m + kRescaleSlack;
-    const float mn = need ? bm : st.m;
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
-    st.l *= alpha;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
-    st.m = mn;
-  }
-#else
   const bool need = bm > st.m + kRescaleSlack;
   if (__any(need)) {
     const float mn = need ? bm : st.m;
@@ -177,7 +142,6 @@ __device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4]
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
     st.m = mn;
   }
-#endif
   float sum = 0.0f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -276,32 +240,6 @@ __device__ __forceinline__ void pipeline(int cnt, Load &&load, Compute &&compute
   }
 }
 
-// Three-buffer version: units k+1 and k+2 are in flight while unit k is
-// consumed.  Every step issues the same loads; load(T&, k, live) with
-// live == false must issue them without memory traffic (zero-size buffer
-// resources), so the compiler's wait counts are the same on every path.
-template <typename T, typename Load, typename Compute>
-__device__ __forceinline__ void pipeline3(int cnt, Load &&load, Compute &&compute) {
-  if (cnt <= 0) return;
-  T a(0), b(1), c(2);
-  load(a, 0, true);
-  load(b, 1, 1 < cnt);
-  for (int k = 0; k < cnt; k += 3) {
-    load(c, k + 2, k + 2 < cnt);
-    stage_fence();
-    compute(a, k);
-    stage_fence();
-    load(a, k + 3, k + 3 < cnt);
-    stage_fence();
-    if (k + 1 < cnt) compute(b, k + 1);
-    stage_fence();
-    load(b, k + 4, k + 4 < cnt);
-    stage_fence();
-    if (k + 2 < cnt) compute(c, k + 2);
-    stage_fence();
-  }
-}
-
 // ---------------------------------------------------------------------------
 // INT8 / FP8: a unit is a pair of 16-token blocks
 // ---------------------------------------------------------------------------
@@ -313,13 +251,11 @@ struct Pair8 {
   __device__ explicit Pair8(int = 0) {}
 };
 
-// live == false issues the same loads through zero-size resources.
 template <int KS, int VS>
 __device__ __forceinline__ void load_pair8(Pair8 &t, const DecodeArgs &a, int ph0, int ph1,
-                                           int h, int lane, int qd, bool live = true) {
+                                           int h, int lane, int qd) {
   const int ph[2] = {ph0, ph1};
-  // wave-uniform by construction (see load_group4)
-  const uint32_t cb = (uint32_t)uniform(live ? 2048 : 0), sb = (uint32_t)uniform(live ? 64 : 0);
+  constexpr uint32_t cb = 2048, sb = 64;  // bytes of a code chunk / a scale row
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t chunk = (size_t)ph[u] * a.num_kv_heads + h;
@@ -464,19 +400,14 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const bool last_masked = (c0 + 2 * npairs) * kBlock > end_tok;
     const int nfull = npairs - (last_masked ? 1 : 0);
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Pair8 &t, int k, bool live) {
-      const int j0 = live ? 2 * (wave + kWaves * k) : 0;
-      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd,
-                         live);
+    auto load = [&](Pair8 &t, int k) {
+      const int j0 = 2 * (wave + kWaves * k);
+      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd);
     };
     auto compute = [&](Pair8 &t, int) {
       compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
     };
-#if KVQ_Q8_DEPTH == 3
-    pipeline3<Pair8>(cnt, load, compute);
-#else
-    pipeline<Pair8>(cnt, [&](Pair8 &t, int k) { load(t, k, true); }, compute);
-#endif
+    pipeline<Pair8>(cnt, load, compute);
     if (last_masked && wave == nfull % kWaves) {
       const int j0 = 2 * nfull;
       const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
@@ -533,15 +464,11 @@ struct Group4 {
   __device__ explicit Group4(int = 0) {}
 };
 
-// pm: physical block of this lane's K-scale row (block lane/16 of the
-// group).  live == false: the code loads go through zero-size resources and
-// the scale loads re-read the first group; their values are unused.
+// pm: physical block of this lane's K-scale row (block lane/16 of the group).
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
-                                            int pm, int h, int lane, bool live) {
+                                            int pm, int h, int lane) {
   const int H = a.num_kv_heads;
-  // wave-uniform by construction; said explicitly so the resource stays in
-  // scalar registers (a per-lane size would make every load a lane loop)
-  const uint32_t bytes = (uint32_t)uniform(live ? 1024 : 0);
+  constexpr uint32_t bytes = 1024;  // one (block, head) code chunk
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t chunk = (size_t)ph[u] * H + h;
@@ -573,9 +500,9 @@ struct Group4C {
 
 // pm as for load_group4; pv: physical block (l%16)/4 of the group.
 __device__ __forceinline__ void load_group4c(Group4C &t, const DecodeArgs &a, const int (&ph)[4],
-                                             int pm, int pv, int h, int lane, bool live) {
+                                             int pm, int pv, int h, int lane) {
   const int H = a.num_kv_heads;
-  const uint32_t bytes = (uint32_t)uniform(live ? 1024 : 0);
+  constexpr uint32_t bytes = 1024;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t chunk = (size_t)ph[u] * H + h;
@@ -627,14 +554,10 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     scl[8 * (lane >> 2) + ko.x] = t.ks[0];
     scl[8 * (lane >> 2) + ko.y] = t.ks[1];
   }
-#if KVQ_INT4_VBIAS
   // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code:
   // their weights carry 1/16 (exact)
   const float vsf = (lane & 2) ? 0.0625f : 1.0f;
   *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0] * vsf, t.vs[1] * vsf};
-#else
-  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0], t.vs[1]};
-#endif
   // Scores, channel chunk by chunk: q' = q * s_c for channels 32qd+8j..+7
   // as fp16 hi + lo in the k-slot order of the nibble conversion, applied
   // to the chunk of all four blocks.
@@ -683,7 +606,6 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     const f32x4 g0b = {vb0[0], vb0[2], vb1[0], vb1[2]}, g1b = {vb0[1], vb0[3], vb1[1], vb1[3]};
     const f16x8 pb0 = p_operand(p0 * g0a, p1 * g0b);
     const f16x8 pb1 = p_operand(p0 * g1a, p1 * g1b);
-#if KVQ_INT4_VBIAS
     // every row of the bias operand is the per-k-slot bias of the biased
     // conversion (1032 for slots 0,1,4,5; 1152 for 2,3,6,7), negated
     const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
@@ -697,13 +619,6 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     // matrix instructions after the previous one)
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
-#else
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w = pair_tile(t.v[2 * pr][j >> 1], t.v[2 * pr + 1][j >> 1], j & 1);
-      st.o[j] = mfma32(int4x8_to_f16(w), j < 4 ? pb0 : pb1, st.o[j]);
-    }
-#endif
   }
 }
 
@@ -725,23 +640,19 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4 &t, int k, bool live) {
-      const int j0 = live ? 4 * (wave + kWaves * k) : 0;
+    auto load = [&](Group4 &t, int k) {
+      const int j0 = 4 * (wave + kWaves * k);
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
       // a per-lane LDS read: selecting among ph[] per lane would become a
       // private-array access, whose scratch load joins the in-order vmcnt
       // queue and makes every group wait for all loads in flight
-      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane, live);
+      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane);
     };
     auto compute = [&](Group4 &t, int) {
       compute_group4(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
     };
-#if KVQ_INT4_DEPTH == 3
-    pipeline3<Group4>(cnt, load, compute);
-#else
-    pipeline<Group4>(cnt, [&](Group4 &t, int k) { load(t, k, true); }, compute);
-#endif
+    pipeline<Group4>(cnt, load, compute);
   }
 }
 
@@ -820,7 +731,6 @@ __device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
 template <int PR>
 __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, const f16x8 &pb0,
                                              const f16x8 &pb1) {
-#if KVQ_INT4_VBIAS
   const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
   const f16x8 abias = {b0, b0, b1, b1, b0, b0, b1, b1};
 #pragma unroll
@@ -830,13 +740,6 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, cons
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
-#else
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = pair_tile(t.v[2 * PR][j >> 1], t.v[2 * PR + 1][j >> 1], j & 1);
-    st.o[j] = mfma32(int4x8_to_f16(w), j < 4 ? pb0 : pb1, st.o[j]);
-  }
-#endif
 }
 
 // qv[hh]: this lane's query values of head hh at channels 8(lane/4) +
@@ -878,12 +781,8 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
   f32x4 p;
   softmax_update_c(st, s, p);
   // weights times the V scales of this lane's tokens (channel groups 0, 1)
-#if KVQ_INT4_VBIAS
   // tokens 2, 3 of every 4 meet value codes stored as 1152 + 16 code
   const float p2 = p[2] * 0.0625f, p3 = p[3] * 0.0625f;
-#else
-  const float p2 = p[2], p3 = p[3];
-#endif
   const uint32_t d0[2] = {pack_rne(p[0] * t.vsa[0], p[1] * t.vsa[2]),
                           pack_rne(p2 * t.vsb[0], p3 * t.vsb[2])};
   const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
@@ -929,20 +828,16 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4C &t, int k, bool live) {
-      const int j0 = live ? 4 * (wave + kWaves * k) : 0;
+    auto load = [&](Group4C &t, int k) {
+      const int j0 = 4 * (wave + kWaves * k);
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
-      load_group4c(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane, live);
+      load_group4c(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
     };
     auto compute = [&](Group4C &t, int) {
       compute_group4c(st, t, qv, qb, qrd, a.qk_scale, lane, n);
     };
-#if KVQ_INT4_DEPTH == 3
-    pipeline3<Group4C>(cnt, load, compute);
-#else
-    pipeline<Group4C>(cnt, [&](Group4C &t, int k) { load(t, k, true); }, compute);
-#endif
+    pipeline<Group4C>(cnt, load, compute);
   }
   // back to one head per lane (n < 4): this lane's share of head n's sum
   st.l = bank_sum(st.l);
