@@ -76,6 +76,11 @@ def _cpu_unit(args):
             k_hat, v_hat = oracle.kivi_dequantize(full)
             oracle.decode_attention(q, k_hat, v_hat, scale)
             return time.perf_counter() - t0
+        if w.dtype == "fp16":
+            # unquantized cache: the new token is stored as is
+            t0 = time.perf_counter()
+            oracle.decode_attention(q, k, v, scale)
+            return time.perf_counter() - t0
         if w.k_gran == "token":
             kc, ks = oracle.quantize_per_token(k, w.dtype)
             vc, vs = oracle.quantize_per_token(v, w.dtype)

@@ -26,6 +26,9 @@
  *    ([intelli] §6 Q1; [oh-bug] section "为什么长上下文更需要 KV Cache
  *    Quantization").
  *
+ *  - An unquantized FP16 cache through the same kernels, the baseline of
+ *    the memory / latency comparison ([intelli] §5).
+ *
  * Conventions for every entry point:
  *  - All buffers are caller-owned DEVICE pointers except the kvq_layout and
  *    kvq_cache structs themselves, which are host memory read during the call
@@ -85,6 +88,15 @@
  *   v_resid : fp16 [ring_rows][H][RING/4][128][4]; token t at slot
  *             s = t % RING is element [s>>2][c][s&3].
  * Both granularity fields must be KVQ_PER_CHANNEL (K) and KVQ_PER_TOKEN (V).
+ *
+ * ---- FP16 (unquantized) layout: fp16 [NB][H][2048] for each of K and V ----
+ * The baseline the quantized formats are measured against ([intelli] §5:
+ * INT8 against FP16 memory and latency).  Values are stored as given; one
+ * (block, head) chunk is 4096 bytes.  Byte offset of (slot s, channel c):
+ *   K: 1024*((c>>3)&3) + 256*(c>>5) + 16*s + 2*(c&7)
+ *   V: 1024*(c>>5) + 256*(s>>2) + 16*(c&15) + 8*((c>>4)&1) + 2*(s&3)
+ * k_codes / v_codes point at these arrays.  There are no scales: the
+ * granularity fields are ignored and k_scales / v_scales may be NULL.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -109,7 +121,8 @@ typedef enum kvq_status {
 typedef enum kvq_dtype {
   KVQ_INT8 = 1,     /* 1 byte per value, symmetric, divisor 127             */
   KVQ_FP8_E4M3 = 2, /* 1 byte per value, OCP E4M3, divisor 448              */
-  KVQ_INT4 = 3      /* 0.5 byte per value, KIVI grouping, divisor 7         */
+  KVQ_INT4 = 3,     /* 0.5 byte per value, KIVI grouping, divisor 7         */
+  KVQ_FP16 = 4      /* 2 bytes per value, unquantized                       */
 } kvq_dtype;
 
 typedef enum kvq_granularity {
@@ -178,7 +191,7 @@ size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
  *   max_new_per_seq: host bound on n_b.
  * INT8/FP8: writes codes (and per-token scales when the granularity is
  * KVQ_PER_TOKEN) into the block slots.  Static scales are read from the
- * cache's scale arrays.
+ * cache's scale arrays.  FP16: stores the values in the block slots.
  * INT4: first quantizes every 64-token group that leaves the fp16 window
  * (from the ring or straight from k_new/v_new) into INT4 blocks with its
  * scales, then stores the remaining new tokens in the ring (two launches,
@@ -196,7 +209,7 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
  *   out[b][hq][:] = sum_t softmax_t(s_t) * v_hat[t],
  *   s_t = softmax_scale * dot(q[b][hq], k_hat[t]),  t < seq_lens[b],
  * with KV head hq / (Hq/H), k_hat/v_hat the dequantized values (code*scale,
- * or fp16 for INT4 residual tokens).
+ * or fp16 for INT4 residual tokens and for an FP16 cache).
  *   q        : fp16 [batch][Hq][128]
  *   out      : fp32 [batch][Hq][128]; rows with seq_lens[b] == 0 get zeros.
  *   workspace: device buffer of at least kvq_decode_workspace_bytes(layout,
@@ -224,9 +237,10 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
  *                  seq_lens[b] == 0 take no token and their entry is unread.
  *   q, block_tables, seq_lens, max_seq_len, softmax_scale, out, workspace,
  *   workspace_bytes: as for kvq_paged_decode.
- * INT8/FP8: a single launch (plus the partition merge when the launch is
- * split): the workgroup that streams a row's last partition quantizes and
- * stores the row's token (codes and per-token scales) before streaming.
+ * INT8/FP8/FP16: a single launch (plus the partition merge when the launch
+ * is split): the workgroup that streams a row's last partition quantizes
+ * (FP16: copies) and stores the row's token (codes and per-token scales)
+ * before streaming.
  * INT4: the kvq_write launches, then the decode launches.
  * Errors: as for kvq_paged_decode; additionally KVQ_ERR_INVALID_ARG when
  * k_new or v_new is NULL (batch > 0) and KVQ_ERR_ALIGNMENT when either is

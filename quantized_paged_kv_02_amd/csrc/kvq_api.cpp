@@ -20,6 +20,7 @@ constexpr int kGroup = 64;
 constexpr long kCUs = 256;
 constexpr long kWgOverheadInt4 = 16;
 constexpr long kWgOverheadQ8 = 8;
+constexpr long kWgOverheadF16 = 4;  // a block streams twice the bytes of INT8
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -31,10 +32,13 @@ int kivi_len(int s, int residual) {
 kvq_status check_layout(const kvq_layout *L) {
   if (!L) return KVQ_ERR_INVALID_ARG;
   if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
-  if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4)
+  if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4 &&
+      L->dtype != KVQ_FP16)
     return KVQ_ERR_INVALID_ARG;
-  if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
-  if (L->v_gran < KVQ_PER_TENSOR || L->v_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
+  if (L->dtype != KVQ_FP16) {  // an FP16 cache has no scales
+    if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
+    if (L->v_gran < KVQ_PER_TENSOR || L->v_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
+  }
   if (L->num_kv_heads < 1 || L->num_q_heads < 1) return KVQ_ERR_INVALID_ARG;
   if (L->num_q_heads % L->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
   if (L->num_blocks < 1 || L->max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
@@ -54,10 +58,11 @@ kvq_status check_layout(const kvq_layout *L) {
 
 kvq_status check_cache(const kvq_layout *L, const kvq_cache *C, int32_t batch) {
   if (!C) return KVQ_ERR_INVALID_ARG;
-  if (!C->k_codes || !C->v_codes || !C->k_scales || !C->v_scales) return KVQ_ERR_INVALID_ARG;
-  if (!aligned16(C->k_codes) || !aligned16(C->v_codes) || !aligned16(C->k_scales) ||
-      !aligned16(C->v_scales))
-    return KVQ_ERR_ALIGNMENT;
+  if (!C->k_codes || !C->v_codes) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(C->k_codes) || !aligned16(C->v_codes)) return KVQ_ERR_ALIGNMENT;
+  if (L->dtype == KVQ_FP16) return KVQ_OK;  // no scales, no ring
+  if (!C->k_scales || !C->v_scales) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(C->k_scales) || !aligned16(C->v_scales)) return KVQ_ERR_ALIGNMENT;
   if (L->dtype == KVQ_INT4) {
     if (!C->k_resid || !C->v_resid) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(C->k_resid) || !aligned16(C->v_resid)) return KVQ_ERR_ALIGNMENT;
@@ -93,7 +98,9 @@ Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
     const long resident =
         kCUs * kvq::decode_wg_per_cu(L->dtype, kvq::decode_scale_kind(L->k_gran),
                                      kvq::decode_scale_kind(L->v_gran));
-    const long overhead = int4 ? kWgOverheadInt4 : kWgOverheadQ8;
+    const long overhead = int4                       ? kWgOverheadInt4
+                          : L->dtype == KVQ_FP16 ? kWgOverheadF16
+                                                 : kWgOverheadQ8;
     const long top = blocks > quantum ? blocks : quantum;
     long best_t = -1;
     pb = quantum;
@@ -208,6 +215,8 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
     // groups leaving the window: at most ceil(n/64) + 1 per row
     const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup + 1;
     e = kvq::launch_write_int4(a, batch, max_new_per_seq, max_groups, s);
+  } else if (layout->dtype == KVQ_FP16) {
+    e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);
   } else {
     e = kvq::launch_write_q8(a, layout->dtype, batch, max_new_per_seq, s);
   }

@@ -8,17 +8,20 @@
 
 namespace kvq {
 
-enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3 };  // kvq_dtype values
+enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4 };  // kvq_dtype values
 // Granularity as the decode kernel sees it: a scale that is uniform over a
 // (row, KV head) (per-tensor or per-head), per channel, or per token.
 enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
 
 // Decode workgroups (four wavefronts) guaranteed resident per CU for a cache
 // dtype and K / V scale kinds: the kernel's register bound and the partition
-// plan's round size.  INT4 and FP8 with per-token V and non-uniform K scales
-// need the larger per-wave register budget of two per CU.
+// plan's round size.  INT4, FP16 (twice the bytes in flight per unit) and
+// FP8 with per-token V and non-uniform K scales need the larger per-wave
+// register budget of two per CU.
 constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
-  return dtype == kInt4 ? 2 : (dtype == kFp8 && v_kind == kToken && k_kind != kUniform) ? 2 : 3;
+  return (dtype == kInt4 || dtype == kFp16) ? 2
+         : (dtype == kFp8 && v_kind == kToken && k_kind != kUniform) ? 2
+                                                                      : 3;
 }
 
 struct WriteArgs {
@@ -51,7 +54,7 @@ struct DecodeArgs {
   const uint16_t *q;
   const int32_t *block_tables;
   const int32_t *seq_lens;
-  // Fused append (INT8/FP8): row b's new token, fp16 [B][H][128] at position
+  // Fused append (INT8/FP8/FP16): row b's new token, fp16 [B][H][128] at position
   // seq_lens[b] - 1, quantized and stored (codes, per-token scales) by the
   // workgroup that streams the row's last partition.  Null: no append.
   const uint16_t *k_new;
@@ -81,6 +84,7 @@ int decode_scale_kind(int granularity);
 
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch,
                            int max_new, hipStream_t stream);
+hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStream_t stream);
 hipError_t launch_write_int4(const WriteArgs &a, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind,

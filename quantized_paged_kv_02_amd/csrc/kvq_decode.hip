@@ -43,6 +43,11 @@
 // scales (and INT4 group scales) fold into q, kept exact as an fp16 hi/lo
 // pair; per-token V scales fold into p, uniform and per-channel V scales are
 // applied to o once per wave.
+//
+// An unquantized FP16 cache ([intelli] §5, the baseline of the INT8 memory
+// and latency comparison) runs through the same skeleton: its layout puts
+// each lane's fp16 operands in 16-byte runs, so a pair of blocks is sixteen
+// loads and the matrix-core products with no conversion and no scales.
 #include "kvq_args.h"
 #include "kvq_device.h"
 #include "kvq_quant.h"
@@ -337,6 +342,80 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP16 (unquantized): a unit is a pair of 16-token blocks whose 16-byte
+// loads are the matrix-core operands as they stand
+// ---------------------------------------------------------------------------
+struct Pair16 {
+  u32x4 k[2][4];  // block u, quarter j: channels 32qd+8j..+7 of token l%16
+  u32x4 v[2][4];  // block u, quarter j: tokens 4qd..4qd+3 of channel 32j+l%16,
+                  // then of channel 32j+16+l%16
+  __device__ explicit Pair16(int = 0) {}
+};
+
+__device__ __forceinline__ void load_pair16(Pair16 &t, const DecodeArgs &a, int ph0, int ph1,
+                                            int h, int lane) {
+  constexpr uint32_t cb = 4096;  // bytes of a (block, head) chunk
+  const size_t c0 = ((size_t)ph0 * a.num_kv_heads + h) * cb;
+  const size_t c1 = ((size_t)ph1 * a.num_kv_heads + h) * cb;
+  const rsrc_t k0 = make_rsrc(a.k_codes + c0, cb), k1 = make_rsrc(a.k_codes + c1, cb);
+  const rsrc_t v0 = make_rsrc(a.v_codes + c0, cb), v1 = make_rsrc(a.v_codes + c1, cb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.k[0][j] = bld16(k0, 16 * lane + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.k[1][j] = bld16(k1, 16 * lane + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.v[0][j] = bld16(v0, 16 * lane + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.v[1][j] = bld16(v1, 16 * lane + 1024 * j);
+}
+
+// V operand of output tile j (channels 16j + l%16): the lane's 4 tokens of
+// block 0, then of block 1
+__device__ __forceinline__ f16x8 value_operand16(const Pair16 &t, int j) {
+  const int w = 2 * (j & 1);
+  return cat(u2_to_f16x4(u32x2{t.v[0][j >> 1][w], t.v[0][j >> 1][w + 1]}),
+             u2_to_f16x4(u32x2{t.v[1][j >> 1][w], t.v[1][j >> 1][w + 1]}));
+}
+
+// valid: tokens of the pair that are attended (TAIL only), 1..32.
+template <bool TAIL>
+__device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16x8 (&bq)[4],
+                                               float kmul, int valid, int qd) {
+  f32x4 s[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[u] = mfma32(u4_to_f16x8(t.k[u][j]), bq[j], s[u]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = s[u][r] * kmul;
+      s[u][r] = (TAIL && 16 * u + 4 * qd + r >= valid) ? kNegInf : v;
+    }
+  }
+  f32x4 p0, p1;
+  softmax_update(st, s[0], s[1], p0, p1);
+  const f16x8 pb = p_operand(p0, p1);
+  if (TAIL) {
+    // zero the values of unattended tokens (stale, possibly NaN): dword w
+    // of a quarter holds tokens 2(w&1), 2(w&1)+1 of the lane's four
+    const int v0 = valid - 4 * qd, v1 = valid - 16 - 4 * qd;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        t.v[0][j][w] = keep_bytes(t.v[0][j][w], 2 * (v0 - 2 * (w & 1)));
+        t.v[1][j][w] = keep_bytes(t.v[1][j][w], 2 * (v1 - 2 * (w & 1)));
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(value_operand16(t, j), pb, st.o[j]);
+}
+
+template <int DT> struct UnitOf { using T = Pair8; };
+template <> struct UnitOf<kFp16> { using T = Pair16; };
+
 // Query operand of the score product for this lane's channels 32qd..32qd+31
 // (as 4 x 8 fp16), zero for the 16 - g padding columns.
 __device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int b, int h, int n,
@@ -359,7 +438,10 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
   load_q(qr, a, b, h, n, qd);
   f16x8 bq[4], bq_lo[4];
   float kmul = a.qk_scale;
-  if constexpr (KS == kChannel) {
+  if constexpr (DT == kFp16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bq[j] = bq_lo[j] = u4_to_f16x8(qr[j]);
+  } else if constexpr (KS == kChannel) {
     const float *ksc = a.k_scales + h * kHeadDim + 32 * qd;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -400,24 +482,41 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const bool last_masked = (c0 + 2 * npairs) * kBlock > end_tok;
     const int nfull = npairs - (last_masked ? 1 : 0);
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Pair8 &t, int k) {
+    using Unit = typename UnitOf<DT>::T;
+    auto load_unit = [&](Unit &t, int ph0, int ph1) {
+      if constexpr (DT == kFp16) {
+        load_pair16(t, a, ph0, ph1, h, lane);
+      } else {
+        load_pair8<KS, VS>(t, a, ph0, ph1, h, lane, qd);
+      }
+    };
+    auto load = [&](Unit &t, int k) {
       const int j0 = 2 * (wave + kWaves * k);
-      load_pair8<KS, VS>(t, a, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]), h, lane, qd);
+      load_unit(t, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]));
     };
-    auto compute = [&](Pair8 &t, int) {
-      compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
+    auto compute = [&](Unit &t, int) {
+      if constexpr (DT == kFp16) {
+        compute_pair16<false>(st, t, bq, kmul, 32, qd);
+      } else {
+        compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
+      }
     };
-    pipeline<Pair8>(cnt, load, compute);
+    pipeline<Unit>(cnt, load, compute);
     if (last_masked && wave == nfull % kWaves) {
       const int j0 = 2 * nfull;
       const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
       const int ph0 = uniform(sh.s.ids[j0]);
       const int ph1 = c0 + j0 + 1 < c1 ? uniform(sh.s.ids[j0 + 1]) : ph0;
-      Pair8 t;
-      load_pair8<KS, VS>(t, a, ph0, ph1, h, lane, qd);
-      compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid, qd);
+      Unit t;
+      load_unit(t, ph0, ph1);
+      if constexpr (DT == kFp16) {
+        compute_pair16<true>(st, t, bq, kmul, valid, qd);
+      } else {
+        compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid, qd);
+      }
     }
   }
+  if constexpr (DT == kFp16) return;  // no scales
   // uniform and per-channel V scales multiply o once
   if constexpr (VS == kUniform) {
     const float s = a.v_scales[h * a.v_head_stride];
@@ -983,6 +1082,26 @@ __device__ __forceinline__ void append_token_q8(const DecodeArgs &a, int b, int 
   if (kind == kToken && lane == 0) scales[chunk * kBlock + slot] = q.scale;
 }
 
+// Fused append of row b's new token for KV head h (FP16): wave 0 stores K,
+// wave 1 V, as the write kernel does.
+__device__ __forceinline__ void append_token_f16(const DecodeArgs &a, int b, int h, int seq_len,
+                                                 int wave, int lane) {
+  if (wave >= 2) return;
+  const bool is_v = wave == 1;
+  const int H = a.num_kv_heads;
+  const int pos = seq_len - 1;
+  const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kBlock];
+  const uint16_t *src = (is_v ? a.v_new : a.k_new) + ((size_t)b * H + h) * kHeadDim;
+  const uint32_t raw = reinterpret_cast<const uint32_t *>(src)[lane];
+  uint8_t *chunk = const_cast<uint8_t *>(is_v ? a.v_codes : a.k_codes) +
+                   ((size_t)phys * H + h) * 4096;
+  if (is_v) {
+    store_v_f16(chunk, pos % kBlock, lane, raw);
+  } else {
+    store_k_f16(chunk, pos % kBlock, lane, raw);
+  }
+}
+
 // G4: INT4 cache with a query group of at most 4 (compact score layout).
 template <int DT, int KS, int VS, bool G4>
 __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
@@ -1045,7 +1164,11 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     if (a.k_new != nullptr && p == n_main - 1) {
       // this workgroup streams the row's last block: store the new token
       // first, complete (every counter drained) before any wave reads it
-      append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
+      if constexpr (DT == kFp16) {
+        append_token_f16(a, b, h, seq_len, wave, lane);
+      } else {
+        append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -1054,8 +1177,8 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
   merge_and_store(a, sh, st, b, h, p, direct, wave, lane, tid);
 }
 
-// INT8 / FP8 and INT4 caches get separate kernels so that each is held to
-// the register budget of its own occupancy.
+// INT8 / FP8 / FP16 and INT4 caches get separate kernels so that each is
+// held to the register budget of its own occupancy.
 template <int DT, int KS, int VS>
 __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, KS, VS)) void kvq_paged_decode_kernel(
     DecodeArgs a) {
@@ -1175,6 +1298,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
     hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   } else if (dtype == kInt4) {
     hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  } else if (dtype == kFp16) {
+    hipLaunchKernelGGL((kvq_paged_decode_kernel<kFp16, kUniform, kUniform>), grid, dim3(kThreads),
+                       0, stream, a);
   } else if (dtype == kFp8) {
     launch_k<kFp8>(a, k_kind, v_kind, grid, stream);
   } else {

@@ -91,4 +91,29 @@ __device__ __forceinline__ void store_v_codes(uint8_t *chunk, int slot, int lane
   chunk[v8_offset(slot, 2 * lane + 1)] = (uint8_t)q.q1;
 }
 
+// FP16 (unquantized) cache: byte offset of (slot s, channel c) inside a
+// (block, head) chunk of 16 tokens x 128 channels x 2 bytes.
+//   K: 1024*((c>>3)&3) + 256*(c>>5) + 16*s + 2*(c&7)
+//   V: 1024*(c>>5) + 256*(s>>2) + 16*(c&15) + 8*((c>>4)&1) + 2*(s&3)
+// Lane l of a wavefront then reads, with one 16-byte load per 1 KiB quarter,
+// channels 32qd+8j..+7 of token l%16 (K, quarter j) and tokens 4qd..4qd+3
+// of channels 32j+l%16 and 32j+16+l%16 (V, quarter j), qd = l/16: its
+// matrix-core operands, as for the 8-bit layouts.
+__device__ __forceinline__ int k16_offset(int s, int c) {
+  return 1024 * ((c >> 3) & 3) + 256 * (c >> 5) + 16 * s + 2 * (c & 7);
+}
+__device__ __forceinline__ int v16_offset(int s, int c) {
+  return 1024 * (c >> 5) + 256 * (s >> 2) + 16 * (c & 15) + 8 * ((c >> 4) & 1) + 2 * (s & 3);
+}
+
+// Store fp16 values of channels 2 lane, 2 lane + 1 (one dword of K; two
+// halves of V) at `slot` of a 4 KiB (block, head) chunk.
+__device__ __forceinline__ void store_k_f16(uint8_t *chunk, int slot, int lane, uint32_t pair) {
+  *reinterpret_cast<uint32_t *>(chunk + k16_offset(slot, 2 * lane)) = pair;
+}
+__device__ __forceinline__ void store_v_f16(uint8_t *chunk, int slot, int lane, uint32_t pair) {
+  *reinterpret_cast<uint16_t *>(chunk + v16_offset(slot, 2 * lane)) = (uint16_t)(pair & 0xFFFFu);
+  *reinterpret_cast<uint16_t *>(chunk + v16_offset(slot, 2 * lane + 1)) = (uint16_t)(pair >> 16);
+}
+
 }  // namespace kvq

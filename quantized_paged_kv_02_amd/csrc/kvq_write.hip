@@ -1,4 +1,4 @@
-// Quantize-on-write kernels.
+// Quantize-on-write kernels (and the plain scatter of an FP16 cache).
 //
 // INT8 / FP8: one wavefront per (new token, KV head) quantizes the token's K
 // and V vectors (128 values each, two per lane; the rule is in kvq_quant.h)
@@ -65,6 +65,26 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
     if (a.k_gran == kPerToken) a.k_scales[tsi] = qk.scale;
     if (a.v_gran == kPerToken) a.v_scales[tsi] = qv.scale;
   }
+}
+
+// FP16 (unquantized) cache: the same scatter with the values stored as they
+// are, in the 4 KiB-per-(block, head) operand layout of kvq_quant.h.
+__global__ __launch_bounds__(64) void kvq_write_f16_kernel(WriteArgs a) {
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
+  if (i >= n_new) return;
+  const int pos = a.seq_lens[b] - n_new + i;
+  const size_t src = ((size_t)(c_begin + i) * a.num_kv_heads + h) * kHeadDim;
+  const uint32_t rk = reinterpret_cast<const uint32_t *>(a.k_new + src)[lane];
+  const uint32_t rv = reinterpret_cast<const uint32_t *>(a.v_new + src)[lane];
+  const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + pos / kBlock];
+  const size_t chunk = (size_t)phys * a.num_kv_heads + h;
+  store_k_f16(a.k_codes + chunk * 4096, pos % kBlock, lane, rk);
+  store_v_f16(a.v_codes + chunk * 4096, pos % kBlock, lane, rv);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,6 +311,12 @@ hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new
   } else {
     hipLaunchKernelGGL(kvq_write_q8_kernel<kInt8>, grid, dim3(64), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStream_t stream) {
+  hipLaunchKernelGGL(kvq_write_f16_kernel, dim3(max_new, a.num_kv_heads, batch), dim3(64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -35,8 +35,8 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     seq: int | tuple            # fixed length, or (lo, hi) uniform inclusive
-    dtype: str                  # "int8" | "fp8" | "int4"
-    k_gran: str                 # "tensor" | "head" | "channel" | "token"
+    dtype: str                  # "int8" | "fp8" | "int4" | "fp16" (unquantized)
+    k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16)
     v_gran: str
     table: str = "identity"     # "identity" | "shuffled"
     channel_outliers: tuple = ()    # (count, factor, tensors) e.g. (4, 10.0, "kvq")
@@ -74,6 +74,15 @@ WORKLOADS = {
     "llama3-70b-fp8": Workload(
         "llama3-70b-fp8", 80, 24, 64, 8, 16384, "fp8", "tensor", "tensor",
         description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, FP8 per-tensor"),
+    # unquantized baselines of the INT8 comparison ([intelli] §5): the INT8
+    # workloads' shapes and inputs with an FP16 cache
+    "llama2-7b-fp16": Workload(
+        "llama2-7b-fp16", 32, 4, 32, 32, 2048, "fp16", "none", "none",
+        element_outliers=(0.01, 8.0, "kv"),
+        description="Llama-2-7B shape: 32 layers, 32/32 heads, batch 4, seq 2048, FP16 cache"),
+    "llama3-70b-fp16": Workload(
+        "llama3-70b-fp16", 80, 24, 64, 8, 16384, "fp16", "none", "none",
+        description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, FP16 cache"),
 }
 
 

@@ -17,11 +17,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-INT8, FP8_E4M3, INT4 = 1, 2, 3
+INT8, FP8_E4M3, INT4, FP16 = 1, 2, 3, 4
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
-DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4}
+DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
-         "token": PER_TOKEN}
+         "token": PER_TOKEN,
+         "none": PER_TENSOR}   # FP16 cache: no scales, the field is ignored
 
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_ALIGNMENT", -4: "KVQ_ERR_WORKSPACE",
@@ -159,6 +160,11 @@ def alloc_cache(layout: Layout, ring_rows: int = 0, device="cuda",
         k_resid = torch.empty((ring_rows, h, ring, 128), dtype=torch.float16, device=device)
         v_resid = torch.empty((ring_rows, h, ring // 4, 128, 4), dtype=torch.float16,
                               device=device)
+    elif layout.dtype == FP16:
+        # unquantized: 4 KiB of fp16 per (block, head), no scales
+        k_codes = torch.empty((nb, h, 2048), dtype=torch.float16, device=device)
+        v_codes = torch.empty((nb, h, 2048), dtype=torch.float16, device=device)
+        k_scales = v_scales = k_resid = v_resid = None
     else:
         k_codes = torch.empty((nb, h, 2048), dtype=torch.uint8, device=device)
         v_codes = torch.empty((nb, h, 2048), dtype=torch.uint8, device=device)
@@ -189,7 +195,8 @@ def decode_workspace_bytes(layout: Layout, batch: int, max_seq_len: int) -> int:
 
 
 def alloc_workspace(layout: Layout, batch: int, max_seq_len: int, device="cuda"):
-    """Zero-filled decode workspace (the arrival counters start at zero)."""
+    """Decode workspace (zero-filled, although no contents are read before
+    being written)."""
     n = decode_workspace_bytes(layout, batch, max_seq_len)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 

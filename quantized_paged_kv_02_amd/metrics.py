@@ -10,7 +10,7 @@ Quantization 生产实战", section "为什么长上下文更需要 KV Cache
 Quantization"), so these bytes over the kernel time is the figure compared
 with the HBM roofline.  Sizes follow the per-value byte counts of the
 [oh-bug] section "KV Cache 的基本内存模型" (INT8/FP8 1 byte, INT4 half a
-byte) plus the fp32 scales of each granularity.
+byte, FP16 2 bytes) plus the fp32 scales of each granularity.
 """
 
 from __future__ import annotations
@@ -45,13 +45,16 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
             total += hkv * nq * 2 * 4                 # V per-token scales, 2 groups
             total += hkv * r * d * 2 * 2              # fp16 K and V residual
             total += (nq // BLOCK) * 4                # block-table entries
+        elif dtype == "fp16":
+            total += 2 * hkv * s * d * 2              # K and V values, 2 bytes
+            total += ((s + BLOCK - 1) // BLOCK) * 4
         else:
             total += 2 * hkv * s * d                  # K and V codes, 1 byte
             for gran in (k_gran, v_gran):
                 if gran == "token":
                     total += hkv * s * 4
             total += ((s + BLOCK - 1) // BLOCK) * 4
-    if dtype != "int4":
+    if dtype not in ("int4", "fp16"):
         for gran in (k_gran, v_gran):
             if gran != "token":
                 uniform_scales += _scale_bytes_uniform(gran, hkv)
@@ -66,8 +69,10 @@ def decode_flops(lens, num_q_heads: int) -> int:
 
 def write_bytes(dtype: str, k_gran: str, v_gran: str, n_new: int, num_kv_heads: int) -> int:
     """Bytes of one INT8/FP8 quantize-on-write of ``n_new`` tokens: fp16 K/V
-    read, codes (and per-token scales) written."""
+    read, codes (and per-token scales) written.  FP16: K/V read and stored."""
     hkv, d = num_kv_heads, HEAD_DIM
+    if dtype == "fp16":
+        return n_new * hkv * d * 2 * 2 * 2
     total = n_new * hkv * d * 2 * 2 + n_new * hkv * d * 2
     for gran in (k_gran, v_gran):
         if gran == "token":

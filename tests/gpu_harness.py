@@ -37,6 +37,8 @@ class CaseResult:
 
 
 def _static(w, gran, tensors, dtype):
+    if dtype == "fp16":
+        return None
     if gran in ("tensor", "head"):
         s = inputs.calibrated_scales(tensors, gran, w.num_kv_heads)
         if dtype == "int8":   # same recipe with the INT8 divisor
@@ -54,6 +56,10 @@ def _static(w, gran, tensors, dtype):
 
 def fill_garbage(cache):
     """Poison every pool byte so reads of unwritten slots would show."""
+    if cache.layout.dtype == 4:        # FP16 values
+        cache.k_codes.fill_(float("nan"))
+        cache.v_codes.fill_(float("nan"))
+        return
     cache.k_codes.fill_(0x7F)          # E4M3 NaN pattern
     cache.v_codes.fill_(0xFF)
     if cache.k_resid is not None:
@@ -151,7 +157,8 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         rep_outs.append(o)
     torch.cuda.synchronize()
     pools = {name: getattr(cache, name).cpu().numpy()
-             for name in ("k_codes", "v_codes", "k_scales", "v_scales")}
+             for name in ("k_codes", "v_codes", "k_scales", "v_scales")
+             if getattr(cache, name) is not None}
     if cache.k_resid is not None:
         pools["k_resid"] = cache.k_resid.cpu().numpy()
         pools["v_resid"] = cache.v_resid.cpu().numpy()
@@ -192,6 +199,14 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
             assert np.array_equal(rv.view(np.uint16), kv["v_resid"].view(np.uint16)), \
                 f"row {r}: ring V"
         k_hat, v_hat = oracle.kivi_dequantize(kv)
+    elif w.dtype == "fp16":
+        # unquantized: the cache holds the inputs' fp16 bits, attended as such
+        if check_codes:
+            for which, x in (("k", kb), ("v", vb)):
+                g = lv.logical_codes(p[f"{which}_codes"], row, s, which, "fp16")
+                assert np.array_equal(g.view(np.uint16), x.view(np.uint16)), \
+                    f"row {r}: fp16 {which} values differ"
+        k_hat, v_hat = kb, vb
     else:
         out = []
         for which, x, gran, static in (("k", kb, w.k_gran, res.k_static),

@@ -26,6 +26,13 @@ _P = 2 * (_J & 1) + (_E >> 1) + 4 * (_E & 1)
 V4_BYTE = 16 * _U + 4 * _W + (_P >> 1)
 V4_NIB = _P & 1
 
+# FP16 chunks (4096 bytes = 2048 fp16 per (block, head)): element offsets
+K16_OFF = (1024 * ((C_IDX >> 3) & 3) + 256 * (C_IDX >> 5) + 16 * S_IDX + 2 * (C_IDX & 7)) // 2
+V16_OFF = (1024 * (C_IDX >> 5) + 256 * (S_IDX >> 2) + 16 * (C_IDX & 15)
+           + 8 * ((C_IDX >> 4) & 1) + 2 * (S_IDX & 3)) // 2
+
+assert sorted(K16_OFF.ravel().tolist()) == list(range(2048))
+assert sorted(V16_OFF.ravel().tolist()) == list(range(2048))
 assert sorted(K8_OFF.ravel().tolist()) == list(range(2048))
 assert sorted(V8_OFF.ravel().tolist()) == list(range(2048))
 assert sorted((2 * K4_BYTE + K4_NIB).ravel().tolist()) == list(range(2048))
@@ -35,6 +42,12 @@ assert sorted((2 * V4_BYTE + V4_NIB).ravel().tolist()) == list(range(2048))
 def chunk8(pool_chunk, which):
     """[2048] uint8 chunk -> [16 slots, 128 channels] uint8 codes."""
     off = K8_OFF if which == "k" else V8_OFF
+    return np.asarray(pool_chunk)[off]
+
+
+def chunk16(pool_chunk, which):
+    """[2048] fp16 chunk -> [16 slots, 128 channels] fp16 values."""
+    off = K16_OFF if which == "k" else V16_OFF
     return np.asarray(pool_chunk)[off]
 
 
@@ -49,16 +62,19 @@ def chunk4(pool_chunk, which):
 
 def logical_codes(pool, table_row, n_tokens, which, dtype):
     """pool [NB, H, bytes] -> codes [n_tokens, H, 128] (uint8 for INT8/FP8
-    bit patterns, int8 for INT4)."""
+    bit patterns, int8 for INT4, the fp16 values for an FP16 pool)."""
     pool = np.asarray(pool)
     h = pool.shape[1]
-    out = np.zeros((n_tokens, h, 128), np.int8 if dtype == "int4" else np.uint8)
+    kind = {"int4": np.int8, "fp16": np.float16}.get(dtype, np.uint8)
+    out = np.zeros((n_tokens, h, 128), kind)
     for j in range((n_tokens + 15) // 16):
         phys = int(table_row[j])
         n = min(16, n_tokens - 16 * j)
         for hh in range(h):
             if dtype == "int4":
                 c = chunk4(pool[phys, hh], which)
+            elif dtype == "fp16":
+                c = chunk16(pool[phys, hh], which)
             else:
                 c = chunk8(pool[phys, hh], which)
             out[16 * j:16 * j + n, hh] = c[:n]

@@ -179,3 +179,21 @@ def test_entry_points_reject_before_launch():
     assert _write(lay, c, max_new=10 ** 6) == CAP
     assert _write(lay, c, total=0) == OK             # empty write is a no-op
     assert _write(lay, c, batch=0) == OK
+
+
+def test_fp16_cache_rules():
+    # an FP16 cache has no scales: NULL scale pointers and any granularity
+    # field are accepted, the code arrays are still required and aligned
+    lay = _layout(dtype=4, k_gran=77, v_gran=-5)
+    bare = _cache(k_scales=None, v_scales=None)
+    assert kvq.validate(lay, bare, 2, 100) == OK
+    assert kvq.validate(lay, _cache(k_codes=None, k_scales=None, v_scales=None), 2, 100) == INV
+    assert kvq.validate(lay, _cache(v_codes=FAKE + 2, k_scales=None, v_scales=None), 2,
+                        100) == ALN
+    assert kvq.validate(_layout(dtype=5), bare, 2, 100) == INV
+    assert kvq.validate(_layout(dtype=4, split_tokens=24), bare, 2, 100) == INV
+    assert _decode(lay, bare, q=None) == INV
+    assert _write(lay, bare, cu=FAKE + 4) == ALN
+    assert _write_decode(lay, bare, vn=None) == INV
+    # same partition plan rules: a split launch needs partials
+    assert kvq.decode_workspace_bytes(_layout(dtype=4, split_tokens=16), 2, 100) > 0

@@ -99,7 +99,8 @@ def test_int8_chunked_writes(chunks):
     check_rows(run_case(w, [300, 1000, 17], chunks=chunks, split_tokens=128))
 
 
-@pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("int4", "channel", "token")])
+@pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("int4", "channel", "token"),
+                                         ("fp16", "none", "none")])
 def test_repeated_split_launches_on_one_workspace(dtype, kg, vg):
     # many partitions per row; launches that reuse one workspace (partials
     # left by the previous launch) must agree bit for bit
@@ -109,3 +110,31 @@ def test_repeated_split_launches_on_one_workspace(dtype, kg, vg):
         assert np.array_equal(o.view(np.uint32), res.out.view(np.uint32))
     check_rows(res, rows=[0, 1, 3])
     assert np.all(res.out[2] == 0)
+
+
+# --- unquantized FP16 cache: values stored bit for bit, attended as they are
+
+@pytest.mark.parametrize("lens,split", [([1, 37, 300], 64), ([16, 17, 31, 32, 33], 0),
+                                        ([0, 1, 0, 2], 0), ([777, 15, 2000], 256),
+                                        ([100, 257, 31], 4096)])
+def test_fp16_cache(lens, split):
+    w = _small("fp16", "none", "none", table="shuffled",
+               channel_outliers=(4, 10.0, "kvq"))
+    res = run_case(w, lens, split_tokens=split, decode_twice=True)
+    live = [r for r, s in enumerate(lens) if s > 0]
+    check_rows(res, rows=live)
+    for r, s in enumerate(lens):
+        if s == 0:
+            assert np.all(res.out[r] == 0)
+    assert np.array_equal(res.out, res.out2)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1), (16, 2), (12, 3)])
+def test_fp16_group_sizes(hq, hkv):
+    w = _small("fp16", "none", "none", hq=hq, hkv=hkv)
+    check_rows(run_case(w, [16, 33, 129], split_tokens=32))
+
+
+def test_fp16_chunked_writes():
+    w = _small("fp16", "none", "none", table="shuffled")
+    check_rows(run_case(w, [300, 1000, 17], chunks=3, split_tokens=128))

@@ -30,6 +30,7 @@ CASES = [
     ("fp8", "head", "head", "shuffled"),
     ("fp8", "channel", "token", "identity"),
     ("int4", "channel", "token", "shuffled"),
+    ("fp16", "none", "none", "shuffled"),
 ]
 
 LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2]]
