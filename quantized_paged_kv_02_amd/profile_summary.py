@@ -30,7 +30,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_paged_kv_02_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h")]
+                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h", "kvq_quant.h")]
 
 
 def kernel_source_hash() -> str:
