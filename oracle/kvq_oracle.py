@@ -34,7 +34,9 @@ __all__ = [
     "e4m3_decode_table", "e4m3_encode", "quantize_e4m3", "dequantize",
     "quantize_per_token", "quantize_static", "kivi_quantized_len",
     "kivi_quantize_k_group", "kivi_quantize_v_tokens", "pack_int4",
-    "unpack_int4", "kivi_quantize", "kivi_dequantize", "decode_attention",
+    "unpack_int4", "kivi_quantize", "kivi_dequantize", "INT4_UMAX",
+    "affine_params", "quantize_affine", "kivi_affine_quantize_k_group",
+    "kivi_affine_quantize_v_tokens", "decode_attention",
     "decode_attention_partials", "merge_partials", "paged_gather",
     "paged_scatter",
 ]
@@ -319,7 +321,7 @@ def unpack_int4(packed):
     return out.astype(np.int8)
 
 
-def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP):
+def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False):
     """Quantize a whole sequence's K and V [S, Hkv, D] (fp16) KIVI-style.
 
     Returns a dict with
@@ -327,6 +329,9 @@ def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP):
       k_codes   [nq, Hkv, D] int8,  k_scales [nq // group, Hkv, D] fp32,
       v_codes   [nq, Hkv, D] int8,  v_scales [nq, Hkv, D // group] fp32,
       k_resid, v_resid  [S - nq, Hkv, D] fp16 (unchanged inputs).
+    With ``affine`` the groups are quantized asymmetrically: codes are uint8
+    in [0, 15] and ``k_zp`` / ``v_zp`` (int64, shaped like the scales) hold
+    the zero points.
     Each group depends only on its own 64 tokens, so quantizing the final
     state equals quantizing group by group as the sequence grows.
     """
@@ -334,35 +339,123 @@ def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP):
     v = np.asarray(v, np.float16)
     s_len, hkv, d = k.shape
     nq = kivi_quantized_len(s_len, residual, group)
-    k_codes = np.zeros((nq, hkv, d), np.int8)
+    code_t = np.uint8 if affine else np.int8
+    k_codes = np.zeros((nq, hkv, d), code_t)
     k_scales = np.zeros((nq // group, hkv, d), np.float32)
+    k_zp = np.zeros((nq // group, hkv, d), np.int64)
     for gi in range(nq // group):
         for h in range(hkv):
-            c, s = kivi_quantize_k_group(k[gi * group:(gi + 1) * group, h, :])
+            kg = k[gi * group:(gi + 1) * group, h, :]
+            if affine:
+                c, s, z = kivi_affine_quantize_k_group(kg)
+                k_zp[gi, h, :] = z
+            else:
+                c, s = kivi_quantize_k_group(kg)
             k_codes[gi * group:(gi + 1) * group, h, :] = c
             k_scales[gi, h, :] = s
-    v_codes = np.zeros((nq, hkv, d), np.int8)
+    v_codes = np.zeros((nq, hkv, d), code_t)
     v_scales = np.zeros((nq, hkv, d // group), np.float32)
+    v_zp = np.zeros((nq, hkv, d // group), np.int64)
     for h in range(hkv):
-        c, s = kivi_quantize_v_tokens(v[:nq, h, :], group)
+        if affine:
+            c, s, z = kivi_affine_quantize_v_tokens(v[:nq, h, :], group)
+            v_zp[:, h, :] = z
+        else:
+            c, s = kivi_quantize_v_tokens(v[:nq, h, :], group)
         v_codes[:, h, :] = c
         v_scales[:, h, :] = s
-    return {"nq": nq, "k_codes": k_codes, "k_scales": k_scales,
-            "v_codes": v_codes, "v_scales": v_scales,
-            "k_resid": k[nq:].copy(), "v_resid": v[nq:].copy()}
+    out = {"nq": nq, "k_codes": k_codes, "k_scales": k_scales,
+           "v_codes": v_codes, "v_scales": v_scales,
+           "k_resid": k[nq:].copy(), "v_resid": v[nq:].copy()}
+    if affine:
+        out["k_zp"] = k_zp
+        out["v_zp"] = v_zp
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Asymmetric (affine) INT4 KIVI groups ([oh-bug] section "量化不是简单'截断精度'":
+# the affine form X_q = round(X / scale) + zero_point, dequantized as
+# (X_q - zero_point) * scale; the page's references name KIVI as an
+# asymmetric scheme).  Same groups as the symmetric cache: K per channel over
+# 64 tokens, V per token over 64 channels.
+# ---------------------------------------------------------------------------
+
+# unsigned 4-bit codes 0 .. 15
+INT4_UMAX = 15
+
+
+def affine_params(x, qmax, axis):
+    """Scale and integer zero point of the groups of ``x`` reduced over
+    ``axis``.
+
+    The page gives the affine form but not how its two parameters are
+    chosen.  Reading: the group's range is widened to contain zero (so zero
+    is a code and the zero point an integer), ``lo = min(min x, 0)``,
+    ``hi = max(max x, 0)``; ``scale = (hi - lo) / qmax`` and
+    ``zero_point = clamp(round(-lo / scale), 0, qmax)``, fp32 arithmetic,
+    round half to even.  A group of zeros has scale 0 and zero point 0.
+    Returns (scale fp32, zero_point int64).
+    """
+    x = np.asarray(x, np.float32)
+    lo = np.minimum(x.min(axis=axis), np.float32(0)).astype(np.float32)
+    hi = np.maximum(x.max(axis=axis), np.float32(0)).astype(np.float32)
+    scale = ((hi - lo).astype(np.float32) / np.float32(qmax)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    zp = np.rint((-lo).astype(np.float32) / safe)
+    zp = np.where(scale > 0, np.clip(zp, 0, qmax), 0)
+    return scale, zp.astype(np.int64)
+
+
+def quantize_affine(x, scale, zero_point, qmax):
+    """``q = clamp(round(x / scale) + zero_point, 0, qmax)`` (fp32 division,
+    round half to even); a zero scale gives code 0.  ``scale`` and
+    ``zero_point`` broadcast against ``x``.  Returns uint8 codes."""
+    x = np.asarray(x, np.float32)
+    s = np.asarray(scale, np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    q = np.rint(x / safe) + np.asarray(zero_point, np.float64)
+    q = np.where(s > 0, np.clip(q, 0, qmax), 0)
+    return q.astype(np.uint8)
+
+
+def kivi_affine_quantize_k_group(k_group):
+    """K of one 64-token group and one KV head, [64, D] fp16 -> (codes [64,
+    D] uint8 in [0, 15], scales [D] fp32, zero points [D] int64), one
+    (scale, zero point) per channel over the group's tokens."""
+    k = np.asarray(k_group, np.float32)
+    s, z = affine_params(k, INT4_UMAX, axis=0)
+    return quantize_affine(k, s[None, :], z[None, :], INT4_UMAX), s, z
+
+
+def kivi_affine_quantize_v_tokens(v_tokens, group=KIVI_GROUP):
+    """V rows [T, D] -> (codes [T, D] uint8, scales [T, D // group] fp32, zero
+    points [T, D // group]): one (scale, zero point) per token and channel
+    group."""
+    v = np.asarray(v_tokens, np.float32)
+    t, d = v.shape
+    vg = v.reshape(t, d // group, group)
+    s, z = affine_params(vg, INT4_UMAX, axis=-1)
+    q = quantize_affine(vg, s[..., None], z[..., None], INT4_UMAX)
+    return q.reshape(t, d), s, z
 
 
 def kivi_dequantize(kv, group=KIVI_GROUP):
     """K_hat, V_hat [S, Hkv, D] fp64 from :func:`kivi_quantize` output: INT4
-    tokens as code * scale, residual tokens as their fp16 values."""
+    tokens as code * scale (affine: (code - zero_point) * scale), residual
+    tokens as their fp16 values."""
     nq = kv["nq"]
     hkv, d = kv["k_codes"].shape[1], kv["k_codes"].shape[2]
     # K: token t of group t // group uses that group's per-channel scales
     kc = kv["k_codes"].astype(np.float64).reshape(nq // group, group, hkv, d)
+    if "k_zp" in kv:
+        kc = kc - kv["k_zp"].astype(np.float64)[:, None, :, :]
     ks = kv["k_scales"].astype(np.float64)[:, None, :, :]
     k_hat_q = (kc * ks).reshape(nq, hkv, d)
     # V: channel c of a token uses the token's scale of channel group c // group
     vc = kv["v_codes"].astype(np.float64).reshape(nq, hkv, d // group, group)
+    if "v_zp" in kv:
+        vc = vc - kv["v_zp"].astype(np.float64)[..., None]
     vs = kv["v_scales"].astype(np.float64)[..., None]
     v_hat_q = (vc * vs).reshape(nq, hkv, d)
     k_hat = np.concatenate([k_hat_q, kv["k_resid"].astype(np.float64)], axis=0)
