@@ -89,6 +89,20 @@
  *             s = t % RING is element [s>>2][c][s&3].
  * Both granularity fields must be KVQ_PER_CHANNEL (K) and KVQ_PER_TOKEN (V).
  *
+ * ---- INT4 affine (KVQ_INT4_AFFINE) -------------------------------------------
+ * The affine form of [oh-bug] section "量化不是简单'截断精度'": code =
+ * clamp(round(x / scale) + zero_point, 0, 15), value = (code - zero_point) *
+ * scale.  Per group the range is widened to contain zero: lo = min(min x,
+ * 0), hi = max(max x, 0), scale = (hi - lo) / 15 and zero_point =
+ * clamp(round(-lo / scale), 0, 15) (fp32, round half to even; a group of
+ * zeros has scale 0, zero point 0, codes 0).  Groups, residual window, ring
+ * and code positions are those of KVQ_INT4; codes are unsigned nibbles.
+ *   k_scales: fp32 [NB][H][40]; floats 0..31 are the per-channel scales of
+ *             the INT4 layout, the 32 bytes of floats 32..39 the uint8 zero
+ *             points of the same channels (byte i: channel 32*(j%4)+i).
+ *   v_scales: fp32 [NB][H][40]; floats 0..31 are [16][2] as for INT4, the
+ *             32 bytes of floats 32..39 the uint8 zero points [16][2].
+ *
  * ---- FP16 (unquantized) layout: fp16 [NB][H][2048] for each of K and V ----
  * The baseline the quantized formats are measured against ([intelli] §5:
  * INT8 against FP16 memory and latency).  Values are stored as given; one
@@ -122,7 +136,9 @@ typedef enum kvq_dtype {
   KVQ_INT8 = 1,     /* 1 byte per value, symmetric, divisor 127             */
   KVQ_FP8_E4M3 = 2, /* 1 byte per value, OCP E4M3, divisor 448              */
   KVQ_INT4 = 3,     /* 0.5 byte per value, KIVI grouping, divisor 7         */
-  KVQ_FP16 = 4      /* 2 bytes per value, unquantized                       */
+  KVQ_FP16 = 4,     /* 2 bytes per value, unquantized                       */
+  KVQ_INT4_AFFINE = 5 /* INT4 KIVI grouping, asymmetric: codes 0..15 with a
+                         zero point per group                               */
 } kvq_dtype;
 
 typedef enum kvq_granularity {

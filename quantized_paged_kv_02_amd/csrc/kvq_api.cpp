@@ -24,6 +24,9 @@ constexpr long kWgOverheadF16 = 4;  // a block streams twice the bytes of INT8
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// KIVI-grouped INT4 cache (symmetric or affine)
+bool kivi(const kvq_layout *L) { return L->dtype == KVQ_INT4 || L->dtype == KVQ_INT4_AFFINE; }
+
 int kivi_len(int s, int residual) {
   const int n = s - residual;
   return n > 0 ? (n / kGroup) * kGroup : 0;
@@ -33,7 +36,7 @@ kvq_status check_layout(const kvq_layout *L) {
   if (!L) return KVQ_ERR_INVALID_ARG;
   if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4 &&
-      L->dtype != KVQ_FP16)
+      L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE)
     return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_FP16) {  // an FP16 cache has no scales
     if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
@@ -45,7 +48,7 @@ kvq_status check_layout(const kvq_layout *L) {
   if (L->split_tokens < 0) return KVQ_ERR_INVALID_ARG;
   if (L->head_dim != kHeadDim || L->block_size != kBlock) return KVQ_ERR_UNSUPPORTED;
   if (L->num_q_heads / L->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
-  if (L->dtype == KVQ_INT4) {
+  if (kivi(L)) {
     if (L->k_gran != KVQ_PER_CHANNEL || L->v_gran != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
     if (L->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
     if (L->residual_len < kGroup || L->residual_len % kGroup != 0) return KVQ_ERR_UNSUPPORTED;
@@ -63,7 +66,7 @@ kvq_status check_cache(const kvq_layout *L, const kvq_cache *C, int32_t batch) {
   if (L->dtype == KVQ_FP16) return KVQ_OK;  // no scales, no ring
   if (!C->k_scales || !C->v_scales) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(C->k_scales) || !aligned16(C->v_scales)) return KVQ_ERR_ALIGNMENT;
-  if (L->dtype == KVQ_INT4) {
+  if (kivi(L)) {
     if (!C->k_resid || !C->v_resid) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(C->k_resid) || !aligned16(C->v_resid)) return KVQ_ERR_ALIGNMENT;
     if (C->ring_rows < batch) return KVQ_ERR_CAPACITY;
@@ -80,7 +83,7 @@ struct Plan {
 
 Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
   Plan p{};
-  const bool int4 = L->dtype == KVQ_INT4;
+  const bool int4 = kivi(L);
   const int blocks = int4 ? kivi_len(max_seq_len, L->residual_len) / kBlock
                           : (max_seq_len + kBlock - 1) / kBlock;
   // a workgroup's four waves take units of 2 blocks (INT8/FP8) or one
@@ -211,10 +214,11 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   hipError_t e;
-  if (layout->dtype == KVQ_INT4) {
+  if (kivi(layout)) {
     // groups leaving the window: at most ceil(n/64) + 1 per row
     const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup + 1;
-    e = kvq::launch_write_int4(a, batch, max_new_per_seq, max_groups, s);
+    e = kvq::launch_write_int4(a, layout->dtype == KVQ_INT4_AFFINE, batch, max_new_per_seq,
+                               max_groups, s);
   } else if (layout->dtype == KVQ_FP16) {
     e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);
   } else {
@@ -311,7 +315,7 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   if (st != KVQ_OK || !launch) return st;
   if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
-  if (layout->dtype != KVQ_INT4) {
+  if (!kivi(layout)) {
     a.k_new = k_new;
     a.v_new = v_new;
     return decode_launch(layout, a, batch, stream);
@@ -336,7 +340,8 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   w.residual = layout->residual_len;
   w.ring = layout->residual_len + kGroup;
   (void)hipGetLastError();
-  const hipError_t e = kvq::launch_write_int4(w, batch, 1, 2, static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq::launch_write_int4(w, layout->dtype == KVQ_INT4_AFFINE, batch, 1, 2,
+                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
   return decode_launch(layout, a, batch, stream);
 }

@@ -8,7 +8,9 @@
 
 namespace kvq {
 
-enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4 };  // kvq_dtype values
+enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5 };  // kvq_dtype
+// KIVI-grouped INT4 caches, symmetric or affine
+constexpr bool is_kivi(int dtype) { return dtype == kInt4 || dtype == kInt4Affine; }
 // Granularity as the decode kernel sees it: a scale that is uniform over a
 // (row, KV head) (per-tensor or per-head), per channel, or per token.
 enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
@@ -19,7 +21,7 @@ enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
 // FP8 with per-token V and non-uniform K scales need the larger per-wave
 // register budget of two per CU.
 constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
-  return (dtype == kInt4 || dtype == kFp16) ? 2
+  return (is_kivi(dtype) || dtype == kFp16) ? 2
          : (dtype == kFp8 && v_kind == kToken && k_kind != kUniform) ? 2
                                                                       : 3;
 }
@@ -85,7 +87,8 @@ int decode_scale_kind(int granularity);
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch,
                            int max_new, hipStream_t stream);
 hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStream_t stream);
-hipError_t launch_write_int4(const WriteArgs &a, int batch, int max_new,
+// affine: asymmetric groups (unsigned codes, zero points beside the scales)
+hipError_t launch_write_int4(const WriteArgs &a, bool affine, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind,
                          int v_kind, int batch, hipStream_t stream);

@@ -77,7 +77,9 @@ struct Softmax {
 // then the four wave states for the merge.
 struct StreamLds {
   int ids[kIdChunk];
-  float scl[kWaves][256];   // INT4: K scales [128 channels], V scales [64 tok][2]
+  // INT4: K scales [128 channels], V scales [64 tok][2]; affine INT4 also
+  // the zero points, laid out the same way from float 256 on
+  float scl[kWaves][512];
   // INT4: the group's queries, zero past the group; rows padded by 16 bytes
   // so the 16 head rows of one read start in different banks
   f16 q[16][kQRow];
@@ -560,12 +562,17 @@ struct Group4 {
   u32x4 v[4];   // block u: nibbles of 4 tokens x 8 channel tiles
   float ks[2];  // K scales of channels 8(l/4) + koff_pair(l) (block l/16)
   float vs[2];  // V scales (channel groups 0, 1) of token l of the group
+  uint32_t kz;  // affine: zero points of those K channels (bytes 0, 1)
+  uint32_t vz;  // affine: zero points of those V scales (bytes 0, 1)
   __device__ explicit Group4(int = 0) {}
 };
 
 // pm: physical block of this lane's K-scale row (block lane/16 of the group).
+// AFF: scale rows of 40 floats, the zero points in the last 32 bytes.
+template <bool AFF>
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
                                             int pm, int h, int lane) {
+  constexpr int kRow = AFF ? 40 : 32;  // floats per (block, head) scale row
   const int H = a.num_kv_heads;
   constexpr uint32_t bytes = 1024;  // one (block, head) code chunk
 #pragma unroll
@@ -577,13 +584,20 @@ __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, cons
   const size_t chunk = (size_t)pm * H + h;
   // channels koff_pair(lane) of k-slot chunk lane/4, held by block lane/16
   const int2 ko = koff_pair(lane);
-  const float *ksp = a.k_scales + chunk * 32 + 8 * ((lane >> 2) & 3);
-  const float2 vs =
-      *reinterpret_cast<const float2 *>(a.v_scales + (chunk * kBlock + (lane & 15)) * 2);
+  const float *krow = a.k_scales + chunk * kRow;
+  const float *vrow = a.v_scales + chunk * kRow;
+  const float *ksp = krow + 8 * ((lane >> 2) & 3);
+  const float2 vs = *reinterpret_cast<const float2 *>(vrow + 2 * (lane & 15));
   t.ks[0] = ksp[ko.x];
   t.ks[1] = ksp[ko.y];
   t.vs[0] = vs.x;
   t.vs[1] = vs.y;
+  if constexpr (AFF) {
+    const uint8_t *kzp = reinterpret_cast<const uint8_t *>(krow + 32) + 8 * ((lane >> 2) & 3);
+    t.kz = (uint32_t)kzp[ko.x] | ((uint32_t)kzp[ko.y] << 8);
+    t.vz = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(vrow + 32) +
+                                               2 * (lane & 15));
+  }
 }
 
 // The group as the compact path reads it: K scales as above, and the V
@@ -644,6 +658,34 @@ __device__ __forceinline__ f16x8 int4x8_to_f16(uint32_t x) {
 // k-slot order produced by int4x8_to_f16 (nibble index of slot e)
 __device__ __forceinline__ int int4_kslot(int e) { return (e >> 1) + 4 * (e & 1); }
 
+// Affine codes: 8 unsigned nibbles minus their zero points, exact, in the
+// k-slot order of int4x8_to_f16.  Low nibbles under the fp16 exponent of
+// 1024 give 1024 + u, high nibbles 1024 + 16 u (times 1/16: 64 + u); `sub`
+// holds -(1024 + z) for slot pairs 0 and 2 and -(64 + z) for 1 and 3.
+__device__ __forceinline__ f16x8 uint4x8_minus_zp(uint32_t x, const uint32_t (&sub)[4]) {
+  const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const uint32_t y = x >> 8;
+  uint32_t r[4];
+  r[0] = as_u32(as_f16x2((x & 0x000F000Fu) | 0x64006400u) + as_f16x2(sub[0]));
+  r[1] = as_u32(as_f16x2((x & 0x00F000F0u) | 0x64006400u) * sixteenth + as_f16x2(sub[1]));
+  r[2] = as_u32(as_f16x2((y & 0x000F000Fu) | 0x64006400u) + as_f16x2(sub[2]));
+  r[3] = as_u32(as_f16x2((y & 0x00F000F0u) | 0x64006400u) * sixteenth + as_f16x2(sub[3]));
+  return pairs_to_f16x8(r);
+}
+
+// Affine value codes: 8 unsigned nibbles -> 1024 + u (k-slots 0,1,4,5) and
+// 1024 + 16 u (k-slots 2,3,6,7), exact; the bias is removed after the
+// product, with the zero points.
+__device__ __forceinline__ f16x8 uint4x8_to_f16_biased(uint32_t x) {
+  const uint32_t y = x >> 8;
+  const uint32_t r[4] = {(x & 0x000F000Fu) | 0x64006400u, (x & 0x00F000F0u) | 0x64006400u,
+                         (y & 0x000F000Fu) | 0x64006400u, (y & 0x00F000F0u) | 0x64006400u};
+  return pairs_to_f16x8(r);
+}
+
+// AFF: affine codes; the zero points are staged beside the scales (float
+// 256 on) and enter the key conversion and the value bias operand.
+template <bool AFF>
 __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, const f16 *qs,
                                                float *scl, float qk_scale, int lane, int n,
                                                int qd) {
@@ -652,9 +694,15 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     const int2 ko = koff_pair(lane);
     scl[8 * (lane >> 2) + ko.x] = t.ks[0];
     scl[8 * (lane >> 2) + ko.y] = t.ks[1];
+    if constexpr (AFF) {
+      scl[256 + 8 * (lane >> 2) + ko.x] = (float)(t.kz & 0xFFu);
+      scl[256 + 8 * (lane >> 2) + ko.y] = (float)(t.kz >> 8);
+      *reinterpret_cast<float2 *>(scl + 384 + 2 * lane) =
+          float2{(float)(t.vz & 0xFFu), (float)(t.vz >> 8)};
+    }
   }
-  // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code:
-  // their weights carry 1/16 (exact)
+  // tokens 2, 3 of every 4 meet the value codes stored as 1152 + 16 code
+  // (affine: 1024 + 16 code): their weights carry 1/16 (exact)
   const float vsf = (lane & 2) ? 0.0625f : 1.0f;
   *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0] * vsf, t.vs[1] * vsf};
   // Scores, channel chunk by chunk: q' = q * s_c for channels 32qd+8j..+7
@@ -677,12 +725,28 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
       split_hi_lo(x0, x1, hi[e2], lo[e2]);
     }
     const f16x8 bhi = pairs_to_f16x8(hi), blo = pairs_to_f16x8(lo);
+    // affine: code - zero point of channels 32qd+8j..+7, slot pairs (0,4)
+    // (1,5) (2,6) (3,7) of the conversion
+    uint32_t sub[4];
+    if constexpr (AFF) {
+      const f32x4 z0 = *reinterpret_cast<const f32x4 *>(scl + 256 + 32 * qd + 8 * j);
+      const f32x4 z1 = *reinterpret_cast<const f32x4 *>(scl + 256 + 32 * qd + 8 * j + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float base = (i & 1) ? 64.0f : 1024.0f;
+        sub[i] = pack_rtz(-(base + z0[i]), -(base + z1[i]));
+      }
+    }
     // all hi products, then all lo products: an accumulator's two updates
     // are four matrix instructions apart
     f16x8 av[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      av[u] = int4x8_to_f16(t.k[u][j]);
+      if constexpr (AFF) {
+        av[u] = uint4x8_minus_zp(t.k[u][j], sub);
+      } else {
+        av[u] = int4x8_to_f16(t.k[u][j]);
+      }
       acc[u] = mfma32(av[u], bhi, acc[u]);
     }
 #pragma unroll
@@ -706,21 +770,41 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
     const f16x8 pb0 = p_operand(p0 * g0a, p1 * g0b);
     const f16x8 pb1 = p_operand(p0 * g1a, p1 * g1b);
     // every row of the bias operand is the per-k-slot bias of the biased
-    // conversion (1032 for slots 0,1,4,5; 1152 for 2,3,6,7), negated
-    const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
-    const f16x8 abias = {b0, b0, b1, b1, b0, b0, b1, b1};
+    // conversion (1032 for slots 0,1,4,5; 1152 for 2,3,6,7), negated.
+    // Affine: the bias of slot k is 1024 + z (low nibbles) or 1024 + 16 z
+    // (high nibbles) with z the zero point of the slot's token and the
+    // tile's channel group, so it differs per lane.
+    f16x8 abias0, abias1;
+    if constexpr (AFF) {
+      const float *zp = scl + 384 + 2 * (32 * pr + 4 * qd);
+      const f32x4 za0 = *reinterpret_cast<const f32x4 *>(zp);        // b0 tokens 0,1
+      const f32x4 za1 = *reinterpret_cast<const f32x4 *>(zp + 4);    // b0 tokens 2,3
+      const f32x4 zb0 = *reinterpret_cast<const f32x4 *>(zp + 32);   // b1 tokens 0,1
+      const f32x4 zb1 = *reinterpret_cast<const f32x4 *>(zp + 36);   // b1 tokens 2,3
+      auto lo = [](float z) { return (f16)(-(1024.0f + z)); };
+      auto hi = [](float z) { return (f16)(-(1024.0f + 16.0f * z)); };
+      abias0 = f16x8{lo(za0[0]), lo(za0[2]), hi(za1[0]), hi(za1[2]),
+                     lo(zb0[0]), lo(zb0[2]), hi(zb1[0]), hi(zb1[2])};
+      abias1 = f16x8{lo(za0[1]), lo(za0[3]), hi(za1[1]), hi(za1[3]),
+                     lo(zb0[1]), lo(zb0[3]), hi(zb1[1]), hi(zb1[3])};
+    } else {
+      const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
+      abias0 = abias1 = f16x8{b0, b0, b1, b1, b0, b0, b1, b1};
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w = pair_tile(t.v[2 * pr][j >> 1], t.v[2 * pr + 1][j >> 1], j & 1);
-      st.o[j] = mfma32(int4x8_to_f16_biased(w), j < 4 ? pb0 : pb1, st.o[j]);
+      const f16x8 av = AFF ? uint4x8_to_f16_biased(w) : int4x8_to_f16_biased(w);
+      st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
     }
     // bias cancellation after all eight tiles (each o[j] update is eight
     // matrix instructions after the previous one)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
+    for (int j = 0; j < 8; ++j) st.o[j] = mfma32(j < 4 ? abias0 : abias1, j < 4 ? pb0 : pb1, st.o[j]);
   }
 }
 
+template <bool AFF>
 __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
                             int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
                             int pre_id) {
@@ -746,10 +830,10 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
       // a per-lane LDS read: selecting among ph[] per lane would become a
       // private-array access, whose scratch load joins the in-order vmcnt
       // queue and makes every group wait for all loads in flight
-      load_group4(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane);
+      load_group4<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane);
     };
     auto compute = [&](Group4 &t, int) {
-      compute_group4(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
+      compute_group4<AFF>(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
     };
     pipeline<Group4>(cnt, load, compute);
   }
@@ -1119,7 +1203,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
                          ? a.block_tables[(size_t)b * a.max_blocks_per_seq + blk0 + tid]
                          : 0;
   u32x4 qrow = {0u, 0u, 0u, 0u};
-  if constexpr (DT == kInt4) {
+  if constexpr (is_kivi(DT)) {
     const int hn = tid >> 4, c8 = tid & 15;
     if (hn < a.group)
       qrow = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
@@ -1143,7 +1227,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
 
   Softmax st;
   softmax_init(st);
-  if constexpr (DT == kInt4) {
+  if constexpr (is_kivi(DT)) {
     // the fp16 residual tokens ride with the row's last partition, so a
     // launch has no short extra workgroups to leave a ragged last round
     const int nq = kivi_quantized_len(seq_len, a.residual);
@@ -1155,7 +1239,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
       stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
-      stream_int4(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      stream_int4<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
     }
   } else {
@@ -1186,11 +1270,13 @@ __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, KS, VS)) void kvq_pa
   decode_workgroup<DT, KS, VS, false>(a, sh);
 }
 
-template <bool G4>
-__global__ __launch_bounds__(kThreads, decode_wg_per_cu(kInt4, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
+// DT: kInt4 or kInt4Affine (the compact G4 layout is built for kInt4 only)
+template <int DT, bool G4>
+__global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
     DecodeArgs a) {
+  static_assert(is_kivi(DT) && (DT == kInt4 || !G4), "compact layout: symmetric INT4 only");
   __shared__ SharedLds sh;
-  decode_workgroup<kInt4, kChannel, kToken, G4>(a, sh);
+  decode_workgroup<DT, kChannel, kToken, G4>(a, sh);
 }
 
 // Log-sum-exp merge of the partition partials of each (row, query head):
@@ -1295,9 +1381,14 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
                          hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, batch);
   if (dtype == kInt4 && a.group <= 4) {
-    hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, true>), grid, dim3(kThreads), 0,
+                       stream, a);
   } else if (dtype == kInt4) {
-    hipLaunchKernelGGL(kvq_paged_decode_int4_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, false>), grid, dim3(kThreads), 0,
+                       stream, a);
+  } else if (dtype == kInt4Affine) {
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, false>), grid, dim3(kThreads),
+                       0, stream, a);
   } else if (dtype == kFp16) {
     hipLaunchKernelGGL((kvq_paged_decode_kernel<kFp16, kUniform, kUniform>), grid, dim3(kThreads),
                        0, stream, a);
@@ -1310,7 +1401,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   if (e != hipSuccess || a.slots == 1) return e;
   const int rows = batch * a.num_q_heads;
   hipLaunchKernelGGL(kvq_partition_reduce_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, a,
-                     dtype == kInt4 ? 1 : 0);
+                     is_kivi(dtype) ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -101,12 +101,34 @@ __device__ __forceinline__ int kivi_len(int s, int residual) {
 // call's new tokens), the scales are reduced across threads, and every
 // thread then quantizes exactly the 32 nibbles of one 16-byte unit of the
 // block layout and writes it with one store.
+//
+// AFF: asymmetric groups ([oh-bug] "量化不是简单'截断精度'", the affine
+// form): over the group's range widened to contain zero, scale = (hi - lo)
+// / 15 and zero point = clamp(round(-lo / scale), 0, 15); codes are
+// clamp(round(x / scale) + zero point, 0, 15), unsigned.  Scale rows are 40
+// floats per (block, head), the last 32 bytes holding the zero points.
 constexpr int kFlushRow = kHeadDim + 8;  // padded LDS row (fp16)
 
+// Affine parameters of a group with minimum lo <= 0 <= maximum hi.
+__device__ __forceinline__ float2 affine_params(float lo, float hi) {
+  const float s = (hi - lo) / 15.0f;
+  const float z = s > 0.0f ? fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f) : 0.0f;
+  return float2{s, z};
+}
+__device__ __forceinline__ uint32_t quant_affine(float x, float s, float z) {
+  if (s == 0.0f) return 0u;
+  const float y = fminf(fmaxf(rintf(x / s) + z, 0.0f), 15.0f);
+  return (uint32_t)(int)y;
+}
+
+template <bool AFF>
 __device__ void int4_flush(const WriteArgs &a, int bx) {
+  constexpr int kRow = AFF ? 40 : 32;   // floats per (block, head) scale row
   __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
   __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
+  __shared__ float partn[AFF ? 4 : 1][kHeadDim];  // K affine: channel minima
   __shared__ float sc[kHeadDim];        // K: [128] channel scales; V: [64][2] token scales
+  __shared__ float zs[AFF ? kHeadDim : 1];  // affine zero points, as sc
   __shared__ int phys_s[4];
 
   const int gs = bx >> 1;
@@ -177,24 +199,47 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
   __syncthreads();
 
   if (!is_v) {
-    // K scales: max over the group's 64 tokens of |K[:, c]| / 7
+    // K scales: max over the group's 64 tokens of |K[:, c]| / 7 (affine: the
+    // channel's minimum and maximum, each starting from 0)
     {
       const int cp = tid & 63, qq = tid >> 6;
-      float m0 = 0.0f, m1 = 0.0f;
+      float m0 = 0.0f, m1 = 0.0f, n0 = 0.0f, n1 = 0.0f;
 #pragma unroll 4
       for (int i = 0; i < 16; ++i) {
         const f16x2 v = *reinterpret_cast<const f16x2 *>(&x[16 * qq + i][2 * cp]);
-        m0 = fmaxf(m0, fabsf((float)v.x));
-        m1 = fmaxf(m1, fabsf((float)v.y));
+        if constexpr (AFF) {
+          m0 = fmaxf(m0, (float)v.x);
+          m1 = fmaxf(m1, (float)v.y);
+          n0 = fminf(n0, (float)v.x);
+          n1 = fminf(n1, (float)v.y);
+        } else {
+          m0 = fmaxf(m0, fabsf((float)v.x));
+          m1 = fmaxf(m1, fabsf((float)v.y));
+        }
       }
       part[qq][2 * cp] = m0;
       part[qq][2 * cp + 1] = m1;
+      if constexpr (AFF) {
+        partn[qq][2 * cp] = n0;
+        partn[qq][2 * cp + 1] = n1;
+      }
     }
     __syncthreads();
     if (tid < kHeadDim) {
-      const float amax = fmaxf(fmaxf(part[0][tid], part[1][tid]), fmaxf(part[2][tid], part[3][tid]));
-      sc[tid] = amax / 7.0f;
-      a.k_scales[((size_t)phys_s[tid >> 5] * H + h) * 32 + (tid & 31)] = amax / 7.0f;
+      const float mx = fmaxf(fmaxf(part[0][tid], part[1][tid]), fmaxf(part[2][tid], part[3][tid]));
+      float *row = a.k_scales + ((size_t)phys_s[tid >> 5] * H + h) * kRow;
+      if constexpr (AFF) {
+        const float mn =
+            fminf(fminf(partn[0][tid], partn[1][tid]), fminf(partn[2][tid], partn[3][tid]));
+        const float2 sz = affine_params(mn, mx);
+        sc[tid] = sz.x;
+        zs[tid] = sz.y;
+        row[tid & 31] = sz.x;
+        reinterpret_cast<uint8_t *>(row + 32)[tid & 31] = (uint8_t)(int)sz.y;
+      } else {
+        sc[tid] = mx / 7.0f;
+        row[tid & 31] = mx / 7.0f;
+      }
     }
     __syncthreads();
     // one unit: channels 32cb .. 32cb+31 of token tt, nibble e of dword d is
@@ -207,7 +252,9 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       uint32_t word = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t q = quant_int((float)v[e], sc[32 * cb + 8 * d + e], -8.0f, 7.0f) & 0xFu;
+        const int c = 32 * cb + 8 * d + e;
+        const uint32_t q = AFF ? quant_affine((float)v[e], sc[c], zs[c])
+                               : quant_int((float)v[e], sc[c], -8.0f, 7.0f) & 0xFu;
         word |= q << (4 * e);
       }
       out[d] = word;
@@ -216,20 +263,39 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
     *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
   } else {
     // V scales: per token, max over each 64-channel half of |V| / 7
+    // (affine: the half's minimum and maximum, each starting from 0)
     {
       const int tt = tid >> 2, qq = tid & 3;
-      float m = 0.0f;
+      float m = 0.0f, mn = 0.0f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * qq + 8 * d]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (AFF) {
+            m = fmaxf(m, (float)v[e]);
+            mn = fminf(mn, (float)v[e]);
+          } else {
+            m = fmaxf(m, fabsf((float)v[e]));
+          }
+        }
       }
       m = fmaxf(m, __shfl_xor(m, 1, 64));
+      if constexpr (AFF) mn = fminf(mn, __shfl_xor(mn, 1, 64));
       if ((qq & 1) == 0) {
-        const float s = m / 7.0f;
-        sc[2 * tt + (qq >> 1)] = s;
-        a.v_scales[(((size_t)phys_s[tt >> 4] * H + h) * kBlock + (tt & 15)) * 2 + (qq >> 1)] = s;
+        const int k = 2 * (tt & 15) + (qq >> 1);  // [slot][channel group]
+        float *row = a.v_scales + ((size_t)phys_s[tt >> 4] * H + h) * kRow;
+        if constexpr (AFF) {
+          const float2 sz = affine_params(mn, m);
+          sc[2 * tt + (qq >> 1)] = sz.x;
+          zs[2 * tt + (qq >> 1)] = sz.y;
+          row[k] = sz.x;
+          reinterpret_cast<uint8_t *>(row + 32)[k] = (uint8_t)(int)sz.y;
+        } else {
+          const float s = m / 7.0f;
+          sc[2 * tt + (qq >> 1)] = s;
+          row[k] = s;
+        }
       }
     }
     __syncthreads();
@@ -243,11 +309,12 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
     for (int e = 0; e < 4; ++e) {
       const int tt = 16 * ub + 4 * quad + e;
       const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
+      const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = 16 * j + m;
-        const uint32_t q =
-            quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
+        const uint32_t q = AFF ? quant_affine((float)x[tt][c], j < 4 ? s0 : s1, j < 4 ? z0 : z1)
+                               : quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
         const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
         out[j >> 1] |= q << (4 * p);
       }
@@ -257,8 +324,9 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
   }
 }
 
+template <bool AFF>
 __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
-  int4_flush(a, blockIdx.x);
+  int4_flush<AFF>(a, blockIdx.x);
 }
 
 // Append the new tokens that stay fp16 to the ring.
@@ -293,9 +361,10 @@ __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
 // append.  Only for calls that add at most one token per row: the appended
 // token is then fewer than R + G positions after any token the flush reads
 // from the ring, so its ring slot is never one of them.
+template <bool AFF>
 __global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a, int groups) {
   if ((int)blockIdx.x < 2 * groups) {
-    int4_flush(a, blockIdx.x);
+    int4_flush<AFF>(a, blockIdx.x);
   } else if (threadIdx.x < 64) {
     append_token(a, blockIdx.x - 2 * groups, blockIdx.y, blockIdx.z, threadIdx.x);
   }
@@ -320,17 +389,26 @@ hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_write_int4(const WriteArgs &a, int batch, int max_new,
+hipError_t launch_write_int4(const WriteArgs &a, bool affine, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream) {
   if (max_new == 1 && max_flush_groups > 0) {
-    hipLaunchKernelGGL(kvq_int4_flush_append_kernel,
-                       dim3(2 * max_flush_groups + 1, a.num_kv_heads, batch), dim3(256), 0,
-                       stream, a, max_flush_groups);
+    const dim3 grid(2 * max_flush_groups + 1, a.num_kv_heads, batch);
+    if (affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<true>, grid, dim3(256), 0, stream, a,
+                         max_flush_groups);
+    } else {
+      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<false>, grid, dim3(256), 0, stream, a,
+                         max_flush_groups);
+    }
     return hipGetLastError();
   }
   if (max_flush_groups > 0) {
-    hipLaunchKernelGGL(kvq_int4_flush_kernel, dim3(2 * max_flush_groups, a.num_kv_heads, batch),
-                       dim3(256), 0, stream, a);
+    const dim3 grid(2 * max_flush_groups, a.num_kv_heads, batch);
+    if (affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_kernel<true>, grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(kvq_int4_flush_kernel<false>, grid, dim3(256), 0, stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -35,12 +35,13 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     seq: int | tuple            # fixed length, or (lo, hi) uniform inclusive
-    dtype: str                  # "int8" | "fp8" | "int4" | "fp16" (unquantized)
+    dtype: str                  # "int8" | "fp8" | "int4" | "int4-affine" | "fp16" (unquantized)
     k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16)
     v_gran: str
     table: str = "identity"     # "identity" | "shuffled"
     channel_outliers: tuple = ()    # (count, factor, tensors) e.g. (4, 10.0, "kvq")
     element_outliers: tuple = ()    # (prob, factor, tensors)
+    shift: tuple = ()               # (offset, tensors): mean added before fp16 rounding
     residual_len: int = 128
     description: str = field(default="", compare=False)
 
@@ -74,6 +75,13 @@ WORKLOADS = {
     "llama3-70b-fp8": Workload(
         "llama3-70b-fp8", 80, 24, 64, 8, 16384, "fp8", "tensor", "tensor",
         description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, FP8 per-tensor"),
+    # the KIVI workload with asymmetric (affine) groups; V shifted off zero
+    # so the zero points matter
+    "kivi-int4-affine": Workload(
+        "kivi-int4-affine", 32, 16, 32, 8, 32768, "int4-affine", "channel", "token",
+        channel_outliers=(8, 10.0, "k"), shift=(0.5, "v"),
+        description="KIVI INT4 affine: 32 layers, 32/8 heads, batch 16, seq 32768, K per-channel, "
+                    "V per-token, group 64, zero points, fp16 residual 128; V ~ N(0.5, 1)"),
     # unquantized baselines of the INT8 comparison ([intelli] §5): the INT8
     # workloads' shapes and inputs with an FP16 cache
     "llama2-7b-fp16": Workload(
@@ -141,6 +149,8 @@ def _draw(w: Workload, shape, tensor: str, seed: int, layer: int, row: int, devi
         prob, factor = w.element_outliers[0], w.element_outliers[1]
         u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
         x = torch.where(u < prob, x * factor, x)
+    if w.shift and tensor in w.shift[1]:
+        x = x + w.shift[0]
     return x.to(torch.float16)
 
 

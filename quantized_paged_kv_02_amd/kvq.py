@@ -17,9 +17,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-INT8, FP8_E4M3, INT4, FP16 = 1, 2, 3, 4
+INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE = 1, 2, 3, 4, 5
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
-DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16}
+DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16,
+          "int4-affine": INT4_AFFINE}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
          "token": PER_TOKEN,
          "none": PER_TENSOR}   # FP16 cache: no scales, the field is ignored
@@ -151,11 +152,15 @@ def alloc_cache(layout: Layout, ring_rows: int = 0, device="cuda",
     """Allocate one layer's pool.  Static scales (per tensor/head/channel)
     are copied in from ``k_static``/``v_static``."""
     nb, h = layout.num_blocks, layout.num_kv_heads
-    if layout.dtype == INT4:
+    if layout.dtype in (INT4, INT4_AFFINE):
         k_codes = torch.empty((nb, h, 1024), dtype=torch.uint8, device=device)
         v_codes = torch.empty((nb, h, 1024), dtype=torch.uint8, device=device)
-        k_scales = torch.empty((nb, h, 32), dtype=torch.float32, device=device)
-        v_scales = torch.empty((nb, h, 16, 2), dtype=torch.float32, device=device)
+        if layout.dtype == INT4:
+            k_scales = torch.empty((nb, h, 32), dtype=torch.float32, device=device)
+            v_scales = torch.empty((nb, h, 16, 2), dtype=torch.float32, device=device)
+        else:   # 32 scales + 32 zero-point bytes per (block, head)
+            k_scales = torch.empty((nb, h, 40), dtype=torch.float32, device=device)
+            v_scales = torch.empty((nb, h, 40), dtype=torch.float32, device=device)
         ring = layout.residual_len + layout.group_size
         k_resid = torch.empty((ring_rows, h, ring, 128), dtype=torch.float16, device=device)
         v_resid = torch.empty((ring_rows, h, ring // 4, 128, 4), dtype=torch.float16,

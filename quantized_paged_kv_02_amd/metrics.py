@@ -10,7 +10,8 @@ Quantization 生产实战", section "为什么长上下文更需要 KV Cache
 Quantization"), so these bytes over the kernel time is the figure compared
 with the HBM roofline.  Sizes follow the per-value byte counts of the
 [oh-bug] section "KV Cache 的基本内存模型" (INT8/FP8 1 byte, INT4 half a
-byte, FP16 2 bytes) plus the fp32 scales of each granularity.
+byte, FP16 2 bytes) plus the fp32 scales of each granularity (and the
+one-byte zero points of the affine INT4 groups).
 """
 
 from __future__ import annotations
@@ -37,12 +38,15 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
     total = b * hq * d * 2 + b * hq * d * 4          # q fp16 in, out fp32
     uniform_scales = 0
     for s in (int(x) for x in lens):
-        if dtype == "int4":
+        if dtype in ("int4", "int4-affine"):
             nq = kivi_quantized_len(s, residual)
             r = s - nq
             total += hkv * nq * d                     # K and V nibbles: 2 x nq x d / 2
             total += hkv * (nq // GROUP) * d * 4      # K per-channel group scales
             total += hkv * nq * 2 * 4                 # V per-token scales, 2 groups
+            if dtype == "int4-affine":
+                total += hkv * (nq // GROUP) * d      # K zero points, 1 byte each
+                total += hkv * nq * 2                 # V zero points
             total += hkv * r * d * 2 * 2              # fp16 K and V residual
             total += (nq // BLOCK) * 4                # block-table entries
         elif dtype == "fp16":
@@ -54,7 +58,7 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
                 if gran == "token":
                     total += hkv * s * 4
             total += ((s + BLOCK - 1) // BLOCK) * 4
-    if dtype not in ("int4", "fp16"):
+    if dtype not in ("int4", "int4-affine", "fp16"):
         for gran in (k_gran, v_gran):
             if gran != "token":
                 uniform_scales += _scale_bytes_uniform(gran, hkv)

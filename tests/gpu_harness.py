@@ -65,7 +65,7 @@ def fill_garbage(cache):
     if cache.k_resid is not None:
         cache.k_resid.fill_(float("nan"))
         cache.v_resid.fill_(float("nan"))
-    int4 = cache.layout.dtype == 3
+    int4 = cache.layout.dtype in (3, 5)
     if int4 or cache.layout.k_gran == 3:
         cache.k_scales.fill_(float("nan"))
     if int4 or cache.layout.v_gran == 3:
@@ -97,7 +97,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     prefill_k = [k[:max(int(s) - 1, 0)] for k, s in zip(ks, lens)]
     prefill_v = [v[:max(int(s) - 1, 0)] for v, s in zip(vs, lens)]
     k_static = v_static = None
-    if w.dtype != "int4":
+    if not w.dtype.startswith("int4"):
         k_static = _static(w, w.k_gran, [t for t in prefill_k if len(t)] or ks, w.dtype)
         v_static = _static(w, w.v_gran, [t for t in prefill_v if len(t)] or vs, w.dtype)
     cache = kvq.alloc_cache(layout, ring_rows=b, device=device,
@@ -178,14 +178,20 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
     kb, vb = res.k[r], res.v[r]
     row = res.table[r]
     p = res.pools
-    if w.dtype == "int4":
-        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len)
+    if w.dtype.startswith("int4"):
+        affine = w.dtype == "int4-affine"
+        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len, affine=affine)
         nq = kv["nq"]
         if check_codes:
-            assert np.array_equal(lv.logical_codes(p["k_codes"], row, nq, "k", "int4"),
+            assert np.array_equal(lv.logical_codes(p["k_codes"], row, nq, "k", w.dtype),
                                   kv["k_codes"]), f"row {r}: INT4 K codes"
-            assert np.array_equal(lv.logical_codes(p["v_codes"], row, nq, "v", "int4"),
+            assert np.array_equal(lv.logical_codes(p["v_codes"], row, nq, "v", w.dtype),
                                   kv["v_codes"]), f"row {r}: INT4 V codes"
+            if affine:
+                assert np.array_equal(lv.int4_k_zero_points(p["k_scales"], row, nq // 64),
+                                      kv["k_zp"]), f"row {r}: INT4 K zero points"
+                assert np.array_equal(lv.int4_v_zero_points(p["v_scales"], row, nq),
+                                      kv["v_zp"]), f"row {r}: INT4 V zero points"
             gks = lv.int4_k_scales(p["k_scales"], row, nq // 64)
             assert np.array_equal(gks.view(np.uint32), kv["k_scales"].view(np.uint32)), \
                 f"row {r}: INT4 K scales"

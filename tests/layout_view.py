@@ -51,12 +51,15 @@ def chunk16(pool_chunk, which):
     return np.asarray(pool_chunk)[off]
 
 
-def chunk4(pool_chunk, which):
-    """[1024] uint8 chunk -> [16, 128] int8 codes in [-8, 7]."""
+def chunk4(pool_chunk, which, signed=True):
+    """[1024] uint8 chunk -> [16, 128] int8 codes in [-8, 7] (unsigned:
+    uint8 codes in [0, 15])."""
     byte = K4_BYTE if which == "k" else V4_BYTE
     nib = K4_NIB if which == "k" else V4_NIB
     b = np.asarray(pool_chunk).astype(np.int64)[byte]
     v = np.where(nib == 1, (b >> 4) & 0xF, b & 0xF)
+    if not signed:
+        return v.astype(np.uint8)
     return np.where(v >= 8, v - 16, v).astype(np.int8)
 
 
@@ -66,13 +69,15 @@ def logical_codes(pool, table_row, n_tokens, which, dtype):
     pool = np.asarray(pool)
     h = pool.shape[1]
     kind = {"int4": np.int8, "fp16": np.float16}.get(dtype, np.uint8)
-    out = np.zeros((n_tokens, h, 128), kind)
+    out = np.zeros((n_tokens, h, 128), kind)   # int4-affine: uint8 codes 0..15
     for j in range((n_tokens + 15) // 16):
         phys = int(table_row[j])
         n = min(16, n_tokens - 16 * j)
         for hh in range(h):
             if dtype == "int4":
                 c = chunk4(pool[phys, hh], which)
+            elif dtype == "int4-affine":
+                c = chunk4(pool[phys, hh], which, signed=False)
             elif dtype == "fp16":
                 c = chunk16(pool[phys, hh], which)
             else:
@@ -92,24 +97,54 @@ def logical_token_scales(scales, table_row, n_tokens):
 
 
 def int4_k_scales(k_scales, table_row, n_groups):
-    """INT4 K scales [NB, H, 32] -> [n_groups, H, 128]: block 4g+u holds
-    channels 32u..32u+31 of group g."""
+    """INT4 K scales [NB, H, 32] (affine: [NB, H, 40], scales first) ->
+    [n_groups, H, 128]: block 4g+u holds channels 32u..32u+31 of group g."""
     k_scales = np.asarray(k_scales)
     h = k_scales.shape[1]
     out = np.zeros((n_groups, h, 128), np.float32)
     for g in range(n_groups):
         for u in range(4):
-            out[g, :, 32 * u:32 * u + 32] = k_scales[int(table_row[4 * g + u])]
+            out[g, :, 32 * u:32 * u + 32] = k_scales[int(table_row[4 * g + u]), :, :32]
     return out
 
 
 def int4_v_scales(v_scales, table_row, n_tokens):
-    """INT4 V scales [NB, H, 16, 2] -> [n_tokens, H, 2]."""
+    """INT4 V scales [NB, H, 16, 2] (affine: [NB, H, 40], scales first) ->
+    [n_tokens, H, 2]."""
     v_scales = np.asarray(v_scales)
+    v_scales = v_scales.reshape(v_scales.shape[0], v_scales.shape[1], -1)[:, :, :32]
+    v_scales = v_scales.reshape(v_scales.shape[0], v_scales.shape[1], 16, 2)
     out = np.zeros((n_tokens, v_scales.shape[1], 2), np.float32)
     for j in range((n_tokens + 15) // 16):
         n = min(16, n_tokens - 16 * j)
         out[16 * j:16 * j + n] = v_scales[int(table_row[j]), :, :n].transpose(1, 0, 2)
+    return out
+
+
+def _zp_bytes(rows):
+    """[NB, H, 40] fp32 affine rows -> [NB, H, 32] uint8 zero points."""
+    rows = np.ascontiguousarray(np.asarray(rows, np.float32))
+    return rows[:, :, 32:40].copy().view(np.uint8)
+
+
+def int4_k_zero_points(k_scales, table_row, n_groups):
+    """Affine K zero points -> [n_groups, H, 128] (same block order as the
+    scales)."""
+    z = _zp_bytes(k_scales)
+    out = np.zeros((n_groups, z.shape[1], 128), np.int64)
+    for g in range(n_groups):
+        for u in range(4):
+            out[g, :, 32 * u:32 * u + 32] = z[int(table_row[4 * g + u])]
+    return out
+
+
+def int4_v_zero_points(v_scales, table_row, n_tokens):
+    """Affine V zero points -> [n_tokens, H, 2]."""
+    z = _zp_bytes(v_scales).reshape(-1, np.asarray(v_scales).shape[1], 16, 2)
+    out = np.zeros((n_tokens, z.shape[1], 2), np.int64)
+    for j in range((n_tokens + 15) // 16):
+        n = min(16, n_tokens - 16 * j)
+        out[16 * j:16 * j + n] = z[int(table_row[j]), :, :n].transpose(1, 0, 2)
     return out
 
 

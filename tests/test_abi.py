@@ -190,10 +190,27 @@ def test_fp16_cache_rules():
     assert kvq.validate(lay, _cache(k_codes=None, k_scales=None, v_scales=None), 2, 100) == INV
     assert kvq.validate(lay, _cache(v_codes=FAKE + 2, k_scales=None, v_scales=None), 2,
                         100) == ALN
-    assert kvq.validate(_layout(dtype=5), bare, 2, 100) == INV
+    assert kvq.validate(_layout(dtype=6), bare, 2, 100) == INV
     assert kvq.validate(_layout(dtype=4, split_tokens=24), bare, 2, 100) == INV
     assert _decode(lay, bare, q=None) == INV
     assert _write(lay, bare, cu=FAKE + 4) == ALN
     assert _write_decode(lay, bare, vn=None) == INV
     # same partition plan rules: a split launch needs partials
     assert kvq.decode_workspace_bytes(_layout(dtype=4, split_tokens=16), 2, 100) > 0
+
+
+def test_int4_affine_rules():
+    # same rules as the symmetric INT4 cache: K per channel, V per token,
+    # group 64, residual a multiple of 64, rings required
+    base = dict(dtype=5, k_gran=2, v_gran=3, residual_len=128, group_size=64)
+    assert kvq.validate(_layout(**base), _cache(int4=True), 2, 100) == OK
+    assert kvq.validate(_layout(**{**base, "v_gran": 2}), _cache(int4=True), 2, 100) == UNS
+    assert kvq.validate(_layout(**{**base, "group_size": 128}), _cache(int4=True), 2, 100) == UNS
+    assert kvq.validate(_layout(**{**base, "split_tokens": 16}), _cache(int4=True), 2, 100) == INV
+    assert kvq.validate(_layout(**base), _cache(int4=False), 2, 100) == INV
+    assert kvq.validate(_layout(**base), _cache(int4=True, k_scales=None), 2, 100) == INV
+    assert kvq.validate(_layout(**base), _cache(int4=True, v_scales=FAKE + 4), 2, 100) == ALN
+    lay = _layout(**{**base, "split_tokens": 64})
+    assert kvq.decode_workspace_bytes(lay, 2, 100) == 0             # residual only
+    assert kvq.decode_workspace_bytes(lay, 2, 128 + 64 + 64) > 0
+    assert _write_decode(_layout(**base), _cache(int4=True), kn=None) == INV

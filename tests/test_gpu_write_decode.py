@@ -31,13 +31,16 @@ CASES = [
     ("fp8", "channel", "token", "identity"),
     ("int4", "channel", "token", "shuffled"),
     ("fp16", "none", "none", "shuffled"),
+    ("int4-affine", "channel", "token", "shuffled"),
 ]
 
 LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2]]
 
 
 def _w(dtype, kg, vg, table):
-    extra = {"channel_outliers": (8, 10.0, "k")} if dtype == "int4" else {}
+    extra = {"channel_outliers": (8, 10.0, "k")} if dtype.startswith("int4") else {}
+    if dtype == "int4-affine":
+        extra["shift"] = (0.5, "v")
     return inputs.scaled_down(W["tiny"], name=f"wd-{dtype}-{kg}-{vg}", batch=4,
                               num_q_heads=8, num_kv_heads=2, dtype=dtype, k_gran=kg,
                               v_gran=vg, table=table, **extra)
