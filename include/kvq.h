@@ -101,7 +101,11 @@
  *             the INT4 layout, the 32 bytes of floats 32..39 the uint8 zero
  *             points of the same channels (byte i: channel 32*(j%4)+i).
  *   v_scales: fp32 [NB][H][40]; floats 0..31 are [16][2] as for INT4, the
- *             32 bytes of floats 32..39 the uint8 zero points [16][2].
+ *             32 bytes of floats 32..39 uint8 zero points, group-transposed:
+ *             the zero point of channel group g of token 16*b + 4*u + e of
+ *             a 64-token group is byte 8*b + 2*e + g of the row of the
+ *             group's block u (b, u, e in 0..3), so one row holds what one
+ *             lane row of the decode kernel needs.
  *
  * ---- FP16 (unquantized) layout: fp16 [NB][H][2048] for each of K and V ----
  * The baseline the quantized formats are measured against ([intelli] §5:

@@ -550,6 +550,54 @@ __device__ __forceinline__ f16x8 int4x8_to_f16_koff(uint32_t x) {
   return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Affine (unsigned) key nibbles in the same slot order: low nibbles read as
+// E4M3 bytes 0000nnnn give u, high nibbles under the exponent of 1024 give
+// 1024 + 16 u; the offsets (the zero points) are removed after the product.
+__device__ __forceinline__ f16x8 uint4x8_to_f16_koff(uint32_t x) {
+  const uint32_t lo = x & 0x0F0F0F0Fu;
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // nibbles 0, 2
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // nibbles 4, 6
+  const f16x2 b = as_f16x2((x & 0x00F000F0u) | 0x64006400u);                     // nibbles 1, 5
+  const f16x2 d = as_f16x2(((x >> 8) & 0x00F000F0u) | 0x64006400u);              // nibbles 3, 7
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Lane k of this lane's 16-lane row (DPP row broadcast).
+template <int K>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  static_assert(K >= 0 && K < 16, "lane within a row");
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + K, 0xF, 0xF, false);
+}
+
+// Offset operand of the affine key conversion for the channels 8j..8j+7 of
+// a lane's 32 (zero-point bytes d0 = channels 0..3, d1 = 4..7): z for the
+// low-nibble slots, 1024 + 16 z for the high ones, in the slot order
+// 0, 2, 1, 5, 4, 6, 3, 7.
+__device__ __forceinline__ f16x8 zp_key_offsets(uint32_t d0, uint32_t d1) {
+  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+      __builtin_amdgcn_perm(d0, d0, 0x0C0C0200u), 512.0f, false);                       // z0, z2
+  const uint32_t s23 = (__builtin_amdgcn_perm(d1, d0, 0x0C050C01u) << 4) | 0x64006400u;  // z1, z5
+  const f16x2 s45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+      __builtin_amdgcn_perm(d1, d1, 0x0C0C0200u), 512.0f, false);                       // z4, z6
+  const uint32_t s67 = (__builtin_amdgcn_perm(d1, d0, 0x0C070C03u) << 4) | 0x64006400u;  // z3, z7
+  return u4_to_f16x8(u32x4{as_u32(s01), s23, as_u32(s45), s67});
+}
+
+// Value bias operand of an affine block pair for channel group g from the
+// pair's 16 zero-point bytes (byte 8b + 2e + g: block b of the pair, token
+// 4qd + e): -(1024 + z) for tokens 0, 1 (low nibbles), -(1024 + 16 z) for
+// tokens 2, 3, block 0 then block 1.
+template <int G>
+__device__ __forceinline__ f16x8 zp_value_bias(const u32x4 &w) {
+  constexpr uint32_t sel = G ? 0x0C030C01u : 0x0C020C00u;  // bytes g, 2 + g -> halves
+  constexpr uint32_t neg1024 = 0xE400E400u;
+  const u32x4 r = {__builtin_amdgcn_perm(w[0], w[0], sel) | neg1024,
+                   (__builtin_amdgcn_perm(w[1], w[1], sel) << 4) | neg1024,
+                   __builtin_amdgcn_perm(w[2], w[2], sel) | neg1024,
+                   (__builtin_amdgcn_perm(w[3], w[3], sel) << 4) | neg1024};
+  return u4_to_f16x8(r);
+}
+
 // The two channels (within a k-slot chunk of 8) of lane l's slot pair
 // 2(l%4), 2(l%4)+1 in the offset conversion's order: (0,2) (1,5) (4,6) (3,7).
 __device__ __forceinline__ int2 koff_pair(int lane) {
@@ -568,10 +616,12 @@ struct Group4 {
 };
 
 // pm: physical block of this lane's K-scale row (block lane/16 of the group).
-// AFF: scale rows of 40 floats, the zero points in the last 32 bytes.
+// AFF: scale rows of 40 floats, the zero points in the last 32 bytes; pz:
+// physical block (lane%16)/4 of the group, whose V row holds this lane's
+// token's zero points (group-transposed).
 template <bool AFF>
 __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, const int (&ph)[4],
-                                            int pm, int h, int lane) {
+                                            int pm, int pz, int h, int lane) {
   constexpr int kRow = AFF ? 40 : 32;  // floats per (block, head) scale row
   const int H = a.num_kv_heads;
   constexpr uint32_t bytes = 1024;  // one (block, head) code chunk
@@ -595,8 +645,9 @@ __device__ __forceinline__ void load_group4(Group4 &t, const DecodeArgs &a, cons
   if constexpr (AFF) {
     const uint8_t *kzp = reinterpret_cast<const uint8_t *>(krow + 32) + 8 * ((lane >> 2) & 3);
     t.kz = (uint32_t)kzp[ko.x] | ((uint32_t)kzp[ko.y] << 8);
-    t.vz = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(vrow + 32) +
-                                               2 * (lane & 15));
+    const float *zrow = a.v_scales + ((size_t)pz * H + h) * kRow;
+    t.vz = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(zrow + 32) +
+                                               8 * (lane >> 4) + 2 * (lane & 3));
   }
 }
 
@@ -608,12 +659,21 @@ struct Group4C {
   u32x4 v[4];
   float ks[2];
   f32x4 vsa, vsb;
+  // affine: dword l%16 of the 64 zero-point bytes this lane's row of the
+  // wave needs: K zero points of channels 32qd..32qd+31 (dwords 0..7), then
+  // V zero points of tokens 4qd..4qd+3 of blocks 0..3 (dwords 8..15).  Each
+  // lane loads one dword; row broadcasts hand them to the whole row.
+  uint32_t zw;
   __device__ explicit Group4C(int = 0) {}
 };
 
-// pm as for load_group4; pv: physical block (l%16)/4 of the group.
+// pm as for load_group4; pv: physical block (l%16)/4 of the group.  AFF:
+// rows of 40 floats; the zero points this lane's operands need are the
+// last 32 bytes of block qd's K and V rows.
+template <bool AFF>
 __device__ __forceinline__ void load_group4c(Group4C &t, const DecodeArgs &a, const int (&ph)[4],
                                              int pm, int pv, int h, int lane) {
+  constexpr int kRow = AFF ? 40 : 32;
   const int H = a.num_kv_heads;
   constexpr uint32_t bytes = 1024;
 #pragma unroll
@@ -623,12 +683,18 @@ __device__ __forceinline__ void load_group4c(Group4C &t, const DecodeArgs &a, co
     t.v[u] = bld16(make_rsrc(a.v_codes + chunk * 1024, bytes), 16 * lane);
   }
   const int2 ko = koff_pair(lane);
-  const float *ksp = a.k_scales + ((size_t)pm * H + h) * 32 + 8 * ((lane >> 2) & 3);
+  const float *krow = a.k_scales + ((size_t)pm * H + h) * kRow;
+  const float *ksp = krow + 8 * ((lane >> 2) & 3);
   t.ks[0] = ksp[ko.x];
   t.ks[1] = ksp[ko.y];
-  const float *vsp = a.v_scales + ((size_t)pv * H + h) * (kBlock * 2) + 8 * (lane >> 4);
+  const float *vsp = a.v_scales + ((size_t)pv * H + h) * kRow + 8 * (lane >> 4);
   t.vsa = ld16f(vsp);
   t.vsb = ld16f(vsp + 4);
+  if constexpr (AFF) {
+    const int n = lane & 15;
+    const float *zrow = (n < 8 ? a.k_scales : a.v_scales) + ((size_t)pm * H + h) * kRow + 32;
+    t.zw = reinterpret_cast<const uint32_t *>(zrow)[n & 7];
+  }
 }
 
 // Join block b0's and block b1's nibbles of channel tile j (dword j>>1 of
@@ -830,7 +896,8 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
       // a per-lane LDS read: selecting among ph[] per lane would become a
       // private-array access, whose scratch load joins the in-order vmcnt
       // queue and makes every group wait for all loads in flight
-      load_group4<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], h, lane);
+      load_group4<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + ((lane & 15) >> 2)],
+                       h, lane);
     };
     auto compute = [&](Group4 &t, int) {
       compute_group4<AFF>(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
@@ -911,24 +978,34 @@ __device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
   return u4_to_f16x8(w);
 }
 
-template <int PR>
+template <int PR, bool AFF>
 __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, const f16x8 &pb0,
                                              const f16x8 &pb1) {
-  const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
-  const f16x8 abias = {b0, b0, b1, b1, b0, b0, b1, b1};
+  f16x8 abias0, abias1;
+  if constexpr (AFF) {
+    const u32x4 w = {row_bcast<8 + 4 * PR>(t.zw), row_bcast<9 + 4 * PR>(t.zw),
+                     row_bcast<10 + 4 * PR>(t.zw), row_bcast<11 + 4 * PR>(t.zw)};
+    abias0 = zp_value_bias<0>(w);
+    abias1 = zp_value_bias<1>(w);
+  } else {
+    const f16 b0 = (f16)-1032.0f, b1 = (f16)-1152.0f;
+    abias0 = abias1 = f16x8{b0, b0, b1, b1, b0, b0, b1, b1};
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t w = pair_tile(t.v[2 * PR][j >> 1], t.v[2 * PR + 1][j >> 1], j & 1);
-    st.o[j] = mfma32(int4x8_to_f16_biased(w), j < 4 ? pb0 : pb1, st.o[j]);
+    const f16x8 av = AFF ? uint4x8_to_f16_biased(w) : int4x8_to_f16_biased(w);
+    st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(abias, j < 4 ? pb0 : pb1, st.o[j]);
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(j < 4 ? abias0 : abias1, j < 4 ? pb0 : pb1, st.o[j]);
 }
 
 // qv[hh]: this lane's query values of head hh at channels 8(lane/4) +
 // koff_pair(lane), times 1/16 for the high-nibble slots; qb: this wave's q'
 // rows; qrd: dword offset of this lane's score-operand row (hi row of head
 // n%4 in even banks, lo row in odd banks) and row group.
+template <bool AFF>
 __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
                                                 const float (&qv)[4][2], uint32_t *qb, int qrd,
                                                 float qk_scale, int lane, int n) {
@@ -941,8 +1018,9 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
     qb[(4 + hh) * kQbRow + lane] = lo;
   }
   // every row of the offset operand is the conversion's per-slot offset
+  // (affine: the zero points of this lane's channels, per chunk j)
   const f16 o_lo = (f16)8.0f, o_hi = (f16)1152.0f;
-  const f16x8 aoff = {o_lo, o_lo, o_hi, o_hi, o_lo, o_lo, o_hi, o_hi};
+  const f16x8 aoff_sym = {o_lo, o_lo, o_hi, o_hi, o_lo, o_lo, o_hi, o_hi};
   f16x8 bq[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -953,7 +1031,20 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = mfma32(int4x8_to_f16_koff(t.k[u][j]), bq[j], acc[u]);
+    for (int u = 0; u < 4; ++u) {
+      const f16x8 av = AFF ? uint4x8_to_f16_koff(t.k[u][j]) : int4x8_to_f16_koff(t.k[u][j]);
+      acc[u] = mfma32(av, bq[j], acc[u]);
+    }
+    f16x8 aoff = aoff_sym;
+    if constexpr (AFF) {
+      // zero-point dwords 2j, 2j+1 of the row (channels 8j..8j+7)
+      uint32_t d0, d1;
+      if (j == 0) { d0 = row_bcast<0>(t.zw); d1 = row_bcast<1>(t.zw); }
+      else if (j == 1) { d0 = row_bcast<2>(t.zw); d1 = row_bcast<3>(t.zw); }
+      else if (j == 2) { d0 = row_bcast<4>(t.zw); d1 = row_bcast<5>(t.zw); }
+      else { d0 = row_bcast<6>(t.zw); d1 = row_bcast<7>(t.zw); }
+      aoff = zp_key_offsets(d0, d1);
+    }
     ac = mfma32(aoff, bq[j], ac);
   }
   // every row of ac holds the offsets' products with head n%4's hi / lo
@@ -970,10 +1061,11 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
                           pack_rne(p2 * t.vsb[0], p3 * t.vsb[2])};
   const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
                           pack_rne(p2 * t.vsb[1], p3 * t.vsb[3])};
-  value_pair_c<0>(st, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
-  value_pair_c<1>(st, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
+  value_pair_c<0, AFF>(st, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
+  value_pair_c<1, AFF>(st, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
 }
 
+template <bool AFF>
 __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
                              int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
                              int pre_id) {
@@ -1015,10 +1107,10 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
       const int j0 = 4 * (wave + kWaves * k);
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
-      load_group4c(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
+      load_group4c<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
     };
     auto compute = [&](Group4C &t, int) {
-      compute_group4c(st, t, qv, qb, qrd, a.qk_scale, lane, n);
+      compute_group4c<AFF>(st, t, qv, qb, qrd, a.qk_scale, lane, n);
     };
     pipeline<Group4C>(cnt, load, compute);
   }
@@ -1237,7 +1329,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       // the window first: its loads and arithmetic overlap the start of the
       // INT4 stream instead of trailing it with nothing else in flight
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
-      stream_int4c(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      stream_int4c<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
       stream_int4<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
@@ -1270,11 +1362,11 @@ __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, KS, VS)) void kvq_pa
   decode_workgroup<DT, KS, VS, false>(a, sh);
 }
 
-// DT: kInt4 or kInt4Affine (the compact G4 layout is built for kInt4 only)
+// DT: kInt4 or kInt4Affine
 template <int DT, bool G4>
 __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
     DecodeArgs a) {
-  static_assert(is_kivi(DT) && (DT == kInt4 || !G4), "compact layout: symmetric INT4 only");
+  static_assert(is_kivi(DT), "KIVI-grouped INT4 caches only");
   __shared__ SharedLds sh;
   decode_workgroup<DT, kChannel, kToken, G4>(a, sh);
 }
@@ -1386,6 +1478,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   } else if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, false>), grid, dim3(kThreads), 0,
                        stream, a);
+  } else if (dtype == kInt4Affine && a.group <= 4) {
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, true>), grid, dim3(kThreads),
+                       0, stream, a);
   } else if (dtype == kInt4Affine) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, false>), grid, dim3(kThreads),
                        0, stream, a);

@@ -290,7 +290,12 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
           sc[2 * tt + (qq >> 1)] = sz.x;
           zs[2 * tt + (qq >> 1)] = sz.y;
           row[k] = sz.x;
-          reinterpret_cast<uint8_t *>(row + 32)[k] = (uint8_t)(int)sz.y;
+          // zero points group-transposed: token 16b + 4u + e of the group
+          // goes to the row of the group's block u, byte 8b + 2e + g
+          const int s16 = tt & 15;
+          float *zrow = a.v_scales + ((size_t)phys_s[s16 >> 2] * H + h) * kRow;
+          reinterpret_cast<uint8_t *>(zrow + 32)[8 * (tt >> 4) + 2 * (s16 & 3) + (qq >> 1)] =
+              (uint8_t)(int)sz.y;
         } else {
           const float s = m / 7.0f;
           sc[2 * tt + (qq >> 1)] = s;

@@ -139,12 +139,17 @@ def int4_k_zero_points(k_scales, table_row, n_groups):
 
 
 def int4_v_zero_points(v_scales, table_row, n_tokens):
-    """Affine V zero points -> [n_tokens, H, 2]."""
-    z = _zp_bytes(v_scales).reshape(-1, np.asarray(v_scales).shape[1], 16, 2)
+    """Affine V zero points -> [n_tokens, H, 2] (n_tokens a multiple of 64):
+    token 16b + 4u + e of group G is byte 8b + 2e + g of the row of the
+    group's block u (logical block 4G + u)."""
+    z = _zp_bytes(v_scales)
     out = np.zeros((n_tokens, z.shape[1], 2), np.int64)
-    for j in range((n_tokens + 15) // 16):
-        n = min(16, n_tokens - 16 * j)
-        out[16 * j:16 * j + n] = z[int(table_row[j]), :, :n].transpose(1, 0, 2)
+    for t in range(n_tokens):
+        grp, r = divmod(t, 64)
+        b, s16 = divmod(r, 16)
+        u, e = divmod(s16, 4)
+        row = z[int(table_row[4 * grp + u])]
+        out[t] = row[:, 8 * b + 2 * e:8 * b + 2 * e + 2]
     return out
 
 
