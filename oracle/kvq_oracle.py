@@ -29,7 +29,9 @@ import numpy as np
 
 __all__ = [
     "BLOCK_SIZE", "INT8_QMIN", "INT8_QMAX", "INT4_QMIN", "INT4_QMAX",
-    "E4M3_MAX", "KIVI_GROUP", "KIVI_RESIDUAL", "BYTES_PER_VALUE",
+    "E4M3_MAX", "E5M2_MAX", "KIVI_GROUP", "KIVI_RESIDUAL", "BYTES_PER_VALUE",
+    "e5m2_value", "e5m2_decode_table", "e5m2_encode", "quantize_e5m2",
+    "calibrate_scales", "quant_divisor",
     "kv_cache_bytes", "absmax_scale", "quantize_int", "e4m3_value",
     "e4m3_decode_table", "e4m3_encode", "quantize_e4m3", "dequantize",
     "quantize_per_token", "quantize_static", "kivi_quantized_len",
@@ -56,6 +58,8 @@ INT4_QMAX = 7
 INT4_QMIN = -8
 # Largest finite OCP E4M3 magnitude (1.75 * 2**8).
 E4M3_MAX = 448.0
+# Largest finite OCP E5M2 magnitude (1.75 * 2**15).
+E5M2_MAX = 57344.0
 # KIVI-style INT4 cache parameters ([oh-bug] section "Transformers：适合实验和
 # 小规模验证": 4 bits, group 64, residual 128).
 KIVI_GROUP = 64
@@ -183,6 +187,71 @@ def e4m3_encode(y):
     return code.astype(np.uint8)
 
 
+def e5m2_value(code):
+    """Real value of one OCP E5M2 byte (1 sign, 5 exponent bits with bias 15,
+    2 mantissa bits; exponent 31 is infinity or NaN), from the format
+    definition.  [yunthe] section "KV Cache量化策略：INT8与FP8精度对比与选择"
+    names E4M3 and E5M2 as the two FP8 formats."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 2) & 0x1F
+    man = code & 0x3
+    if exp == 0x1F:
+        return sign * float("inf") if man == 0 else float("nan")
+    if exp == 0:
+        mag = man * 2.0 ** -16         # subnormal: man/4 * 2**(1-15)
+    else:
+        mag = (1.0 + man / 4.0) * 2.0 ** (exp - 15)
+    return sign * mag
+
+
+def e5m2_decode_table():
+    """All 256 E5M2 codes as float64 (+-inf and NaN where the format has them)."""
+    return np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e5m2_encode(y):
+    """Round fp32 values in [-57344, 57344] to the nearest E5M2 code, ties to
+    the even mantissa, keeping the sign of zero.
+
+    Normal values in [2**e, 2**(e+1)), e >= -14, are spaced 2**(e-2); below
+    2**-14 the spacing is 2**-16.  Rounding |y| to a multiple of the spacing
+    with half-to-even gives the nearest representable value.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    if np.any(np.abs(y) > E5M2_MAX) or np.any(np.isnan(y)):
+        raise ValueError("e5m2_encode expects finite values clamped to +-57344")
+    a = np.abs(y).astype(np.float64)
+    neg = np.signbit(y)
+    _, k = np.frexp(a)
+    e = np.maximum(k - 1, -14)                 # floor(log2 a), floored at -14
+    quantum = np.ldexp(1.0, e - 2)
+    v = np.rint(a / quantum) * quantum         # representable magnitude
+    _, kv = np.frexp(v)
+    ev = kv - 1
+    normal = v >= 2.0 ** -14
+    man_norm = np.where(normal, v / np.ldexp(1.0, np.where(normal, ev, 0)) * 4 - 4, 0)
+    code_norm = ((ev + 15) << 2) | man_norm.astype(np.int64)
+    code_sub = (v / 2.0 ** -16).astype(np.int64)
+    code = np.where(normal, code_norm, code_sub).astype(np.int64)
+    code = code | (neg.astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def quantize_e5m2(x, scale):
+    """E5M2 code of ``clamp(x / scale, -57344, 57344)`` (fp32 division); the
+    E4M3 rule with E5M2's range (dynamic scale = amax / 57344); a zero scale
+    gives +0 codes."""
+    x = np.asarray(x, dtype=np.float32)
+    scale = np.asarray(scale, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = x / scale
+    zero = np.broadcast_to(scale, y.shape) == 0
+    y = np.where(zero, np.float32(0.0), y)
+    y = np.clip(y, np.float32(-E5M2_MAX), np.float32(E5M2_MAX)).astype(np.float32)
+    return e5m2_encode(y)
+
+
 def quantize_e4m3(x, scale):
     """E4M3 code of ``clamp(x / scale, -448, 448)`` (fp32 division).
 
@@ -202,10 +271,13 @@ def quantize_e4m3(x, scale):
 
 def dequantize(codes, scale, dtype):
     """``x_hat = code * scale`` in fp64 (exact).  [intelli] §3.1
-    (``q_x.float() * scale``).  ``dtype`` is "int8", "int4" or "fp8"."""
+    (``q_x.float() * scale``).  ``dtype`` is "int8", "int4", "fp8" (E4M3) or
+    "fp8e5m2"."""
     scale = np.asarray(scale, dtype=np.float64)
     if dtype == "fp8":
         vals = e4m3_decode_table()[np.asarray(codes, np.uint8)]
+    elif dtype == "fp8e5m2":
+        vals = e5m2_decode_table()[np.asarray(codes, np.uint8)]
     else:
         vals = np.asarray(codes).astype(np.float64)
     return vals * scale
@@ -215,8 +287,13 @@ def dequantize(codes, scale, dtype):
 # Granularities for INT8 / FP8 caches
 # ---------------------------------------------------------------------------
 
-def _qdivisor(dtype):
-    return {"int8": INT8_QMAX, "fp8": E4M3_MAX}[dtype]
+def quant_divisor(dtype):
+    """The code range a scale maps max|x| onto: 127 (INT8), 448 (E4M3),
+    57344 (E5M2)."""
+    return {"int8": INT8_QMAX, "fp8": E4M3_MAX, "fp8e5m2": E5M2_MAX}[dtype]
+
+
+_qdivisor = quant_divisor
 
 
 def _quant(x, scale, dtype):
@@ -224,7 +301,37 @@ def _quant(x, scale, dtype):
         return quantize_int(x, scale, INT8_QMIN, INT8_QMAX)
     if dtype == "fp8":
         return quantize_e4m3(x, scale)
+    if dtype == "fp8e5m2":
+        return quantize_e5m2(x, scale)
     raise ValueError(dtype)
+
+
+def calibrate_scales(x, gran, dtype, previous=None):
+    """Static scales from calibration tokens ``x`` [T, Hkv, D] (fp16): the
+    maximum of |x| over the tokens and, per granularity, over the channels
+    ("head", shape [Hkv]) or over heads and channels too ("tensor", [1]);
+    "channel" keeps [Hkv, D].  Scale = amax / divisor in fp32.
+
+    [yunthe] sections "KV Cache量化策略" (scale = max(abs(x)) / 127) and
+    "配置与启动参数" (per-layer K and V scales computed offline from
+    calibration data); [oh-bug] vLLM section (per-tensor and per-head FP8
+    scales from a random-token warmup or calibration data).  Reading: with
+    ``previous`` (scales of earlier calibration batches) the result is the
+    elementwise maximum, i.e. the scale of all batches together.
+    """
+    a = np.abs(np.asarray(x, dtype=np.float32))
+    if gran == "channel":
+        amax = a.max(axis=0)
+    elif gran == "head":
+        amax = a.max(axis=(0, 2))
+    elif gran == "tensor":
+        amax = np.array([a.max()], np.float32)
+    else:
+        raise ValueError(gran)
+    s = (amax.astype(np.float32) / np.float32(quant_divisor(dtype))).astype(np.float32)
+    if previous is not None:
+        s = np.maximum(s, np.asarray(previous, np.float32).reshape(s.shape))
+    return s
 
 
 def quantize_per_token(x, dtype):
