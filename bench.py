@@ -94,10 +94,8 @@ def _cpu_unit(args):
             k_hat = oracle.dequantize(kc, ks[..., None], w.dtype)
             v_hat = oracle.dequantize(vc, vs[..., None], w.dtype)
         else:
-            sk = inputs.calibrated_scales([torch.from_numpy(k[:seq - 1])], w.k_gran,
-                                          w.num_kv_heads)
-            sv = inputs.calibrated_scales([torch.from_numpy(v[:seq - 1])], w.v_gran,
-                                          w.num_kv_heads)
+            sk = oracle.calibrate_scales(k[:seq - 1], w.k_gran, w.dtype)
+            sv = oracle.calibrate_scales(v[:seq - 1], w.v_gran, w.dtype)
             kc = oracle.quantize_static(k, sk, w.k_gran, w.dtype)
             vc = oracle.quantize_static(v, sv, w.v_gran, w.dtype)
             shp = (1, 1, 1) if w.k_gran == "tensor" else (1, -1, 1)
@@ -175,13 +173,16 @@ class Bench:
                 vv.append(v)
             pre_k = [k[:-1] for k in kk]
             pre_v = [v[:-1] for v in vv]
-            k_static = v_static = None
-            if w.dtype != "int4" and w.k_gran in ("tensor", "head"):
-                k_static = inputs.calibrated_scales(pre_k, w.k_gran, w.num_kv_heads)
-            if w.dtype != "int4" and w.v_gran in ("tensor", "head"):
-                v_static = inputs.calibrated_scales(pre_v, w.v_gran, w.num_kv_heads)
-            cache = kvq.alloc_cache(self.layout, ring_rows=b, device=device,
-                                    k_static=k_static, v_static=v_static)
+            cache = kvq.alloc_cache(self.layout, ring_rows=b, device=device)
+            # static scales calibrated by the library from the prefill tokens
+            static = ("tensor", "head", "channel")
+            if w.dtype in ("int8", "fp8", "fp8e5m2") and (w.k_gran in static or
+                                                          w.v_gran in static):
+                ks_ok, vs_ok = w.k_gran in static, w.v_gran in static
+                kvq.calibrate(self.layout, torch.cat(pre_k) if ks_ok else None,
+                              torch.cat(pre_v) if vs_ok else None,
+                              cache.k_scales if ks_ok else None,
+                              cache.v_scales if vs_ok else None)
             n = (lens - 1).astype(np.int32)
             cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32),
                                  device=device)

@@ -12,7 +12,9 @@
  *    -128, 127)  ([intelli] §3.1 对称量化算法; [yunthe] section
  *    "KV Cache量化策略：INT8与FP8精度对比与选择").  Division is one IEEE fp32
  *    division, rounding is half-to-even.  FP8 uses scale = max|x| / 448 and
- *    round-to-nearest-even into E4M3 after clamping to +-448.
+ *    round-to-nearest-even into E4M3 after clamping to +-448; E5M2 (the
+ *    pages' other FP8 format) likewise with 57344 (its largest finite
+ *    value).
  *  - Granularity of the scale: tensor, head, channel or token ([oh-bug]
  *    section "量化不是简单'截断精度'"); dynamic per-token scales are computed
  *    on write ([intelli] §3.2 动态量化策略), static ones are inputs.
@@ -60,6 +62,7 @@
  *   K: 1024*((c>>4)&1) + 256*(c>>5) + 16*s + (c&15)
  *   V: 1024*(c>>6) + 256*(s>>2) + 16*(c&15) + 4*((c>>4)&3) + (s&3)
  * INT8 codes are two's complement; FP8 codes are OCP E4M3 (0x7F/0xFF never
+ * written) or, for KVQ_FP8_E5M2, OCP E5M2 (infinities and NaNs never
  * written).  The orders put each lane's matrix-core operand in one 16-byte
  * run so the decode kernel loads tiles straight into registers.
  *
@@ -67,7 +70,8 @@
  *   KVQ_PER_TENSOR : [1]            (input)
  *   KVQ_PER_HEAD   : [H]            (input)
  *   KVQ_PER_CHANNEL: [H][128]       (input)
- *   KVQ_PER_TOKEN  : [NB][H][16]    (written by kvq_write, max|x|/127 or /448)
+ *   KVQ_PER_TOKEN  : [NB][H][16]    (written by kvq_write, max|x|/127, /448
+ *                                    or /57344)
  * A zero scale quantizes every value to code 0.
  *
  * ---- INT4 (KIVI) layout ------------------------------------------------------
@@ -141,8 +145,9 @@ typedef enum kvq_dtype {
   KVQ_FP8_E4M3 = 2, /* 1 byte per value, OCP E4M3, divisor 448              */
   KVQ_INT4 = 3,     /* 0.5 byte per value, KIVI grouping, divisor 7         */
   KVQ_FP16 = 4,     /* 2 bytes per value, unquantized                       */
-  KVQ_INT4_AFFINE = 5 /* INT4 KIVI grouping, asymmetric: codes 0..15 with a
-                         zero point per group                               */
+  KVQ_INT4_AFFINE = 5, /* INT4 KIVI grouping, asymmetric: codes 0..15 with a
+                          zero point per group                              */
+  KVQ_FP8_E5M2 = 6  /* 1 byte per value, OCP E5M2, divisor 57344            */
 } kvq_dtype;
 
 typedef enum kvq_granularity {
@@ -272,6 +277,36 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
                             int32_t max_seq_len, float softmax_scale,
                             float *out, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* Static-scale calibration ([yunthe] sections "KV Cache量化策略" (scale =
+ * max(abs(x)) / 127) and "配置与启动参数" (per-layer K and V scales computed
+ * offline from calibration data); [oh-bug] vLLM section (per-tensor and
+ * per-head FP8 scales from a random-token warmup or calibration data)).
+ *   k, v         : fp16 [n_tokens][H][128] calibration tokens (e.g. a
+ *                  layer's prefill K and V).
+ *   k_scales, v_scales: the cache's static scale arrays for the layout's
+ *                  granularity ([1], [H] or [H][128]), written as
+ *                  max|x| / 127 (INT8), / 448 (E4M3) or / 57344 (E5M2),
+ *                  max over the tokens and, per granularity, over the
+ *                  head's channels or over everything.  A per-token
+ *                  granularity has no static scale: that tensor's input
+ *                  and output are unread and may be NULL.
+ *   accumulate   : nonzero raises the existing scales to at least the new
+ *                  ones (several calibration batches give the scale of all
+ *                  of them); zero replaces them.
+ *   workspace    : device buffer of kvq_calibrate_workspace_bytes(layout,
+ *                  n_tokens) bytes, 256-byte aligned; contents need no
+ *                  initialisation.
+ * Two launches on `stream`.  Errors: KVQ_ERR_UNSUPPORTED for INT4 and FP16
+ * caches (no static scales) or more than 256 KV heads; KVQ_ERR_INVALID_ARG
+ * for n_tokens < 0 or a missing pointer of a calibrated tensor;
+ * KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE as elsewhere.  n_tokens == 0 does
+ * nothing. */
+size_t kvq_calibrate_workspace_bytes(const kvq_layout *layout, int32_t n_tokens);
+kvq_status kvq_calibrate(const kvq_layout *layout, const uint16_t *k,
+                         const uint16_t *v, int32_t n_tokens, float *k_scales,
+                         float *v_scales, int32_t accumulate, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

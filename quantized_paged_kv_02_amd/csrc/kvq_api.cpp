@@ -36,7 +36,7 @@ kvq_status check_layout(const kvq_layout *L) {
   if (!L) return KVQ_ERR_INVALID_ARG;
   if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4 &&
-      L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE)
+      L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE && L->dtype != KVQ_FP8_E5M2)
     return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_FP16) {  // an FP16 cache has no scales
     if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
@@ -344,6 +344,62 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
   return decode_launch(layout, a, batch, stream);
+}
+
+// ---- static-scale calibration ------------------------------------------------
+
+static int calib_chunks(int32_t n_tokens) {
+  const int c = (n_tokens + 63) / 64;
+  return c < 1 ? 1 : (c > 256 ? 256 : c);
+}
+
+static bool calib_dtype(const kvq_layout *L) {
+  return L->dtype == KVQ_INT8 || L->dtype == KVQ_FP8_E4M3 || L->dtype == KVQ_FP8_E5M2;
+}
+
+size_t kvq_calibrate_workspace_bytes(const kvq_layout *layout, int32_t n_tokens) {
+  if (check_layout(layout) != KVQ_OK || !calib_dtype(layout) || n_tokens <= 0) return 0;
+  const size_t b = (size_t)calib_chunks(n_tokens) * 2 * layout->num_kv_heads * kHeadDim * 4;
+  return round_up(b, 256);
+}
+
+kvq_status kvq_calibrate(const kvq_layout *layout, const uint16_t *k, const uint16_t *v,
+                         int32_t n_tokens, float *k_scales, float *v_scales, int32_t accumulate,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (!calib_dtype(layout)) return KVQ_ERR_UNSUPPORTED;  // no static scales
+  if (layout->num_kv_heads > kvq::kMaxCalibHeads) return KVQ_ERR_UNSUPPORTED;
+  if (n_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  const bool do_k = layout->k_gran != KVQ_PER_TOKEN, do_v = layout->v_gran != KVQ_PER_TOKEN;
+  if (n_tokens == 0 || (!do_k && !do_v)) return KVQ_OK;
+  if ((do_k && (!k || !k_scales)) || (do_v && (!v || !v_scales))) return KVQ_ERR_INVALID_ARG;
+  if ((do_k && (!aligned16(k) || !aligned16(k_scales))) ||
+      (do_v && (!aligned16(v) || !aligned16(v_scales))))
+    return KVQ_ERR_ALIGNMENT;
+  const size_t need = kvq_calibrate_workspace_bytes(layout, n_tokens);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < need)
+    return KVQ_ERR_WORKSPACE;
+  kvq::CalibArgs a{};
+  a.k = do_k ? k : nullptr;
+  a.v = do_v ? v : nullptr;
+  a.k_scales = do_k ? k_scales : nullptr;
+  a.v_scales = do_v ? v_scales : nullptr;
+  a.partial = static_cast<float *>(workspace);
+  a.n_tokens = n_tokens;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.n_chunks = calib_chunks(n_tokens);
+  a.chunk_tokens = (n_tokens + a.n_chunks - 1) / a.n_chunks;
+  a.k_gran = layout->k_gran;
+  a.v_gran = layout->v_gran;
+  a.accumulate = accumulate ? 1 : 0;
+  a.divisor = layout->dtype == KVQ_INT8 ? 127.0f
+              : layout->dtype == KVQ_FP8_E4M3 ? 448.0f
+                                              : 57344.0f;
+  (void)hipGetLastError();
+  const hipError_t e = kvq::launch_calibrate(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 }  // extern "C"

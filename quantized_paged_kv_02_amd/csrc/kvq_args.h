@@ -8,7 +8,7 @@
 
 namespace kvq {
 
-enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5 };  // kvq_dtype
+enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5, kFp8E5M2 = 6 };  // kvq_dtype
 // KIVI-grouped INT4 caches, symmetric or affine
 constexpr bool is_kivi(int dtype) { return dtype == kInt4 || dtype == kInt4Affine; }
 // Granularity as the decode kernel sees it: a scale that is uniform over a
@@ -18,11 +18,11 @@ enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
 // Decode workgroups (four wavefronts) guaranteed resident per CU for a cache
 // dtype and K / V scale kinds: the kernel's register bound and the partition
 // plan's round size.  INT4, FP16 (twice the bytes in flight per unit) and
-// FP8 with per-token V and non-uniform K scales need the larger per-wave
-// register budget of two per CU.
+// FP8 (E4M3 or E5M2) with per-token V and non-uniform K scales need the
+// larger per-wave register budget of two per CU.
 constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
   return (is_kivi(dtype) || dtype == kFp16) ? 2
-         : (dtype == kFp8 && v_kind == kToken && k_kind != kUniform) ? 2
+         : ((dtype == kFp8 || dtype == kFp8E5M2) && v_kind == kToken && k_kind != kUniform) ? 2
                                                                       : 3;
 }
 
@@ -83,6 +83,27 @@ struct DecodeArgs {
 
 // Kernel-side scale kinds for the decode templates.
 int decode_scale_kind(int granularity);
+
+// Static-scale calibration (kvq_calibrate).  Granularities are kvq_granularity
+// values; a null scale array is not calibrated (per-token granularity).
+constexpr int kCalibTensor = 0, kCalibHead = 1, kCalibChannel = 2;
+constexpr int kMaxCalibHeads = 256;  // KV heads of the per-head reduction in LDS
+struct CalibArgs {
+  const uint16_t *k;     // fp16 [n_tokens][H][128]
+  const uint16_t *v;
+  float *k_scales;
+  float *v_scales;
+  float *partial;        // workspace: [n_chunks][2][H * 128] channel maxima
+  int32_t n_tokens;
+  int32_t num_kv_heads;
+  int32_t chunk_tokens;
+  int32_t n_chunks;
+  int32_t k_gran;
+  int32_t v_gran;
+  int32_t accumulate;    // raise existing scales instead of replacing them
+  float divisor;         // 127, 448 or 57344
+};
+hipError_t launch_calibrate(const CalibArgs &a, hipStream_t stream);
 
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch,
                            int max_new, hipStream_t stream);

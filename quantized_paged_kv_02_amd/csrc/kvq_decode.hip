@@ -173,10 +173,23 @@ __device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
 __device__ __forceinline__ f16x8 u4_to_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ f16x4 u2_to_f16x4(u32x2 v) { return __builtin_bit_cast(f16x4, v); }
 
+// E5M2 codes reach 57344 and their scales are max|x| / 57344: scale-derived
+// fp16 operands (q' = q s_c, p s_v) would fall into fp16 subnormals.  They
+// carry an exact factor 2^7 (so their range is E4M3's, 57344 / 128 = 448),
+// removed again in fp32.
+template <int DT>
+constexpr float operand_boost() { return DT == kFp8E5M2 ? 128.0f : 1.0f; }
+
 template <int DT>
 __device__ __forceinline__ f16x4 codes4_to_f16(uint32_t w) {
   if constexpr (DT == kFp8) {
     return fp8x4_to_f16(w);
+  } else if constexpr (DT == kFp8E5M2) {
+    // an E5M2 byte is the upper byte of the fp16 with the same value
+    const uint32_t lo = __builtin_amdgcn_perm(w, w, 0x010C000Cu);  // bytes 0, 1
+    const uint32_t hi = __builtin_amdgcn_perm(w, w, 0x030C020Cu);  // bytes 2, 3
+    const f16x2 a = as_f16x2(lo), b = as_f16x2(hi);
+    return f16x4{a.x, a.y, b.x, b.y};
   } else {
     return int8x4_to_f16(w);
   }
@@ -316,10 +329,11 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
   f32x4 p0, p1;
   softmax_update(st, s[0], s[1], p0, p1);
   if constexpr (VS == kToken) {
+    constexpr float boost = operand_boost<DT>();  // removed from o at the end
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p0[r] *= t.vs[0][r];
-      p1[r] *= t.vs[1][r];
+      p0[r] *= t.vs[0][r] * boost;
+      p1[r] *= t.vs[1][r] * boost;
       if (TAIL && 4 * qd + r >= valid) p0[r] = 0.0f;
       if (TAIL && 16 + 4 * qd + r >= valid) p1[r] = 0.0f;
     }
@@ -453,14 +467,16 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int e = 2 * e2;
-        const float x0 = (float)hv[e] * a.qk_scale * (e < 4 ? s0[e] : s1[e - 4]);
-        const float x1 = (float)hv[e + 1] * a.qk_scale * (e + 1 < 4 ? s0[e + 1] : s1[e - 3]);
+        constexpr float boost = operand_boost<DT>();
+        const float x0 = (float)hv[e] * a.qk_scale * (e < 4 ? s0[e] : s1[e - 4]) * boost;
+        const float x1 =
+            (float)hv[e + 1] * a.qk_scale * (e + 1 < 4 ? s0[e + 1] : s1[e - 3]) * boost;
         split_hi_lo(x0, x1, hi[e2], lo[e2]);
       }
       bq[j] = pairs_to_f16x8(hi);
       bq_lo[j] = pairs_to_f16x8(lo);
     }
-    kmul = 1.0f;
+    kmul = 1.0f / operand_boost<DT>();
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -519,7 +535,12 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     }
   }
   if constexpr (DT == kFp16) return;  // no scales
-  // uniform and per-channel V scales multiply o once
+  // uniform and per-channel V scales multiply o once (per-token ones rode
+  // on the weights, with the operand boost to remove)
+  if constexpr (VS == kToken && operand_boost<DT>() != 1.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= 1.0f / operand_boost<DT>();
+  }
   if constexpr (VS == kUniform) {
     const float s = a.v_scales[h * a.v_head_stride];
 #pragma unroll
@@ -1489,6 +1510,8 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
                        0, stream, a);
   } else if (dtype == kFp8) {
     launch_k<kFp8>(a, k_kind, v_kind, grid, stream);
+  } else if (dtype == kFp8E5M2) {
+    launch_k<kFp8E5M2>(a, k_kind, v_kind, grid, stream);
   } else {
     launch_k<kInt8>(a, k_kind, v_kind, grid, stream);
   }

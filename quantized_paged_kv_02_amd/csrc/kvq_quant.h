@@ -3,7 +3,8 @@
 // [intelli] "大模型KV Cache显存优化与量化技术实践" §3.1 对称量化算法 and
 // [yunthe] "KV Cache量化压缩技术与vLLM推理引擎显存优化实战", section
 // "KV Cache量化策略：INT8与FP8精度对比与选择": scale = max|x| / 127 (448 for
-// E4M3), code = clamp(round(x / scale)); dynamic per-token scales follow
+// E4M3, 57344 for E5M2, the page's two FP8 formats), code = clamp(round(x /
+// scale)); dynamic per-token scales follow
 // [intelli] §3.2 动态量化策略.  fp32 division is the correctly rounded IEEE
 // one (the library is built without fast-math); rounding is rintf
 // (half-to-even).
@@ -36,10 +37,18 @@ __device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float 
   return (uint32_t)(int)y;
 }
 
-__device__ __forceinline__ float fp8_prescale(float x, float s) {
+// x / s clamped to the format's finite range (448 E4M3, 57344 E5M2).
+__device__ __forceinline__ float fp8_prescale(float x, float s, float top) {
   if (s == 0.0f) return 0.0f;
   const float y = x / s;
-  return fminf(fmaxf(y, -448.0f), 448.0f);
+  return fminf(fmaxf(y, -top), top);
+}
+
+// max|x| divisor of a dynamic scale ([yunthe] section "KV Cache量化策略"):
+// the largest code magnitude of the format
+template <int DT>
+constexpr float code_top() {
+  return DT == kFp8 ? 448.0f : (DT == kFp8E5M2 ? 57344.0f : 127.0f);
 }
 
 // Codes of channels 2 lane, 2 lane + 1 of one tensor (K or V) of one
@@ -63,13 +72,19 @@ __device__ __forceinline__ CodePair quantize_pair(uint32_t raw, int gran, float2
   float s0 = st.x, s1 = st.y;
   if (gran == kPerToken) {
     const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    s0 = s1 = amax / (DT == kFp8 ? 448.0f : 127.0f);
+    s0 = s1 = amax / code_top<DT>();
   }
   CodePair r;
   r.scale = s0;
   if (DT == kFp8) {
     const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-        fp8_prescale(x0, s0), fp8_prescale(x1, s1), 0, false);
+        fp8_prescale(x0, s0, 448.0f), fp8_prescale(x1, s1, 448.0f), 0, false);
+    r.q0 = pk & 0xFFu;
+    r.q1 = (pk >> 8) & 0xFFu;
+  } else if (DT == kFp8E5M2) {
+    // OCP E5M2, round to nearest even (the hardware conversion)
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(
+        fp8_prescale(x0, s0, 57344.0f), fp8_prescale(x1, s1, 57344.0f), 0, false);
     r.q0 = pk & 0xFFu;
     r.q1 = (pk >> 8) & 0xFFu;
   } else {

@@ -382,6 +382,8 @@ hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new
   const dim3 grid(max_new, a.num_kv_heads, batch);
   if (dtype == kFp8) {
     hipLaunchKernelGGL(kvq_write_q8_kernel<kFp8>, grid, dim3(64), 0, stream, a);
+  } else if (dtype == kFp8E5M2) {
+    hipLaunchKernelGGL(kvq_write_q8_kernel<kFp8E5M2>, grid, dim3(64), 0, stream, a);
   } else {
     hipLaunchKernelGGL(kvq_write_q8_kernel<kInt8>, grid, dim3(64), 0, stream, a);
   }

@@ -35,7 +35,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     seq: int | tuple            # fixed length, or (lo, hi) uniform inclusive
-    dtype: str                  # "int8" | "fp8" | "int4" | "int4-affine" | "fp16" (unquantized)
+    dtype: str                  # "int8" | "fp8" | "fp8e5m2" | "int4" | "int4-affine" | "fp16"
     k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16)
     v_gran: str
     table: str = "identity"     # "identity" | "shuffled"
@@ -75,6 +75,11 @@ WORKLOADS = {
     "llama3-70b-fp8": Workload(
         "llama3-70b-fp8", 80, 24, 64, 8, 16384, "fp8", "tensor", "tensor",
         description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, FP8 per-tensor"),
+    # the 70B FP8 workload with the pages' other FP8 format
+    "llama3-70b-fp8e5m2": Workload(
+        "llama3-70b-fp8e5m2", 80, 24, 64, 8, 16384, "fp8e5m2", "tensor", "tensor",
+        description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, "
+                    "FP8 E5M2 per-tensor"),
     # the KIVI workload with asymmetric (affine) groups; V shifted off zero
     # so the zero points matter
     "kivi-int4-affine": Workload(
@@ -167,20 +172,6 @@ def gen_kv(w: Workload, layer: int, row: int, n_tokens: int, device="cpu", seed:
 def gen_q(w: Workload, layer: int, device="cpu", seed: int = 0, batch: int | None = None):
     b = w.batch if batch is None else batch
     return _draw(w, (b, w.num_q_heads, HEAD_DIM), "q", seed, layer, -1, device)
-
-
-def calibrated_scales(tensors, gran: str, num_kv_heads: int) -> np.ndarray:
-    """Static fp32 scales from prefill data: max|x| / 448 per head
-    ("head") or over everything ("tensor").  ``tensors`` is an iterable of
-    fp16 [S, Hkv, 128] torch tensors."""
-    amax = None
-    for t in tensors:
-        a = t.abs().amax(dim=(0, 2)).float()
-        amax = a if amax is None else torch.maximum(amax, a)
-    amax = amax.cpu().numpy().astype(np.float32)
-    if gran == "tensor":
-        amax = np.array([amax.max()], np.float32)
-    return (amax / np.float32(448.0)).astype(np.float32)
 
 
 def scaled_down(w: Workload, **kw) -> Workload:

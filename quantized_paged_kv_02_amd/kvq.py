@@ -17,10 +17,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE = 1, 2, 3, 4, 5
+INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2 = 1, 2, 3, 4, 5, 6
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
 DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16,
-          "int4-affine": INT4_AFFINE}
+          "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
          "token": PER_TOKEN,
          "none": PER_TENSOR}   # FP16 cache: no scales, the field is ignored
@@ -30,7 +30,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -5: "KVQ_ERR_CAPACITY", -6: "KVQ_ERR_HIP"}
 
 EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
-            "kvq_write", "kvq_paged_decode", "kvq_write_decode")
+            "kvq_write", "kvq_paged_decode", "kvq_write_decode",
+            "kvq_calibrate_workspace_bytes", "kvq_calibrate")
 
 
 class Layout(ctypes.Structure):
@@ -91,6 +92,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_write_decode.restype = I32
     lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
                                      P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_calibrate_workspace_bytes.restype = SZ
+    lib.kvq_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32]
+    lib.kvq_calibrate.restype = I32
+    lib.kvq_calibrate.argtypes = [ctypes.POINTER(Layout), P, P, I32, P, P, I32, P, SZ, P]
     return lib
 
 
@@ -245,3 +250,24 @@ def write_decode(cache: KVCache, k_new, v_new, q, block_tables, seq_lens, max_se
                               _stream_handle(stream))
     if st != 0:
         raise KvqError(st, "kvq_write_decode")
+
+
+def calibrate_workspace_bytes(layout: Layout, n_tokens: int) -> int:
+    return LIB.kvq_calibrate_workspace_bytes(ctypes.byref(layout), n_tokens)
+
+
+def calibrate(layout: Layout, k, v, k_scales, v_scales, accumulate: bool = False,
+              workspace=None, stream=None) -> None:
+    """kvq_calibrate: static scales from fp16 calibration tokens k, v
+    [n_tokens, H, 128] into the scale tensors (see kvq.h).  A workspace is
+    allocated when none is given."""
+    n = int(k.shape[0]) if k is not None else int(v.shape[0])
+    if workspace is None:
+        dev = (k if k is not None else v).device
+        workspace = torch.empty(max(calibrate_workspace_bytes(layout, n), 256),
+                                dtype=torch.uint8, device=dev)
+    st = LIB.kvq_calibrate(ctypes.byref(layout), _ptr(k), _ptr(v), n, _ptr(k_scales),
+                           _ptr(v_scales), 1 if accumulate else 0, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != 0:
+        raise KvqError(st, "kvq_calibrate")

@@ -37,21 +37,14 @@ class CaseResult:
 
 
 def _static(w, gran, tensors, dtype):
-    if dtype == "fp16":
+    """Static scales from the rows' prefill tokens, by the oracle's
+    calibration (rows folded in one at a time)."""
+    if dtype == "fp16" or gran not in ("tensor", "head", "channel"):
         return None
-    if gran in ("tensor", "head"):
-        s = inputs.calibrated_scales(tensors, gran, w.num_kv_heads)
-        if dtype == "int8":   # same recipe with the INT8 divisor
-            s = (s * np.float32(448.0) / np.float32(127.0)).astype(np.float32)
-        return s
-    if gran == "channel":
-        amax = None
-        for t in tensors:
-            a = t.abs().amax(dim=0).float()
-            amax = a if amax is None else torch.maximum(amax, a)
-        div = np.float32(448.0 if dtype == "fp8" else 127.0)
-        return (amax.cpu().numpy().astype(np.float32) / div).astype(np.float32)
-    return None
+    s = None
+    for t in tensors:
+        s = oracle.calibrate_scales(t.cpu().numpy(), gran, dtype, previous=s)
+    return s
 
 
 def fill_garbage(cache):

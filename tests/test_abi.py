@@ -214,3 +214,38 @@ def test_int4_affine_rules():
     assert kvq.decode_workspace_bytes(lay, 2, 100) == 0             # residual only
     assert kvq.decode_workspace_bytes(lay, 2, 128 + 64 + 64) > 0
     assert _write_decode(_layout(**base), _cache(int4=True), kn=None) == INV
+
+
+def _calibrate(lay, k=FAKE, v=FAKE, n=100, ks=FAKE, vs=FAKE, acc=0, ws=FAKE, ws_bytes=1 << 30):
+    return kvq.LIB.kvq_calibrate(ctypes.byref(lay), k, v, n, ks, vs, acc, ws, ws_bytes, None)
+
+
+def test_calibrate_rules():
+    lay = _layout(dtype=2, k_gran=0, v_gran=1)                 # FP8, tensor / head
+    need = kvq.calibrate_workspace_bytes(lay, 100)
+    # two chunks of partial channel maxima (100 tokens, 64 per chunk), K and V
+    assert need == 2 * 2 * 2 * 128 * 4
+    assert kvq.calibrate_workspace_bytes(lay, 10 ** 6) == 256 * 2 * 2 * 128 * 4   # capped
+    assert kvq.calibrate_workspace_bytes(lay, 0) == 0
+    assert _calibrate(lay, n=-1) == INV
+    assert _calibrate(lay, n=0) == OK                      # nothing to do
+    assert _calibrate(lay, k=None) == INV
+    assert _calibrate(lay, vs=None) == INV
+    assert _calibrate(lay, k=FAKE + 2) == ALN
+    assert _calibrate(lay, ws=None) == WS
+    assert _calibrate(lay, ws=FAKE + 64) == WS
+    assert _calibrate(lay, ws_bytes=need - 1) == WS
+    # per-token tensors are not calibrated: their pointers may be NULL
+    tok = _layout(dtype=1, k_gran=3, v_gran=3)
+    assert _calibrate(tok, k=None, v=None, ks=None, vs=None) == OK
+    # no static scales: INT4, affine INT4, FP16
+    for dt, kg, vg in ((3, 2, 3), (5, 2, 3), (4, 0, 0)):
+        assert _calibrate(_layout(dtype=dt, k_gran=kg, v_gran=vg)) == UNS
+    assert _calibrate(_layout(dtype=2, k_gran=0, v_gran=0, num_kv_heads=257,
+                              num_q_heads=257)) == UNS
+
+
+def test_fp8_e5m2_layout_is_accepted():
+    lay = _layout(dtype=6, k_gran=3, v_gran=0)
+    assert kvq.validate(lay, _cache(), 2, 100) == OK
+    assert kvq.decode_workspace_bytes(_layout(dtype=6, split_tokens=16), 2, 100) > 0

@@ -34,7 +34,7 @@ def test_tiny_workload_whole():
 GRANS = ["tensor", "head", "channel", "token"]
 
 
-@pytest.mark.parametrize("dtype", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype", ["int8", "fp8", "fp8e5m2"])
 @pytest.mark.parametrize("kg", GRANS)
 @pytest.mark.parametrize("vg", GRANS)
 def test_granularities(dtype, kg, vg):

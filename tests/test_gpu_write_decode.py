@@ -32,6 +32,8 @@ CASES = [
     ("int4", "channel", "token", "shuffled"),
     ("fp16", "none", "none", "shuffled"),
     ("int4-affine", "channel", "token", "shuffled"),
+    ("fp8e5m2", "channel", "token", "shuffled"),
+    ("fp8e5m2", "tensor", "head", "identity"),
 ]
 
 LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2]]
