@@ -163,6 +163,7 @@ class Bench:
         self.layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads,
                                       w.num_kv_heads, nb, table.shape[1], 0, w.residual_len)
         b = w.batch
+        self.calibrate = None
         self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)
         self.caches, self.k_new, self.v_new, self.q, self.out = [], [], [], [], []
         for layer in range(w.layers):
@@ -179,10 +180,30 @@ class Bench:
             if w.dtype in ("int8", "fp8", "fp8e5m2") and (w.k_gran in static or
                                                           w.v_gran in static):
                 ks_ok, vs_ok = w.k_gran in static, w.v_gran in static
-                kvq.calibrate(self.layout, torch.cat(pre_k) if ks_ok else None,
-                              torch.cat(pre_v) if vs_ok else None,
-                              cache.k_scales if ks_ok else None,
-                              cache.v_scales if vs_ok else None)
+                ck = torch.cat(pre_k) if ks_ok else None
+                cv = torch.cat(pre_v) if vs_ok else None
+                cks = cache.k_scales if ks_ok else None
+                cvs = cache.v_scales if vs_ok else None
+                kvq.calibrate(self.layout, ck, cv, cks, cvs)
+                if layer == 0:
+                    # time the calibration of one layer's prefill: repeated
+                    # accumulating calls leave the scales as they are
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(3):
+                        kvq.calibrate(self.layout, ck, cv, cks, cvs, accumulate=True)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    n_tok = int((ck if ck is not None else cv).shape[0])
+                    nbytes = n_tok * w.num_kv_heads * 128 * 2 * (int(ks_ok) + int(vs_ok))
+                    us = e0.elapsed_time(e1) * 1e3 / 3
+                    self.calibrate = {
+                        "call": "kvq_calibrate of one layer's prefill K/V", "tokens": n_tok,
+                        "bytes_read": nbytes, "us": round(us, 2),
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                del ck, cv
             n = (lens - 1).astype(np.int32)
             cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32),
                                  device=device)
@@ -363,6 +384,8 @@ def run(args):
     }
     if copy_probe is not None:
         result["copy_probe"] = copy_probe
+    if bench.calibrate is not None:
+        result["calibrate"] = bench.calibrate
     print(json.dumps(result), flush=True)
 
 

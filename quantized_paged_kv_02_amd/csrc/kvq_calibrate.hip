@@ -40,14 +40,24 @@ __global__ __launch_bounds__(256) void kvq_calibrate_partial_kernel(CalibArgs a)
 #pragma unroll
   for (int e = 0; e < 8; ++e) m[e] = 0.0f;
   if (oct < n_oct) {
-    for (int t = t0 + tl; t < t1; t += kTokLanes) {
-      const u32x4 w = ld16(x + ((size_t)t * n_oct + oct) * 8);
+    // kUnroll tokens per step, all loads issued before any use; tokens past
+    // the chunk are skipped by predication
+    constexpr int kUnroll = 8;
+    for (int t = t0 + tl; t < t1; t += kTokLanes * kUnroll) {
+      u32x4 w[kUnroll];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 p = as_f16x2(w[e]);
-        m[2 * e] = fmaxf(m[2 * e], fabsf((float)p.x));
-        m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf((float)p.y));
+      for (int i = 0; i < kUnroll; ++i) {
+        const int ti = t + kTokLanes * i;
+        w[i] = ti < t1 ? ld16(x + ((size_t)ti * n_oct + oct) * 8) : u32x4{0u, 0u, 0u, 0u};
       }
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 p = as_f16x2(w[i][e]);
+          m[2 * e] = fmaxf(m[2 * e], fabsf((float)p.x));
+          m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf((float)p.y));
+        }
     }
   }
 #pragma unroll
@@ -94,6 +104,7 @@ __global__ __launch_bounds__(1024) void kvq_calibrate_finalize_kernel(CalibArgs 
   // channel c of the 1024-thread sweep: thread tid takes c = tid, tid+1024, ...
   for (int c = tid; c < nch; c += blockDim.x) {
     float v = 0.0f;
+#pragma unroll 8
     for (int q = 0; q < a.n_chunks; ++q) v = fmaxf(v, part[q * stride + c]);
     if (gran == kCalibChannel) {
       const float s = v / a.divisor;
