@@ -30,6 +30,9 @@
  *
  *  - An unquantized FP16 cache through the same kernels, the baseline of
  *    the memory / latency comparison ([intelli] §5).
+ *  - An asymmetric INT4 KIVI cache (the affine form with integer zero
+ *    points of [oh-bug] section "量化不是简单'截断精度'") and static-scale
+ *    calibration from calibration tokens ([yunthe] section "配置与启动参数").
  *
  * Conventions for every entry point:
  *  - All buffers are caller-owned DEVICE pointers except the kvq_layout and
