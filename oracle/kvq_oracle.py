@@ -40,6 +40,7 @@ __all__ = [
     "affine_params", "quantize_affine", "kivi_affine_quantize_k_group",
     "kivi_affine_quantize_v_tokens", "decode_attention",
     "decode_attention_partials", "merge_partials", "paged_gather",
+    "multi_query_attention",
     "paged_scatter",
 ]
 
@@ -623,6 +624,30 @@ def decode_attention(q, k_hat, v_hat, softmax_scale):
         p = np.exp(s)
         p = p / p.sum()
         out[hq] = p @ v_hat[:, h, :]
+    return out
+
+
+def multi_query_attention(q, k_hat, v_hat, softmax_scale):
+    """Several new query tokens of one sequence over its cache: q [Nq, Hq,
+    D] are the queries of the last Nq positions S - Nq .. S - 1 (their K/V
+    already cached), and query j attends to tokens 0 .. S - Nq + j
+    (causal).  Returns [Nq, Hq, D] in fp64; a query with no visible token
+    (S - Nq + j < 0) gives zeros.
+
+    The step beside decode that [oh-bug] sections "为什么长上下文更需要 KV
+    Cache Quantization" and "常见误区" describe reading the whole cached
+    history: speculative verification or chunked prefill over the quantized
+    cache.  Reading: every query sees the full prefix up to and including
+    its own position, as in causal self-attention.
+    """
+    q = np.asarray(q, np.float64)
+    nq = q.shape[0]
+    s_len = k_hat.shape[0]
+    out = np.zeros(q.shape, np.float64)
+    for j in range(nq):
+        vis = s_len - nq + j + 1
+        if vis > 0:
+            out[j] = decode_attention(q[j], k_hat[:vis], v_hat[:vis], softmax_scale)
     return out
 
 

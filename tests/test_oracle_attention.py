@@ -112,3 +112,44 @@ def test_quantized_attention_lossless_case_matches_sdpa():
                                 oracle.dequantize(vc, vs[..., None], "int8"), 0.088)
     b = oracle.decode_attention(q, k.astype(np.float64), v.astype(np.float64), 0.088)
     assert np.array_equal(a, b)
+
+
+# --- several query tokens per sequence (causal) -------------------------------
+
+@pytest.mark.parametrize("nq,hq,hkv,s", [(1, 4, 2, 37), (4, 8, 2, 50), (8, 2, 2, 9),
+                                         (3, 4, 4, 2)])
+def test_multi_query_matches_torch_causal_sdpa(nq, hq, hkv, s):
+    # the queries are the last nq positions of a causal self-attention over
+    # the s cached tokens: torch's SDPA with a boolean mask (an independent
+    # library routine, fp64, KV heads repeated)
+    g = np.random.default_rng(nq * 100 + s)
+    q = g.standard_normal((nq, hq, 128))
+    k = g.standard_normal((s, hkv, 128))
+    v = g.standard_normal((s, hkv, 128))
+    scale = 1 / np.sqrt(128)
+    got = oracle.multi_query_attention(q, k, v, scale)
+    rep = hq // hkv
+    kt = torch.from_numpy(np.repeat(k, rep, axis=1)).permute(1, 0, 2)     # [hq, s, d]
+    vt = torch.from_numpy(np.repeat(v, rep, axis=1)).permute(1, 0, 2)
+    qt = torch.from_numpy(q).permute(1, 0, 2)                             # [hq, nq, d]
+    pos = np.arange(nq)[:, None] + (s - nq)
+    mask = torch.from_numpy(np.arange(s)[None, :] <= pos)                 # [nq, s]
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=scale).permute(1, 0, 2).numpy()
+    visible = (pos[:, 0] >= 0)
+    assert np.allclose(got[visible], want[visible], atol=1e-12, rtol=1e-12)
+    assert np.all(got[~visible] == 0)
+
+
+def test_multi_query_last_query_is_plain_decode():
+    g = np.random.default_rng(8)
+    q = g.standard_normal((5, 4, 128))
+    k = g.standard_normal((40, 2, 128))
+    v = g.standard_normal((40, 2, 128))
+    got = oracle.multi_query_attention(q, k, v, 0.1)
+    assert np.array_equal(got[-1], oracle.decode_attention(q[-1], k, v, 0.1))
+    # query 0 sees 36 tokens: the value of token 39 cannot reach it
+    v2 = v.copy()
+    v2[39] += 100.0
+    got2 = oracle.multi_query_attention(q, k, v2, 0.1)
+    assert np.array_equal(got2[0], got[0]) and not np.allclose(got2[-1], got[-1])
