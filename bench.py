@@ -150,10 +150,11 @@ def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
 # ---------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, w: inputs.Workload, device="cuda"):
+    def __init__(self, w: inputs.Workload, device="cuda", n_query: int = 0):
         import torch
         from quantized_paged_kv_02_amd import kvq
         self.torch, self.kvq, self.w = torch, kvq, w
+        self.n_query = n_query
         lens = inputs.seq_lens(w)
         self.lens = lens
         table, nb = inputs.block_tables(w, lens)
@@ -210,13 +211,25 @@ class Bench:
             kvq.write(cache, torch.cat(pre_k).contiguous(), torch.cat(pre_v).contiguous(), cu,
                       self.table, torch.as_tensor(n, device=device), int(n.max()))
             self.caches.append(cache)
-            self.k_new.append(torch.cat([k[-1:] for k in kk]).contiguous())
-            self.v_new.append(torch.cat([v[-1:] for v in vv]).contiguous())
-            self.q.append(inputs.gen_q(w, layer, device, 0))
-            self.out.append(torch.empty((b, w.num_q_heads, 128), dtype=torch.float32,
-                                        device=device))
+            nq = max(n_query, 1)   # new tokens per row and step
+            self.k_new.append(torch.cat([k[-nq:] for k in kk]).contiguous())
+            self.v_new.append(torch.cat([v[-nq:] for v in vv]).contiguous())
+            if n_query:
+                self.q.append(inputs.gen_q(w, layer, device, 0, batch=b * n_query).reshape(
+                    b, n_query, w.num_q_heads, 128).contiguous())
+                self.out.append(torch.empty((b, n_query, w.num_q_heads, 128),
+                                            dtype=torch.float32, device=device))
+            else:
+                self.q.append(inputs.gen_q(w, layer, device, 0))
+                self.out.append(torch.empty((b, w.num_q_heads, 128), dtype=torch.float32,
+                                            device=device))
             del kk, vv, pre_k, pre_v
-        self.ws = kvq.alloc_workspace(self.layout, b, self.max_len, device)
+        if n_query:
+            self.cu_nq = torch.arange(b + 1, dtype=torch.int32, device=device) * n_query
+            nbytes = kvq.paged_decode_mq_workspace_bytes(self.layout, n_query, b, self.max_len)
+            self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        else:
+            self.ws = kvq.alloc_workspace(self.layout, b, self.max_len, device)
         self.scale = 1.0 / math.sqrt(128)
         torch.cuda.synchronize()
 
@@ -226,6 +239,20 @@ class Bench:
         then kvq_paged_decode.  events (with write=False) bracket each
         kvq_paged_decode launch."""
         kvq = self.kvq
+        if self.n_query:
+            # several query tokens per row: rewrite the rows' last n_query
+            # tokens (the draft tokens' K/V), then attend with all of them
+            for layer in range(self.w.layers):
+                if write:
+                    kvq.write(self.caches[layer], self.k_new[layer], self.v_new[layer],
+                              self.cu_nq, self.table, self.lens_t, self.n_query)
+                if events is not None:
+                    events[layer][0].record()
+                kvq.paged_decode_mq(self.caches[layer], self.q[layer], self.table, self.lens_t,
+                                    self.max_len, self.scale, self.out[layer], self.ws)
+                if events is not None:
+                    events[layer][1].record()
+            return
         for layer in range(self.w.layers):
             if write and fused and events is None:
                 kvq.write_decode(self.caches[layer], self.k_new[layer], self.v_new[layer],
@@ -252,7 +279,7 @@ def run(args):
         cpu = cpu_baseline(w, inputs.seq_lens(w), workers=args.cpu_workers)
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    bench = Bench(w)
+    bench = Bench(w, n_query=args.n_query)
     b = w.batch
     L = w.layers
     layer_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, bench.lens,
@@ -342,7 +369,7 @@ def run(args):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        ent = t.get(w.name)
+        ent = t.get(w.name) if not args.n_query else None   # decode launches only
         if ent and t.get("kernel_source_hash") == kernel_source_hash():
             traffic = ent.get("bytes_per_launch")
 
@@ -360,15 +387,18 @@ def run(args):
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "tokens_per_s": round(b / (ms * 1e-3), 2),
+        "tokens_per_s": round(b * max(args.n_query, 1) / (ms * 1e-3), 2),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "config": {
             "workload": w.name, "description": w.description, "layers": L, "batch": b,
             "seq_len": int(w.max_seq) if not isinstance(w.seq, tuple) else list(w.seq),
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "kv_dtype": w.dtype, "k_granularity": w.k_gran, "v_granularity": w.v_gran,
-            "block_tables": w.table,
-            "step": ("per layer: kvq_write of 1 token/row + kvq_paged_decode" if args.separate
+            "block_tables": w.table, "n_query": max(args.n_query, 1),
+            "step": (f"per layer: kvq_write of the last {args.n_query} tokens/row + "
+                     f"kvq_paged_decode_mq ({args.n_query} causal queries/row)" if args.n_query
+                     else "per layer: kvq_write of 1 token/row + kvq_paged_decode"
+                     if args.separate
                      else "per layer: kvq_write_decode (1 token/row appended, then decoded)"),
             "launch": "hip graph" if graph is not None else "eager",
             "algorithmic_bytes_per_step": step_bytes,
@@ -376,7 +406,10 @@ def run(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": DECODE_KERNEL, "bytes_per_launch": layer_bytes,
+            "kernel": DECODE_KERNEL.replace("kvq_paged_decode launch",
+                                            "kvq_paged_decode_mq launch")
+            if args.n_query else DECODE_KERNEL,
+            "bytes_per_launch": layer_bytes,
             "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs),
             "timing": kernel_timing,
         },
@@ -399,6 +432,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch from Python, no HIP graph")
     ap.add_argument("--separate", action="store_true",
                     help="step with kvq_write + kvq_paged_decode instead of kvq_write_decode")
+    ap.add_argument("--n-query", type=int, default=0,
+                    help="query tokens per row and step (kvq_paged_decode_mq); 0: decode")
     ap.add_argument("--kernel-samples", type=int, default=10,
                     help="extra synchronised replays for the per-launch timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")

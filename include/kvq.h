@@ -281,6 +281,31 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
                             float *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* Decode attention for several new query tokens per row (speculative
+ * verification of draft tokens, or a chunk of prefill, over the cache; the
+ * whole-history read of [oh-bug] section "为什么长上下文更需要 KV Cache
+ * Quantization" shared by n_query queries):
+ *   q   : fp16 [batch][n_query][Hq][128]; query j of row b sits at position
+ *         seq_lens[b] - n_query + j (its K/V already written, e.g. by
+ *         kvq_write) and attends to tokens 0 .. seq_lens[b] - n_query + j.
+ *   out : fp32 [batch][n_query][Hq][128]; a query with no visible token
+ *         (seq_lens[b] - n_query + j < 0) gets zeros.
+ *   workspace: kvq_paged_decode_mq_workspace_bytes(layout, n_query, batch,
+ *         max_seq_len) bytes; otherwise as for kvq_paged_decode (n_query = 1
+ *         gives exactly kvq_paged_decode's results).
+ * The K/V stream is read once for all queries: the score product's 16
+ * columns hold (query, head) pairs.  Errors: as for kvq_paged_decode;
+ * KVQ_ERR_INVALID_ARG for n_query < 1; KVQ_ERR_UNSUPPORTED when n_query *
+ * (Hq / H) > 16 or for INT4 caches. */
+size_t kvq_paged_decode_mq_workspace_bytes(const kvq_layout *layout, int32_t n_query,
+                                           int32_t batch, int32_t max_seq_len);
+kvq_status kvq_paged_decode_mq(const kvq_layout *layout, const kvq_cache *cache,
+                               const uint16_t *q, int32_t n_query,
+                               const int32_t *block_tables, const int32_t *seq_lens,
+                               int32_t batch, int32_t max_seq_len, float softmax_scale,
+                               float *out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Static-scale calibration ([yunthe] sections "KV Cache量化策略" (scale =
  * max(abs(x)) / 127) and "配置与启动参数" (per-layer K and V scales computed
  * offline from calibration data); [oh-bug] vLLM section (per-tensor and

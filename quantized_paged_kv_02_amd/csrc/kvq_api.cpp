@@ -131,12 +131,14 @@ struct WorkspaceLayout {
   size_t m_off, l_off, o_off, total;
 };
 
-// Partials of every (row, query head, partition slot); none when the plan
-// has a single slot (the decode kernel then writes the output directly).
-WorkspaceLayout workspace_layout(const kvq_layout *L, int32_t batch, const Plan &p) {
+// Partials of every (row, query token, query head, partition slot); none
+// when the plan has a single slot (the decode kernel then writes the output
+// directly).
+WorkspaceLayout workspace_layout(const kvq_layout *L, int32_t batch, const Plan &p,
+                                 int32_t n_query = 1) {
   WorkspaceLayout w{};
   if (p.slots <= 1) return w;
-  const size_t rows = (size_t)batch * L->num_q_heads * p.slots;
+  const size_t rows = (size_t)batch * n_query * L->num_q_heads * p.slots;
   w.m_off = 0;
   w.l_off = w.m_off + round_up(rows * sizeof(float), 256);
   w.o_off = w.l_off + round_up(rows * sizeof(float), 256);
@@ -233,7 +235,8 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
                                const uint16_t *q, const int32_t *block_tables,
                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                float softmax_scale, float *out, void *workspace,
-                               size_t workspace_bytes, kvq::DecodeArgs *a, bool *launch) {
+                               size_t workspace_bytes, kvq::DecodeArgs *a, bool *launch,
+                               int32_t n_query = 1) {
   *launch = false;
   kvq_status st = kvq_validate(layout, cache, batch, max_seq_len);
   if (st != KVQ_OK) return st;
@@ -244,7 +247,7 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(layout, batch, max_seq_len);
-  const WorkspaceLayout w = workspace_layout(layout, batch, p);
+  const WorkspaceLayout w = workspace_layout(layout, batch, p, n_query);
   if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
                       workspace_bytes < w.total))
     return KVQ_ERR_WORKSPACE;
@@ -268,6 +271,8 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
   a->num_q_heads = layout->num_q_heads;
   a->num_kv_heads = layout->num_kv_heads;
   a->group = layout->num_q_heads / layout->num_kv_heads;
+  a->n_query = n_query;
+  a->cols = n_query * a->group;
   a->max_blocks_per_seq = layout->max_blocks_per_seq;
   a->part_blocks = p.part_blocks;
   a->num_parts = p.num_parts;
@@ -343,6 +348,41 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   const hipError_t e = kvq::launch_write_int4(w, layout->dtype == KVQ_INT4_AFFINE, batch, 1, 2,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
+  return decode_launch(layout, a, batch, stream);
+}
+
+// ---- several query tokens per row ----------------------------------------------
+
+static kvq_status check_mq(const kvq_layout *layout, int32_t n_query) {
+  const kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (n_query < 1) return KVQ_ERR_INVALID_ARG;
+  if (kivi(layout)) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)n_query * (layout->num_q_heads / layout->num_kv_heads) > 16)
+    return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+size_t kvq_paged_decode_mq_workspace_bytes(const kvq_layout *layout, int32_t n_query,
+                                           int32_t batch, int32_t max_seq_len) {
+  if (check_mq(layout, n_query) != KVQ_OK || batch < 0 || max_seq_len < 0) return 0;
+  const Plan p = make_plan(layout, batch, max_seq_len);
+  return workspace_layout(layout, batch, p, n_query).total;
+}
+
+kvq_status kvq_paged_decode_mq(const kvq_layout *layout, const kvq_cache *cache,
+                               const uint16_t *q, int32_t n_query, const int32_t *block_tables,
+                               const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                               float softmax_scale, float *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  const kvq_status st0 = check_mq(layout, n_query);
+  if (st0 != KVQ_OK) return st0;
+  kvq::DecodeArgs a;
+  bool launch;
+  const kvq_status st = decode_setup(layout, cache, q, block_tables, seq_lens, batch,
+                                     max_seq_len, softmax_scale, out, workspace,
+                                     workspace_bytes, &a, &launch, n_query);
+  if (st != KVQ_OK || !launch) return st;
   return decode_launch(layout, a, batch, stream);
 }
 

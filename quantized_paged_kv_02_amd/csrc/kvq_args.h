@@ -61,14 +61,19 @@ struct DecodeArgs {
   // workgroup that streams the row's last partition.  Null: no append.
   const uint16_t *k_new;
   const uint16_t *v_new;
-  float *out;
-  float *ws_o;      // [B][Hq][slots][128] unnormalised partial outputs
-  float *ws_m;      // [B][Hq][slots] partial running max (log2 domain)
-  float *ws_l;      // [B][Hq][slots] partial softmax sums
+  float *out;       // [B][Nq][Hq][128]
+  float *ws_o;      // [B][Nq][Hq][slots][128] unnormalised partial outputs
+  float *ws_m;      // [B][Nq][Hq][slots] partial running max (log2 domain)
+  float *ws_l;      // [B][Nq][Hq][slots] partial softmax sums
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;            // Hq / H
+  // Query tokens per row (1 for decode): query j of row b sits at position
+  // seq_lens[b] - n_query + j and sees tokens up to it.  The score product's
+  // columns are (query j, head) pairs, column n = j * group + head.
+  int32_t n_query;
+  int32_t cols;             // n_query * group <= 16
   int32_t max_blocks_per_seq;
   int32_t part_blocks;      // blocks per main partition
   int32_t num_parts;        // main partitions in the grid

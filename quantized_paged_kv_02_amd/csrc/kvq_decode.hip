@@ -124,10 +124,13 @@ __device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, con
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
     st.m = mn;
   }
+  // a column that has seen only masked scores keeps m = -inf: its weights
+  // are exp2(-inf) = 0, not exp2(-inf - -inf)
+  const float mref = st.m == kNegInf ? 0.0f : st.m;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    p0[r] = __builtin_amdgcn_exp2f(s0[r] - st.m);
-    p1[r] = __builtin_amdgcn_exp2f(s1[r] - st.m);
+    p0[r] = __builtin_amdgcn_exp2f(s0[r] - mref);
+    p1[r] = __builtin_amdgcn_exp2f(s1[r] - mref);
   }
   st.l += ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
 }
@@ -308,11 +311,13 @@ __device__ __forceinline__ f32x4 block_scores8(const u32x4 (&k)[2], const f16x8 
   return s;
 }
 
-// valid: tokens of the pair that are attended (TAIL only), 1..32.
+// TAIL only: valid_s = tokens of the pair this lane's column attends to
+// (may be <= 0), valid_v = tokens of the pair that exist (1..32, the same
+// for every lane; values past it are zeroed).
 template <int DT, int KS, int VS, bool TAIL>
 __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8 (&bq)[4],
-                                              const f16x8 (&bq_lo)[4], float kmul, int valid,
-                                              int qd) {
+                                              const f16x8 (&bq_lo)[4], float kmul, int valid_s,
+                                              int valid_v, int qd) {
   f32x4 s[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -322,7 +327,7 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
       float v = s[u][r];
       if constexpr (KS == kToken) v *= t.ks[u][r] * kmul;
       else v *= kmul;
-      if (TAIL && 16 * u + 4 * qd + r >= valid) v = kNegInf;
+      if (TAIL && 16 * u + 4 * qd + r >= valid_s) v = kNegInf;
       s[u][r] = v;
     }
   }
@@ -334,14 +339,14 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
     for (int r = 0; r < 4; ++r) {
       p0[r] *= t.vs[0][r] * boost;
       p1[r] *= t.vs[1][r] * boost;
-      if (TAIL && 4 * qd + r >= valid) p0[r] = 0.0f;
-      if (TAIL && 16 + 4 * qd + r >= valid) p1[r] = 0.0f;
+      if (TAIL && 4 * qd + r >= valid_s) p0[r] = 0.0f;
+      if (TAIL && 16 + 4 * qd + r >= valid_s) p1[r] = 0.0f;
     }
   }
   const f16x8 pb = p_operand(p0, p1);
   if (TAIL) {
-    // zero the codes of unattended tokens (their bytes may be stale or NaN)
-    const int v0 = valid - 4 * qd, v1 = valid - 16 - 4 * qd;
+    // zero the codes of tokens past the end (their bytes may be stale or NaN)
+    const int v0 = valid_v - 4 * qd, v1 = valid_v - 16 - 4 * qd;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -394,10 +399,10 @@ __device__ __forceinline__ f16x8 value_operand16(const Pair16 &t, int j) {
              u2_to_f16x4(u32x2{t.v[1][j >> 1][w], t.v[1][j >> 1][w + 1]}));
 }
 
-// valid: tokens of the pair that are attended (TAIL only), 1..32.
+// valid_s, valid_v as for compute_pair8.
 template <bool TAIL>
 __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16x8 (&bq)[4],
-                                               float kmul, int valid, int qd) {
+                                               float kmul, int valid_s, int valid_v, int qd) {
   f32x4 s[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -407,7 +412,7 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float v = s[u][r] * kmul;
-      s[u][r] = (TAIL && 16 * u + 4 * qd + r >= valid) ? kNegInf : v;
+      s[u][r] = (TAIL && 16 * u + 4 * qd + r >= valid_s) ? kNegInf : v;
     }
   }
   f32x4 p0, p1;
@@ -416,7 +421,7 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
   if (TAIL) {
     // zero the values of unattended tokens (stale, possibly NaN): dword w
     // of a quarter holds tokens 2(w&1), 2(w&1)+1 of the lane's four
-    const int v0 = valid - 4 * qd, v1 = valid - 16 - 4 * qd;
+    const int v0 = valid_v - 4 * qd, v1 = valid_v - 16 - 4 * qd;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -433,12 +438,15 @@ template <int DT> struct UnitOf { using T = Pair8; };
 template <> struct UnitOf<kFp16> { using T = Pair16; };
 
 // Query operand of the score product for this lane's channels 32qd..32qd+31
-// (as 4 x 8 fp16), zero for the 16 - g padding columns.
+// (as 4 x 8 fp16), zero for the 16 - cols padding columns.  Column n is
+// query token n / g, head h*g + n % g.
 __device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int b, int h, int n,
                                        int qd) {
-  const bool live = n < a.group;
-  const int hq = h * a.group + (live ? n : 0);
-  const uint16_t *qp = a.q + ((size_t)b * a.num_q_heads + hq) * kHeadDim + 32 * qd;
+  const bool live = n < a.cols;
+  const int qt = live ? n / a.group : 0;
+  const int hq = h * a.group + (live ? n - qt * a.group : 0);
+  const uint16_t *qp =
+      a.q + (((size_t)b * a.n_query + qt) * a.num_q_heads + hq) * kHeadDim + 32 * qd;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const u32x4 v = ld16(qp + 8 * j);
@@ -494,11 +502,13 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const int c1 = min(blk1, c0 + kIdChunk);
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int npairs = (c1 - c0 + 1) / 2;
-    // the last pair is masked when it holds the row's partial block or only
-    // one block of the chunk
+    // Pairs wholly visible to every column run unmasked.  The rest are
+    // masked per column: the row's partial block, a chunk's odd last block
+    // and, with several query tokens, the last positions that only the
+    // later queries see (at most two pairs in all).
     const int end_tok = min(seq_len, c1 * kBlock);
-    const bool last_masked = (c0 + 2 * npairs) * kBlock > end_tok;
-    const int nfull = npairs - (last_masked ? 1 : 0);
+    const int all_end = min(seq_len - a.n_query + 1, end_tok);
+    const int nfull = max(0, min(npairs, (all_end - c0 * kBlock) / (2 * kBlock)));
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
     using Unit = typename UnitOf<DT>::T;
     auto load_unit = [&](Unit &t, int ph0, int ph1) {
@@ -514,23 +524,31 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     };
     auto compute = [&](Unit &t, int) {
       if constexpr (DT == kFp16) {
-        compute_pair16<false>(st, t, bq, kmul, 32, qd);
+        compute_pair16<false>(st, t, bq, kmul, 32, 32, qd);
       } else {
-        compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, qd);
+        compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, 32, qd);
       }
     };
     pipeline<Unit>(cnt, load, compute);
-    if (last_masked && wave == nfull % kWaves) {
-      const int j0 = 2 * nfull;
-      const int valid = end_tok - (c0 + j0) * kBlock;  // 1..31
+    // masked pairs (at most two: no wave owns more than one), each by the
+    // wave the round-robin gives it
+    const int i = nfull + (wave - nfull % kWaves + kWaves) % kWaves;
+    if (i < npairs) {
+      const int j0 = 2 * i;
+      const int start = (c0 + j0) * kBlock;
+      const int valid_v = end_tok - start;  // 1..32
+      // position of this lane's column's query token (padding columns: the
+      // last); computed here so it is not live across the pipeline
+      const int last_pos = seq_len - a.n_query + (n < a.cols ? n / a.group : a.n_query - 1);
+      const int valid_s = min(valid_v, last_pos + 1 - start);
       const int ph0 = uniform(sh.s.ids[j0]);
       const int ph1 = c0 + j0 + 1 < c1 ? uniform(sh.s.ids[j0 + 1]) : ph0;
       Unit t;
       load_unit(t, ph0, ph1);
       if constexpr (DT == kFp16) {
-        compute_pair16<true>(st, t, bq, kmul, valid, qd);
+        compute_pair16<true>(st, t, bq, kmul, valid_s, valid_v, qd);
       } else {
-        compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid, qd);
+        compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid_s, valid_v, qd);
       }
     }
   }
@@ -1209,9 +1227,9 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
   for (int j = 0; j < 8; ++j)
     *reinterpret_cast<f32x4 *>(&sh.g.o[wave][n][16 * j + 4 * qd]) = st.o[j];
   __syncthreads();
-  // thread -> (head slot hn, channels 8*c8 .. 8*c8+7)
+  // thread -> (column hn, channels 8*c8 .. 8*c8+7)
   const int hn = tid >> 4, c8 = tid & 15;
-  if (hn >= a.group) return;
+  if (hn >= a.cols) return;
   float big = kNegInf;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) big = fmaxf(big, sh.g.m[w][hn]);
@@ -1226,9 +1244,12 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
     acc0 += f * *reinterpret_cast<const f32x4 *>(&sh.g.o[w][hn][8 * c8]);
     acc1 += f * *reinterpret_cast<const f32x4 *>(&sh.g.o[w][hn][8 * c8 + 4]);
   }
-  const size_t row = (size_t)b * a.num_q_heads + h * a.group + hn;
+  const int qt = hn / a.group;
+  const size_t row =
+      ((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group + (hn - qt * a.group);
   if (direct) {
-    const float inv = 1.0f / lt;
+    // a query that saw no token (several queries, short row) gets zeros
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     float *out = a.out + row * kHeadDim + 8 * c8;
     *reinterpret_cast<f32x4 *>(out) = acc0 * inv;
     *reinterpret_cast<f32x4 *>(out + 4) = acc1 * inv;
@@ -1328,8 +1349,11 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     // rows of length 0: zeros (written here only when no reduce follows)
     if (direct && p == 0) {
       const int hn = tid >> 4, c8 = tid & 15;
-      if (hn < a.group) {
-        float *out = a.out + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8;
+      if (hn < a.cols) {
+        const int qt = hn / a.group;
+        float *out = a.out +
+                     (((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group +
+                      (hn - qt * a.group)) * kHeadDim + 8 * c8;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4 *>(out) = z;
         *reinterpret_cast<f32x4 *>(out + 4) = z;
@@ -1402,9 +1426,9 @@ __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, kChannel, kToken)) v
 // More than eight partitions merge chunk by chunk with a running max.
 __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a, int is_int4) {
   constexpr int kUnroll = 8;
-  const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, hq) row
+  const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, query, hq) row
   const int c4 = threadIdx.x & 31;
-  const int b = gid / a.num_q_heads;
+  const int b = gid / (a.num_q_heads * a.n_query);
   if (b >= a.batch) return;
   const size_t base = (size_t)gid * a.slots;
   float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
@@ -1445,13 +1469,15 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       if (p0 + i < total) {
-        const float w = __builtin_amdgcn_exp2f(mv[i] - big);
+        // a partition a query saw nothing of (m = -inf) weighs 0
+        const float w = mv[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - big);
         lt += w * lv[i];
         acc += w * ov[i];
       }
     }
   }
-  *reinterpret_cast<f32x4 *>(out) = acc * (1.0f / lt);
+  // a query that saw no token (several queries, short row) gets zeros
+  *reinterpret_cast<f32x4 *>(out) = lt > 0.0f ? acc * (1.0f / lt) : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 template <int DT, int KS>
@@ -1517,7 +1543,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.slots == 1) return e;
-  const int rows = batch * a.num_q_heads;
+  const int rows = batch * a.n_query * a.num_q_heads;
   hipLaunchKernelGGL(kvq_partition_reduce_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, a,
                      is_kivi(dtype) ? 1 : 0);
   return hipGetLastError();

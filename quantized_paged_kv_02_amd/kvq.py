@@ -31,7 +31,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
 
 EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
             "kvq_write", "kvq_paged_decode", "kvq_write_decode",
-            "kvq_calibrate_workspace_bytes", "kvq_calibrate")
+            "kvq_calibrate_workspace_bytes", "kvq_calibrate",
+            "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq")
 
 
 class Layout(ctypes.Structure):
@@ -92,6 +93,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_write_decode.restype = I32
     lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
                                      P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_paged_decode_mq_workspace_bytes.restype = SZ
+    lib.kvq_paged_decode_mq_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32, I32, I32]
+    lib.kvq_paged_decode_mq.restype = I32
+    lib.kvq_paged_decode_mq.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, I32,
+                                        P, P, I32, I32, ctypes.c_float, P, P, SZ, P]
     lib.kvq_calibrate_workspace_bytes.restype = SZ
     lib.kvq_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32]
     lib.kvq_calibrate.restype = I32
@@ -271,3 +277,23 @@ def calibrate(layout: Layout, k, v, k_scales, v_scales, accumulate: bool = False
                            workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if st != 0:
         raise KvqError(st, "kvq_calibrate")
+
+
+def paged_decode_mq_workspace_bytes(layout: Layout, n_query: int, batch: int,
+                                    max_seq_len: int) -> int:
+    return LIB.kvq_paged_decode_mq_workspace_bytes(ctypes.byref(layout), n_query, batch,
+                                                   max_seq_len)
+
+
+def paged_decode_mq(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
+                    softmax_scale: float, out, workspace, stream=None) -> None:
+    """kvq_paged_decode_mq: q [batch, n_query, Hq, 128] (see kvq.h)."""
+    batch, n_query = int(q.shape[0]), int(q.shape[1])
+    c = cache.struct()
+    st = LIB.kvq_paged_decode_mq(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(q), n_query,
+                                 _ptr(block_tables), _ptr(seq_lens), batch, max_seq_len,
+                                 float(softmax_scale), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream))
+    if st != 0:
+        raise KvqError(st, "kvq_paged_decode_mq")

@@ -67,7 +67,7 @@ def fill_garbage(cache):
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
              table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
-             device="cuda"):
+             n_query=0, device="cuda"):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
@@ -121,13 +121,25 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32), device=device)
         kvq.write(cache, kn, vn, cu, table_t, torch.as_tensor(lens, device=device), 1)
 
-    q = inputs.gen_q(w, layer, device, seed, batch=b)
-    out = torch.full((b, w.num_q_heads, 128), float("nan"), dtype=torch.float32, device=device)
     max_len = int(lens.max()) if b else 0
-    ws = kvq.alloc_workspace(layout, b, max_len, device)
     scale = 1.0 / math.sqrt(128)
     lens_t = torch.as_tensor(lens, device=device)
-    if fused:
+    if n_query:
+        # several query tokens per row: the last n_query positions (cached)
+        q = inputs.gen_q(w, layer, device, seed, batch=b * n_query).reshape(
+            b, n_query, w.num_q_heads, 128).contiguous()
+        out = torch.full((b, n_query, w.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                         device=device)
+        nbytes = kvq.paged_decode_mq_workspace_bytes(layout, n_query, b, max_len)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    else:
+        q = inputs.gen_q(w, layer, device, seed, batch=b)
+        out = torch.full((b, w.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                         device=device)
+        ws = kvq.alloc_workspace(layout, b, max_len, device)
+    if n_query:
+        kvq.paged_decode_mq(cache, q, table_t, lens_t, max_len, scale, out, ws)
+    elif fused:
         # entry r is row r's decode token; rows of length 0 keep zeros (unread)
         kn = torch.zeros((b, w.num_kv_heads, 128), dtype=torch.float16, device=device)
         vn = torch.zeros_like(kn)
@@ -141,7 +153,10 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     out2 = None
     if decode_twice:
         out2 = torch.full_like(out, float("nan"))
-        kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, out2, ws)
+        if n_query:
+            kvq.paged_decode_mq(cache, q, table_t, lens_t, max_len, scale, out2, ws)
+        else:
+            kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, out2, ws)
     # further launches on the same workspace (`repeats` of them)
     rep_outs = []
     for _ in range(repeats):
@@ -160,6 +175,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     if decode_twice:
         res.out2 = out2.cpu().numpy()
     res.repeat_outs = [o.cpu().numpy() for o in rep_outs]
+    res.n_query = n_query
     return res
 
 
@@ -235,6 +251,9 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
                                        f"first {bad[:3].tolist()}")
             out.append(oracle.dequantize(codes, scb, w.dtype))
         k_hat, v_hat = out
+    if getattr(res, "n_query", 0):
+        return oracle.multi_query_attention(res.q[r].astype(np.float64), k_hat, v_hat,
+                                            res.softmax_scale)
     return oracle.decode_attention(res.q[r].astype(np.float64), k_hat, v_hat, res.softmax_scale)
 
 

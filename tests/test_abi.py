@@ -249,3 +249,23 @@ def test_fp8_e5m2_layout_is_accepted():
     lay = _layout(dtype=6, k_gran=3, v_gran=0)
     assert kvq.validate(lay, _cache(), 2, 100) == OK
     assert kvq.decode_workspace_bytes(_layout(dtype=6, split_tokens=16), 2, 100) > 0
+
+
+def _decode_mq(lay, cache, nq=2, q=FAKE, batch=2, max_len=100, ws=FAKE, ws_bytes=1 << 30):
+    return kvq.LIB.kvq_paged_decode_mq(ctypes.byref(lay), ctypes.byref(cache), q, nq, FAKE,
+                                       FAKE, batch, max_len, 0.1, FAKE, ws, ws_bytes, None)
+
+
+def test_multi_query_rules():
+    lay = _layout(split_tokens=16)                        # g = 4
+    one = kvq.paged_decode_mq_workspace_bytes(lay, 1, 2, 100)
+    assert one == kvq.decode_workspace_bytes(lay, 2, 100) and one > 0
+    assert kvq.paged_decode_mq_workspace_bytes(lay, 4, 2, 100) > one
+    assert kvq.paged_decode_mq_workspace_bytes(lay, 5, 2, 100) == 0      # 5 x 4 > 16 columns
+    assert _decode_mq(lay, _cache(), nq=0) == INV
+    assert _decode_mq(lay, _cache(), nq=5) == UNS
+    assert _decode_mq(lay, _cache(), q=None) == INV
+    assert _decode_mq(lay, _cache(), ws_bytes=16) == WS
+    assert _decode_mq(lay, _cache(), batch=0) == OK
+    lay4 = _layout(dtype=3, k_gran=2, v_gran=3)
+    assert _decode_mq(lay4, _cache(int4=True), nq=1) == UNS
