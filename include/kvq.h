@@ -296,7 +296,9 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
  * The K/V stream is read once for all queries: the score product's 16
  * columns hold (query, head) pairs.  Errors: as for kvq_paged_decode;
  * KVQ_ERR_INVALID_ARG for n_query < 1; KVQ_ERR_UNSUPPORTED when n_query *
- * (Hq / H) > 16 or for INT4 caches. */
+ * (Hq / H) > 16.  INT4 caches: the INT4 groups are seen by every query
+ * (they end a residual window before the newest token); the fp16 window
+ * is masked per query. */
 size_t kvq_paged_decode_mq_workspace_bytes(const kvq_layout *layout, int32_t n_query,
                                            int32_t batch, int32_t max_seq_len);
 kvq_status kvq_paged_decode_mq(const kvq_layout *layout, const kvq_cache *cache,

@@ -357,7 +357,6 @@ static kvq_status check_mq(const kvq_layout *layout, int32_t n_query) {
   const kvq_status st = check_layout(layout);
   if (st != KVQ_OK) return st;
   if (n_query < 1) return KVQ_ERR_INVALID_ARG;
-  if (kivi(layout)) return KVQ_ERR_UNSUPPORTED;
   if ((int64_t)n_query * (layout->num_q_heads / layout->num_kv_heads) > 16)
     return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;

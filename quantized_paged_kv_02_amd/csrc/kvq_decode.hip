@@ -1168,6 +1168,10 @@ __device__ void stream_ring(Softmax &st, const DecodeArgs &a, int b, int h, int 
 #pragma unroll
   for (int j = 0; j < 4; ++j) bq[j] = u4_to_f16x8(qr[j]);
   const int nq = kivi_quantized_len(seq_len, a.residual);
+  // last position this lane's column sees (several queries per row: the
+  // INT4 groups end at least a residual window before the newest token, so
+  // only the fp16 window needs per-column masks)
+  const int last_pos = seq_len - a.n_query + (n < a.cols ? n / a.group : a.n_query - 1);
   const size_t row = (size_t)b * a.num_kv_heads + h;
   const uint16_t *kr = a.k_resid + row * a.ring * kHeadDim;
   const uint16_t *vr = a.v_resid + row * (a.ring / 4) * kHeadDim * 4;
@@ -1186,9 +1190,10 @@ __device__ void stream_ring(Softmax &st, const DecodeArgs &a, int b, int h, int 
         const u32x4 kv = ld16(kr + (size_t)(slot0 + n) * kHeadDim + 32 * qd + 8 * j);
         acc = mfma32(u4_to_f16x8(kv), bq[j], acc);
       }
-      const int valid = seq_len - (tok + 4 * qd);
+      const int valid = seq_len - (tok + 4 * qd);               // tokens that exist
+      const int valid_s = min(valid, last_pos + 1 - (tok + 4 * qd));  // and are seen
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[u][r] = r < valid ? acc[r] * a.qk_scale : kNegInf;
+      for (int r = 0; r < 4; ++r) s[u][r] = r < valid_s ? acc[r] * a.qk_scale : kNegInf;
       const uint16_t *vq = vr + ((size_t)(slot0 / 4 + qd) * kHeadDim + n) * 4;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1339,8 +1344,11 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
   u32x4 qrow = {0u, 0u, 0u, 0u};
   if constexpr (is_kivi(DT)) {
     const int hn = tid >> 4, c8 = tid & 15;
-    if (hn < a.group)
-      qrow = ld16(a.q + ((size_t)b * a.num_q_heads + h * a.group + hn) * kHeadDim + 8 * c8);
+    if (hn < a.cols) {  // column hn: query token hn / g, head hn % g
+      const int qt = hn / a.group;
+      qrow = ld16(a.q + (((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group +
+                         (hn - qt * a.group)) * kHeadDim + 8 * c8);
+    }
   }
   const int seq_len = a.seq_lens[b];
   const bool direct = a.slots == 1;
@@ -1519,13 +1527,14 @@ int decode_scale_kind(int granularity) {
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind, int batch,
                          hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, batch);
-  if (dtype == kInt4 && a.group <= 4) {
+  // the compact INT4 layout holds one query token's four heads per block
+  if (dtype == kInt4 && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, true>), grid, dim3(kThreads), 0,
                        stream, a);
   } else if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, false>), grid, dim3(kThreads), 0,
                        stream, a);
-  } else if (dtype == kInt4Affine && a.group <= 4) {
+  } else if (dtype == kInt4Affine && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, true>), grid, dim3(kThreads),
                        0, stream, a);
   } else if (dtype == kInt4Affine) {

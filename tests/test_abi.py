@@ -268,4 +268,6 @@ def test_multi_query_rules():
     assert _decode_mq(lay, _cache(), ws_bytes=16) == WS
     assert _decode_mq(lay, _cache(), batch=0) == OK
     lay4 = _layout(dtype=3, k_gran=2, v_gran=3)
-    assert _decode_mq(lay4, _cache(int4=True), nq=1) == UNS
+    assert _decode_mq(lay4, _cache(int4=True), nq=5) == UNS
+    assert kvq.paged_decode_mq_workspace_bytes(_layout(dtype=5, k_gran=2, v_gran=3,
+                                                       split_tokens=64), 4, 2, 1000) > 0

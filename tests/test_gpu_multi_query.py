@@ -1,6 +1,6 @@
 """GPU parity of kvq_paged_decode_mq (several query tokens per row over the
 cache, causal): every query's output against the oracle's multi-query
-attention over the same dequantized cache, for each non-INT4 format, query
+attention over the same dequantized cache, for every format, query
 counts up to the 16 product columns, rows shorter than the query count
 (queries that see no token give zeros), masked spans crossing pair and
 partition boundaries, and n_query = 1 equal bit for bit to plain decode."""
@@ -23,7 +23,8 @@ def _w(dtype, kg, vg, hq, hkv, table="shuffled"):
 
 
 FORMATS = [("int8", "token", "token"), ("fp8", "head", "head"), ("fp16", "none", "none"),
-           ("fp8e5m2", "channel", "token")]
+           ("fp8e5m2", "channel", "token"), ("int4", "channel", "token"),
+           ("int4-affine", "channel", "token")]
 
 
 @pytest.mark.parametrize("dtype,kg,vg", FORMATS)
