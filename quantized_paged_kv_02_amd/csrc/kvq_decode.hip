@@ -136,8 +136,8 @@ __device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, con
 }
 
 // The same for four blocks at once (one max and one rescale decision).
-__device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4],
-                                                f32x4 (&p)[4]) {
+__device__ __forceinline__ void softmax_update4(Softmax &st, f32x4 (&vb)[2],
+                                                const f32x4 (&s)[4], f32x4 (&p)[4]) {
   float bm = kNegInf;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -150,6 +150,8 @@ __device__ __forceinline__ void softmax_update4(Softmax &st, const f32x4 (&s)[4]
     st.l *= alpha;
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    vb[0] *= alpha;
+    vb[1] *= alpha;
     st.m = mn;
   }
   float sum = 0.0f;
@@ -791,7 +793,8 @@ __device__ __forceinline__ f16x8 uint4x8_to_f16_biased(uint32_t x) {
 // AFF: affine codes; the zero points are staged beside the scales (float
 // 256 on) and enter the key conversion and the value bias operand.
 template <bool AFF>
-__device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, const f16 *qs,
+__device__ __forceinline__ void compute_group4(Softmax &st, f32x4 (&vb)[2], const Group4 &t,
+                                               const f16 *qs,
                                                float *scl, float qk_scale, int lane, int n,
                                                int qd) {
   // stage the group's scales in this wave's LDS slot (in-order within a wave)
@@ -860,7 +863,7 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
   f32x4 pg[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] *= qk_scale;
-  softmax_update4(st, acc, pg);
+  softmax_update4(st, vb, acc, pg);
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
     const f32x4 &p0 = pg[2 * pr], &p1 = pg[2 * pr + 1];
@@ -902,10 +905,10 @@ __device__ __forceinline__ void compute_group4(Softmax &st, const Group4 &t, con
       const f16x8 av = AFF ? uint4x8_to_f16_biased(w) : int4x8_to_f16_biased(w);
       st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
     }
-    // bias cancellation after all eight tiles (each o[j] update is eight
-    // matrix instructions after the previous one)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] = mfma32(j < 4 ? abias0 : abias1, j < 4 ? pb0 : pb1, st.o[j]);
+    // bias cancellation: the operand's rows are alike, so one product per
+    // channel group into its accumulator, added to the tiles at the end
+    vb[0] = mfma32(abias0, pb0, vb[0]);
+    vb[1] = mfma32(abias1, pb1, vb[1]);
   }
 }
 
@@ -917,6 +920,7 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
   // the group's queries (fp16, zero rows past the group) stay in LDS and are
   // re-read per channel chunk, which keeps them out of the register budget
   *reinterpret_cast<u32x4 *>(&sh.s.q[tid >> 4][8 * (tid & 15)]) = qrow;
+  f32x4 vb[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -939,10 +943,13 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
                        h, lane);
     };
     auto compute = [&](Group4 &t, int) {
-      compute_group4<AFF>(st, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
+      compute_group4<AFF>(st, vb, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
     };
     pipeline<Group4>(cnt, load, compute);
   }
+  // the value bias of each channel group, once into its four tiles
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] += vb[j >> 2];
 }
 
 // ---------------------------------------------------------------------------
@@ -985,7 +992,8 @@ __device__ __forceinline__ float all_banks(float x) {
 // Online softmax on compact scores.  The running max moves only when some
 // score exceeds it by more than the slack; only then is the head-wide max
 // taken (over the four banks and the four row groups).
-__device__ __forceinline__ void softmax_update_c(Softmax &st, const f32x4 &s, f32x4 &p) {
+__device__ __forceinline__ void softmax_update_c(Softmax &st, f32x4 (&vb)[2], const f32x4 &s,
+                                                 f32x4 &p) {
   const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   if (__any(lm > st.m + kRescaleSlack)) {
     const float bm = max_over_quads(bank_max(lm));
@@ -996,6 +1004,8 @@ __device__ __forceinline__ void softmax_update_c(Softmax &st, const f32x4 &s, f3
     // o column n belongs to head n; for n < 4 that is this lane's head
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    vb[0] *= alpha;
+    vb[1] *= alpha;
     st.m = mn;
   }
 #pragma unroll
@@ -1017,9 +1027,13 @@ __device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
   return u4_to_f16x8(w);
 }
 
+// The bias operand's rows are all alike, so its product adds the same
+// value to every channel row of a channel group's four tiles: it goes to
+// one accumulator per group (vb), added to o once at the end, instead of
+// one product per tile.
 template <int PR, bool AFF>
-__device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, const f16x8 &pb0,
-                                             const f16x8 &pb1) {
+__device__ __forceinline__ void value_pair_c(Softmax &st, f32x4 (&vb)[2], const Group4C &t,
+                                             const f16x8 &pb0, const f16x8 &pb1) {
   f16x8 abias0, abias1;
   if constexpr (AFF) {
     const u32x4 w = {row_bcast<8 + 4 * PR>(t.zw), row_bcast<9 + 4 * PR>(t.zw),
@@ -1036,8 +1050,8 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, cons
     const f16x8 av = AFF ? uint4x8_to_f16_biased(w) : int4x8_to_f16_biased(w);
     st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(j < 4 ? abias0 : abias1, j < 4 ? pb0 : pb1, st.o[j]);
+  vb[0] = mfma32(abias0, pb0, vb[0]);
+  vb[1] = mfma32(abias1, pb1, vb[1]);
 }
 
 // qv[hh]: this lane's query values of head hh at channels 8(lane/4) +
@@ -1045,7 +1059,7 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, const Group4C &t, cons
 // rows; qrd: dword offset of this lane's score-operand row (hi row of head
 // n%4 in even banks, lo row in odd banks) and row group.
 template <bool AFF>
-__device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
+__device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[2], const Group4C &t,
                                                 const float (&qv)[4][2], uint32_t *qb, int qrd,
                                                 float qk_scale, int lane, int n) {
   // q' of this lane's two channels for the four heads (dword `lane` of each row)
@@ -1092,7 +1106,7 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
-  softmax_update_c(st, s, p);
+  softmax_update_c(st, vb, s, p);
   // weights times the V scales of this lane's tokens (channel groups 0, 1)
   // tokens 2, 3 of every 4 meet value codes stored as 1152 + 16 code
   const float p2 = p[2] * 0.0625f, p3 = p[3] * 0.0625f;
@@ -1100,8 +1114,8 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, const Group4C &t,
                           pack_rne(p2 * t.vsb[0], p3 * t.vsb[2])};
   const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
                           pack_rne(p2 * t.vsb[1], p3 * t.vsb[3])};
-  value_pair_c<0, AFF>(st, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
-  value_pair_c<1, AFF>(st, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
+  value_pair_c<0, AFF>(st, vb, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
+  value_pair_c<1, AFF>(st, vb, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
 }
 
 template <bool AFF>
@@ -1132,6 +1146,7 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   st.m = dpp_f32<kRowShr + 8, 0x4>(st.m, st.m);
   st.m = dpp_f32<kRowShr + 12, 0x8>(st.m, st.m);
   st.l = n < 4 ? st.l : 0.0f;
+  f32x4 vb[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -1149,10 +1164,13 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
       load_group4c<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
     };
     auto compute = [&](Group4C &t, int) {
-      compute_group4c<AFF>(st, t, qv, qb, qrd, a.qk_scale, lane, n);
+      compute_group4c<AFF>(st, vb, t, qv, qb, qrd, a.qk_scale, lane, n);
     };
     pipeline<Group4C>(cnt, load, compute);
   }
+  // the value bias of each channel group, once into its four tiles
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] += vb[j >> 2];
   // back to one head per lane (n < 4): this lane's share of head n's sum
   st.l = bank_sum(st.l);
 }
