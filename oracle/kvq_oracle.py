@@ -429,7 +429,7 @@ def unpack_int4(packed):
     return out.astype(np.int8)
 
 
-def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False):
+def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False, bits=4):
     """Quantize a whole sequence's K and V [S, Hkv, D] (fp16) KIVI-style.
 
     Returns a dict with
@@ -438,8 +438,8 @@ def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False):
       v_codes   [nq, Hkv, D] int8,  v_scales [nq, Hkv, D // group] fp32,
       k_resid, v_resid  [S - nq, Hkv, D] fp16 (unchanged inputs).
     With ``affine`` the groups are quantized asymmetrically: codes are uint8
-    in [0, 15] and ``k_zp`` / ``v_zp`` (int64, shaped like the scales) hold
-    the zero points.
+    in [0, 2**bits - 1] (``bits`` 4 or 2) and ``k_zp`` / ``v_zp`` (int64,
+    shaped like the scales) hold the zero points.
     Each group depends only on its own 64 tokens, so quantizing the final
     state equals quantizing group by group as the sequence grows.
     """
@@ -455,7 +455,7 @@ def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False):
         for h in range(hkv):
             kg = k[gi * group:(gi + 1) * group, h, :]
             if affine:
-                c, s, z = kivi_affine_quantize_k_group(kg)
+                c, s, z = kivi_affine_quantize_k_group(kg, qmax=(1 << bits) - 1)
                 k_zp[gi, h, :] = z
             else:
                 c, s = kivi_quantize_k_group(kg)
@@ -466,7 +466,7 @@ def kivi_quantize(k, v, residual=KIVI_RESIDUAL, group=KIVI_GROUP, affine=False):
     v_zp = np.zeros((nq, hkv, d // group), np.int64)
     for h in range(hkv):
         if affine:
-            c, s, z = kivi_affine_quantize_v_tokens(v[:nq, h, :], group)
+            c, s, z = kivi_affine_quantize_v_tokens(v[:nq, h, :], group, qmax=(1 << bits) - 1)
             v_zp[:, h, :] = z
         else:
             c, s = kivi_quantize_v_tokens(v[:nq, h, :], group)
@@ -527,24 +527,26 @@ def quantize_affine(x, scale, zero_point, qmax):
     return q.astype(np.uint8)
 
 
-def kivi_affine_quantize_k_group(k_group):
+def kivi_affine_quantize_k_group(k_group, qmax=INT4_UMAX):
     """K of one 64-token group and one KV head, [64, D] fp16 -> (codes [64,
-    D] uint8 in [0, 15], scales [D] fp32, zero points [D] int64), one
-    (scale, zero point) per channel over the group's tokens."""
+    D] uint8 in [0, qmax], scales [D] fp32, zero points [D] int64), one
+    (scale, zero point) per channel over the group's tokens.  qmax 15: 4-bit
+    codes; 3: 2-bit ([oh-bug] table: 2-bit caches at 0.25 byte per value;
+    KIVI's scheme, named in its references, is asymmetric 2-bit)."""
     k = np.asarray(k_group, np.float32)
-    s, z = affine_params(k, INT4_UMAX, axis=0)
-    return quantize_affine(k, s[None, :], z[None, :], INT4_UMAX), s, z
+    s, z = affine_params(k, qmax, axis=0)
+    return quantize_affine(k, s[None, :], z[None, :], qmax), s, z
 
 
-def kivi_affine_quantize_v_tokens(v_tokens, group=KIVI_GROUP):
+def kivi_affine_quantize_v_tokens(v_tokens, group=KIVI_GROUP, qmax=INT4_UMAX):
     """V rows [T, D] -> (codes [T, D] uint8, scales [T, D // group] fp32, zero
     points [T, D // group]): one (scale, zero point) per token and channel
     group."""
     v = np.asarray(v_tokens, np.float32)
     t, d = v.shape
     vg = v.reshape(t, d // group, group)
-    s, z = affine_params(vg, INT4_UMAX, axis=-1)
-    q = quantize_affine(vg, s[..., None], z[..., None], INT4_UMAX)
+    s, z = affine_params(vg, qmax, axis=-1)
+    q = quantize_affine(vg, s[..., None], z[..., None], qmax)
     return q.reshape(t, d), s, z
 
 

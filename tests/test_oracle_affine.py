@@ -134,3 +134,51 @@ def test_kivi_affine_sequence():
     # the affine form fits the shifted V better than the symmetric one
     sym = oracle.kivi_dequantize(oracle.kivi_quantize(k, v))[1]
     assert np.abs(v_hat[:128] - v[:128]).mean() < np.abs(sym[:128] - v[:128]).mean()
+
+
+# --- 2-bit groups (qmax 3) -------------------------------------------------------
+
+@pytest.mark.parametrize("seed,scale,shift", [(0, 1.0, 0.0), (6, 2.0, 1.5), (7, 0.05, -0.3)])
+def test_two_bit_params_match_torch_observer(seed, scale, shift):
+    x = _groups(seed, (64, 128), scale, shift)
+    s, z = oracle.affine_params(x, 3, axis=0)
+    t = torch.from_numpy(np.asarray(x, np.float32))
+    ob = PerChannelMinMaxObserver(ch_axis=1, dtype=torch.quint8,
+                                  qscheme=torch.per_channel_affine, quant_min=0, quant_max=3)
+    ob(t)
+    ts, tz = ob.calculate_qparams()
+    assert np.array_equal(s.view(np.uint32), ts.numpy().astype(np.float32).view(np.uint32))
+    assert np.array_equal(z, tz.numpy().astype(np.int64))
+
+
+def test_two_bit_codes_are_nearest_levels():
+    k = _groups(12, (64, 128), 1.0, 0.2)
+    q, s, z = oracle.kivi_affine_quantize_k_group(k, qmax=3)
+    assert q.max() <= 3
+    for t in range(0, 64, 5):
+        for c in range(128):
+            xf, sf = Fraction(float(k[t, c])), Fraction(float(s[c]))
+            dist = [abs(xf - (cc - int(z[c])) * sf) for cc in range(4)]
+            if dist[int(q[t, c])] != min(dist):
+                r = xf / sf
+                frac = r - (r.numerator // r.denominator)
+                assert abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 18), (t, c)
+    v = _groups(13, (20, 128), 1.0, 0.5)
+    qv, sv, zv = oracle.kivi_affine_quantize_v_tokens(v, qmax=3)
+    err = np.abs((qv.astype(np.float64).reshape(20, 2, 64) - zv[..., None]) *
+                 sv[..., None].astype(np.float64) - v.astype(np.float64).reshape(20, 2, 64))
+    assert np.all(err <= sv[..., None] * (0.5 + 1e-6))
+
+
+def test_two_bit_sequence():
+    g = np.random.default_rng(9)
+    k = g.standard_normal((260, 2, 128)).astype(np.float16)
+    v = g.standard_normal((260, 2, 128)).astype(np.float16)
+    kv = oracle.kivi_quantize(k, v, affine=True, bits=2)
+    assert kv["nq"] == 128 and kv["k_codes"].max() <= 3 and kv["v_codes"].max() <= 3
+    k_hat, v_hat = oracle.kivi_dequantize(kv)
+    ks = np.repeat(kv["k_scales"], 64, axis=0).astype(np.float64)
+    assert np.all(np.abs(k_hat[:128] - k[:128]) <= ks * (0.5 + 1e-6))
+    # four levels reconstruct worse than sixteen
+    k4 = oracle.kivi_dequantize(oracle.kivi_quantize(k, v, affine=True))[0]
+    assert np.abs(k_hat[:128] - k[:128]).mean() > np.abs(k4[:128] - k[:128]).mean()
