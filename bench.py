@@ -65,18 +65,21 @@ def _cpu_unit(args):
     q = inputs.gen_q(w, layer, "cpu", 0)[row].numpy().astype(np.float64)
     scale = 1.0 / math.sqrt(inputs.HEAD_DIM)
     with threadpool_limits(limits=1):
-        if w.dtype.startswith("int4"):
-            affine = w.dtype == "int4-affine"
-            full = oracle.kivi_quantize(k, v, residual=w.residual_len, affine=affine)
+        if w.dtype in ("int4", "int4-affine", "int2-affine"):
+            affine = w.dtype != "int4"
+            bits = 2 if w.dtype == "int2-affine" else 4
+            qmax = (1 << bits) - 1
+            full = oracle.kivi_quantize(k, v, residual=w.residual_len, affine=affine, bits=bits)
             nq_old = oracle.kivi_quantized_len(seq - 1, w.residual_len)
-            qk = oracle.kivi_affine_quantize_k_group if affine else oracle.kivi_quantize_k_group
-            qv = (oracle.kivi_affine_quantize_v_tokens if affine
-                  else oracle.kivi_quantize_v_tokens)
             t0 = time.perf_counter()
             for g0 in range(nq_old, full["nq"], 64):
                 for h in range(w.num_kv_heads):
-                    qk(k[g0:g0 + 64, h])
-                    qv(v[g0:g0 + 64, h])
+                    if affine:
+                        oracle.kivi_affine_quantize_k_group(k[g0:g0 + 64, h], qmax=qmax)
+                        oracle.kivi_affine_quantize_v_tokens(v[g0:g0 + 64, h], qmax=qmax)
+                    else:
+                        oracle.kivi_quantize_k_group(k[g0:g0 + 64, h])
+                        oracle.kivi_quantize_v_tokens(v[g0:g0 + 64, h])
             k_hat, v_hat = oracle.kivi_dequantize(full)
             oracle.decode_attention(q, k_hat, v_hat, scale)
             return time.perf_counter() - t0

@@ -114,6 +114,19 @@
  *             group's block u (b, u, e in 0..3), so one row holds what one
  *             lane row of the decode kernel needs.
  *
+ * ---- 2-bit affine (KVQ_INT2_AFFINE) -------------------------------------------
+ * The KVQ_INT4_AFFINE rule with codes 0..3 (scale = (hi - lo) / 3), the
+ * 2-bit entry of [oh-bug] section "KV Cache 的基本内存模型" (0.25 byte per
+ * value) and KIVI's asymmetric 2-bit scheme named in its references.
+ * Groups, residual window, ring and the 40-float scale / zero-point rows
+ * are those of KVQ_INT4_AFFINE.  Query groups Hq / H of at most 4, one
+ * query per row (kvq_paged_decode_mq takes n_query = 1 only).
+ *   k_codes : uint8 [NB][H][512]; (slot s, channel c) at byte
+ *             128*(c>>5) + 8*s + ((c&31)>>2), bits 2*(c&3).
+ *   v_codes : uint8 [NB][H][512]; with j = c>>4, e = s&3 and
+ *             pos(e) = 0, 2, 1, 3 for e = 0..3: byte
+ *             8*((c&15) + 16*(s>>2)) + 4*(j>>2) + pos(e), bits 2*(j&3).
+ *
  * ---- FP16 (unquantized) layout: fp16 [NB][H][2048] for each of K and V ----
  * The baseline the quantized formats are measured against ([intelli] §5:
  * INT8 against FP16 memory and latency).  Values are stored as given; one
@@ -150,7 +163,9 @@ typedef enum kvq_dtype {
   KVQ_FP16 = 4,     /* 2 bytes per value, unquantized                       */
   KVQ_INT4_AFFINE = 5, /* INT4 KIVI grouping, asymmetric: codes 0..15 with a
                           zero point per group                              */
-  KVQ_FP8_E5M2 = 6  /* 1 byte per value, OCP E5M2, divisor 57344            */
+  KVQ_FP8_E5M2 = 6, /* 1 byte per value, OCP E5M2, divisor 57344            */
+  KVQ_INT2_AFFINE = 7 /* 2-bit KIVI: 0.25 byte per value, codes 0..3 with a
+                         zero point per group                               */
 } kvq_dtype;
 
 typedef enum kvq_granularity {

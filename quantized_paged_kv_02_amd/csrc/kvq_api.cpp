@@ -25,7 +25,9 @@ constexpr long kWgOverheadF16 = 4;  // a block streams twice the bytes of INT8
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // KIVI-grouped INT4 cache (symmetric or affine)
-bool kivi(const kvq_layout *L) { return L->dtype == KVQ_INT4 || L->dtype == KVQ_INT4_AFFINE; }
+bool kivi(const kvq_layout *L) {
+  return L->dtype == KVQ_INT4 || L->dtype == KVQ_INT4_AFFINE || L->dtype == KVQ_INT2_AFFINE;
+}
 
 int kivi_len(int s, int residual) {
   const int n = s - residual;
@@ -36,7 +38,8 @@ kvq_status check_layout(const kvq_layout *L) {
   if (!L) return KVQ_ERR_INVALID_ARG;
   if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4 &&
-      L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE && L->dtype != KVQ_FP8_E5M2)
+      L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE && L->dtype != KVQ_FP8_E5M2 &&
+      L->dtype != KVQ_INT2_AFFINE)
     return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_FP16) {  // an FP16 cache has no scales
     if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
@@ -49,6 +52,9 @@ kvq_status check_layout(const kvq_layout *L) {
   if (L->head_dim != kHeadDim || L->block_size != kBlock) return KVQ_ERR_UNSUPPORTED;
   if (L->num_q_heads / L->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
   if (kivi(L)) {
+    // 2-bit decode is built for query groups of at most four
+    if (L->dtype == KVQ_INT2_AFFINE && L->num_q_heads / L->num_kv_heads > 4)
+      return KVQ_ERR_UNSUPPORTED;
     if (L->k_gran != KVQ_PER_CHANNEL || L->v_gran != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
     if (L->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
     if (L->residual_len < kGroup || L->residual_len % kGroup != 0) return KVQ_ERR_UNSUPPORTED;
@@ -219,8 +225,7 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
   if (kivi(layout)) {
     // groups leaving the window: at most ceil(n/64) + 1 per row
     const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup + 1;
-    e = kvq::launch_write_int4(a, layout->dtype == KVQ_INT4_AFFINE, batch, max_new_per_seq,
-                               max_groups, s);
+    e = kvq::launch_write_int4(a, layout->dtype, batch, max_new_per_seq, max_groups, s);
   } else if (layout->dtype == KVQ_FP16) {
     e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);
   } else {
@@ -345,8 +350,8 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   w.residual = layout->residual_len;
   w.ring = layout->residual_len + kGroup;
   (void)hipGetLastError();
-  const hipError_t e = kvq::launch_write_int4(w, layout->dtype == KVQ_INT4_AFFINE, batch, 1, 2,
-                                              static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      kvq::launch_write_int4(w, layout->dtype, batch, 1, 2, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
   return decode_launch(layout, a, batch, stream);
 }
@@ -357,6 +362,7 @@ static kvq_status check_mq(const kvq_layout *layout, int32_t n_query) {
   const kvq_status st = check_layout(layout);
   if (st != KVQ_OK) return st;
   if (n_query < 1) return KVQ_ERR_INVALID_ARG;
+  if (layout->dtype == KVQ_INT2_AFFINE && n_query > 1) return KVQ_ERR_UNSUPPORTED;
   if ((int64_t)n_query * (layout->num_q_heads / layout->num_kv_heads) > 16)
     return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;

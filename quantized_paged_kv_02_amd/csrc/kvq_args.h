@@ -8,9 +8,15 @@
 
 namespace kvq {
 
-enum Dtype : int { kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5, kFp8E5M2 = 6 };  // kvq_dtype
-// KIVI-grouped INT4 caches, symmetric or affine
-constexpr bool is_kivi(int dtype) { return dtype == kInt4 || dtype == kInt4Affine; }
+enum Dtype : int {  // kvq_dtype
+  kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5, kFp8E5M2 = 6, kInt2Affine = 7
+};
+// KIVI-grouped caches: INT4 symmetric or affine, 2-bit affine
+constexpr bool is_kivi(int dtype) {
+  return dtype == kInt4 || dtype == kInt4Affine || dtype == kInt2Affine;
+}
+// bytes of one (block, head) code chunk of a KIVI-grouped cache
+constexpr int kivi_chunk_bytes(int dtype) { return dtype == kInt2Affine ? 512 : 1024; }
 // Granularity as the decode kernel sees it: a scale that is uniform over a
 // (row, KV head) (per-tensor or per-head), per channel, or per token.
 enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
@@ -113,8 +119,9 @@ hipError_t launch_calibrate(const CalibArgs &a, hipStream_t stream);
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch,
                            int max_new, hipStream_t stream);
 hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStream_t stream);
-// affine: asymmetric groups (unsigned codes, zero points beside the scales)
-hipError_t launch_write_int4(const WriteArgs &a, bool affine, int batch, int max_new,
+// dtype: kInt4, kInt4Affine or kInt2Affine (affine groups: unsigned codes,
+// zero points beside the scales)
+hipError_t launch_write_int4(const WriteArgs &a, int dtype, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind,
                          int v_kind, int batch, hipStream_t stream);

@@ -992,7 +992,7 @@ __device__ __forceinline__ float all_banks(float x) {
 // Online softmax on compact scores.  The running max moves only when some
 // score exceeds it by more than the slack; only then is the head-wide max
 // taken (over the four banks and the four row groups).
-__device__ __forceinline__ void softmax_update_c(Softmax &st, f32x4 (&vb)[2], const f32x4 &s,
+__device__ __forceinline__ void softmax_update_c(Softmax &st, f32x4 (&vb)[4], const f32x4 &s,
                                                  f32x4 &p) {
   const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   if (__any(lm > st.m + kRescaleSlack)) {
@@ -1004,8 +1004,8 @@ __device__ __forceinline__ void softmax_update_c(Softmax &st, f32x4 (&vb)[2], co
     // o column n belongs to head n; for n < 4 that is this lane's head
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
-    vb[0] *= alpha;
-    vb[1] *= alpha;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vb[g] *= alpha;
     st.m = mn;
   }
 #pragma unroll
@@ -1032,7 +1032,7 @@ __device__ __forceinline__ f16x8 p_operand_c(const uint32_t (&d)[2]) {
 // one accumulator per group (vb), added to o once at the end, instead of
 // one product per tile.
 template <int PR, bool AFF>
-__device__ __forceinline__ void value_pair_c(Softmax &st, f32x4 (&vb)[2], const Group4C &t,
+__device__ __forceinline__ void value_pair_c(Softmax &st, f32x4 (&vb)[4], const Group4C &t,
                                              const f16x8 &pb0, const f16x8 &pb1) {
   f16x8 abias0, abias1;
   if constexpr (AFF) {
@@ -1059,7 +1059,7 @@ __device__ __forceinline__ void value_pair_c(Softmax &st, f32x4 (&vb)[2], const 
 // rows; qrd: dword offset of this lane's score-operand row (hi row of head
 // n%4 in even banks, lo row in odd banks) and row group.
 template <bool AFF>
-__device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[2], const Group4C &t,
+__device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[4], const Group4C &t,
                                                 const float (&qv)[4][2], uint32_t *qb, int qrd,
                                                 float qk_scale, int lane, int n) {
   // q' of this lane's two channels for the four heads (dword `lane` of each row)
@@ -1118,7 +1118,182 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[2], con
   value_pair_c<1, AFF>(st, vb, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
 }
 
-template <bool AFF>
+// ---------------------------------------------------------------------------
+// 2-bit affine KIVI on the compact layout.  Key codes: a dword holds 16
+// channels (2 bits each); masking one 2-bit field per fp16 half under the
+// exponent of 1024, less 1024, gives 4^k u for fields k = 0..3 of bytes 0
+// and 2 (and of bytes 1 and 3 after a shift by 8), so one dword yields two
+// operands of 8 channels: slots (2k, 2k+1) hold channels (k, k+8) or
+// (4+k, 12+k), weight 4^-k folded into q'.  Value codes are stored by token
+// (byte order t0, t2, t1, t3; four tiles per byte), so the same masks give
+// tile k's pairs (t0, t1) and (t2, t3), less 1024 exactly: a tile carries
+// the factor 4^k, removed at the end.
+// ---------------------------------------------------------------------------
+struct Group2C {
+  u32x2 k[4];   // block u: codes of channels 32qd..32qd+31, token l%16
+  u32x2 v[4];   // block u: tokens 4qd..4qd+3 of channels 16j + l%16, j = 0..7
+  float ks[2];
+  f32x4 vsa, vsb;
+  uint32_t zw;  // as Group4C
+  __device__ explicit Group2C(int = 0) {}
+};
+
+__device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Channel (within its 32) of the first of lane l's two q' channels: chunk
+// J = (l/4)%4, pair i = l%4 -> 16(J/2) + 4(J%2) + i; the second is +8.
+__device__ __forceinline__ int k2_chan(int lane) {
+  const int J = (lane >> 2) & 3, i = lane & 3;
+  return 16 * (J >> 1) + 4 * (J & 1) + i;
+}
+
+__device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, const int (&ph)[4],
+                                             int pm, int pv, int h, int lane) {
+  constexpr int kRow = 40;
+  const int H = a.num_kv_heads;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t chunk = (size_t)ph[u] * H + h;
+    t.k[u] = bld8(make_rsrc(a.k_codes + chunk * 512, 512), 8 * lane);
+    t.v[u] = bld8(make_rsrc(a.v_codes + chunk * 512, 512), 8 * lane);
+  }
+  const float *krow = a.k_scales + ((size_t)pm * H + h) * kRow;
+  const int c = k2_chan(lane);
+  t.ks[0] = krow[c];
+  t.ks[1] = krow[c + 8];
+  const float *vsp = a.v_scales + ((size_t)pv * H + h) * kRow + 8 * (lane >> 4);
+  t.vsa = ld16f(vsp);
+  t.vsb = ld16f(vsp + 4);
+  const int n = lane & 15;
+  const float *zrow = (n < 8 ? a.k_scales : a.v_scales) + ((size_t)pm * H + h) * kRow + 32;
+  t.zw = reinterpret_cast<const uint32_t *>(zrow)[n & 7];
+}
+
+// The four fp16 pairs of 2-bit fields k = 0..3 of bytes 0 and 2 of x:
+// 4^k u, exact (the splice gives 1024 + 4^k u; the 1024, large next to the
+// codes' range, is removed here rather than from the fp32 score sums).
+__device__ __forceinline__ f16x8 uint2x8_to_f16(uint32_t x) {
+  const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+  const u32x4 r = {as_u32(as_f16x2((x & 0x00030003u) | 0x64006400u) + m1024),
+                   as_u32(as_f16x2((x & 0x000C000Cu) | 0x64006400u) + m1024),
+                   as_u32(as_f16x2((x & 0x00300030u) | 0x64006400u) + m1024),
+                   as_u32(as_f16x2((x & 0x00C000C0u) | 0x64006400u) + m1024)};
+  return u4_to_f16x8(r);
+}
+
+// Key offset operand of chunk J: 4^k z for slots (2k, 2k+1) = channels
+// (c0 + k, c0 + k + 8), c0 = 16(J/2) + 4(J%2); zero-point dwords (channels
+// 4i .. 4i+3 in dword i) come by row broadcast.
+template <int J>
+__device__ __forceinline__ f16x8 zp2_key_offsets(uint32_t zw) {
+  constexpr int lo = 4 * (J >> 1) + (J & 1);
+  const uint32_t dl = row_bcast<lo>(zw), dh = row_bcast<lo + 2>(zw);
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t sel = (uint32_t)k | 0x0C00u | ((uint32_t)(4 + k) << 16) | 0x0C000000u;
+    const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+    r[k] = as_u32(as_f16x2((__builtin_amdgcn_perm(dh, dl, sel) << (2 * k)) | 0x64006400u) +
+                  m1024);
+  }
+  return u4_to_f16x8(r);
+}
+
+// Zero points (as fp16, exact) of the slots of block pair PR for channel
+// group G: tokens 0..3 of block 2PR, then of block 2PR+1.
+template <int PR, int G>
+__device__ __forceinline__ f16x8 zp2_value_points(uint32_t zw) {
+  constexpr uint32_t sel = G ? 0x0C0C0301u : 0x0C0C0200u;  // bytes g, 2 + g -> bytes 0, 1
+  u32x4 r;
+  const uint32_t w0 = row_bcast<8 + 4 * PR>(zw), w1 = row_bcast<9 + 4 * PR>(zw);
+  const uint32_t w2 = row_bcast<10 + 4 * PR>(zw), w3 = row_bcast<11 + 4 * PR>(zw);
+  r[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w0, w0, sel), 512.0f, false));
+  r[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w1, w1, sel), 512.0f, false));
+  r[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w2, w2, sel), 512.0f, false));
+  r[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w3, w3, sel), 512.0f, false));
+  return u4_to_f16x8(r);
+}
+
+// Value product of block pair PR: tile j = 4jh + k from the masks of field
+// k over each block's dword jh (and the dword shifted by 8), less 1024
+// exactly (the codes' range 0..3 is small next to the splice's 1024, which
+// would otherwise cost the fp32 sums their low bits).  vb[2 + g] takes the
+// weights times the zero points.
+template <int PR>
+__device__ __forceinline__ void value_pair2c(Softmax &st, f32x4 (&vb)[4], const Group2C &t,
+                                             const f16x8 &pb0, const f16x8 &pb1) {
+  const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+#pragma unroll
+  for (int jh = 0; jh < 2; ++jh) {
+    const uint32_t m0 = t.v[2 * PR][jh], m1 = t.v[2 * PR + 1][jh];
+    const uint32_t n0 = m0 >> 8, n1 = m1 >> 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t mask = 0x00030003u << (2 * k);
+      const u32x4 r = {as_u32(as_f16x2((m0 & mask) | 0x64006400u) + m1024),
+                       as_u32(as_f16x2((n0 & mask) | 0x64006400u) + m1024),
+                       as_u32(as_f16x2((m1 & mask) | 0x64006400u) + m1024),
+                       as_u32(as_f16x2((n1 & mask) | 0x64006400u) + m1024)};
+      const int j = 4 * jh + k;
+      st.o[j] = mfma32(u4_to_f16x8(r), jh ? pb1 : pb0, st.o[j]);
+    }
+  }
+  vb[2] = mfma32(zp2_value_points<PR, 0>(t.zw), pb0, vb[2]);
+  vb[3] = mfma32(zp2_value_points<PR, 1>(t.zw), pb1, vb[3]);
+}
+
+__device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], const Group2C &t,
+                                                const float (&qv)[4][2], uint32_t *qb, int qrd,
+                                                float qk_scale, int lane, int n) {
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    uint32_t hi, lo;
+    split_hi_lo(qv[hh][0] * t.ks[0], qv[hh][1] * t.ks[1], hi, lo);
+    qb[hh * kQbRow + lane] = hi;
+    qb[(4 + hh) * kQbRow + lane] = lo;
+  }
+  f16x8 bq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bq[j] = u4_to_f16x8(*reinterpret_cast<const u32x4 *>(qb + qrd + 4 * j));
+  f32x4 acc[4], ac = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] = mfma32(uint2x8_to_f16(t.k[u][w]), bq[2 * w], acc[u]);
+      acc[u] = mfma32(uint2x8_to_f16(t.k[u][w] >> 8), bq[2 * w + 1], acc[u]);
+    }
+  }
+  ac = mfma32(zp2_key_offsets<0>(t.zw), bq[0], ac);
+  ac = mfma32(zp2_key_offsets<1>(t.zw), bq[1], ac);
+  ac = mfma32(zp2_key_offsets<2>(t.zw), bq[2], ac);
+  ac = mfma32(zp2_key_offsets<3>(t.zw), bq[3], ac);
+  const float off = all_banks(ac[0]);
+  f32x4 s = pack_scores(acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
+  f32x4 p;
+  softmax_update_c(st, vb, s, p);
+  // weights times the V scales of this lane's tokens (channel groups 0, 1);
+  // the value codes carry their per-tile factor, not a per-token one
+  const uint32_t d0[2] = {pack_rne(p[0] * t.vsa[0], p[1] * t.vsa[2]),
+                          pack_rne(p[2] * t.vsb[0], p[3] * t.vsb[2])};
+  const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
+                          pack_rne(p[2] * t.vsb[1], p[3] * t.vsb[3])};
+  value_pair2c<0>(st, vb, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
+  value_pair2c<1>(st, vb, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
+}
+
+template <int DT> struct CompactUnit { using T = Group4C; };
+template <> struct CompactUnit<kInt2Affine> { using T = Group2C; };
+
+// DT: kInt4, kInt4Affine or kInt2Affine
+template <int DT>
 __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
                              int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
                              int pre_id) {
@@ -1126,8 +1301,18 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   *reinterpret_cast<u32x4 *>(&sh.s.q[tid >> 4][8 * (tid & 15)]) = qrow;
   uint32_t *qb = &sh.s.qb[wave][0][0][0];
   __syncthreads();
+  constexpr bool AFF = DT != kInt4;
   float qv[4][2];
-  {
+  if constexpr (DT == kInt2Affine) {
+    // the pair's 2-bit field k = lane % 4 carries 4^k x code: q' / 4^k
+    const int c = 32 * qd + k2_chan(lane);
+    const float f = 1.0f / (float)(1 << (2 * (lane & 3)));
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      qv[hh][0] = (float)sh.s.q[hh][c] * f;
+      qv[hh][1] = (float)sh.s.q[hh][c + 8] * f;
+    }
+  } else {
     const int2 ko = koff_pair(lane);
     const int c = 8 * (lane >> 2);
     // high-nibble slots (odd lanes) carry 16 x code: their q' is taken / 16
@@ -1146,7 +1331,9 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   st.m = dpp_f32<kRowShr + 8, 0x4>(st.m, st.m);
   st.m = dpp_f32<kRowShr + 12, 0x8>(st.m, st.m);
   st.l = n < 4 ? st.l : 0.0f;
-  f32x4 vb[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 vb[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) vb[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nq = kivi_quantized_len(seq_len, a.residual);
   const int n_blocks = nq / kBlock;
   const int blk0 = p * a.part_blocks;
@@ -1157,20 +1344,38 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4C &t, int k) {
+    using Unit = typename CompactUnit<DT>::T;
+    auto load = [&](Unit &t, int k) {
       const int j0 = 4 * (wave + kWaves * k);
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
-      load_group4c<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
+      if constexpr (DT == kInt2Affine) {
+        load_group2c(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h, lane);
+      } else {
+        load_group4c<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + (n >> 2)], h,
+                          lane);
+      }
     };
-    auto compute = [&](Group4C &t, int) {
-      compute_group4c<AFF>(st, vb, t, qv, qb, qrd, a.qk_scale, lane, n);
+    auto compute = [&](Unit &t, int) {
+      if constexpr (DT == kInt2Affine) {
+        compute_group2c(st, vb, t, qv, qb, qrd, a.qk_scale, lane, n);
+      } else {
+        compute_group4c<AFF>(st, vb, t, qv, qb, qrd, a.qk_scale, lane, n);
+      }
     };
-    pipeline<Group4C>(cnt, load, compute);
+    pipeline<Unit>(cnt, load, compute);
   }
-  // the value bias of each channel group, once into its four tiles
+  if constexpr (DT == kInt2Affine) {
+    // tile j = 4g + k: remove the factor 4^k, then the zero points of
+    // channel group g
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] += vb[j >> 2];
+    for (int j = 0; j < 8; ++j)
+      st.o[j] = st.o[j] * (1.0f / (float)(1 << (2 * (j & 3)))) - vb[2 + (j >> 2)];
+  } else {
+    // the value bias of each channel group, once into its four tiles
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] += vb[j >> 2];
+  }
   // back to one head per lane (n < 4): this lane's share of head n's sum
   st.l = bank_sum(st.l);
 }
@@ -1396,11 +1601,16 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     const int nq = kivi_quantized_len(seq_len, a.residual);
     const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
     if (p >= n_main) return;
-    if constexpr (G4) {
+    if constexpr (G4 && DT == kInt2Affine) {
+      // the 2-bit stream rescales its whole output at the end, so the
+      // window follows it
+      stream_int4c<DT>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
+    } else if constexpr (G4) {
       // the window first: its loads and arithmetic overlap the start of the
       // INT4 stream instead of trailing it with nothing else in flight
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
-      stream_int4c<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      stream_int4c<DT>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
       stream_int4<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
@@ -1438,6 +1648,7 @@ template <int DT, bool G4>
 __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
     DecodeArgs a) {
   static_assert(is_kivi(DT), "KIVI-grouped INT4 caches only");
+  static_assert(DT != kInt2Affine || G4, "2-bit codes: compact layout only");
   __shared__ SharedLds sh;
   decode_workgroup<DT, kChannel, kToken, G4>(a, sh);
 }
@@ -1552,6 +1763,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   } else if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, false>), grid, dim3(kThreads), 0,
                        stream, a);
+  } else if (dtype == kInt2Affine) {  // the host admits g <= 4, one query
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt2Affine, true>), grid, dim3(kThreads),
+                       0, stream, a);
   } else if (dtype == kInt4Affine && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, true>), grid, dim3(kThreads),
                        0, stream, a);

@@ -109,20 +109,27 @@ __device__ __forceinline__ int kivi_len(int s, int residual) {
 // floats per (block, head), the last 32 bytes holding the zero points.
 constexpr int kFlushRow = kHeadDim + 8;  // padded LDS row (fp16)
 
-// Affine parameters of a group with minimum lo <= 0 <= maximum hi.
-__device__ __forceinline__ float2 affine_params(float lo, float hi) {
-  const float s = (hi - lo) / 15.0f;
-  const float z = s > 0.0f ? fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f) : 0.0f;
+// Affine parameters of a group with minimum lo <= 0 <= maximum hi, codes
+// 0 .. qmax.
+__device__ __forceinline__ float2 affine_params(float lo, float hi, float qmax) {
+  const float s = (hi - lo) / qmax;
+  const float z = s > 0.0f ? fminf(fmaxf(rintf(-lo / s), 0.0f), qmax) : 0.0f;
   return float2{s, z};
 }
-__device__ __forceinline__ uint32_t quant_affine(float x, float s, float z) {
+__device__ __forceinline__ uint32_t quant_affine(float x, float s, float z, float qmax) {
   if (s == 0.0f) return 0u;
-  const float y = fminf(fmaxf(rintf(x / s) + z, 0.0f), 15.0f);
+  const float y = fminf(fmaxf(rintf(x / s) + z, 0.0f), qmax);
   return (uint32_t)(int)y;
 }
 
-template <bool AFF>
+// DT: kInt4 (symmetric), kInt4Affine or kInt2Affine (2-bit codes: 512-byte
+// chunks, the code layouts of kvq.h).
+template <int DT>
 __device__ void int4_flush(const WriteArgs &a, int bx) {
+  constexpr bool AFF = DT != kInt4;
+  constexpr bool TWO = DT == kInt2Affine;
+  constexpr float kQmax = TWO ? 3.0f : 15.0f;
+  constexpr int kChunk = kivi_chunk_bytes(DT);
   constexpr int kRow = AFF ? 40 : 32;   // floats per (block, head) scale row
   __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
   __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
@@ -231,7 +238,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       if constexpr (AFF) {
         const float mn =
             fminf(fminf(partn[0][tid], partn[1][tid]), fminf(partn[2][tid], partn[3][tid]));
-        const float2 sz = affine_params(mn, mx);
+        const float2 sz = affine_params(mn, mx, kQmax);
         sc[tid] = sz.x;
         zs[tid] = sz.y;
         row[tid & 31] = sz.x;
@@ -242,25 +249,41 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       }
     }
     __syncthreads();
-    // one unit: channels 32cb .. 32cb+31 of token tt, nibble e of dword d is
-    // channel 32cb + 8d + e
+    // one unit: channels 32cb .. 32cb+31 of token tt; INT4: nibble e of dword
+    // d is channel 32cb + 8d + e; 2-bit: bits 2e of dword d are channel
+    // 32cb + 16d + e
     const int tt = tid >> 2, cb = tid & 3;
-    u32x4 out;
+    uint8_t *chunk = a.k_codes + ((size_t)phys_s[tt >> 4] * H + h) * kChunk;
+    if constexpr (TWO) {
+      u32x2 out;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
-      uint32_t word = 0;
+      for (int d = 0; d < 2; ++d) {
+        uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * cb + 8 * d + e;
-        const uint32_t q = AFF ? quant_affine((float)v[e], sc[c], zs[c])
-                               : quant_int((float)v[e], sc[c], -8.0f, 7.0f) & 0xFu;
-        word |= q << (4 * e);
+        for (int e = 0; e < 16; ++e) {
+          const int c = 32 * cb + 16 * d + e;
+          word |= quant_affine((float)x[tt][c], sc[c], zs[c], kQmax) << (2 * e);
+        }
+        out[d] = word;
       }
-      out[d] = word;
+      *reinterpret_cast<u32x2 *>(chunk + 128 * cb + 8 * (tt & 15)) = out;
+    } else {
+      u32x4 out;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * cb + 8 * d + e;
+          const uint32_t q = AFF ? quant_affine((float)v[e], sc[c], zs[c], kQmax)
+                                 : quant_int((float)v[e], sc[c], -8.0f, 7.0f) & 0xFu;
+          word |= q << (4 * e);
+        }
+        out[d] = word;
+      }
+      *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
     }
-    uint8_t *chunk = a.k_codes + ((size_t)phys_s[tt >> 4] * H + h) * 1024;
-    *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
   } else {
     // V scales: per token, max over each 64-channel half of |V| / 7
     // (affine: the half's minimum and maximum, each starting from 0)
@@ -286,7 +309,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
         const int k = 2 * (tt & 15) + (qq >> 1);  // [slot][channel group]
         float *row = a.v_scales + ((size_t)phys_s[tt >> 4] * H + h) * kRow;
         if constexpr (AFF) {
-          const float2 sz = affine_params(mn, m);
+          const float2 sz = affine_params(mn, m, kQmax);
           sc[2 * tt + (qq >> 1)] = sz.x;
           zs[2 * tt + (qq >> 1)] = sz.y;
           row[k] = sz.x;
@@ -309,29 +332,48 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
     // 2(j&1) + (e>>1) + 4(e&1)
     const int ub = tid >> 6, u = tid & 63;
     const int m = u & 15, quad = u >> 4;
-    u32x4 out = {0u, 0u, 0u, 0u};
+    uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * kChunk;
+    if constexpr (TWO) {
+      // 2-bit: dword j>>2, byte pos(e) = 0, 2, 1, 3 of token e, bits 2(j&3)
+      u32x2 out = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tt = 16 * ub + 4 * quad + e;
-      const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
-      const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const int tt = 16 * ub + 4 * quad + e;
+        const int pos = (e == 1) ? 2 : (e == 2 ? 1 : e);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = 16 * j + m;
-        const uint32_t q = AFF ? quant_affine((float)x[tt][c], j < 4 ? s0 : s1, j < 4 ? z0 : z1)
-                               : quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
-        const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
-        out[j >> 1] |= q << (4 * p);
+        for (int j = 0; j < 8; ++j) {
+          const int c = 16 * j + m;
+          const int g = j >> 2;
+          const uint32_t q = quant_affine((float)x[tt][c], sc[2 * tt + g], zs[2 * tt + g], kQmax);
+          out[j >> 2] |= q << (8 * pos + 2 * (j & 3));
+        }
       }
+      *reinterpret_cast<u32x2 *>(chunk + 8 * u) = out;
+    } else {
+      u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tt = 16 * ub + 4 * quad + e;
+        const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
+        const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = 16 * j + m;
+          const uint32_t q =
+              AFF ? quant_affine((float)x[tt][c], j < 4 ? s0 : s1, j < 4 ? z0 : z1, kQmax)
+                  : quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
+          const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
+          out[j >> 1] |= q << (4 * p);
+        }
+      }
+      *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;
     }
-    uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * 1024;
-    *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;
   }
 }
 
-template <bool AFF>
+template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
-  int4_flush<AFF>(a, blockIdx.x);
+  int4_flush<DT>(a, blockIdx.x);
 }
 
 // Append the new tokens that stay fp16 to the ring.
@@ -366,10 +408,10 @@ __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
 // append.  Only for calls that add at most one token per row: the appended
 // token is then fewer than R + G positions after any token the flush reads
 // from the ring, so its ring slot is never one of them.
-template <bool AFF>
+template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a, int groups) {
   if ((int)blockIdx.x < 2 * groups) {
-    int4_flush<AFF>(a, blockIdx.x);
+    int4_flush<DT>(a, blockIdx.x);
   } else if (threadIdx.x < 64) {
     append_token(a, blockIdx.x - 2 * groups, blockIdx.y, blockIdx.z, threadIdx.x);
   }
@@ -396,25 +438,30 @@ hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_write_int4(const WriteArgs &a, bool affine, int batch, int max_new,
+hipError_t launch_write_int4(const WriteArgs &a, int dtype, int batch, int max_new,
                              int max_flush_groups, hipStream_t stream) {
   if (max_new == 1 && max_flush_groups > 0) {
     const dim3 grid(2 * max_flush_groups + 1, a.num_kv_heads, batch);
-    if (affine) {
-      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<true>, grid, dim3(256), 0, stream, a,
-                         max_flush_groups);
+    if (dtype == kInt2Affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<kInt2Affine>, grid, dim3(256), 0, stream,
+                         a, max_flush_groups);
+    } else if (dtype == kInt4Affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<kInt4Affine>, grid, dim3(256), 0, stream,
+                         a, max_flush_groups);
     } else {
-      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<false>, grid, dim3(256), 0, stream, a,
+      hipLaunchKernelGGL(kvq_int4_flush_append_kernel<kInt4>, grid, dim3(256), 0, stream, a,
                          max_flush_groups);
     }
     return hipGetLastError();
   }
   if (max_flush_groups > 0) {
     const dim3 grid(2 * max_flush_groups, a.num_kv_heads, batch);
-    if (affine) {
-      hipLaunchKernelGGL(kvq_int4_flush_kernel<true>, grid, dim3(256), 0, stream, a);
+    if (dtype == kInt2Affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_kernel<kInt2Affine>, grid, dim3(256), 0, stream, a);
+    } else if (dtype == kInt4Affine) {
+      hipLaunchKernelGGL(kvq_int4_flush_kernel<kInt4Affine>, grid, dim3(256), 0, stream, a);
     } else {
-      hipLaunchKernelGGL(kvq_int4_flush_kernel<false>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(kvq_int4_flush_kernel<kInt4>, grid, dim3(256), 0, stream, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

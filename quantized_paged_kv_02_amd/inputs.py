@@ -35,7 +35,8 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     seq: int | tuple            # fixed length, or (lo, hi) uniform inclusive
-    dtype: str                  # "int8" | "fp8" | "fp8e5m2" | "int4" | "int4-affine" | "fp16"
+    dtype: str                  # "int8" | "fp8" | "fp8e5m2" | "int4" | "int4-affine" |
+                                # "int2-affine" | "fp16"
     k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16)
     v_gran: str
     table: str = "identity"     # "identity" | "shuffled"
@@ -87,6 +88,12 @@ WORKLOADS = {
         channel_outliers=(8, 10.0, "k"), shift=(0.5, "v"),
         description="KIVI INT4 affine: 32 layers, 32/8 heads, batch 16, seq 32768, K per-channel, "
                     "V per-token, group 64, zero points, fp16 residual 128; V ~ N(0.5, 1)"),
+    # the same with 2-bit codes
+    "kivi-int2-affine": Workload(
+        "kivi-int2-affine", 32, 16, 32, 8, 32768, "int2-affine", "channel", "token",
+        channel_outliers=(8, 10.0, "k"), shift=(0.5, "v"),
+        description="KIVI 2-bit affine: 32 layers, 32/8 heads, batch 16, seq 32768, K "
+                    "per-channel, V per-token, group 64, zero points, fp16 residual 128"),
     # unquantized baselines of the INT8 comparison ([intelli] §5): the INT8
     # workloads' shapes and inputs with an FP16 cache
     "llama2-7b-fp16": Workload(

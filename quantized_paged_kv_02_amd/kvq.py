@@ -17,10 +17,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2 = 1, 2, 3, 4, 5, 6
+INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2, INT2_AFFINE = 1, 2, 3, 4, 5, 6, 7
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
 DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16,
-          "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2}
+          "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2, "int2-affine": INT2_AFFINE}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
          "token": PER_TOKEN,
          "none": PER_TENSOR}   # FP16 cache: no scales, the field is ignored
@@ -163,9 +163,10 @@ def alloc_cache(layout: Layout, ring_rows: int = 0, device="cuda",
     """Allocate one layer's pool.  Static scales (per tensor/head/channel)
     are copied in from ``k_static``/``v_static``."""
     nb, h = layout.num_blocks, layout.num_kv_heads
-    if layout.dtype in (INT4, INT4_AFFINE):
-        k_codes = torch.empty((nb, h, 1024), dtype=torch.uint8, device=device)
-        v_codes = torch.empty((nb, h, 1024), dtype=torch.uint8, device=device)
+    if layout.dtype in (INT4, INT4_AFFINE, INT2_AFFINE):
+        cb = 512 if layout.dtype == INT2_AFFINE else 1024   # code bytes per (block, head)
+        k_codes = torch.empty((nb, h, cb), dtype=torch.uint8, device=device)
+        v_codes = torch.empty((nb, h, cb), dtype=torch.uint8, device=device)
         if layout.dtype == INT4:
             k_scales = torch.empty((nb, h, 32), dtype=torch.float32, device=device)
             v_scales = torch.empty((nb, h, 16, 2), dtype=torch.float32, device=device)

@@ -38,13 +38,16 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
     total = b * hq * d * 2 + b * hq * d * 4          # q fp16 in, out fp32
     uniform_scales = 0
     for s in (int(x) for x in lens):
-        if dtype in ("int4", "int4-affine"):
+        if dtype in ("int4", "int4-affine", "int2-affine"):
             nq = kivi_quantized_len(s, residual)
             r = s - nq
-            total += hkv * nq * d                     # K and V nibbles: 2 x nq x d / 2
+            if dtype == "int2-affine":
+                total += hkv * nq * d // 2            # K and V 2-bit codes: 2 x nq x d / 4
+            else:
+                total += hkv * nq * d                 # K and V nibbles: 2 x nq x d / 2
             total += hkv * (nq // GROUP) * d * 4      # K per-channel group scales
             total += hkv * nq * 2 * 4                 # V per-token scales, 2 groups
-            if dtype == "int4-affine":
+            if dtype != "int4":
                 total += hkv * (nq // GROUP) * d      # K zero points, 1 byte each
                 total += hkv * nq * 2                 # V zero points
             total += hkv * r * d * 2 * 2              # fp16 K and V residual
@@ -58,7 +61,7 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
                 if gran == "token":
                     total += hkv * s * 4
             total += ((s + BLOCK - 1) // BLOCK) * 4
-    if dtype not in ("int4", "int4-affine", "fp16"):
+    if dtype not in ("int4", "int4-affine", "int2-affine", "fp16"):
         for gran in (k_gran, v_gran):
             if gran != "token":
                 uniform_scales += _scale_bytes_uniform(gran, hkv)

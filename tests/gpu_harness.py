@@ -19,6 +19,7 @@ from tests import layout_view as lv
 
 ATOL = 2e-3
 RTOL = 1e-2
+KIVI = ("int4", "int4-affine", "int2-affine")   # KIVI-grouped caches
 
 
 @dataclass
@@ -58,7 +59,7 @@ def fill_garbage(cache):
     if cache.k_resid is not None:
         cache.k_resid.fill_(float("nan"))
         cache.v_resid.fill_(float("nan"))
-    int4 = cache.layout.dtype in (3, 5)
+    int4 = cache.layout.dtype in (3, 5, 7)
     if int4 or cache.layout.k_gran == 3:
         cache.k_scales.fill_(float("nan"))
     if int4 or cache.layout.v_gran == 3:
@@ -90,7 +91,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     prefill_k = [k[:max(int(s) - 1, 0)] for k, s in zip(ks, lens)]
     prefill_v = [v[:max(int(s) - 1, 0)] for v, s in zip(vs, lens)]
     k_static = v_static = None
-    if not w.dtype.startswith("int4"):
+    if w.dtype not in KIVI:
         k_static = _static(w, w.k_gran, [t for t in prefill_k if len(t)] or ks, w.dtype)
         v_static = _static(w, w.v_gran, [t for t in prefill_v if len(t)] or vs, w.dtype)
     cache = kvq.alloc_cache(layout, ring_rows=b, device=device,
@@ -187,9 +188,10 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
     kb, vb = res.k[r], res.v[r]
     row = res.table[r]
     p = res.pools
-    if w.dtype.startswith("int4"):
-        affine = w.dtype == "int4-affine"
-        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len, affine=affine)
+    if w.dtype in KIVI:
+        affine = w.dtype != "int4"
+        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len, affine=affine,
+                                  bits=2 if w.dtype == "int2-affine" else 4)
         nq = kv["nq"]
         if check_codes:
             assert np.array_equal(lv.logical_codes(p["k_codes"], row, nq, "k", w.dtype),

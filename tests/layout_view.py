@@ -31,6 +31,15 @@ K16_OFF = (1024 * ((C_IDX >> 3) & 3) + 256 * (C_IDX >> 5) + 16 * S_IDX + 2 * (C_
 V16_OFF = (1024 * (C_IDX >> 5) + 256 * (S_IDX >> 2) + 16 * (C_IDX & 15)
            + 8 * ((C_IDX >> 4) & 1) + 2 * (S_IDX & 3)) // 2
 
+# 2-bit chunks (512 bytes per (block, head)): byte offset and bit position
+K2_BYTE = 128 * (C_IDX >> 5) + 8 * S_IDX + ((C_IDX & 31) >> 2)
+K2_BIT = np.broadcast_to(2 * (C_IDX & 3), (16, 128))
+_POS = np.array([0, 2, 1, 3])[S_IDX & 3]
+V2_BYTE = 8 * ((C_IDX & 15) + 16 * (S_IDX >> 2)) + 4 * ((C_IDX >> 4) >> 2) + _POS
+V2_BIT = np.broadcast_to(2 * ((C_IDX >> 4) & 3), (16, 128))
+assert sorted((4 * K2_BYTE + K2_BIT // 2).ravel().tolist()) == list(range(2048))
+assert sorted((4 * V2_BYTE + V2_BIT // 2).ravel().tolist()) == list(range(2048))
+
 assert sorted(K16_OFF.ravel().tolist()) == list(range(2048))
 assert sorted(V16_OFF.ravel().tolist()) == list(range(2048))
 assert sorted(K8_OFF.ravel().tolist()) == list(range(2048))
@@ -49,6 +58,14 @@ def chunk16(pool_chunk, which):
     """[2048] fp16 chunk -> [16 slots, 128 channels] fp16 values."""
     off = K16_OFF if which == "k" else V16_OFF
     return np.asarray(pool_chunk)[off]
+
+
+def chunk2(pool_chunk, which):
+    """[512] uint8 chunk -> [16, 128] uint8 2-bit codes in [0, 3]."""
+    byte = K2_BYTE if which == "k" else V2_BYTE
+    bit = K2_BIT if which == "k" else V2_BIT
+    b = np.asarray(pool_chunk).astype(np.int64)[byte]
+    return ((b >> bit) & 3).astype(np.uint8)
 
 
 def chunk4(pool_chunk, which, signed=True):
@@ -78,6 +95,8 @@ def logical_codes(pool, table_row, n_tokens, which, dtype):
                 c = chunk4(pool[phys, hh], which)
             elif dtype == "int4-affine":
                 c = chunk4(pool[phys, hh], which, signed=False)
+            elif dtype == "int2-affine":
+                c = chunk2(pool[phys, hh], which)
             elif dtype == "fp16":
                 c = chunk16(pool[phys, hh], which)
             else:

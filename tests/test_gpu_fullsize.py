@@ -33,7 +33,8 @@ def _sample_rows(lens, seed):
 @pytest.mark.timeout(400)
 @pytest.mark.parametrize("name", ["llama2-7b", "llama3-8b-gqa", "kivi-int4", "llama3-70b-int8",
                                   "llama3-70b-fp8", "llama2-7b-fp16", "llama3-70b-fp16",
-                                  "kivi-int4-affine", "llama3-70b-fp8e5m2"])
+                                  "kivi-int4-affine", "llama3-70b-fp8e5m2",
+                                  "kivi-int2-affine"])
 def test_fullsize_layer(name):
     w = W[name]
     lens = inputs.seq_lens(w)

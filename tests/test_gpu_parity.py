@@ -101,7 +101,8 @@ def test_int8_chunked_writes(chunks):
 
 @pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("int4", "channel", "token"),
                                          ("fp16", "none", "none"),
-                                         ("int4-affine", "channel", "token")])
+                                         ("int4-affine", "channel", "token"),
+                                         ("int2-affine", "channel", "token")])
 def test_repeated_split_launches_on_one_workspace(dtype, kg, vg):
     # many partitions per row; launches that reuse one workspace (partials
     # left by the previous launch) must agree bit for bit
@@ -175,4 +176,38 @@ def test_int4_affine_chunked_writes(chunks):
 def test_int4_affine_residual_64_and_constant_groups():
     # residual window 64; no outliers and V without shift (zero points near 8)
     w = _small("int4-affine", "channel", "token", residual_len=64, table="shuffled")
+    check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))
+
+
+# --- 2-bit affine KIVI groups (query groups of at most four)
+
+def _two_bit(**kw):
+    kw.setdefault("channel_outliers", (8, 10.0, "k"))
+    return _small("int2-affine", "channel", "token", shift=(0.5, "v"), **kw)
+
+
+@pytest.mark.parametrize("lens,split", [([100, 192, 777], 64), ([1, 128, 129], 0),
+                                        ([191, 192, 193], 128), ([640, 64, 2000], 256),
+                                        ([0, 255, 0], 0)])
+def test_int2_affine(lens, split):
+    res = run_case(_two_bit(table="shuffled"), lens, split_tokens=split, decode_twice=True)
+    check_rows(res, rows=[r for r, s in enumerate(lens) if s > 0])
+    for r, s in enumerate(lens):
+        if s == 0:
+            assert np.all(res.out[r] == 0)
+    assert np.array_equal(res.out, res.out2)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (4, 1)])
+def test_int2_affine_group_sizes(hq, hkv):
+    check_rows(run_case(_two_bit(hq=hq, hkv=hkv), [300, 700, 192], split_tokens=128))
+
+
+@pytest.mark.parametrize("chunks", [3, 7])
+def test_int2_affine_chunked_writes(chunks):
+    check_rows(run_case(_two_bit(), [300, 1000, 450], chunks=chunks, split_tokens=64))
+
+
+def test_int2_affine_residual_64():
+    w = _small("int2-affine", "channel", "token", residual_len=64, table="shuffled")
     check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))

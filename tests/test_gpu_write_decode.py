@@ -32,6 +32,7 @@ CASES = [
     ("int4", "channel", "token", "shuffled"),
     ("fp16", "none", "none", "shuffled"),
     ("int4-affine", "channel", "token", "shuffled"),
+    ("int2-affine", "channel", "token", "identity"),
     ("fp8e5m2", "channel", "token", "shuffled"),
     ("fp8e5m2", "tensor", "head", "identity"),
 ]
@@ -40,8 +41,9 @@ LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2]]
 
 
 def _w(dtype, kg, vg, table):
-    extra = {"channel_outliers": (8, 10.0, "k")} if dtype.startswith("int4") else {}
-    if dtype == "int4-affine":
+    extra = {"channel_outliers": (8, 10.0, "k")} if dtype in ("int4", "int4-affine",
+                                                              "int2-affine") else {}
+    if dtype in ("int4-affine", "int2-affine"):
         extra["shift"] = (0.5, "v")
     return inputs.scaled_down(W["tiny"], name=f"wd-{dtype}-{kg}-{vg}", batch=4,
                               num_q_heads=8, num_kv_heads=2, dtype=dtype, k_gran=kg,
