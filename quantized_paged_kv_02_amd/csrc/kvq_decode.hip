@@ -48,6 +48,13 @@
 // and latency comparison) runs through the same skeleton: its layout puts
 // each lane's fp16 operands in 16-byte runs, so a pair of blocks is sixteen
 // loads and the matrix-core products with no conversion and no scales.
+//
+// Further formats on the same skeleton: FP8 E5M2 (codes are the upper byte
+// of an fp16; scale-derived fp16 operands carry an exact 2^7), affine INT4
+// and 2-bit KIVI groups ([oh-bug] "量化不是简单'截断精度'": the zero points
+// enter through offset and bias operands of the matrix products).  Several
+// query tokens per row use the score product's columns for (query, head)
+// pairs and mask the last block pairs per column.
 #include "kvq_args.h"
 #include "kvq_device.h"
 #include "kvq_quant.h"

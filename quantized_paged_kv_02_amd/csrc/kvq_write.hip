@@ -1,4 +1,6 @@
-// Quantize-on-write kernels (and the plain scatter of an FP16 cache).
+// Quantize-on-write kernels (and the plain scatter of an FP16 cache):
+// INT8 / FP8 (E4M3, E5M2) per token vector, KIVI groups (INT4 symmetric,
+// INT4 and 2-bit affine).
 //
 // INT8 / FP8: one wavefront per (new token, KV head) quantizes the token's K
 // and V vectors (128 values each, two per lane; the rule is in kvq_quant.h)
