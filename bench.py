@@ -166,6 +166,9 @@ class Bench:
         self.max_len = int(lens.max())
         self.layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads,
                                       w.num_kv_heads, nb, table.shape[1], 0, w.residual_len)
+        # the partition length for the rows' real lengths (known here, as
+        # in a serving scheduler); equal-length batches get the automatic plan
+        self.layout.split_tokens = kvq.plan_split_tokens(self.layout, lens)
         b = w.batch
         self.calibrate = None
         self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)
@@ -404,6 +407,7 @@ def run(args):
                      if args.separate
                      else "per layer: kvq_write_decode (1 token/row appended, then decoded)"),
             "launch": "hip graph" if graph is not None else "eager",
+            "split_tokens": int(bench.layout.split_tokens),
             "algorithmic_bytes_per_step": step_bytes,
         },
         "roofline": {

@@ -296,6 +296,22 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
                             float *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* Partition length for a batch whose row lengths the caller knows on the
+ * host (a serving scheduler does): the split_tokens value (tokens, a
+ * multiple of 16; of 64 for INT4 caches) that the automatic plan's search
+ * picks over the real lengths instead of taking every row to be
+ * max_blocks_per_seq blocks long, raised to at least half of each
+ * resident workgroup's balanced share of the blocks.  Equal lengths give
+ * the automatic plan back; unequal ones get fewer, longer partitions, so
+ * the short rows' workgroups leave less of the chip idle.  Set
+ * layout->split_tokens to it before sizing the workspace and decoding.  host_seq_lens: HOST int32 [batch], the lengths the decode
+ * will see.  Returns the length (> 0) or a negative kvq_status
+ * (KVQ_ERR_INVALID_ARG: NULL lengths with batch > 0, a negative length;
+ * KVQ_ERR_CAPACITY: a length beyond max_blocks_per_seq * 16; layout
+ * errors as kvq_validate).  Host only, no HIP call. */
+int32_t kvq_plan_split_tokens(const kvq_layout *layout, const int32_t *host_seq_lens,
+                              int32_t batch);
+
 /* Decode attention for several new query tokens per row (speculative
  * verification of draft tokens, or a chunk of prefill, over the cache; the
  * whole-history read of [oh-bug] section "为什么长上下文更需要 KV Cache

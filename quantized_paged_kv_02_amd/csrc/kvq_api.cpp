@@ -87,43 +87,74 @@ struct Plan {
   int slots;        // partial slots per (row, query head)
 };
 
+// Blocks of a row of length s that the decode streams.
+int row_blocks(const kvq_layout *L, int32_t s) {
+  return kivi(L) ? kivi_len(s, L->residual_len) / kBlock : (s + kBlock - 1) / kBlock;
+}
+
+// Partition length (blocks) that minimises (dispatch rounds) x (blocks per
+// workgroup + fixed cost): a launch whose last round is nearly empty wastes
+// a whole workgroup time, and the longest workgroup sets the round's time.
+// With host_lens the workgroup count is the rows' own partitions; without,
+// every row is taken to be max_blocks long.
+int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
+                       const int32_t *host_lens) {
+  const bool int4 = kivi(L);
+  // a workgroup's four waves take units of 2 blocks (INT8/FP8) or one
+  // 64-token group (INT4) in turn; partitions give each wave whole units
+  const int quantum = int4 ? 16 : 8;
+  const long resident =
+      kCUs * kvq::decode_wg_per_cu(L->dtype, kvq::decode_scale_kind(L->k_gran),
+                                   kvq::decode_scale_kind(L->v_gran));
+  const long overhead = int4                       ? kWgOverheadInt4
+                        : L->dtype == KVQ_FP16 ? kWgOverheadF16
+                                               : kWgOverheadQ8;
+  const long top = max_blocks > quantum ? max_blocks : quantum;
+  long best_t = -1;
+  int pb = quantum;
+  for (long c = quantum; c <= top + quantum - 1; c += quantum) {
+    const long parts = (max_blocks + c - 1) / c;
+    if (parts > 4096) continue;
+    long wgs = 0;
+    if (host_lens != nullptr) {
+      for (int32_t b = 0; b < batch; ++b) {
+        const long nb = row_blocks(L, host_lens[b]);
+        long pr = (nb + c - 1) / c;
+        if (int4 && host_lens[b] > 0 && pr < 1) pr = 1;  // the fp16 window alone
+        wgs += pr;
+      }
+      wgs *= L->num_kv_heads;
+    } else {
+      wgs = (long)batch * L->num_kv_heads * (parts > 0 ? parts : 1);
+    }
+    const long rounds = (wgs + resident - 1) / resident;
+    const long t = (rounds > 0 ? rounds : 1) * (c + overhead);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      pb = (int)c;
+    }
+  }
+  if (host_lens != nullptr) {
+    // With real lengths the model can favour thousands of short workgroups
+    // whose partials, merges and dispatch it prices too low: keep
+    // partitions at least half of a balanced share of the work.
+    long work = 0;
+    for (int32_t b = 0; b < batch; ++b) work += row_blocks(L, host_lens[b]);
+    work *= L->num_kv_heads;
+    long floor_c = (work + 2 * resident - 1) / (2 * resident);
+    floor_c = (floor_c + quantum - 1) / quantum * quantum;
+    if (floor_c > top) floor_c = (top + quantum - 1) / quantum * quantum;
+    if (pb < floor_c) pb = (int)floor_c;
+  }
+  return pb;
+}
+
 Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
   Plan p{};
   const bool int4 = kivi(L);
-  const int blocks = int4 ? kivi_len(max_seq_len, L->residual_len) / kBlock
-                          : (max_seq_len + kBlock - 1) / kBlock;
-  // a workgroup's four waves take units of 2 blocks (INT8/FP8) or one
-  // 64-token group (INT4) in turn; automatic partitions give each wave
-  // whole units
-  const int quantum = int4 ? 16 : 8;
-  int pb;
-  if (L->split_tokens > 0) {
-    pb = L->split_tokens / kBlock;
-  } else {
-    // Pick the partition length that minimises (dispatch rounds) x (blocks
-    // per workgroup + fixed cost): a launch whose last round is nearly
-    // empty wastes a whole workgroup time.
-    const long units = (long)batch * L->num_kv_heads;
-    const long resident =
-        kCUs * kvq::decode_wg_per_cu(L->dtype, kvq::decode_scale_kind(L->k_gran),
-                                     kvq::decode_scale_kind(L->v_gran));
-    const long overhead = int4                       ? kWgOverheadInt4
-                          : L->dtype == KVQ_FP16 ? kWgOverheadF16
-                                                 : kWgOverheadQ8;
-    const long top = blocks > quantum ? blocks : quantum;
-    long best_t = -1;
-    pb = quantum;
-    for (long c = quantum; c <= top + quantum - 1; c += quantum) {
-      const long parts = (blocks + c - 1) / c;
-      if (parts > 4096) continue;
-      const long rounds = (units * (parts > 0 ? parts : 1) + resident - 1) / resident;
-      const long t = rounds * (c + overhead);
-      if (best_t < 0 || t < best_t) {
-        best_t = t;
-        pb = (int)c;
-      }
-    }
-  }
+  const int blocks = row_blocks(L, max_seq_len);
+  int pb = L->split_tokens > 0 ? L->split_tokens / kBlock
+                               : choose_part_blocks(L, batch, blocks, nullptr);
   if (pb < (int4 ? 4 : 1)) pb = int4 ? 4 : 1;
   p.part_blocks = pb;
   p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 1;  // >= 1: empty rows, INT4 rings
@@ -354,6 +385,23 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
       kvq::launch_write_int4(w, layout->dtype, batch, 1, 2, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
   return decode_launch(layout, a, batch, stream);
+}
+
+// ---- partition planning from host-known lengths ---------------------------------
+
+int32_t kvq_plan_split_tokens(const kvq_layout *layout, const int32_t *host_seq_lens,
+                              int32_t batch) {
+  const kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || (batch > 0 && host_seq_lens == nullptr)) return KVQ_ERR_INVALID_ARG;
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (host_seq_lens[b] < 0) return KVQ_ERR_INVALID_ARG;
+    if (host_seq_lens[b] > max_len) max_len = host_seq_lens[b];
+  }
+  if ((int64_t)max_len > (int64_t)layout->max_blocks_per_seq * kBlock) return KVQ_ERR_CAPACITY;
+  const int pb = choose_part_blocks(layout, batch, row_blocks(layout, max_len), host_seq_lens);
+  return pb * kBlock;
 }
 
 // ---- several query tokens per row ----------------------------------------------

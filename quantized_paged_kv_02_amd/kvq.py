@@ -32,7 +32,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
 EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
             "kvq_write", "kvq_paged_decode", "kvq_write_decode",
             "kvq_calibrate_workspace_bytes", "kvq_calibrate",
-            "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq")
+            "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq",
+            "kvq_plan_split_tokens")
 
 
 class Layout(ctypes.Structure):
@@ -93,6 +94,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_write_decode.restype = I32
     lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
                                      P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_plan_split_tokens.restype = I32
+    lib.kvq_plan_split_tokens.argtypes = [ctypes.POINTER(Layout), P, I32]
     lib.kvq_paged_decode_mq_workspace_bytes.restype = SZ
     lib.kvq_paged_decode_mq_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32, I32, I32]
     lib.kvq_paged_decode_mq.restype = I32
@@ -298,3 +301,15 @@ def paged_decode_mq(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
                                  _stream_handle(stream))
     if st != 0:
         raise KvqError(st, "kvq_paged_decode_mq")
+
+
+def plan_split_tokens(layout: Layout, host_seq_lens) -> int:
+    """kvq_plan_split_tokens: the partition length for these host-known row
+    lengths (see kvq.h); raises on error."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(host_seq_lens, dtype=np.int32))
+    r = LIB.kvq_plan_split_tokens(ctypes.byref(layout),
+                                  lens.ctypes.data if lens.size else None, int(lens.size))
+    if r <= 0:
+        raise KvqError(r, "kvq_plan_split_tokens")
+    return int(r)

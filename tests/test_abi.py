@@ -283,3 +283,25 @@ def test_int2_affine_rules():
     assert _decode_mq(_layout(**base), _cache(int4=True), nq=2) == UNS
     assert kvq.paged_decode_mq_workspace_bytes(_layout(**base), 2, 2, 1000) == 0
     assert _calibrate(_layout(**base)) == UNS
+
+
+def test_plan_split_tokens():
+    lay = _layout()                                              # INT8, 16 blocks per row max
+    lens = [256, 256]
+    sp = kvq.plan_split_tokens(lay, lens)
+    assert sp > 0 and sp % 16 == 0
+    # equal lengths: the automatic plan's workspace
+    lay2 = _layout(split_tokens=sp)
+    assert kvq.decode_workspace_bytes(lay2, 2, 256) == kvq.decode_workspace_bytes(lay, 2, 256)
+    # INT4: a multiple of 64 tokens
+    lay4 = _layout(dtype=3, k_gran=2, v_gran=3, max_blocks_per_seq=64)
+    assert kvq.plan_split_tokens(lay4, [1000, 200]) % 64 == 0
+    lib = kvq.LIB
+    assert lib.kvq_plan_split_tokens(ctypes.byref(lay), None, 2) == INV
+    import numpy as np
+    neg = np.array([5, -1], np.int32)
+    assert lib.kvq_plan_split_tokens(ctypes.byref(lay), neg.ctypes.data, 2) == INV
+    big = np.array([16 * 16 + 1], np.int32)
+    assert lib.kvq_plan_split_tokens(ctypes.byref(lay), big.ctypes.data, 1) == CAP
+    assert lib.kvq_plan_split_tokens(ctypes.byref(lay), None, 0) > 0
+    assert lib.kvq_plan_split_tokens(ctypes.byref(_layout(head_dim=64)), None, 0) == UNS

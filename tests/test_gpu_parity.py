@@ -211,3 +211,19 @@ def test_int2_affine_chunked_writes(chunks):
 def test_int2_affine_residual_64():
     w = _small("int2-affine", "channel", "token", residual_len=64, table="shuffled")
     check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))
+
+
+@pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("fp8", "head", "head"),
+                                         ("int4", "channel", "token")])
+def test_planned_split_on_ragged_rows(dtype, kg, vg):
+    # the host planner's partition length for unequal rows
+    from quantized_paged_kv_02_amd import kvq
+    extra = {"channel_outliers": (8, 10.0, "k")} if dtype == "int4" else {}
+    w = _small(dtype, kg, vg, table="shuffled", **extra)
+    lens = np.array([17, 300, 1000, 5, 64, 777, 2000, 130], np.int32)
+    table, nb = inputs.block_tables(w, lens)
+    lay = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads, w.num_kv_heads, nb,
+                          table.shape[1], 0, w.residual_len)
+    split = kvq.plan_split_tokens(lay, lens)
+    res = run_case(w, lens, split_tokens=split, table=table)
+    check_rows(res)
