@@ -376,7 +376,10 @@ def run(args):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         ent = t.get(w.name) if not args.n_query else None   # decode launches only
-        if ent and t.get("kernel_source_hash") == kernel_source_hash():
+        # counters taken with other kernels or another partition length
+        # describe other launches
+        if (ent and t.get("kernel_source_hash") == kernel_source_hash()
+                and ent.get("split_tokens") == int(bench.layout.split_tokens)):
             traffic = ent.get("bytes_per_launch")
 
     step_gbs = step_bytes / (ms * 1e-3) / 1e9

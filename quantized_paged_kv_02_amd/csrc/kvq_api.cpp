@@ -21,6 +21,9 @@ constexpr long kCUs = 256;
 constexpr long kWgOverheadInt4 = 16;
 constexpr long kWgOverheadQ8 = 8;
 constexpr long kWgOverheadF16 = 4;  // a block streams twice the bytes of INT8
+// Rows of at least this many blocks make a launch long enough that HBM
+// efficiency, not fixed latency, decides the plan.
+constexpr long kStreamMinBlocks = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -92,11 +95,13 @@ int row_blocks(const kvq_layout *L, int32_t s) {
   return kivi(L) ? kivi_len(s, L->residual_len) / kBlock : (s + kBlock - 1) / kBlock;
 }
 
-// Partition length (blocks) that minimises (dispatch rounds) x (blocks per
-// workgroup + fixed cost): a launch whose last round is nearly empty wastes
-// a whole workgroup time, and the longest workgroup sets the round's time.
-// With host_lens the workgroup count is the rows' own partitions; without,
-// every row is taken to be max_blocks long.
+// Partition length (blocks).  Long rows: the shortest length that keeps
+// the launch to one workgroup per CU.  Short rows (the launch is bound by
+// fixed latency): the length that minimises (dispatch rounds) x (blocks
+// per workgroup + fixed cost), where a launch whose last round is nearly
+// empty wastes a whole workgroup time and the longest workgroup sets the
+// round's time.  With host_lens the workgroup count is the rows' own
+// partitions; without, every row is taken to be max_blocks long.
 int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
                        const int32_t *host_lens) {
   const bool int4 = kivi(L);
@@ -110,11 +115,8 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
                         : L->dtype == KVQ_FP16 ? kWgOverheadF16
                                                : kWgOverheadQ8;
   const long top = max_blocks > quantum ? max_blocks : quantum;
-  long best_t = -1;
-  int pb = quantum;
-  for (long c = quantum; c <= top + quantum - 1; c += quantum) {
-    const long parts = (max_blocks + c - 1) / c;
-    if (parts > 4096) continue;
+  // workgroups of a launch whose partitions hold c blocks
+  auto workgroups = [&](long c) {
     long wgs = 0;
     if (host_lens != nullptr) {
       for (int32_t b = 0; b < batch; ++b) {
@@ -123,10 +125,29 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
         if (int4 && host_lens[b] > 0 && pr < 1) pr = 1;  // the fp16 window alone
         wgs += pr;
       }
-      wgs *= L->num_kv_heads;
-    } else {
-      wgs = (long)batch * L->num_kv_heads * (parts > 0 ? parts : 1);
+      return wgs * L->num_kv_heads;
     }
+    const long parts = (max_blocks + c - 1) / c;
+    return (long)batch * L->num_kv_heads * (parts > 0 ? parts : 1);
+  };
+  if (L->dtype != KVQ_INT2_AFFINE && top >= kStreamMinBlocks) {
+    // Long rows, HBM-bound formats: at most one workgroup per CU (the
+    // dispatcher spreads up to one per CU before it doubles any), with the
+    // shortest partitions that allow it.  Measured on the shapes of long
+    // decode: more resident workgroups per CU contend for HBM and lose
+    // 5-9 % (INT4 and FP8, 2-4 workgroups per CU), and a single partition
+    // per row also drops the merge launch.  With more (row, head) pairs
+    // than CUs, one partition per row.
+    for (long c = quantum; c < top; c += quantum)
+      if (workgroups(c) <= kCUs) return (int)c;
+    return (int)((top + quantum - 1) / quantum * quantum);
+  }
+  long best_t = -1;
+  int pb = quantum;
+  for (long c = quantum; c <= top + quantum - 1; c += quantum) {
+    const long parts = (max_blocks + c - 1) / c;
+    if (parts > 4096) continue;
+    const long wgs = workgroups(c);
     const long rounds = (wgs + resident - 1) / resident;
     const long t = (rounds > 0 ? rounds : 1) * (c + overhead);
     if (best_t < 0 || t < best_t) {

@@ -93,7 +93,7 @@ def _per_launch(rows, copy_bytes_kib: float):
 
 
 def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fetch: str,
-            cmd_write: str, out: str) -> None:
+            cmd_write: str, out: str, split_tokens: int | None = None) -> None:
     copy_kib = copy_mib * 1024.0
     rd, rf, n_rd = _per_launch(_counter(fetch_dir, "FETCH_SIZE"), copy_kib)
     wr, wf, n_wr = _per_launch(_counter(write_dir, "WRITE_SIZE"), copy_kib)
@@ -110,6 +110,7 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fe
         "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
         "fetch_scale": round(rf, 4), "write_scale": round(wf, 4),
         "dispatches": [n_rd, n_wr], "command_fetch": cmd_fetch, "command_write": cmd_write,
+        "split_tokens": split_tokens,
     }
     with open(out, "w") as f:
         json.dump(data, f, indent=1)
@@ -134,12 +135,14 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--split-tokens", type=int, default=None,
+                   help="the partition length the profiled launches used")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         stats(a.dir, a.command, a.out)
     else:
         traffic(a.fetch_dir, a.write_dir, a.workload, a.copy_mib, a.command_fetch,
-                a.command_write, a.out)
+                a.command_write, a.out, a.split_tokens)
 
 
 if __name__ == "__main__":
