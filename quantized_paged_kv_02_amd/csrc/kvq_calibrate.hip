@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void kvq_calibrate_partial_kernel(CalibArgs a)
 #pragma unroll
       for (int i = 0; i < kUnroll; ++i) {
         const int ti = t + kTokLanes * i;
-        w[i] = ti < t1 ? ld16(x + ((size_t)ti * n_oct + oct) * 8) : u32x4{0u, 0u, 0u, 0u};
+        w[i] = ti < t1 ? ld16_stream(x + ((size_t)ti * n_oct + oct) * 8) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int i = 0; i < kUnroll; ++i)

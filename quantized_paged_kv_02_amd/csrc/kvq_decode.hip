@@ -1146,7 +1146,8 @@ struct Group2C {
 };
 
 __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
 }
 
 // Channel (within its 32) of the first of lane l's two q' channels: chunk
