@@ -142,13 +142,24 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
       if (workgroups(c) <= kCUs) return (int)c;
     return (int)((top + quantum - 1) / quantum * quantum);
   }
+  // Workgroups that run as one round.  The 8-bit formats count one per CU:
+  // a second or third resident workgroup on a CU adds no throughput there
+  // (Llama-2-7B shape, INT8, 128 blocks per row, 128 (row, head) pairs:
+  // 1024-token partitions, 256 workgroups, 19.6 us per launch against 20.3
+  // us at 512 tokens and 21.3 us at 384, the round model at three per CU's
+  // choice).  FP16 streams twice the bytes per block and does gain from a
+  // second workgroup (512 tokens: 30.4 us; 1024: 37.3 us), as INT4 is
+  // taken to.
+  const bool one_per_cu = L->dtype == KVQ_INT8 || L->dtype == KVQ_FP8_E4M3 ||
+                          L->dtype == KVQ_FP8_E5M2;
+  const long round_wgs = one_per_cu ? kCUs : resident;
   long best_t = -1;
   int pb = quantum;
   for (long c = quantum; c <= top + quantum - 1; c += quantum) {
     const long parts = (max_blocks + c - 1) / c;
     if (parts > 4096) continue;
     const long wgs = workgroups(c);
-    const long rounds = (wgs + resident - 1) / resident;
+    const long rounds = (wgs + round_wgs - 1) / round_wgs;
     const long t = (rounds > 0 ? rounds : 1) * (c + overhead);
     if (best_t < 0 || t < best_t) {
       best_t = t;
@@ -162,7 +173,7 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
     long work = 0;
     for (int32_t b = 0; b < batch; ++b) work += row_blocks(L, host_lens[b]);
     work *= L->num_kv_heads;
-    long floor_c = (work + 2 * resident - 1) / (2 * resident);
+    long floor_c = (work + 2 * round_wgs - 1) / (2 * round_wgs);
     floor_c = (floor_c + quantum - 1) / quantum * quantum;
     if (floor_c > top) floor_c = (top + quantum - 1) / quantum * quantum;
     if (pb < floor_c) pb = (int)floor_c;
