@@ -262,7 +262,9 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
  * Split-K: one launch computes partials per token partition (four
  * wavefronts per partition, merged in LDS), a second launch merges the
  * partitions of each (row, query head) by log-sum-exp in a fixed order, so
- * results are bitwise reproducible. */
+ * results are bitwise reproducible.  KVQ_ERR_UNSUPPORTED when the launch
+ * would need 2^24 workgroups or more (partitions x rows, rounded up to a
+ * multiple of 8, x KV heads); a larger split_tokens avoids it. */
 kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
                             const uint16_t *q, const int32_t *block_tables,
                             const int32_t *seq_lens, int32_t batch,

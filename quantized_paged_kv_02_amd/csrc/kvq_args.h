@@ -89,6 +89,10 @@ struct DecodeArgs {
   int32_t residual;         // INT4 residual length
   int32_t k_head_stride;    // 0 for a per-tensor K scale, 1 per head
   int32_t v_head_stride;
+  // Neighbouring KV heads share 128-byte lines of the scale rows (per-token
+  // INT8/FP8 rows, affine KIVI rows): the heads of one (row, partition) are
+  // then dispatched to one XCD (see wg_coord in kvq_decode.hip).
+  int32_t xcd_heads;
   float qk_scale;           // softmax_scale * log2(e)
 };
 

@@ -1557,11 +1557,39 @@ __device__ __forceinline__ void append_token_f16(const DecodeArgs &a, int b, int
 }
 
 // G4: INT4 cache with a query group of at most 4 (compact score layout).
+// Workgroup -> (partition p, KV head h, row b).  The dispatcher deals a
+// launch's workgroups to the eight XCDs in turn (workgroup i to XCD i % 8),
+// and each XCD has its own L2.  Where neighbouring heads of one block share
+// 128-byte lines of the scale rows (per-token rows of 64 bytes, affine KIVI
+// rows of 160: a.xcd_heads), all heads of one (row, partition) go to one
+// XCD: workgroup i takes head (i / 8) % H of pair bp = ((i / 8) / H) * 8 +
+// i % 8, bp = b * num_parts + p.  Otherwise the plain order: partition
+// fastest, then head, then row.  The grid holds the (row, partition) pairs
+// padded to a multiple of 8, times H; padding workgroups exit at once.
+struct WgCoord {
+  int p, h, b;
+  bool live;
+};
+__device__ __forceinline__ WgCoord wg_coord(const DecodeArgs &a) {
+  const int i = blockIdx.x;
+  if (a.xcd_heads) {
+    const int j = i >> 3;
+    const int bp = (j / a.num_kv_heads) * 8 + (i & 7);
+    return {bp % a.num_parts, j % a.num_kv_heads, bp / a.num_parts,
+            bp < a.num_parts * a.batch};
+  }
+  const int r = i / a.num_parts;
+  const int b = r / a.num_kv_heads;
+  return {i - r * a.num_parts, r - b * a.num_kv_heads, b, b < a.batch};
+}
+
 template <int DT, int KS, int VS, bool G4>
 __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
-  const int p = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const WgCoord wc = wg_coord(a);
+  if (!wc.live) return;
+  const int p = wc.p;
+  const int h = wc.h;
+  const int b = wc.b;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // Loads that do not need the row length are issued before it arrives: the
@@ -1763,7 +1791,10 @@ int decode_scale_kind(int granularity) {
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind, int batch,
                          hipStream_t stream) {
-  const dim3 grid(a.num_parts, a.num_kv_heads, batch);
+  // one workgroup per (partition, KV head, row), ordered for the XCDs by
+  // wg_coord: the (row, partition) pairs padded to a multiple of eight
+  const long pairs8 = ((long)a.num_parts * batch + 7) / 8 * 8;
+  const dim3 grid((unsigned)(pairs8 * a.num_kv_heads));
   // the compact INT4 layout holds one query token's four heads per block
   if (dtype == kInt4 && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, true>), grid, dim3(kThreads), 0,

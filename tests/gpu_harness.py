@@ -68,11 +68,13 @@ def fill_garbage(cache):
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
              table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
-             n_query=0, device="cuda"):
+             n_query=0, host_plan=False, device="cuda"):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
-    step instead of by kvq_write before kvq_paged_decode."""
+    step instead of by kvq_write before kvq_paged_decode.  ``host_plan``:
+    partition as bench.py does, from the rows' lengths on the host
+    (kvq_plan_split_tokens), instead of ``split_tokens``."""
     from quantized_paged_kv_02_amd import kvq
     lens = np.asarray(lens, np.int32)
     b = len(lens)
@@ -83,6 +85,8 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     mbs = table.shape[1]
     layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads, w.num_kv_heads,
                              nb, mbs, split_tokens, w.residual_len)
+    if host_plan:
+        layout.split_tokens = kvq.plan_split_tokens(layout, lens)
     ks, vs = [], []
     for r in range(b):
         k, v = inputs.gen_kv(w, layer, r, int(lens[r]), device, seed)

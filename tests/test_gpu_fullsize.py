@@ -1,6 +1,6 @@
 """GPU parity at the workloads' full per-layer sizes, in the launch
-configuration bench.py uses (automatic partitioning, the workload's block
-tables), on sampled rows.
+configuration bench.py uses (partitions planned from the rows' lengths by
+kvq_plan_split_tokens, the workload's block tables), on sampled rows.
 
 Each case builds one layer of a workload at its real batch, head counts and
 sequence lengths through the C ABI (prefill of S-1 tokens, then the decode
@@ -39,7 +39,7 @@ def test_fullsize_layer(name):
     w = W[name]
     lens = inputs.seq_lens(w)
     layer = 1          # any layer: layers differ only in their seeded data
-    res = run_case(w, lens, layer=layer, decode_twice=True)
+    res = run_case(w, lens, layer=layer, decode_twice=True, host_plan=True)
     assert np.all(np.isfinite(res.out)), "non-finite outputs"
     assert np.array_equal(res.out, res.out2), "decode is not bitwise reproducible"
     rows = _sample_rows(lens, seed=7)
