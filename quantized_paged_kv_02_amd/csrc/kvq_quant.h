@@ -37,6 +37,45 @@ __device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float 
   return (uint32_t)(int)y;
 }
 
+// q[i] = rintf(x[i] / s[i]), each quotient rounded as IEEE fp32 division
+// rounds it, for |x / s| <= 16, from r[i] = 1 / s[i] (correctly rounded).
+// Two roundings put a product x * r within |x / s| * 2^-23 <= 2^-19 of the
+// quotient, and the quotient's own rounding is at most 2^-20 there, so the
+// product is within 2^-18 of the rounded quotient (the test below may see
+// the product before its rounding: another 2^-20 at most).  Both round to
+// the same integer unless the product lies within 2^-17 of a half-integer
+// (or is not finite); if any lane of the wavefront has such a value, the
+// whole wavefront takes the divisions instead.  One multiply per value in
+// the common case, and the same integers as the division: the KIVI flush
+// quantizes with it (|x / s| <= qmax there; a zero scale gives code 0 after
+// this, whatever q holds).
+template <int N>
+__device__ __forceinline__ void rint_quotients(float (&q)[N], const float (&x)[N],
+                                               const float (&s)[N], const float (&r)[N]) {
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float y = x[i] * r[i];
+    const float f = y - floorf(y);
+    near |= !(fabsf(f - 0.5f) > 0x1p-17f);
+    q[i] = rintf(y);
+  }
+  if (__any(near)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = rintf(x[i] / s[i]);
+  }
+}
+// Codes from rounded quotients: clamp(q, lo, hi) (symmetric) and clamp(q +
+// z, 0, qmax) (affine), 0 for a zero scale.
+__device__ __forceinline__ uint32_t int_code(float q, float s, float lo, float hi) {
+  if (s == 0.0f) return 0u;
+  return (uint32_t)(int)fminf(fmaxf(q, lo), hi);
+}
+__device__ __forceinline__ uint32_t affine_code(float q, float s, float z, float qmax) {
+  if (s == 0.0f) return 0u;
+  return (uint32_t)(int)fminf(fmaxf(q + z, 0.0f), qmax);
+}
+
 // x / s clamped to the format's finite range (448 E4M3, 57344 E5M2).
 __device__ __forceinline__ float fp8_prescale(float x, float s, float top) {
   if (s == 0.0f) return 0.0f;

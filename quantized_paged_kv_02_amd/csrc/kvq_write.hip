@@ -118,11 +118,9 @@ __device__ __forceinline__ float2 affine_params(float lo, float hi, float qmax) 
   const float z = s > 0.0f ? fminf(fmaxf(rintf(-lo / s), 0.0f), qmax) : 0.0f;
   return float2{s, z};
 }
-__device__ __forceinline__ uint32_t quant_affine(float x, float s, float z, float qmax) {
-  if (s == 0.0f) return 0u;
-  const float y = fminf(fmaxf(rintf(x / s) + z, 0.0f), qmax);
-  return (uint32_t)(int)y;
-}
+// The reciprocal a flush quantizes with (see rint_quotients; 0 for a zero
+// scale, whose codes are 0 whatever the quotient).
+__device__ __forceinline__ float recip(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
 
 // DT: kInt4 (symmetric), kInt4Affine or kInt2Affine (2-bit codes: 512-byte
 // chunks, the code layouts of kvq.h).
@@ -137,6 +135,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
   __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
   __shared__ float partn[AFF ? 4 : 1][kHeadDim];  // K affine: channel minima
   __shared__ float sc[kHeadDim];        // K: [128] channel scales; V: [64][2] token scales
+  __shared__ float rc[kHeadDim];        // 1 / sc
   __shared__ float zs[AFF ? kHeadDim : 1];  // affine zero points, as sc
   __shared__ int phys_s[4];
 
@@ -242,11 +241,13 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
             fminf(fminf(partn[0][tid], partn[1][tid]), fminf(partn[2][tid], partn[3][tid]));
         const float2 sz = affine_params(mn, mx, kQmax);
         sc[tid] = sz.x;
+        rc[tid] = recip(sz.x);
         zs[tid] = sz.y;
         row[tid & 31] = sz.x;
         reinterpret_cast<uint8_t *>(row + 32)[tid & 31] = (uint8_t)(int)sz.y;
       } else {
         sc[tid] = mx / 7.0f;
+        rc[tid] = recip(mx / 7.0f);
         row[tid & 31] = mx / 7.0f;
       }
     }
@@ -260,12 +261,19 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       u32x2 out;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        uint32_t word = 0;
+        float xv[16], sv[16], rv[16], qv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = 32 * cb + 16 * d + e;
-          word |= quant_affine((float)x[tt][c], sc[c], zs[c], kQmax) << (2 * e);
+          xv[e] = (float)x[tt][c];
+          sv[e] = sc[c];
+          rv[e] = rc[c];
         }
+        rint_quotients(qv, xv, sv, rv);
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          word |= affine_code(qv[e], sv[e], zs[32 * cb + 16 * d + e], kQmax) << (2 * e);
         out[d] = word;
       }
       *reinterpret_cast<u32x2 *>(chunk + 128 * cb + 8 * (tt & 15)) = out;
@@ -274,12 +282,21 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
+        float xv[8], sv[8], rv[8], qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * cb + 8 * d + e;
+          xv[e] = (float)v[e];
+          sv[e] = sc[c];
+          rv[e] = rc[c];
+        }
+        rint_quotients(qv, xv, sv, rv);
         uint32_t word = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = 32 * cb + 8 * d + e;
-          const uint32_t q = AFF ? quant_affine((float)v[e], sc[c], zs[c], kQmax)
-                                 : quant_int((float)v[e], sc[c], -8.0f, 7.0f) & 0xFu;
+          const uint32_t q = AFF ? affine_code(qv[e], sv[e], zs[c], kQmax)
+                                 : int_code(qv[e], sv[e], -8.0f, 7.0f) & 0xFu;
           word |= q << (4 * e);
         }
         out[d] = word;
@@ -313,6 +330,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
         if constexpr (AFF) {
           const float2 sz = affine_params(mn, m, kQmax);
           sc[2 * tt + (qq >> 1)] = sz.x;
+          rc[2 * tt + (qq >> 1)] = recip(sz.x);
           zs[2 * tt + (qq >> 1)] = sz.y;
           row[k] = sz.x;
           // zero points group-transposed: token 16b + 4u + e of the group
@@ -324,6 +342,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
         } else {
           const float s = m / 7.0f;
           sc[2 * tt + (qq >> 1)] = s;
+          rc[2 * tt + (qq >> 1)] = recip(s);
           row[k] = s;
         }
       }
@@ -342,11 +361,18 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
         const int pos = (e == 1) ? 2 : (e == 2 ? 1 : e);
+        float xv[8], sv[8], rv[8], qv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int c = 16 * j + m;
           const int g = j >> 2;
-          const uint32_t q = quant_affine((float)x[tt][c], sc[2 * tt + g], zs[2 * tt + g], kQmax);
+          xv[j] = (float)x[tt][16 * j + m];
+          sv[j] = sc[2 * tt + g];
+          rv[j] = rc[2 * tt + g];
+        }
+        rint_quotients(qv, xv, sv, rv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t q = affine_code(qv[j], sv[j], zs[2 * tt + (j >> 2)], kQmax);
           out[j >> 2] |= q << (8 * pos + 2 * (j & 3));
         }
       }
@@ -357,13 +383,20 @@ __device__ void int4_flush(const WriteArgs &a, int bx) {
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
         const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
+        const float r0 = rc[2 * tt], r1 = rc[2 * tt + 1];
         const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
+        float xv[8], sv[8], rv[8], qv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int c = 16 * j + m;
-          const uint32_t q =
-              AFF ? quant_affine((float)x[tt][c], j < 4 ? s0 : s1, j < 4 ? z0 : z1, kQmax)
-                  : quant_int((float)x[tt][c], j < 4 ? s0 : s1, -8.0f, 7.0f) & 0xFu;
+          xv[j] = (float)x[tt][16 * j + m];
+          sv[j] = j < 4 ? s0 : s1;
+          rv[j] = j < 4 ? r0 : r1;
+        }
+        rint_quotients(qv, xv, sv, rv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t q = AFF ? affine_code(qv[j], sv[j], j < 4 ? z0 : z1, kQmax)
+                                 : int_code(qv[j], sv[j], -8.0f, 7.0f) & 0xFu;
           const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
           out[j >> 1] |= q << (4 * p);
         }
