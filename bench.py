@@ -242,11 +242,10 @@ class Bench:
         self.scale = 1.0 / math.sqrt(128)
         torch.cuda.synchronize()
 
-    def step(self, events=None, write=True, fused=True):
+    def step(self, write=True, fused=True):
         """One decode step over all layers: append each row's new token and
         decode.  fused: one kvq_write_decode call per layer, else kvq_write
-        then kvq_paged_decode.  events (with write=False) bracket each
-        kvq_paged_decode launch."""
+        then kvq_paged_decode; write=False: the decode launches alone."""
         kvq = self.kvq
         if self.n_query:
             # several query tokens per row: rewrite the rows' last n_query
@@ -255,15 +254,11 @@ class Bench:
                 if write:
                     kvq.write(self.caches[layer], self.k_new[layer], self.v_new[layer],
                               self.cu_nq, self.table, self.lens_t, self.n_query)
-                if events is not None:
-                    events[layer][0].record()
                 kvq.paged_decode_mq(self.caches[layer], self.q[layer], self.table, self.lens_t,
                                     self.max_len, self.scale, self.out[layer], self.ws)
-                if events is not None:
-                    events[layer][1].record()
             return
         for layer in range(self.w.layers):
-            if write and fused and events is None:
+            if write and fused:
                 kvq.write_decode(self.caches[layer], self.k_new[layer], self.v_new[layer],
                                  self.q[layer], self.table, self.lens_t, self.max_len,
                                  self.scale, self.out[layer], self.ws)
@@ -271,12 +266,8 @@ class Bench:
             if write:
                 kvq.write(self.caches[layer], self.k_new[layer], self.v_new[layer],
                           self.ones_cu, self.table, self.lens_t, 1)
-            if events is not None:
-                events[layer][0].record()
             kvq.paged_decode(self.caches[layer], self.q[layer], self.table, self.lens_t,
                              self.max_len, self.scale, self.out[layer], self.ws)
-            if events is not None:
-                events[layer][1].record()
 
 
 def run(args):
@@ -336,19 +327,23 @@ def run(args):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
 
-    # Decode-kernel launch durations: HIP event pairs around each decode
-    # launch on the stream it runs on.  A spin kernel keeps the stream busy
-    # while all launches and events are queued, so each pair brackets one
-    # kernel and no host launch latency.
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(L)]
+    # Decode-launch duration: one HIP event pair, on the stream the launches
+    # run on, around the L decode launches of a step (one per layer, back to
+    # back, the write launches left out), elapsed / L.  A spin kernel keeps
+    # the stream busy while they are queued, so no host launch latency falls
+    # inside; no marker sits between launches.
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
     durs = []
     for _ in range(max(1, args.kernel_samples)):
         torch.cuda._sleep(int(2e7))
-        bench.step(events, write=False)
+        k0.record()
+        bench.step(write=False)
+        k1.record()
         torch.cuda.synchronize()
-        durs += [e0.elapsed_time(e1) for e0, e1 in events]
-    kernel_timing = "HIP event pairs around each decode launch, queued behind a spin kernel"
+        durs.append(k0.elapsed_time(k1) / L)
+    kernel_timing = ("HIP events around the step's decode launches (one per layer, back to "
+                     "back, queued behind a spin kernel), elapsed / launches")
     kern_ms = float(np.mean(durs))
 
     copy_probe = None
@@ -423,7 +418,7 @@ def run(args):
                                             "kvq_paged_decode_mq launch")
             if args.n_query else DECODE_KERNEL,
             "bytes_per_launch": layer_bytes,
-            "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs),
+            "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs) * L,
             "timing": kernel_timing,
         },
         "cpu_baseline": cpu,
