@@ -181,6 +181,18 @@ def test_entry_points_reject_before_launch():
     assert _write(lay, c, batch=0) == OK
 
 
+def test_decode_rejects_oversized_grid():
+    # one block per partition over 2^20 tokens: 65536 partitions per row, so
+    # 128 rows x 2 KV heads need 2^24 workgroups of 256 threads (the 1-D
+    # grid's 32-bit work-item count overflows)
+    lay = _layout(split_tokens=16, max_blocks_per_seq=65536, num_blocks=1 << 20)
+    c = _cache()
+    assert _decode(lay, c, batch=128, max_len=1 << 20) == UNS
+    assert _write_decode(lay, c, batch=128, max_len=1 << 20) == UNS
+    # one row fewer fits the grid; its partials then exceed the workspace
+    assert _decode(lay, c, batch=127, max_len=1 << 20) == WS
+
+
 def test_fp16_cache_rules():
     # an FP16 cache has no scales: NULL scale pointers and any granularity
     # field are accepted, the code arrays are still required and aligned
