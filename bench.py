@@ -329,21 +329,33 @@ def run(args):
 
     # Decode-launch duration: one HIP event pair, on the stream the launches
     # run on, around the L decode launches of a step (one per layer, back to
-    # back, the write launches left out), elapsed / L.  A spin kernel keeps
-    # the stream busy while they are queued, so no host launch latency falls
-    # inside; no marker sits between launches.
+    # back, the write launches left out), elapsed / L.  They run as the timed
+    # step runs them: from a HIP graph of those launches (eagerly with
+    # --eager, each queued behind a spin kernel so no host latency falls
+    # inside).  No marker sits between launches.
+    dgraph = None
+    if not args.eager:
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            bench.step(write=False)
+        dgraph.replay()
+        torch.cuda.synchronize()
     k0 = torch.cuda.Event(enable_timing=True)
     k1 = torch.cuda.Event(enable_timing=True)
     durs = []
     for _ in range(max(1, args.kernel_samples)):
         torch.cuda._sleep(int(2e7))
         k0.record()
-        bench.step(write=False)
+        if dgraph is not None:
+            dgraph.replay()
+        else:
+            bench.step(write=False)
         k1.record()
         torch.cuda.synchronize()
         durs.append(k0.elapsed_time(k1) / L)
     kernel_timing = ("HIP events around the step's decode launches (one per layer, back to "
-                     "back, queued behind a spin kernel), elapsed / launches")
+                     "back, " + ("launched eagerly behind a spin kernel" if dgraph is None
+                                 else "replayed from a HIP graph") + "), elapsed / launches")
     kern_ms = float(np.mean(durs))
 
     copy_probe = None
