@@ -41,9 +41,17 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 # the configuration the decode bandwidth target (>= 70 % of HBM peak) is set
 # on.  Every other workload runs with --workload.
 DEFAULT_WORKLOAD = "kivi-int4"
-DECODE_KERNEL = ("kvq_paged_decode launch: kvq_paged_decode_kernel + "
-                 "kvq_partition_reduce_kernel (the reduce is skipped when one partition "
-                 "covers every row)")
+
+
+def decode_kernel_label(dtype: str, n_query: int) -> str:
+    """The kernels one decode launch runs, as rocprofv3 names them."""
+    entry = "kvq_paged_decode_mq" if n_query else "kvq_paged_decode"
+    kern = ("kvq_paged_decode_int4_kernel" if dtype in ("int4", "int4-affine", "int2-affine")
+            else "kvq_paged_decode_kernel")
+    return (f"{entry} launch: {kern} + kvq_partition_reduce_kernel (the reduce is skipped "
+            "when one partition covers every row)")
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
@@ -426,9 +434,7 @@ def run(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": DECODE_KERNEL.replace("kvq_paged_decode launch",
-                                            "kvq_paged_decode_mq launch")
-            if args.n_query else DECODE_KERNEL,
+            "kernel": decode_kernel_label(w.dtype, args.n_query),
             "bytes_per_launch": layer_bytes,
             "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs) * L,
             "timing": kernel_timing,
