@@ -286,8 +286,10 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
   (void)hipGetLastError();
   hipError_t e;
   if (kivi(layout)) {
-    // groups leaving the window: at most ceil(n/64) + 1 per row
-    const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup + 1;
+    // groups leaving the window when a row grows by n tokens to length S:
+    // nq(S) - nq(S - n) = 64 (floor((S - 128) / 64) - floor((S - n - 128) /
+    // 64)) <= 64 ceil(n / 64) (less while S - n < 128), so ceil(n / 64)
+    const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup;
     e = kvq::launch_write_int4(a, layout->dtype, batch, max_new_per_seq, max_groups, s);
   } else if (layout->dtype == KVQ_FP16) {
     e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);
@@ -428,7 +430,7 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   w.ring = layout->residual_len + kGroup;
   (void)hipGetLastError();
   const hipError_t e =
-      kvq::launch_write_int4(w, layout->dtype, batch, 1, 2, static_cast<hipStream_t>(stream));
+      kvq::launch_write_int4(w, layout->dtype, batch, 1, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return KVQ_ERR_HIP;
   return decode_launch(layout, a, batch, stream);
 }
