@@ -80,6 +80,10 @@
  * ---- INT4 (KIVI) layout ------------------------------------------------------
  * The first nq(S) = max(0, floor((S-R)/G))*G tokens of a sequence are INT4;
  * tokens nq(S) .. S-1 (R to R+G-1 of them once S >= R) stay fp16 in a ring.
+ * A written sequence of length S also holds the INT4 blocks of the group
+ * that leaves the window at length S+1 (groups 0 .. nq(S+1)-1 in all):
+ * writes flush each group one token early, so that a one-token decode step
+ * can flush concurrently with its attention, which does not read it.
  *   k_codes : uint8 [NB][H][1024]; (slot s, channel c) at byte
  *             256*(c>>5) + 16*s + ((c&31)>>1), low nibble for even c.
  *   v_codes : uint8 [NB][H][1024]; with j = c>>4, u = (c&15) + 16*(s>>2),
@@ -235,10 +239,12 @@ size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
  * INT8/FP8: writes codes (and per-token scales when the granularity is
  * KVQ_PER_TOKEN) into the block slots.  Static scales are read from the
  * cache's scale arrays.  FP16: stores the values in the block slots.
- * INT4: first quantizes every 64-token group that leaves the fp16 window
- * (from the ring or straight from k_new/v_new) into INT4 blocks with its
- * scales, then stores the remaining new tokens in the ring (two launches,
- * in that order, so a ring slot is read before it is reused).
+ * INT4: first quantizes the 64-token groups nq(S_old+1) .. nq(S_new+1)-1
+ * (those that leave the fp16 window up to length S_new+1, see the INT4
+ * layout; read from the ring or straight from k_new/v_new) into INT4 blocks
+ * with their scales, then stores the new tokens from nq(S_new) on in the
+ * ring (two launches, in that order, so a ring slot is read before it is
+ * reused; one launch when every row takes at most one token).
  * Sequences must be extended in order; positions already written are
  * overwritten with the same values when rewritten. */
 kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
@@ -286,7 +292,11 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
  * is split): the workgroup that streams a row's last partition quantizes
  * (FP16: copies) and stores the row's token (codes and per-token scales)
  * before streaming.
- * INT4: the kvq_write launches, then the decode launches.
+ * INT4: one decode launch (plus the merge) whose last-partition workgroup
+ * of each row stores the token in the ring before reading the window, and
+ * whose 2 x batch x H further workgroups flush the group that leaves the
+ * window at length seq_lens[b]+1, if any; no workgroup of the launch reads
+ * what those write.
  * Errors: as for kvq_paged_decode; additionally KVQ_ERR_INVALID_ARG when
  * k_new or v_new is NULL (batch > 0) and KVQ_ERR_ALIGNMENT when either is
  * not 16-byte aligned.  Nothing is enqueued on error. */

@@ -320,7 +320,8 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
   // one 256-thread workgroup per (partition, KV head, row) in a 1-D grid,
   // (row, partition) pairs padded to a multiple of 8: its work-item count
   // must fit in 32 bits
-  const int64_t pairs8 = ((int64_t)p.num_parts * batch + 7) / 8 * 8;
+  // (a KIVI decode step adds 2 x batch x H flush workgroups)
+  const int64_t pairs8 = ((int64_t)p.num_parts * batch + 7) / 8 * 8 + 2 * (int64_t)batch;
   if (pairs8 * layout->num_kv_heads * 256 >= ((int64_t)1 << 32)) return KVQ_ERR_UNSUPPORTED;
   const WorkspaceLayout w = workspace_layout(layout, batch, p, n_query);
   if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -404,34 +405,12 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
   if (st != KVQ_OK || !launch) return st;
   if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
-  if (!kivi(layout)) {
-    a.k_new = k_new;
-    a.v_new = v_new;
-    return decode_launch(layout, a, batch, stream);
-  }
-  // INT4: the write launches (one token per row, no cu_new), then decode
-  kvq::WriteArgs w{};
-  w.k_codes = static_cast<uint8_t *>(cache->k_codes);
-  w.v_codes = static_cast<uint8_t *>(cache->v_codes);
-  w.k_scales = cache->k_scales;
-  w.v_scales = cache->v_scales;
-  w.k_resid = cache->k_resid;
-  w.v_resid = cache->v_resid;
-  w.k_new = k_new;
-  w.v_new = v_new;
-  w.cu_new = nullptr;
-  w.block_tables = block_tables;
-  w.seq_lens = seq_lens;
-  w.num_kv_heads = layout->num_kv_heads;
-  w.max_blocks_per_seq = layout->max_blocks_per_seq;
-  w.k_gran = layout->k_gran;
-  w.v_gran = layout->v_gran;
-  w.residual = layout->residual_len;
-  w.ring = layout->residual_len + kGroup;
-  (void)hipGetLastError();
-  const hipError_t e =
-      kvq::launch_write_int4(w, layout->dtype, batch, 1, 1, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return KVQ_ERR_HIP;
+  // The workgroup that streams a row's last partition stores the new token
+  // first (INT8 / FP8 / FP16: its codes and scales in the last block; KIVI:
+  // the fp16 ring); a KIVI step also flushes the group that leaves the
+  // window at the next length, in workgroups of the same launch.
+  a.k_new = k_new;
+  a.v_new = v_new;
   return decode_launch(layout, a, batch, stream);
 }
 

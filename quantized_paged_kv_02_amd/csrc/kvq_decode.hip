@@ -57,6 +57,7 @@
 // pairs and mask the last block pairs per column.
 #include "kvq_args.h"
 #include "kvq_device.h"
+#include "kvq_kivi_write.h"
 #include "kvq_quant.h"
 
 namespace kvq {
@@ -1583,8 +1584,55 @@ __device__ __forceinline__ WgCoord wg_coord(const DecodeArgs &a) {
   return {i - r * a.num_parts, r - b * a.num_kv_heads, b, b < a.batch};
 }
 
+// Workgroups of the decode grid: (row, partition) pairs padded to a
+// multiple of 8, times the KV heads (wg_coord).  A KIVI decode step
+// (kvq_write_decode) adds 2 x batch x H flush workgroups after them.
+__device__ __forceinline__ int decode_grid_main(const DecodeArgs &a) {
+  return (a.num_parts * a.batch + 7) / 8 * 8 * a.num_kv_heads;
+}
+
+// The write arguments of one decode step's new tokens (one per row, entry b
+// of k_new / v_new).  The cache arrays are the caller's writable buffers
+// (const in DecodeArgs because streaming only reads them).
+__device__ __forceinline__ WriteArgs step_write_args(const DecodeArgs &a) {
+  WriteArgs w;
+  w.k_codes = const_cast<uint8_t *>(a.k_codes);
+  w.v_codes = const_cast<uint8_t *>(a.v_codes);
+  w.k_scales = const_cast<float *>(a.k_scales);
+  w.v_scales = const_cast<float *>(a.v_scales);
+  w.k_resid = const_cast<uint16_t *>(a.k_resid);
+  w.v_resid = const_cast<uint16_t *>(a.v_resid);
+  w.k_new = a.k_new;
+  w.v_new = a.v_new;
+  w.cu_new = nullptr;
+  w.block_tables = a.block_tables;
+  w.seq_lens = a.seq_lens;
+  w.num_kv_heads = a.num_kv_heads;
+  w.max_blocks_per_seq = a.max_blocks_per_seq;
+  w.k_gran = 0;  // KIVI groups fix their own granularities
+  w.v_gran = 0;
+  w.ring = a.ring;
+  w.residual = a.residual;
+  return w;
+}
+
 template <int DT, int KS, int VS, bool G4>
 __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
+  if constexpr (is_kivi(DT)) {
+    const int main_wgs = decode_grid_main(a);
+    if ((int)blockIdx.x >= main_wgs) {
+      // A decode step's flush of the group that leaves the fp16 window at
+      // the next length (K or V of one (row, KV head)).  No workgroup of
+      // this launch reads what it writes or writes what it reads: the
+      // decode reads groups below nq(S), and the appended token's ring slot
+      // is none of the group's.
+      const int f = blockIdx.x - main_wgs;
+      const int r = f >> 1;
+      const int fb = r / a.num_kv_heads;
+      if (fb < a.batch) int4_flush<DT>(step_write_args(a), f & 1, r - fb * a.num_kv_heads, fb);
+      return;
+    }
+  }
   const WgCoord wc = wg_coord(a);
   if (!wc.live) return;
   const int p = wc.p;
@@ -1637,6 +1685,14 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     const int nq = kivi_quantized_len(seq_len, a.residual);
     const int n_main = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
     if (p >= n_main) return;
+    if (a.k_new != nullptr && p == n_main - 1) {
+      // one decode step: this workgroup streams the row's fp16 window, so it
+      // stores the new token in the ring first and completes the store
+      // (every counter drained, workgroup barrier) before any wave loads it
+      if (wave == 0) append_token(step_write_args(a), 0, h, b, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     if constexpr (G4 && DT == kInt2Affine) {
       // the 2-bit stream rescales its whole output at the end, so the
       // window follows it
@@ -1794,7 +1850,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   // one workgroup per (partition, KV head, row), ordered for the XCDs by
   // wg_coord: the (row, partition) pairs padded to a multiple of eight
   const long pairs8 = ((long)a.num_parts * batch + 7) / 8 * 8;
-  const dim3 grid((unsigned)(pairs8 * a.num_kv_heads));
+  // a KIVI decode step: its flush workgroups (K and V of every (row, head))
+  const long flush = is_kivi(dtype) && a.k_new != nullptr ? 2L * batch * a.num_kv_heads : 0;
+  const dim3 grid((unsigned)(pairs8 * a.num_kv_heads + flush));
   // the compact INT4 layout holds one query token's four heads per block
   if (dtype == kInt4 && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, true>), grid, dim3(kThreads), 0,

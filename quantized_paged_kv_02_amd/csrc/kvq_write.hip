@@ -15,23 +15,11 @@
 // to the fp16 ring.
 #include "kvq_args.h"
 #include "kvq_device.h"
+#include "kvq_kivi_write.h"
 #include "kvq_quant.h"
 
 namespace kvq {
 namespace {
-
-// New tokens of row b: entries [c_begin, c_begin + n_new) of k_new / v_new.
-// Without cu_new every row owns entry b and holds one new token unless the
-// row is empty.
-__device__ __forceinline__ void new_tokens(const WriteArgs &a, int b, int &c_begin, int &n_new) {
-  if (a.cu_new != nullptr) {
-    c_begin = a.cu_new[b];
-    n_new = a.cu_new[b + 1] - c_begin;
-  } else {
-    c_begin = b;
-    n_new = a.seq_lens[b] > 0 ? 1 : 0;
-  }
-}
 
 template <int DT>
 __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
@@ -93,346 +81,9 @@ __global__ __launch_bounds__(64) void kvq_write_f16_kernel(WriteArgs a) {
 // INT4 KIVI
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int kivi_len(int s, int residual) {
-  return kivi_quantized_len(s, residual);
-}
-
-// Flush of one 64-token group leaving the fp16 window, for one (row, KV
-// head) and one of K or V: 256 threads.  The group's fp16 values are
-// gathered into LDS (from the ring for tokens already cached, else from the
-// call's new tokens), the scales are reduced across threads, and every
-// thread then quantizes exactly the 32 nibbles of one 16-byte unit of the
-// block layout and writes it with one store.
-//
-// AFF: asymmetric groups ([oh-bug] "量化不是简单'截断精度'", the affine
-// form): over the group's range widened to contain zero, scale = (hi - lo)
-// / 15 and zero point = clamp(round(-lo / scale), 0, 15); codes are
-// clamp(round(x / scale) + zero point, 0, 15), unsigned.  Scale rows are 40
-// floats per (block, head), the last 32 bytes holding the zero points.
-constexpr int kFlushRow = kHeadDim + 8;  // padded LDS row (fp16)
-
-// Affine parameters of a group with minimum lo <= 0 <= maximum hi, codes
-// 0 .. qmax.
-__device__ __forceinline__ float2 affine_params(float lo, float hi, float qmax) {
-  const float s = (hi - lo) / qmax;
-  const float z = s > 0.0f ? fminf(fmaxf(rintf(-lo / s), 0.0f), qmax) : 0.0f;
-  return float2{s, z};
-}
-// The reciprocal a flush quantizes with (see rint_quotients; 0 for a zero
-// scale, whose codes are 0 whatever the quotient).
-__device__ __forceinline__ float recip(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
-
-// DT: kInt4 (symmetric), kInt4Affine or kInt2Affine (2-bit codes: 512-byte
-// chunks, the code layouts of kvq.h).
-template <int DT>
-__device__ void int4_flush(const WriteArgs &a, int bx) {
-  constexpr bool AFF = DT != kInt4;
-  constexpr bool TWO = DT == kInt2Affine;
-  constexpr float kQmax = TWO ? 3.0f : 15.0f;
-  constexpr int kChunk = kivi_chunk_bytes(DT);
-  constexpr int kRow = AFF ? 40 : 32;   // floats per (block, head) scale row
-  __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
-  __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
-  __shared__ float partn[AFF ? 4 : 1][kHeadDim];  // K affine: channel minima
-  __shared__ float sc[kHeadDim];        // K: [128] channel scales; V: [64][2] token scales
-  __shared__ float rc[kHeadDim];        // 1 / sc
-  __shared__ float zs[AFF ? kHeadDim : 1];  // affine zero points, as sc
-  __shared__ int phys_s[4];
-
-  const int gs = bx >> 1;
-  const bool is_v = (bx & 1) != 0;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int H = a.num_kv_heads;
-  int c_begin, n_new;
-  new_tokens(a, b, c_begin, n_new);
-  const int s_new = a.seq_lens[b];
-  const int s_old = s_new - n_new;
-  const int nq_old = kivi_len(s_old, a.residual);
-  const int nq_new = kivi_len(s_new, a.residual);
-  const int t0 = nq_old + kGroup * gs;
-  if (t0 >= nq_new) return;
-
-  const size_t ring_row = (size_t)b * H + h;
-  const uint16_t *fresh = is_v ? a.v_new : a.k_new;
-  if (!is_v) {
-    // K: 16-byte units (token, 8 channels); ring rows are contiguous
-    for (int e = tid; e < kGroup * 16; e += 256) {
-      const int tt = e >> 4, c8 = (e & 15) * 8;
-      const int t = t0 + tt;
-      const uint16_t *src =
-          t < s_old ? a.k_resid + (ring_row * a.ring + t % a.ring) * kHeadDim + c8
-                    : fresh + ((size_t)(c_begin + t - s_old) * H + h) * kHeadDim + c8;
-      *reinterpret_cast<u32x4 *>(&x[tt][c8]) = ld16(src);
-    }
-  } else {
-    // V: the ring is token-minor in quads ([slot/4][channel][slot%4]); a
-    // 16-byte unit is 2 channels x 4 tokens of one quad
-    for (int e = tid; e < (kGroup / 4) * (kHeadDim / 2); e += 256) {
-      const int q = e >> 6, cp = e & 63;
-      const int tq = t0 + 4 * q;
-      if (tq + 3 < s_old) {
-        const int slot = tq % a.ring;  // multiple of 4: the quad is contiguous
-        const u32x4 w = ld16(a.v_resid + ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim +
-                                          2 * cp) * 4);
-        // w = [c0 t0..t3][c1 t0..t3] as fp16 pairs
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-          const uint32_t hi = (i & 1) ? (w[2 + (i >> 1)] >> 16) : (w[2 + (i >> 1)] & 0xFFFFu);
-          *reinterpret_cast<uint32_t *>(&x[4 * q + i][2 * cp]) = lo | (hi << 16);
-        }
-      } else {
-        for (int i = 0; i < 4; ++i) {
-          const int t = tq + i;
-          uint32_t pr;
-          if (t < s_old) {
-            const int slot = t % a.ring;
-            const uint16_t *vb = a.v_resid +
-                                 ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim + 2 * cp) * 4 +
-                                 (slot & 3);
-            pr = (uint32_t)vb[0] | ((uint32_t)vb[4] << 16);
-          } else {
-            pr = *reinterpret_cast<const uint32_t *>(
-                fresh + ((size_t)(c_begin + t - s_old) * H + h) * kHeadDim + 2 * cp);
-          }
-          *reinterpret_cast<uint32_t *>(&x[4 * q + i][2 * cp]) = pr;
-        }
-      }
-    }
-  }
-  if (tid < 4) {
-    phys_s[tid] = a.block_tables[(size_t)b * a.max_blocks_per_seq + t0 / kBlock + tid];
-  }
-  __syncthreads();
-
-  if (!is_v) {
-    // K scales: max over the group's 64 tokens of |K[:, c]| / 7 (affine: the
-    // channel's minimum and maximum, each starting from 0)
-    {
-      const int cp = tid & 63, qq = tid >> 6;
-      float m0 = 0.0f, m1 = 0.0f, n0 = 0.0f, n1 = 0.0f;
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const f16x2 v = *reinterpret_cast<const f16x2 *>(&x[16 * qq + i][2 * cp]);
-        if constexpr (AFF) {
-          m0 = fmaxf(m0, (float)v.x);
-          m1 = fmaxf(m1, (float)v.y);
-          n0 = fminf(n0, (float)v.x);
-          n1 = fminf(n1, (float)v.y);
-        } else {
-          m0 = fmaxf(m0, fabsf((float)v.x));
-          m1 = fmaxf(m1, fabsf((float)v.y));
-        }
-      }
-      part[qq][2 * cp] = m0;
-      part[qq][2 * cp + 1] = m1;
-      if constexpr (AFF) {
-        partn[qq][2 * cp] = n0;
-        partn[qq][2 * cp + 1] = n1;
-      }
-    }
-    __syncthreads();
-    if (tid < kHeadDim) {
-      const float mx = fmaxf(fmaxf(part[0][tid], part[1][tid]), fmaxf(part[2][tid], part[3][tid]));
-      float *row = a.k_scales + ((size_t)phys_s[tid >> 5] * H + h) * kRow;
-      if constexpr (AFF) {
-        const float mn =
-            fminf(fminf(partn[0][tid], partn[1][tid]), fminf(partn[2][tid], partn[3][tid]));
-        const float2 sz = affine_params(mn, mx, kQmax);
-        sc[tid] = sz.x;
-        rc[tid] = recip(sz.x);
-        zs[tid] = sz.y;
-        row[tid & 31] = sz.x;
-        reinterpret_cast<uint8_t *>(row + 32)[tid & 31] = (uint8_t)(int)sz.y;
-      } else {
-        sc[tid] = mx / 7.0f;
-        rc[tid] = recip(mx / 7.0f);
-        row[tid & 31] = mx / 7.0f;
-      }
-    }
-    __syncthreads();
-    // one unit: channels 32cb .. 32cb+31 of token tt; INT4: nibble e of dword
-    // d is channel 32cb + 8d + e; 2-bit: bits 2e of dword d are channel
-    // 32cb + 16d + e
-    const int tt = tid >> 2, cb = tid & 3;
-    uint8_t *chunk = a.k_codes + ((size_t)phys_s[tt >> 4] * H + h) * kChunk;
-    if constexpr (TWO) {
-      u32x2 out;
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        float xv[16], sv[16], rv[16], qv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = 32 * cb + 16 * d + e;
-          xv[e] = (float)x[tt][c];
-          sv[e] = sc[c];
-          rv[e] = rc[c];
-        }
-        rint_quotients(qv, xv, sv, rv);
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          word |= affine_code(qv[e], sv[e], zs[32 * cb + 16 * d + e], kQmax) << (2 * e);
-        out[d] = word;
-      }
-      *reinterpret_cast<u32x2 *>(chunk + 128 * cb + 8 * (tt & 15)) = out;
-    } else {
-      u32x4 out;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
-        float xv[8], sv[8], rv[8], qv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = 32 * cb + 8 * d + e;
-          xv[e] = (float)v[e];
-          sv[e] = sc[c];
-          rv[e] = rc[c];
-        }
-        rint_quotients(qv, xv, sv, rv);
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = 32 * cb + 8 * d + e;
-          const uint32_t q = AFF ? affine_code(qv[e], sv[e], zs[c], kQmax)
-                                 : int_code(qv[e], sv[e], -8.0f, 7.0f) & 0xFu;
-          word |= q << (4 * e);
-        }
-        out[d] = word;
-      }
-      *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
-    }
-  } else {
-    // V scales: per token, max over each 64-channel half of |V| / 7
-    // (affine: the half's minimum and maximum, each starting from 0)
-    {
-      const int tt = tid >> 2, qq = tid & 3;
-      float m = 0.0f, mn = 0.0f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * qq + 8 * d]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (AFF) {
-            m = fmaxf(m, (float)v[e]);
-            mn = fminf(mn, (float)v[e]);
-          } else {
-            m = fmaxf(m, fabsf((float)v[e]));
-          }
-        }
-      }
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      if constexpr (AFF) mn = fminf(mn, __shfl_xor(mn, 1, 64));
-      if ((qq & 1) == 0) {
-        const int k = 2 * (tt & 15) + (qq >> 1);  // [slot][channel group]
-        float *row = a.v_scales + ((size_t)phys_s[tt >> 4] * H + h) * kRow;
-        if constexpr (AFF) {
-          const float2 sz = affine_params(mn, m, kQmax);
-          sc[2 * tt + (qq >> 1)] = sz.x;
-          rc[2 * tt + (qq >> 1)] = recip(sz.x);
-          zs[2 * tt + (qq >> 1)] = sz.y;
-          row[k] = sz.x;
-          // zero points group-transposed: token 16b + 4u + e of the group
-          // goes to the row of the group's block u, byte 8b + 2e + g
-          const int s16 = tt & 15;
-          float *zrow = a.v_scales + ((size_t)phys_s[s16 >> 2] * H + h) * kRow;
-          reinterpret_cast<uint8_t *>(zrow + 32)[8 * (tt >> 4) + 2 * (s16 & 3) + (qq >> 1)] =
-              (uint8_t)(int)sz.y;
-        } else {
-          const float s = m / 7.0f;
-          sc[2 * tt + (qq >> 1)] = s;
-          rc[2 * tt + (qq >> 1)] = recip(s);
-          row[k] = s;
-        }
-      }
-    }
-    __syncthreads();
-    // one unit u of block ub: channels 16j + m (j = 0..7) of the quad's four
-    // tokens; dword w holds tiles 2w and 2w+1, token e of tile j at nibble
-    // 2(j&1) + (e>>1) + 4(e&1)
-    const int ub = tid >> 6, u = tid & 63;
-    const int m = u & 15, quad = u >> 4;
-    uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * kChunk;
-    if constexpr (TWO) {
-      // 2-bit: dword j>>2, byte pos(e) = 0, 2, 1, 3 of token e, bits 2(j&3)
-      u32x2 out = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = 16 * ub + 4 * quad + e;
-        const int pos = (e == 1) ? 2 : (e == 2 ? 1 : e);
-        float xv[8], sv[8], rv[8], qv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int g = j >> 2;
-          xv[j] = (float)x[tt][16 * j + m];
-          sv[j] = sc[2 * tt + g];
-          rv[j] = rc[2 * tt + g];
-        }
-        rint_quotients(qv, xv, sv, rv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t q = affine_code(qv[j], sv[j], zs[2 * tt + (j >> 2)], kQmax);
-          out[j >> 2] |= q << (8 * pos + 2 * (j & 3));
-        }
-      }
-      *reinterpret_cast<u32x2 *>(chunk + 8 * u) = out;
-    } else {
-      u32x4 out = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = 16 * ub + 4 * quad + e;
-        const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
-        const float r0 = rc[2 * tt], r1 = rc[2 * tt + 1];
-        const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
-        float xv[8], sv[8], rv[8], qv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xv[j] = (float)x[tt][16 * j + m];
-          sv[j] = j < 4 ? s0 : s1;
-          rv[j] = j < 4 ? r0 : r1;
-        }
-        rint_quotients(qv, xv, sv, rv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t q = AFF ? affine_code(qv[j], sv[j], j < 4 ? z0 : z1, kQmax)
-                                 : int_code(qv[j], sv[j], -8.0f, 7.0f) & 0xFu;
-          const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
-          out[j >> 1] |= q << (4 * p);
-        }
-      }
-      *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;
-    }
-  }
-}
-
 template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
-  int4_flush<DT>(a, blockIdx.x);
-}
-
-// Append the new tokens that stay fp16 to the ring.
-// Store new token i of row b, head h in the fp16 ring (first wave of the
-// workgroup) unless it is already part of a quantized group.
-__device__ __forceinline__ void append_token(const WriteArgs &a, int i, int h, int b, int lane) {
-  const int H = a.num_kv_heads;
-  int c_begin, n_new;
-  new_tokens(a, b, c_begin, n_new);
-  if (i >= n_new) return;
-  const int s_new = a.seq_lens[b];
-  const int pos = s_new - n_new + i;
-  if (pos < kivi_len(s_new, a.residual)) return;  // already quantized
-  const int slot = pos % a.ring;
-  const size_t ring_row = (size_t)b * H + h;
-  const size_t src = ((size_t)(c_begin + i) * H + h) * kHeadDim + 2 * lane;
-  const uint32_t kp = *reinterpret_cast<const uint32_t *>(a.k_new + src);
-  const uint32_t vp = *reinterpret_cast<const uint32_t *>(a.v_new + src);
-  *reinterpret_cast<uint32_t *>(a.k_resid + (ring_row * a.ring + slot) * kHeadDim +
-                                2 * lane) = kp;
-  uint16_t *vb = a.v_resid + ((ring_row * (a.ring / 4) + slot / 4) * kHeadDim + 2 * lane) * 4 +
-                 (slot & 3);
-  vb[0] = (uint16_t)(vp & 0xFFFFu);
-  vb[4] = (uint16_t)(vp >> 16);
+  int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
@@ -446,7 +97,7 @@ __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
 template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a, int groups) {
   if ((int)blockIdx.x < 2 * groups) {
-    int4_flush<DT>(a, blockIdx.x);
+    int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
   } else if (threadIdx.x < 64) {
     append_token(a, blockIdx.x - 2 * groups, blockIdx.y, blockIdx.z, threadIdx.x);
   }

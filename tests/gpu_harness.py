@@ -194,24 +194,32 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
     p = res.pools
     if w.dtype in KIVI:
         affine = w.dtype != "int4"
-        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len, affine=affine,
-                                  bits=2 if w.dtype == "int2-affine" else 4)
+        bits = 2 if w.dtype == "int2-affine" else 4
+        kv = oracle.kivi_quantize(kb, vb, residual=w.residual_len, affine=affine, bits=bits)
         nq = kv["nq"]
         if check_codes:
-            assert np.array_equal(lv.logical_codes(p["k_codes"], row, nq, "k", w.dtype),
-                                  kv["k_codes"]), f"row {r}: INT4 K codes"
-            assert np.array_equal(lv.logical_codes(p["v_codes"], row, nq, "v", w.dtype),
-                                  kv["v_codes"]), f"row {r}: INT4 V codes"
+            # A row of length S also holds, quantized, the group that leaves
+            # the window at length S + 1 (flushed one write early); its tokens
+            # are all older than S, so a repeated last token stands in for
+            # token S.
+            kq = oracle.kivi_quantize(np.concatenate([kb, kb[-1:]]),
+                                      np.concatenate([vb, vb[-1:]]),
+                                      residual=w.residual_len, affine=affine, bits=bits)
+            nq1 = kq["nq"]
+            assert np.array_equal(lv.logical_codes(p["k_codes"], row, nq1, "k", w.dtype),
+                                  kq["k_codes"]), f"row {r}: INT4 K codes"
+            assert np.array_equal(lv.logical_codes(p["v_codes"], row, nq1, "v", w.dtype),
+                                  kq["v_codes"]), f"row {r}: INT4 V codes"
             if affine:
-                assert np.array_equal(lv.int4_k_zero_points(p["k_scales"], row, nq // 64),
-                                      kv["k_zp"]), f"row {r}: INT4 K zero points"
-                assert np.array_equal(lv.int4_v_zero_points(p["v_scales"], row, nq),
-                                      kv["v_zp"]), f"row {r}: INT4 V zero points"
-            gks = lv.int4_k_scales(p["k_scales"], row, nq // 64)
-            assert np.array_equal(gks.view(np.uint32), kv["k_scales"].view(np.uint32)), \
+                assert np.array_equal(lv.int4_k_zero_points(p["k_scales"], row, nq1 // 64),
+                                      kq["k_zp"]), f"row {r}: INT4 K zero points"
+                assert np.array_equal(lv.int4_v_zero_points(p["v_scales"], row, nq1),
+                                      kq["v_zp"]), f"row {r}: INT4 V zero points"
+            gks = lv.int4_k_scales(p["k_scales"], row, nq1 // 64)
+            assert np.array_equal(gks.view(np.uint32), kq["k_scales"].view(np.uint32)), \
                 f"row {r}: INT4 K scales"
-            gvs = lv.int4_v_scales(p["v_scales"], row, nq)
-            assert np.array_equal(gvs.view(np.uint32), kv["v_scales"].view(np.uint32)), \
+            gvs = lv.int4_v_scales(p["v_scales"], row, nq1)
+            assert np.array_equal(gvs.view(np.uint32), kq["v_scales"].view(np.uint32)), \
                 f"row {r}: INT4 V scales"
             ring = w.residual_len + 64
             rk, rv = lv.ring_tokens(p["k_resid"], p["v_resid"], r, np.arange(nq, s), ring)
