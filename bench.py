@@ -178,8 +178,10 @@ class Bench:
         self.layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads,
                                       w.num_kv_heads, nb, table.shape[1], 0, w.residual_len)
         # the partition length for the rows' real lengths (known here, as
-        # in a serving scheduler); equal-length batches get the automatic plan
-        self.layout.split_tokens = kvq.plan_split_tokens(self.layout, lens)
+        # in a serving scheduler); several queries per row take the automatic
+        # plan, which counts the queries
+        if not n_query:
+            self.layout.split_tokens = kvq.plan_split_tokens(self.layout, lens)
         b = w.batch
         self.calibrate = None
         self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)

@@ -103,7 +103,7 @@ int row_blocks(const kvq_layout *L, int32_t s) {
 // round's time.  With host_lens the workgroup count is the rows' own
 // partitions; without, every row is taken to be max_blocks long.
 int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
-                       const int32_t *host_lens) {
+                       const int32_t *host_lens, int32_t n_query = 1) {
   const bool int4 = kivi(L);
   // a workgroup's four waves take units of 2 blocks (INT8/FP8) or one
   // 64-token group (INT4) in turn; partitions give each wave whole units
@@ -138,8 +138,15 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
     // 5-9 % (INT4 and FP8, 2-4 workgroups per CU), and a single partition
     // per row also drops the merge launch.  With more (row, head) pairs
     // than CUs, one partition per row.
+    // The generic INT4 layout (more than four query heads per KV head, or
+    // several queries per row) is bound by its arithmetic instead: two
+    // workgroups per CU hide more of it (KIVI shape, 2 / 4 queries per row:
+    // 8192-token partitions 116.9 / 120.8 us per launch, 16384: 125.8 /
+    // 128.0 us, 4096: 120.0 / 125.0 us).
+    const long per_cu =
+        int4 && (L->num_q_heads / L->num_kv_heads > 4 || n_query > 1) ? 2 : 1;
     for (long c = quantum; c < top; c += quantum)
-      if (workgroups(c) <= kCUs) return (int)c;
+      if (workgroups(c) <= per_cu * kCUs) return (int)c;
     return (int)((top + quantum - 1) / quantum * quantum);
   }
   // Workgroups that run as one round.  The 8-bit formats count one per CU:
@@ -181,12 +188,12 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
   return pb;
 }
 
-Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len) {
+Plan make_plan(const kvq_layout *L, int32_t batch, int32_t max_seq_len, int32_t n_query = 1) {
   Plan p{};
   const bool int4 = kivi(L);
   const int blocks = row_blocks(L, max_seq_len);
   int pb = L->split_tokens > 0 ? L->split_tokens / kBlock
-                               : choose_part_blocks(L, batch, blocks, nullptr);
+                               : choose_part_blocks(L, batch, blocks, nullptr, n_query);
   if (pb < (int4 ? 4 : 1)) pb = int4 ? 4 : 1;
   p.part_blocks = pb;
   p.num_parts = blocks > 0 ? (blocks + pb - 1) / pb : 1;  // >= 1: empty rows, INT4 rings
@@ -316,7 +323,7 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
     return KVQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return KVQ_ERR_INVALID_ARG;
-  const Plan p = make_plan(layout, batch, max_seq_len);
+  const Plan p = make_plan(layout, batch, max_seq_len, n_query);
   // one 256-thread workgroup per (partition, KV head, row) in a 1-D grid,
   // (row, partition) pairs padded to a multiple of 8: its work-item count
   // must fit in 32 bits
@@ -446,7 +453,7 @@ static kvq_status check_mq(const kvq_layout *layout, int32_t n_query) {
 size_t kvq_paged_decode_mq_workspace_bytes(const kvq_layout *layout, int32_t n_query,
                                            int32_t batch, int32_t max_seq_len) {
   if (check_mq(layout, n_query) != KVQ_OK || batch < 0 || max_seq_len < 0) return 0;
-  const Plan p = make_plan(layout, batch, max_seq_len);
+  const Plan p = make_plan(layout, batch, max_seq_len, n_query);
   return workspace_layout(layout, batch, p, n_query).total;
 }
 
