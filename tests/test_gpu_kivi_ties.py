@@ -102,14 +102,16 @@ def _crafted_kv(w, n_tokens, seed, qmax, signed):
 def test_kivi_codes_at_rounding_boundaries(monkeypatch, dtype, qmax, signed, fused):
     w = inputs.scaled_down(W["tiny"], name=f"ties-{dtype}", batch=3, num_q_heads=8,
                            num_kv_heads=2, dtype=dtype, k_gran="channel", v_gran="token")
-    lens = [128 + 64 * 5, 128 + 64 * 2 + 17, 256]
+    lens = [128 + 64 * 5, 128 + 64 * 2 + 17, 256, 128 + 64 * 3 - 1]
 
     def crafted(wl, layer, row, n_tokens, device="cpu", seed=0, offset=0):
         k, v = _crafted_kv(wl, n_tokens, 1000 * seed + 10 * row + layer, qmax, signed)
         return (torch.as_tensor(k, device=device), torch.as_tensor(v, device=device))
 
     monkeypatch.setattr(inputs, "gen_kv", crafted)
-    # fused: the last token arrives with kvq_write_decode; 256 then flushes
-    # the group [64, 128) in the step itself
+    # fused: the last token arrives with kvq_write_decode; at 319 the step
+    # flushes the group [128, 192) in workgroups of its decode launch (one
+    # token before it leaves the window), at 256 it reads [64, 128) flushed
+    # by the write before
     res = run_case(w, lens, split_tokens=64, fused=fused)
     check_rows(res)

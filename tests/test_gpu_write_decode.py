@@ -8,8 +8,9 @@ kvq_paged_decode and once with kvq_write_decode, and requires:
   * the fused run to pass the oracle checks (codes and scales bit-exact,
     attention within atol 2e-3 + rtol 1e-2 of the oracle's fp64 attention).
 Lengths cover empty rows, a single token, a token that opens a new block,
-block boundaries, steps that flush a KIVI group out of the fp16 window and
-several partitions.
+block boundaries, steps that flush a KIVI group (one token before it
+leaves the fp16 window) and steps that read one flushed the step before,
+and several partitions.
 """
 
 import numpy as np
@@ -38,9 +39,12 @@ CASES = [
     ("fp8e5m2", "tensor", "head", "identity"),
 ]
 
-# 192, 256 and 1152 cross a 64-token group boundary of the KIVI caches: the
-# step flushes the group that leaves the fp16 window
-LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2], [192, 256, 1152, 129]]
+# KIVI caches flush a group one token before it leaves the fp16 window: a
+# one-token step to length S flushes when S + 1 - 128 is a multiple of 64
+# (191, 255, 319, 1151), and reads a group flushed by the previous write
+# when S - 128 is (192, 256, 1152)
+LENS = [[0, 1, 16, 17], [33, 0, 300, 129], [1000, 64, 65, 2], [192, 256, 1152, 129],
+        [191, 255, 1151, 319]]
 
 
 def _w(dtype, kg, vg, table):
