@@ -317,3 +317,31 @@ def test_plan_split_tokens():
     assert lib.kvq_plan_split_tokens(ctypes.byref(lay), big.ctypes.data, 1) == CAP
     assert lib.kvq_plan_split_tokens(ctypes.byref(lay), None, 0) > 0
     assert lib.kvq_plan_split_tokens(ctypes.byref(_layout(head_dim=64)), None, 0) == UNS
+
+
+def test_plans_of_the_measured_shapes():
+    """The partition plans measured fastest on MI355X (host-only planner)."""
+    import numpy as np
+    from quantized_paged_kv_02_amd import inputs
+    W = inputs.WORKLOADS
+
+    def layout(w, mbs):
+        return kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads, w.num_kv_heads,
+                               w.batch * mbs, mbs, 0, w.residual_len)
+
+    # INT8 short rows: one workgroup per CU per round (2 x 1024 tokens per row)
+    l2 = layout(W["llama2-7b"], 128)
+    assert kvq.plan_split_tokens(l2, np.full(4, 2048, np.int32)) == 1024
+    # compact INT4: at most one workgroup per CU, the shortest such partition
+    k4 = layout(W["kivi-int4"], 2048)
+    lens = np.full(16, 32768, np.int32)
+    assert kvq.plan_split_tokens(k4, lens) == 16384
+    # 128 partials of 2 slots: (m, l) and o for 16 x 32 query heads
+    one = kvq.decode_workspace_bytes(k4, 16, 32768)
+    assert one == kvq.paged_decode_mq_workspace_bytes(k4, 1, 16, 32768)
+    # several queries per row run on the generic INT4 layout: two
+    # workgroups per CU, so twice the partitions, per query
+    assert kvq.paged_decode_mq_workspace_bytes(k4, 2, 16, 32768) == 4 * one
+    # FP16 short rows keep two resident workgroups per CU per round
+    f16 = layout(W["llama2-7b-fp16"], 128)
+    assert kvq.plan_split_tokens(f16, np.full(4, 2048, np.int32)) == 512
