@@ -139,12 +139,16 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
     // per row also drops the merge launch.  With more (row, head) pairs
     // than CUs, one partition per row.
     // The generic INT4 layout (more than four query heads per KV head, or
-    // several queries per row) is bound by its arithmetic instead: two
-    // workgroups per CU hide more of it (KIVI shape, 2 / 4 queries per row:
-    // 8192-token partitions 116.9 / 120.8 us per launch, 16384: 125.8 /
-    // 128.0 us, 4096: 120.0 / 125.0 us).
-    const long per_cu =
-        int4 && (L->num_q_heads / L->num_kv_heads > 4 || n_query > 1) ? 2 : 1;
+    // several queries per row) and the affine INT4 groups (zero-point
+    // operands) are bound by their arithmetic instead: two workgroups per CU
+    // hide more of it.  KIVI shape, 2 / 4 queries per row: 8192-token
+    // partitions 116.9 / 120.8 us per launch, 16384: 125.8 / 128.0 us;
+    // affine: 109.5 against 113.0 us (symmetric, compact: 104.8 against
+    // 100.0 us, so one per CU there).
+    const long per_cu = int4 && (L->dtype == KVQ_INT4_AFFINE ||
+                                 L->num_q_heads / L->num_kv_heads > 4 || n_query > 1)
+                            ? 2
+                            : 1;
     for (long c = quantum; c < top; c += quantum)
       if (workgroups(c) <= per_cu * kCUs) return (int)c;
     return (int)((top + quantum - 1) / quantum * quantum);

@@ -342,6 +342,9 @@ def test_plans_of_the_measured_shapes():
     # several queries per row run on the generic INT4 layout: two
     # workgroups per CU, so twice the partitions, per query
     assert kvq.paged_decode_mq_workspace_bytes(k4, 2, 16, 32768) == 4 * one
+    # affine INT4 groups: two workgroups per CU (arithmetic-bound)
+    ka = layout(W["kivi-int4-affine"], 2048)
+    assert kvq.plan_split_tokens(ka, lens) == 8192
     # FP16 short rows keep two resident workgroups per CU per round
     f16 = layout(W["llama2-7b-fp16"], 128)
     assert kvq.plan_split_tokens(f16, np.full(4, 2048, np.int32)) == 512
