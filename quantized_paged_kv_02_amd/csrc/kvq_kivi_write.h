@@ -60,7 +60,8 @@ __device__ __forceinline__ float2 affine_params(float lo, float hi, float qmax) 
 __device__ __forceinline__ float recip(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
 
 // DT: kInt4 (symmetric), kInt4Affine or kInt2Affine (2-bit codes: 512-byte
-// chunks, the code layouts of kvq.h).
+// chunks, the code layouts of kvq.h).  bx = 2 x (the call's g-th group of
+// row b) + (0: K, 1: V); h: KV head.
 template <int DT>
 __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
   constexpr bool AFF = DT != kInt4;

@@ -30,7 +30,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_paged_kv_02_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h", "kvq_quant.h")]
+                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_args.h", "kvq_quant.h",
+                            "kvq_kivi_write.h")]
 
 
 def kernel_source_hash() -> str:
