@@ -272,15 +272,23 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
 
 
 def check_rows(res: CaseResult, rows=None, check_codes=True):
+    """Check rows against the oracle; returns the largest absolute error and
+    leaves in ``res.tol_ratio`` the largest error as a fraction of its
+    tolerance, max |got - want| / (ATOL + RTOL |want|) (1.0 = at the bound)."""
     rows = range(len(res.lens)) if rows is None else rows
     worst = 0.0
+    ratio = 0.0
     for r in rows:
         want = oracle_row(res, r, check_codes)
         got = res.out[r].astype(np.float64)
         assert np.all(np.isfinite(got)), f"row {r}: non-finite output"
         err = np.abs(got - want)
         worst = max(worst, float(err.max()))
-        ok = err <= ATOL + RTOL * np.abs(want)
+        bound = ATOL + RTOL * np.abs(want)
+        ratio = max(ratio, float((err / bound).max()))
+        ok = err <= bound
         assert ok.all(), (f"row {r}: {int((~ok).sum())} outputs out of tolerance, "
-                          f"max abs err {err.max():.3e}")
+                          f"max abs err {err.max():.3e}, "
+                          f"max err / tolerance {float((err / bound).max()):.3f}")
+    res.tol_ratio = ratio
     return worst

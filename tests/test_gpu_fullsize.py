@@ -2,13 +2,21 @@
 configuration bench.py uses (partitions planned from the rows' lengths by
 kvq_plan_split_tokens, the workload's block tables), on sampled rows.
 
-Each case builds one layer of a workload at its real batch, head counts and
-sequence lengths through the C ABI (prefill of S-1 tokens, then the decode
-token), runs one decode step twice, and checks:
-  * every output is finite and the two runs are bitwise equal;
+Each case builds two layers of a workload, one at a time, at its real
+batch, head counts and sequence lengths through the C ABI (prefill of S-1
+tokens, then the decode token) and checks for each:
+  * every output is finite and a second decode is bitwise equal;
   * for the sampled rows, the paged codes and scales equal the oracle's bit
     for bit and the attention output is within atol 2e-3 + rtol 1e-2 of the
     oracle's fp64 attention over the same dequantized values.
+The largest error as a fraction of its tolerance is printed per case.
+
+The fused cases run the decode step exactly as bench.py times it: the last
+token arrives with kvq_write_decode (appended inside the decode launch; a
+KIVI step also flushes the group leaving the fp16 window at the next length
+in flush workgroups of the same launch).  The KIVI workload runs at its
+configured length 32768 (no group leaves the window) and at 32767, where
+the step flushes the group [32576, 32640).
 """
 
 import numpy as np
@@ -20,6 +28,7 @@ from tests.gpu_harness import check_rows, run_case
 pytestmark = pytest.mark.gpu
 
 W = inputs.WORKLOADS
+LAYERS = (0, 1)     # layers differ only in their seeded data
 
 
 def _sample_rows(lens, seed):
@@ -30,18 +39,50 @@ def _sample_rows(lens, seed):
     return sorted(rows)
 
 
-@pytest.mark.timeout(400)
+def _run_layers(w, lens, fused=False, label=None):
+    label = label or w.name
+    rows = _sample_rows(lens, seed=7)
+    for layer in LAYERS:
+        print(f"{label}: layer {layer} rows {rows} fused={fused} ...", flush=True)
+        # fused: the second decode (kvq_paged_decode over the cache the step
+        # left) must equal the step's own output bit for bit
+        res = run_case(w, lens, layer=layer, decode_twice=True, host_plan=True, fused=fused)
+        assert np.all(np.isfinite(res.out)), "non-finite outputs"
+        assert np.array_equal(res.out, res.out2), "decode is not bitwise reproducible"
+        err = check_rows(res, rows=rows)
+        print(f"{label}: layer {layer} max abs err {err:.2e}, "
+              f"max err / tolerance {res.tol_ratio:.3f}", flush=True)
+        del res
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["llama2-7b", "llama3-8b-gqa", "kivi-int4", "llama3-70b-int8",
                                   "llama3-70b-fp8", "llama2-7b-fp16", "llama3-70b-fp16",
                                   "kivi-int4-affine", "llama3-70b-fp8e5m2",
                                   "kivi-int2-affine"])
 def test_fullsize_layer(name):
     w = W[name]
-    lens = inputs.seq_lens(w)
-    layer = 1          # any layer: layers differ only in their seeded data
-    res = run_case(w, lens, layer=layer, decode_twice=True, host_plan=True)
-    assert np.all(np.isfinite(res.out)), "non-finite outputs"
-    assert np.array_equal(res.out, res.out2), "decode is not bitwise reproducible"
-    rows = _sample_rows(lens, seed=7)
-    err = check_rows(res, rows=rows)
-    print(f"{name}: rows {rows} max abs err {err:.2e}")
+    _run_layers(w, inputs.seq_lens(w))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,delta", [("kivi-int4", 0), ("kivi-int4", -1),
+                                        ("llama3-70b-int8", 0), ("llama2-7b", 0),
+                                        ("llama3-8b-gqa", 0)])
+def test_fullsize_fused_step(name, delta):
+    """The bench's decode step (kvq_write_decode) at full size; delta -1 is
+    the KIVI step that flushes a group inside its decode launch."""
+    w = W[name]
+    lens = inputs.seq_lens(w) + delta
+    _run_layers(w, lens, fused=True, label=f"{name} S{delta:+d} fused")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("hq", [8, 16, 64, 128])
+def test_fullsize_int4_query_groups(hq):
+    """Symmetric INT4 at the KIVI shape with query groups 1, 2, 8 and 16
+    (8 KV heads): g <= 4 runs the compact layout, larger groups the generic
+    one (the Llama-3-70B shape has g = 8)."""
+    w = inputs.scaled_down(W["kivi-int4"], name=f"kivi-int4-g{hq // 8}", num_q_heads=hq,
+                           batch=4)
+    _run_layers(w, inputs.seq_lens(w), fused=True)

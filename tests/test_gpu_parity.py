@@ -81,6 +81,15 @@ def test_int4_kivi(lens, split):
     assert np.array_equal(res.out, res.out2)
 
 
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2), (32, 2), (12, 3)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_int4_group_sizes(hq, hkv, fused):
+    # symmetric INT4, one query per row: query groups 1, 2 and 4 run the
+    # compact layout, 8 and 16 the generic one
+    w = _small("int4", "channel", "token", hq=hq, hkv=hkv, channel_outliers=(8, 10.0, "k"))
+    check_rows(run_case(w, [300, 700, 191, 1000], split_tokens=128, fused=fused))
+
+
 @pytest.mark.parametrize("chunks", [2, 3, 7])
 def test_int4_chunked_writes(chunks):
     # groups flushed from a mix of ring tokens and new tokens, ring slots reused
