@@ -48,8 +48,14 @@
  *    passed as uint16_t; fp32 is IEEE binary32.
  *  - Host integers (batch, total_new, max_new_per_seq, max_seq_len) size the
  *    grids, because seq_lens lives on the device; they must bound the device
- *    values (max over b of seq_lens[b] <= max_seq_len, new tokens per
- *    sequence <= max_new_per_seq).  Violating a bound is undefined.
+ *    values: seq_lens[b] <= max_seq_len for every row b of a decode
+ *    (kvq_paged_decode, kvq_write_decode, kvq_paged_decode_mq), new tokens
+ *    per sequence <= max_new_per_seq for kvq_write.  A decode row longer
+ *    than max_seq_len gets NaN outputs (and, in kvq_write_decode, its token
+ *    is not appended and, for KIVI caches, no group of it is flushed); a
+ *    kvq_write row with more new tokens than max_new_per_seq is undefined.  Block ids in the
+ *    tables must lie in [0, num_blocks): an id outside is an out-of-bounds
+ *    access.  kvq_check_tables checks host copies of both.
  *  - Non-finite K/V inputs give unspecified codes.
  *
  * One kvq_cache describes ONE layer.  Shapes below use
@@ -323,6 +329,28 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
  * errors as kvq_validate).  Host only, no HIP call. */
 int32_t kvq_plan_split_tokens(const kvq_layout *layout, const int32_t *host_seq_lens,
                               int32_t batch);
+
+/* Host-side check of block tables and row lengths, on HOST copies (the
+ * entry points cannot check device data before launching; a block id out
+ * of range there is an out-of-bounds access).  Checks, in row order:
+ *   0 <= host_seq_lens[b] <= max_seq_len <= max_blocks_per_seq * 16;
+ *   every table entry a kernel touches for row b is a block id in
+ *   [0, num_blocks): entries 0 .. ceil(S_b / 16) - 1, or for KIVI caches
+ *   the INT4 blocks 0 .. nq(S_b + 1) / 16 - 1 (see the INT4 layout);
+ *   no block id appears twice among those entries of all rows (two rows
+ *   sharing a block would overwrite each other's tokens).
+ *   host_block_tables: HOST int32 [batch][max_blocks_per_seq];
+ *   host_seq_lens    : HOST int32 [batch];
+ *   bad_row          : optional (may be NULL); receives the first failing
+ *                      row, or -1.
+ * Returns KVQ_OK; KVQ_ERR_INVALID_ARG for a negative length, an id out of
+ * range or repeated, or NULL arrays with batch > 0; KVQ_ERR_CAPACITY for a
+ * length above max_seq_len or max_seq_len above the table's capacity;
+ * layout errors as kvq_validate.  Host only, no HIP call; O(num_blocks)
+ * host memory. */
+kvq_status kvq_check_tables(const kvq_layout *layout, const int32_t *host_block_tables,
+                            const int32_t *host_seq_lens, int32_t batch,
+                            int32_t max_seq_len, int32_t *bad_row);
 
 /* Decode attention for several new query tokens per row (speculative
  * verification of draft tokens, or a chunk of prefill, over the cache; the

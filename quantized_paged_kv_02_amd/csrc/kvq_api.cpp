@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "kvq_args.h"
 
 namespace {
@@ -361,6 +363,7 @@ static kvq_status decode_setup(const kvq_layout *layout, const kvq_cache *cache,
   a->n_query = n_query;
   a->cols = n_query * a->group;
   a->max_blocks_per_seq = layout->max_blocks_per_seq;
+  a->max_seq_len = max_seq_len;
   a->part_blocks = p.part_blocks;
   a->num_parts = p.num_parts;
   a->slots = p.slots;
@@ -440,6 +443,48 @@ int32_t kvq_plan_split_tokens(const kvq_layout *layout, const int32_t *host_seq_
   if ((int64_t)max_len > (int64_t)layout->max_blocks_per_seq * kBlock) return KVQ_ERR_CAPACITY;
   const int pb = choose_part_blocks(layout, batch, row_blocks(layout, max_len), host_seq_lens);
   return pb * kBlock;
+}
+
+// ---- host-side check of block tables and lengths ------------------------------
+
+kvq_status kvq_check_tables(const kvq_layout *layout, const int32_t *host_block_tables,
+                            const int32_t *host_seq_lens, int32_t batch, int32_t max_seq_len,
+                            int32_t *bad_row) {
+  if (bad_row) *bad_row = -1;
+  const kvq_status st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return KVQ_ERR_INVALID_ARG;
+  if (batch == 0) return KVQ_OK;
+  if (!host_block_tables || !host_seq_lens) return KVQ_ERR_INVALID_ARG;
+  const int64_t mbs = layout->max_blocks_per_seq;
+  if ((int64_t)max_seq_len > mbs * kBlock) return KVQ_ERR_CAPACITY;
+  // one bit per physical block: a block that two table entries name would
+  // be written by both
+  std::vector<uint8_t> used((size_t)layout->num_blocks, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t s = host_seq_lens[b];
+    if (s < 0) {
+      if (bad_row) *bad_row = b;
+      return KVQ_ERR_INVALID_ARG;
+    }
+    if (s > max_seq_len) {
+      if (bad_row) *bad_row = b;
+      return KVQ_ERR_CAPACITY;
+    }
+    // entries the kernels touch: every block of the row (INT8 / FP8 / FP16);
+    // the INT4 blocks of a KIVI row, through the group the next token flushes
+    const int64_t need = kivi(layout) ? kivi_len(s + 1, layout->residual_len) / kBlock
+                                      : ((int64_t)s + kBlock - 1) / kBlock;
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t id = host_block_tables[(int64_t)b * mbs + j];
+      if (id < 0 || id >= layout->num_blocks || used[(size_t)id]) {
+        if (bad_row) *bad_row = b;
+        return KVQ_ERR_INVALID_ARG;
+      }
+      used[(size_t)id] = 1;
+    }
+  }
+  return KVQ_OK;
 }
 
 // ---- several query tokens per row ----------------------------------------------

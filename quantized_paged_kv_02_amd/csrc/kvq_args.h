@@ -81,6 +81,7 @@ struct DecodeArgs {
   int32_t n_query;
   int32_t cols;             // n_query * group <= 16
   int32_t max_blocks_per_seq;
+  int32_t max_seq_len;      // the host's bound; longer rows get NaN outputs
   int32_t part_blocks;      // blocks per main partition
   int32_t num_parts;        // main partitions in the grid
   int32_t slots;            // partial slots per (b, hq) = num_parts;

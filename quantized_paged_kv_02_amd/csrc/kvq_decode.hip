@@ -1485,8 +1485,9 @@ __device__ void merge_and_store(const DecodeArgs &a, SharedLds &sh, Softmax &st,
   const size_t row =
       ((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group + (hn - qt * a.group);
   if (direct) {
-    // a query that saw no token (several queries, short row) gets zeros
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    // a query that saw no token (several queries, short row) gets zeros; a
+    // non-finite sum (NaN or infinite values in the cache) stays visible
+    const float inv = lt != 0.0f ? 1.0f / lt : 0.0f;
     float *out = a.out + row * kHeadDim + 8 * c8;
     *reinterpret_cast<f32x4 *>(out) = acc0 * inv;
     *reinterpret_cast<f32x4 *>(out + 4) = acc1 * inv;
@@ -1616,6 +1617,15 @@ __device__ __forceinline__ WriteArgs step_write_args(const DecodeArgs &a) {
   return w;
 }
 
+// out rows of (row b, KV head h): column hn of this thread (tid / 16), its
+// eight channels 8 (tid % 16) ..
+__device__ __forceinline__ float *out_cols(const DecodeArgs &a, int b, int h, int tid) {
+  const int hn = tid >> 4, c8 = tid & 15;
+  const int qt = hn / a.group;
+  return a.out + (((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group +
+                  (hn - qt * a.group)) * kHeadDim + 8 * c8;
+}
+
 template <int DT, int KS, int VS, bool G4>
 __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds &sh) {
   if constexpr (is_kivi(DT)) {
@@ -1629,7 +1639,10 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       const int f = blockIdx.x - main_wgs;
       const int r = f >> 1;
       const int fb = r / a.num_kv_heads;
-      if (fb < a.batch) int4_flush<DT>(step_write_args(a), f & 1, r - fb * a.num_kv_heads, fb);
+      // a row longer than the launch covers (above the host's max_seq_len)
+      // is left as it is, as its decode workgroups leave it
+      if (fb < a.batch && a.seq_lens[fb] <= a.max_seq_len)
+        int4_flush<DT>(step_write_args(a), f & 1, r - fb * a.num_kv_heads, fb);
       return;
     }
   }
@@ -1662,17 +1675,24 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
 
   if (seq_len <= 0) {
     // rows of length 0: zeros (written here only when no reduce follows)
-    if (direct && p == 0) {
-      const int hn = tid >> 4, c8 = tid & 15;
-      if (hn < a.cols) {
-        const int qt = hn / a.group;
-        float *out = a.out +
-                     (((size_t)b * a.n_query + qt) * a.num_q_heads + h * a.group +
-                      (hn - qt * a.group)) * kHeadDim + 8 * c8;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4 *>(out) = z;
-        *reinterpret_cast<f32x4 *>(out + 4) = z;
-      }
+    if (direct && p == 0 && (tid >> 4) < a.cols) {
+      float *out = out_cols(a, b, h, tid);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4 *>(out) = z;
+      *reinterpret_cast<f32x4 *>(out + 4) = z;
+    }
+    return;
+  }
+  if (seq_len > a.max_seq_len) {
+    // A row longer than the host's max_seq_len may have partitions this
+    // launch does not hold (and, in a decode step, its token is not
+    // appended): its outputs become NaN instead of attention over part of
+    // the row (the partition merge writes them when it runs).
+    if (direct && p == 0 && (tid >> 4) < a.cols) {
+      float *out = out_cols(a, b, h, tid);
+      const float nan = __builtin_nanf("");
+      *reinterpret_cast<f32x4 *>(out) = f32x4{nan, nan, nan, nan};
+      *reinterpret_cast<f32x4 *>(out + 4) = f32x4{nan, nan, nan, nan};
     }
     return;
   }
@@ -1786,6 +1806,13 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
       } else {
         total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
       }
+      if (seq_len > a.max_seq_len) {
+        // the row is longer than the host's max_seq_len: NaN, not a
+        // partial answer
+        const float nan = __builtin_nanf("");
+        *reinterpret_cast<f32x4 *>(out) = f32x4{nan, nan, nan, nan};
+        return;
+      }
     }
     float cm = big;
 #pragma unroll
@@ -1805,8 +1832,9 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
       }
     }
   }
-  // a query that saw no token (several queries, short row) gets zeros
-  *reinterpret_cast<f32x4 *>(out) = lt > 0.0f ? acc * (1.0f / lt) : f32x4{0.f, 0.f, 0.f, 0.f};
+  // a query that saw no token (several queries, short row) gets zeros; a
+  // non-finite sum (NaN or infinite values in the cache) stays visible
+  *reinterpret_cast<f32x4 *>(out) = lt != 0.0f ? acc * (1.0f / lt) : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 template <int DT, int KS>

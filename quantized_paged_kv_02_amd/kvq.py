@@ -33,7 +33,7 @@ EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
             "kvq_write", "kvq_paged_decode", "kvq_write_decode",
             "kvq_calibrate_workspace_bytes", "kvq_calibrate",
             "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq",
-            "kvq_plan_split_tokens")
+            "kvq_plan_split_tokens", "kvq_check_tables")
 
 
 class Layout(ctypes.Structure):
@@ -101,6 +101,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_paged_decode_mq.restype = I32
     lib.kvq_paged_decode_mq.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, I32,
                                         P, P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_check_tables.restype = I32
+    lib.kvq_check_tables.argtypes = [ctypes.POINTER(Layout), P, P, I32, I32,
+                                     ctypes.POINTER(I32)]
     lib.kvq_calibrate_workspace_bytes.restype = SZ
     lib.kvq_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32]
     lib.kvq_calibrate.restype = I32
@@ -126,6 +129,42 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _arg(t, name: str, dtype=None, shape=None, optional: bool = False):
+    """Check one tensor argument before its pointer crosses the C ABI: a
+    contiguous tensor on the current GPU, of ``dtype`` and ``shape`` (None
+    entries of ``shape`` match any size).  The library sees bare pointers,
+    so a wrong dtype, stride or shape would be misread, not reported."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                             f"{tuple('*' if w is None else w for w in shape)}")
+
+
+def _tables(block_tables, seq_lens, layout: Layout) -> int:
+    """Check block_tables int32 [batch, MBS] and seq_lens int32 [batch];
+    returns batch."""
+    _arg(block_tables, "block_tables", torch.int32, (None, layout.max_blocks_per_seq))
+    batch = int(block_tables.shape[0])
+    _arg(seq_lens, "seq_lens", torch.int32, (batch,))
+    return batch
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -146,6 +185,8 @@ class KVCache:
     ring_rows: int
 
     def struct(self) -> Cache:
+        for name in ("k_codes", "v_codes", "k_scales", "v_scales", "k_resid", "v_resid"):
+            _arg(getattr(self, name), f"cache.{name}", optional=True)
         return Cache(_ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scales),
                      _ptr(self.v_scales), _ptr(self.k_resid), _ptr(self.v_resid),
                      self.ring_rows)
@@ -224,8 +265,12 @@ def alloc_workspace(layout: Layout, batch: int, max_seq_len: int, device="cuda")
 def write(cache: KVCache, k_new, v_new, cu_new, block_tables, seq_lens,
           max_new_per_seq: int, stream=None) -> None:
     """kvq_write: quantize-on-write of packed new tokens (see kvq.h)."""
-    batch = block_tables.shape[0]
-    total_new = k_new.shape[0]
+    lay = cache.layout
+    batch = _tables(block_tables, seq_lens, lay)
+    total_new = int(k_new.shape[0]) if isinstance(k_new, torch.Tensor) else 0
+    _arg(k_new, "k_new", torch.float16, (total_new, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", torch.float16, (total_new, lay.num_kv_heads, lay.head_dim))
+    _arg(cu_new, "cu_new", torch.int32, (batch + 1,))
     c = cache.struct()
     st = LIB.kvq_write(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(k_new), _ptr(v_new),
                        _ptr(cu_new), _ptr(block_tables), _ptr(seq_lens), batch, total_new,
@@ -237,7 +282,11 @@ def write(cache: KVCache, k_new, v_new, cu_new, block_tables, seq_lens,
 def paged_decode(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
                  softmax_scale: float, out, workspace, stream=None) -> None:
     """kvq_paged_decode: one decode step of attention (see kvq.h)."""
-    batch = block_tables.shape[0]
+    lay = cache.layout
+    batch = _tables(block_tables, seq_lens, lay)
+    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(workspace, "workspace")
     c = cache.struct()
     st = LIB.kvq_paged_decode(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(q),
                               _ptr(block_tables), _ptr(seq_lens), batch, max_seq_len,
@@ -251,7 +300,13 @@ def paged_decode(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
 def write_decode(cache: KVCache, k_new, v_new, q, block_tables, seq_lens, max_seq_len: int,
                  softmax_scale: float, out, workspace, stream=None) -> None:
     """kvq_write_decode: append one token per row, then decode (see kvq.h)."""
-    batch = block_tables.shape[0]
+    lay = cache.layout
+    batch = _tables(block_tables, seq_lens, lay)
+    _arg(k_new, "k_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(workspace, "workspace")
     c = cache.struct()
     st = LIB.kvq_write_decode(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(k_new),
                               _ptr(v_new), _ptr(q), _ptr(block_tables), _ptr(seq_lens), batch,
@@ -272,6 +327,12 @@ def calibrate(layout: Layout, k, v, k_scales, v_scales, accumulate: bool = False
     [n_tokens, H, 128] into the scale tensors (see kvq.h).  A workspace is
     allocated when none is given."""
     n = int(k.shape[0]) if k is not None else int(v.shape[0])
+    for name, t in (("k", k), ("v", v)):
+        _arg(t, name, torch.float16, (n, layout.num_kv_heads, layout.head_dim), optional=True)
+    for name, t, g in (("k_scales", k_scales, layout.k_gran),
+                       ("v_scales", v_scales, layout.v_gran)):
+        if g != PER_TOKEN:
+            _arg(t, name, torch.float32, scale_shape(layout, g), optional=True)
     if workspace is None:
         dev = (k if k is not None else v).device
         workspace = torch.empty(max(calibrate_workspace_bytes(layout, n), 256),
@@ -292,7 +353,14 @@ def paged_decode_mq_workspace_bytes(layout: Layout, n_query: int, batch: int,
 def paged_decode_mq(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
                     softmax_scale: float, out, workspace, stream=None) -> None:
     """kvq_paged_decode_mq: q [batch, n_query, Hq, 128] (see kvq.h)."""
-    batch, n_query = int(q.shape[0]), int(q.shape[1])
+    lay = cache.layout
+    batch = _tables(block_tables, seq_lens, lay)
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [batch, n_query, Hq, 128] tensor")
+    n_query = int(q.shape[1])
+    _arg(q, "q", torch.float16, (batch, n_query, lay.num_q_heads, lay.head_dim))
+    _arg(out, "out", torch.float32, (batch, n_query, lay.num_q_heads, lay.head_dim))
+    _arg(workspace, "workspace")
     c = cache.struct()
     st = LIB.kvq_paged_decode_mq(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(q), n_query,
                                  _ptr(block_tables), _ptr(seq_lens), batch, max_seq_len,
@@ -313,3 +381,19 @@ def plan_split_tokens(layout: Layout, host_seq_lens) -> int:
     if r <= 0:
         raise KvqError(r, "kvq_plan_split_tokens")
     return int(r)
+
+
+def check_tables(layout: Layout, host_block_tables, host_seq_lens, max_seq_len: int):
+    """kvq_check_tables on host copies: returns (status, first bad row or -1)."""
+    import numpy as np
+    tab = np.ascontiguousarray(np.asarray(host_block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(host_seq_lens, dtype=np.int32))
+    batch = int(lens.size)
+    if batch and tab.shape != (batch, layout.max_blocks_per_seq):
+        raise ValueError(f"host_block_tables has shape {tab.shape}, expected "
+                         f"({batch}, {layout.max_blocks_per_seq})")
+    bad = ctypes.c_int32(-1)
+    st = LIB.kvq_check_tables(ctypes.byref(layout), tab.ctypes.data if batch else None,
+                              lens.ctypes.data if batch else None, batch, int(max_seq_len),
+                              ctypes.byref(bad))
+    return int(st), int(bad.value)

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from quantized_paged_kv_02_amd import kvq
@@ -348,3 +349,58 @@ def test_plans_of_the_measured_shapes():
     # FP16 short rows keep two resident workgroups per CU per round
     f16 = layout(W["llama2-7b-fp16"], 128)
     assert kvq.plan_split_tokens(f16, np.full(4, 2048, np.int32)) == 512
+
+
+# --- host-side check of block tables and lengths (kvq_check_tables)
+
+def _tab_layout(dtype="int8", nb=10, mbs=4):
+    kg, vg = ("channel", "token") if dtype == "int4" else ("token", "token")
+    return kvq.make_layout(dtype, kg, vg, 8, 2, nb, mbs)
+
+
+def test_check_tables_accepts_valid_tables():
+    lay = _tab_layout()
+    tab = [[0, 1, 2, 0], [3, 4, 5, 6]]        # row 0 uses 3 entries (S = 40)
+    assert kvq.check_tables(lay, tab, [40, 64], 64) == (OK, -1)
+    assert kvq.check_tables(lay, tab, [0, 0], 0) == (OK, -1)
+    assert kvq.check_tables(lay, [[0] * 4] * 0, [], 0) == (OK, -1)
+
+
+@pytest.mark.parametrize("tab,lens,max_len,want", [
+    ([[0, 1, 2, 0], [3, 4, 5, 6]], [40, 65], 64, (CAP, 1)),     # length above max_seq_len
+    ([[0, 1, 2, 0], [3, 4, 5, 6]], [-1, 64], 64, (INV, 0)),     # negative length
+    ([[0, 1, 10, 0], [3, 4, 5, 6]], [40, 64], 64, (INV, 0)),    # id == num_blocks
+    ([[0, 1, 2, 0], [3, -4, 5, 6]], [40, 64], 64, (INV, 1)),    # negative id
+    ([[0, 1, 2, 0], [3, 4, 2, 6]], [40, 64], 64, (INV, 1)),     # block used by two rows
+    ([[0, 0, 2, 0], [3, 4, 5, 6]], [40, 64], 64, (INV, 0)),     # used twice in one row
+    ([[0, 1, 2, 0], [3, 4, 5, 6]], [40, 64], 65, (CAP, -1)),    # beyond MBS * 16
+])
+def test_check_tables_rejects(tab, lens, max_len, want):
+    assert kvq.check_tables(_tab_layout(), tab, lens, max_len) == want
+
+
+def test_check_tables_kivi_counts_int4_blocks_only():
+    # KIVI: a row of length S touches the INT4 blocks of groups below
+    # nq(S + 1); S = 255 -> nq(256) = 128 -> 8 blocks, S = 191 -> 4 blocks
+    lay = _tab_layout("int4", nb=20, mbs=16)
+    tab = np.full((2, 16), -1, np.int32)
+    tab[0, :8] = np.arange(8)
+    tab[1, :4] = np.arange(8, 12)
+    assert kvq.check_tables(lay, tab, [255, 191], 256) == (OK, -1)
+    tab[1, 3] = -1
+    assert kvq.check_tables(lay, tab, [255, 191], 256) == (INV, 1)
+    assert kvq.check_tables(lay, tab, [255, 190], 256) == (OK, -1)   # nq(191) = 0
+
+
+def test_binding_rejects_host_tensors():
+    # the binding checks every tensor before a pointer crosses the ABI
+    import torch
+    lay = _tab_layout()
+    t = lambda *s, d=torch.uint8: torch.zeros(s, dtype=d)   # noqa: E731
+    cache = kvq.KVCache(lay, t(10, 2, 2048), t(10, 2, 2048), t(10, 2, 16, d=torch.float32),
+                        t(10, 2, 16, d=torch.float32), None, None, 0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.paged_decode(cache, t(1, 8, 128, d=torch.float16), t(1, 4, d=torch.int32),
+                         t(1, d=torch.int32), 16, 0.1, t(1, 8, 128, d=torch.float32),
+                         t(256))
+
