@@ -38,7 +38,8 @@
  *  - All buffers are caller-owned DEVICE pointers except the kvq_layout and
  *    kvq_cache structs themselves, which are host memory read during the call
  *    only.  The library allocates, frees and synchronises nothing; it keeps no
- *    state between calls and may be called from several host threads.
+ *    state between calls (except the per-GPU partials array of
+ *    kvq_write_decode_noalloc) and may be called from several host threads.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Kernels run
  *    asynchronously on it, in call order.
  *  - Arguments are validated on the host before any launch; on error a
@@ -313,6 +314,31 @@ kvq_status kvq_write_decode(const kvq_layout *layout, const kvq_cache *cache,
                             int32_t max_seq_len, float softmax_scale,
                             float *out, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* kvq_write_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * hipMalloc): the same step, bit for bit, with the split-K partials in a
+ * device array the library holds (KVQ_NOALLOC_SCRATCH_BYTES per GPU, kept
+ * until the process ends) instead of a caller workspace.  Arguments as for
+ * kvq_write_decode without workspace / workspace_bytes; the caller still
+ * owns every other buffer.  The library allocates nothing: the array's
+ * device address is looked up (hipGetSymbolAddress) on the first call on
+ * each device, with the stream's device current.
+ * Errors: as for kvq_write_decode; KVQ_ERR_WORKSPACE when the launch's
+ * partials (kvq_decode_workspace_bytes) exceed KVQ_NOALLOC_SCRATCH_BYTES
+ * (checked before any HIP call; a larger split_tokens needs fewer);
+ * KVQ_ERR_HIP when the array's address cannot be found.
+ * All calls on one GPU share its array, which keeps the last call's
+ * partials (they need no clearing: every one read is written first by the
+ * same call).  Calls that overlap in time on one GPU (several streams or
+ * host threads) race on it and must be serialised by the caller. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_write_decode_noalloc(const kvq_layout *layout, const kvq_cache *cache,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const uint16_t *q, const int32_t *block_tables,
+                                    const int32_t *seq_lens, int32_t batch,
+                                    int32_t max_seq_len, float softmax_scale, float *out,
+                                    void *stream);
 
 /* Partition length for a batch whose row lengths the caller knows on the
  * host (a serving scheduler does): the split_tokens value (tokens, a

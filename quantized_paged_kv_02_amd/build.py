@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libkvq.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["kvq_api.cpp", "kvq_write.hip", "kvq_decode.hip", "kvq_calibrate.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_write.hip", "kvq_decode.hip", "kvq_calibrate.hip",
+           "kvq_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

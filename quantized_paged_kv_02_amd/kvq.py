@@ -33,7 +33,8 @@ EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
             "kvq_write", "kvq_paged_decode", "kvq_write_decode",
             "kvq_calibrate_workspace_bytes", "kvq_calibrate",
             "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq",
-            "kvq_plan_split_tokens", "kvq_check_tables")
+            "kvq_plan_split_tokens", "kvq_check_tables", "kvq_write_decode_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
 class Layout(ctypes.Structure):
@@ -94,6 +95,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_write_decode.restype = I32
     lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
                                      P, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.kvq_write_decode_noalloc.restype = I32
+    lib.kvq_write_decode_noalloc.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P,
+                                             P, P, P, P, I32, I32, ctypes.c_float, P, P]
     lib.kvq_plan_split_tokens.restype = I32
     lib.kvq_plan_split_tokens.argtypes = [ctypes.POINTER(Layout), P, I32]
     lib.kvq_paged_decode_mq_workspace_bytes.restype = SZ
@@ -315,6 +319,25 @@ def write_decode(cache: KVCache, k_new, v_new, q, block_tables, seq_lens, max_se
                               _stream_handle(stream))
     if st != 0:
         raise KvqError(st, "kvq_write_decode")
+
+
+def write_decode_noalloc(cache: KVCache, k_new, v_new, q, block_tables, seq_lens,
+                         max_seq_len: int, softmax_scale: float, out, stream=None) -> None:
+    """kvq_write_decode_noalloc: kvq_write_decode with the partials in the
+    library's per-GPU array (no workspace; see kvq.h)."""
+    lay = cache.layout
+    batch = _tables(block_tables, seq_lens, lay)
+    _arg(k_new, "k_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
+    c = cache.struct()
+    st = LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(c), _ptr(k_new),
+                                      _ptr(v_new), _ptr(q), _ptr(block_tables),
+                                      _ptr(seq_lens), batch, max_seq_len,
+                                      float(softmax_scale), _ptr(out), _stream_handle(stream))
+    if st != 0:
+        raise KvqError(st, "kvq_write_decode_noalloc")
 
 
 def calibrate_workspace_bytes(layout: Layout, n_tokens: int) -> int:

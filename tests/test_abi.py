@@ -404,3 +404,19 @@ def test_binding_rejects_host_tensors():
                          t(1, d=torch.int32), 16, 0.1, t(1, 8, 128, d=torch.float32),
                          t(256))
 
+
+def test_noalloc_rejects_oversized_partials_before_any_hip_call():
+    # 64 rows x 32 query heads x 128 partitions x 520 bytes > 16 MiB: rejected
+    # on the host (fake pointers: nothing is dereferenced or launched)
+    lay = kvq.make_layout("int8", "token", "token", 32, 32, 8192, 128, 16)
+    assert kvq.decode_workspace_bytes(lay, 64, 2048) > kvq.NOALLOC_SCRATCH_BYTES
+    st = kvq.LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(_cache()), FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, 64, 2048, 0.1, FAKE, None)
+    assert st == WS
+    # argument errors come first, as for kvq_write_decode
+    st = kvq.LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(_cache()), FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, 64, 4096, 0.1, FAKE, None)
+    assert st == CAP
+    assert kvq.LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(_cache()), FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, 0, 2048, 0.1, FAKE,
+                                            None) == OK
