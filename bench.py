@@ -1,20 +1,23 @@
 """Decode-step benchmark of libkvq on one MI355X.
 
-One step = for every layer: quantize-on-write of each row's new token
-(kvq_write) and split-K paged decode attention over the whole cache
-(kvq_paged_decode).  The cache is prefilled once, untimed; every step
-rewrites the same position with the same token, so all steps do identical
-work.  The step is captured once into a HIP graph and replayed (``--eager``
-launches it from Python instead).
+One step = for every layer: quantize-on-write of each row's new token and
+split-K paged decode attention over the whole cache, as one
+kvq_write_decode call (``--separate``: kvq_write then kvq_paged_decode).
+The cache is prefilled once, untimed; every step rewrites the same
+position with the same token, so all steps do identical work.  The step is
+captured once into a HIP graph and replayed (``--eager`` launches it from
+Python instead).
 
 Prints ONE JSON line: KV read GB/s of the step (algorithmic decode bytes /
-step time) as ``value``, decode tokens/s, the decode kernel's roofline
-figures (per-launch algorithmic bytes / its HIP-event-timed launch
-duration) and the CPU oracle's rate on a bounded sample of the same
-workload.
+step time) as ``value``, decode tokens/s, the decode launch's roofline
+figures (per-launch algorithmic bytes / its HIP-event-timed duration, also
+against the read rate a loads-only probe reaches, and the rocprofv3
+durations of its decode and merge kernels when profiles/ holds them for
+these sources), on KIVI caches the step that flushes a group, and the CPU
+oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-probe] [--probe]
 """
 
 from __future__ import annotations
@@ -41,6 +44,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 # the configuration the decode bandwidth target (>= 70 % of HBM peak) is set
 # on.  Every other workload runs with --workload.
 DEFAULT_WORKLOAD = "kivi-int4"
+KIVI = ("int4", "int4-affine", "int2-affine")
+PROBE_LIB = os.path.join(ROOT, "quantized_paged_kv_02_amd", "libkvq_probe.so")
+TIMES_FILE = os.path.join(ROOT, "profiles", "decode_kernel_times.json")
 
 
 def decode_kernel_label(dtype: str, n_query: int) -> str:
@@ -61,9 +67,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 def _cpu_unit(args):
     """Quantize one (layer, row) cache with the oracle (untimed), then time
-    the oracle's decode step for it: quantize the new token (INT4: the
-    64-token group that leaves the fp16 window), dequantize the row's cache
-    and run fp64 attention for all query heads.  Returns seconds."""
+    the oracle's decode step for it: the write (quantize the new token;
+    INT4: the 64-token group that leaves the fp16 window) and the attention
+    (dequantize the row's cache, fp64 attention for all query heads).
+    Returns (write seconds, attention seconds)."""
     name, layer, row, seq = args
     from threadpoolctl import threadpool_limits
     import torch
@@ -91,20 +98,22 @@ def _cpu_unit(args):
                     else:
                         oracle.kivi_quantize_k_group(k[g0:g0 + 64, h])
                         oracle.kivi_quantize_v_tokens(v[g0:g0 + 64, h])
+            t1 = time.perf_counter()
             k_hat, v_hat = oracle.kivi_dequantize(full)
             oracle.decode_attention(q, k_hat, v_hat, scale)
-            return time.perf_counter() - t0
+            return t1 - t0, time.perf_counter() - t1
         if w.dtype == "fp16":
             # unquantized cache: the new token is stored as is
             t0 = time.perf_counter()
             oracle.decode_attention(q, k, v, scale)
-            return time.perf_counter() - t0
+            return 0.0, time.perf_counter() - t0
         if w.k_gran == "token":
             kc, ks = oracle.quantize_per_token(k, w.dtype)
             vc, vs = oracle.quantize_per_token(v, w.dtype)
             t0 = time.perf_counter()
             oracle.quantize_per_token(k[seq - 1:], w.dtype)
             oracle.quantize_per_token(v[seq - 1:], w.dtype)
+            t1 = time.perf_counter()
             k_hat = oracle.dequantize(kc, ks[..., None], w.dtype)
             v_hat = oracle.dequantize(vc, vs[..., None], w.dtype)
         else:
@@ -116,47 +125,138 @@ def _cpu_unit(args):
             t0 = time.perf_counter()
             oracle.quantize_static(k[seq - 1:], sk, w.k_gran, w.dtype)
             oracle.quantize_static(v[seq - 1:], sv, w.v_gran, w.dtype)
+            t1 = time.perf_counter()
             k_hat = oracle.dequantize(kc, sk.reshape(shp), w.dtype)
             v_hat = oracle.dequantize(vc, sv.reshape(shp), w.dtype)
         oracle.decode_attention(q, k_hat, v_hat, scale)
-        return time.perf_counter() - t0
+        return t1 - t0, time.perf_counter() - t1
+
+
+def _host_cpu():
+    """(logical CPUs of the host, CPUs this process may run on, CPU model)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    return os.cpu_count() or 1, allowed, model
 
 
 def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
-    """Time the oracle over a bounded sample of (layer, row) units on
-    ``workers`` host processes (one BLAS thread each): one unit per process
-    first, then as many more as fit in about ``target_cpu_s`` seconds of
-    CPU work (never more than the whole step)."""
+    """Time the oracle over a bounded sample of (layer, row) units: first
+    one unit alone in one process (the single-thread figure), then units on
+    ``workers`` host processes at once (one BLAS thread each) until about
+    ``target_cpu_s`` seconds of CPU work (never more than the whole step).
+    Write (quantize the new token) and attention are timed separately."""
     import concurrent.futures as cf
     import multiprocessing as mp
     all_units = [(w.name, layer, row, int(lens[row]))
                  for layer in range(w.layers) for row in range(w.batch)]
     ctx = mp.get_context("spawn")
+
+    def unit_bytes(units):
+        return sum(metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [u[3]], w.num_q_heads,
+                                        w.num_kv_heads, w.residual_len) for u in units)
+
+    # single thread: one process, nothing else running
+    with cf.ProcessPoolExecutor(max_workers=1, mp_context=ctx) as ex:
+        tw1, ta1 = ex.submit(_cpu_unit, all_units[-1]).result()
+    single = {"GBps": round(unit_bytes(all_units[-1:]) / (tw1 + ta1) / 1e9, 4),
+              "tokens_per_s": round(1.0 / ((tw1 + ta1) * w.layers), 4),
+              "write_s": round(tw1, 5), "attention_s": round(ta1, 4),
+              "note": "one (layer, row) unit in one process; tokens/s for one row "
+                      "through all layers"}
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         first = all_units[:min(workers, len(all_units))]
         secs = list(ex.map(_cpu_unit, first))
-        per_unit = sum(secs) / len(secs)
-        more = int(max(0.0, target_cpu_s - sum(secs)) / max(per_unit, 1e-6))
+        per_unit = sum(a + b for a, b in secs) / len(secs)
+        more = int(max(0.0, target_cpu_s - sum(a + b for a, b in secs)) / max(per_unit, 1e-6))
         rest = all_units[len(first):len(first) + more]
         if rest:
             secs += list(ex.map(_cpu_unit, rest))
     units = all_units[:len(secs)]
     n = len(units)
     cores = min(workers, n)
-    sample_bytes = sum(metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, [u[3]],
-                                            w.num_q_heads, w.num_kv_heads, w.residual_len)
-                       for u in units)
+    tw = sum(a for a, _ in secs)
+    ta = sum(b for _, b in secs)
     # units ran concurrently on `cores` processes
-    wall = sum(secs) / cores
-    gbs = sample_bytes / wall / 1e9
-    step_s = sum(secs) / n * w.layers * w.batch / cores
+    wall = (tw + ta) / cores
+    gbs = unit_bytes(units) / wall / 1e9
+    step_s = (tw + ta) / n * w.layers * w.batch / cores
+    nproc, allowed, model = _host_cpu()
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "tokens_per_s": round(w.batch / step_s, 4),
+            "write_s_per_unit": round(tw / n, 5), "attention_s_per_unit": round(ta / n, 4),
+            "single_thread": single, "nproc": nproc, "cpus_allowed": allowed,
+            "cpu_model": model,
             "sample": (f"{n} of {len(all_units)} (layer, row) units of {w.name}; each: "
-                       f"quantize the new token, dequantize the row's cache, fp64 attention "
-                       f"(numpy oracle, 1 BLAS thread per process, {cores} processes); "
-                       f"{sum(secs):.1f} s of CPU work; K/V drawn on the CPU by the same "
-                       f"recipe")}
+                       f"quantize the new token (write), dequantize the row's cache and fp64 "
+                       f"attention (attention); numpy oracle, 1 BLAS thread per process, "
+                       f"{cores} processes at once (the GPU box's CPU share is 16 of its "
+                       f"{nproc} logical CPUs); {tw + ta:.1f} s of CPU work; K/V drawn on "
+                       f"the CPU by the same recipe")}
+
+
+# ---------------------------------------------------------------------------
+# Achievable read bandwidth: the probe of libkvq_probe.so
+# ---------------------------------------------------------------------------
+
+def bandwidth_probe(gib: int = 4, reps: int = 5):
+    """Read ``gib`` GiB in 1 KiB chunks (one 16-byte buffer load per lane,
+    the decode's granule and cache policy) with several grid sizes, in
+    wavefront-strided and in scattered chunk order; each configuration is
+    launched back to back ``reps`` times between one HIP event pair.
+    Returns the best rate (GB/s, 1e9 bytes) and every configuration's."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build it with "
+                         "`python -m quantized_paged_kv_02_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.kvq_probe_read.restype = ctypes.c_int
+    lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)          # every dword xors to 0: the sink is never written
+    grids = (256, 512, 1024, 2048)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def launch(wgs, order):
+        rc = lib.kvq_probe_read(buf.data_ptr(), nbytes, wgs, order, sink.data_ptr(),
+                                stream.cuda_stream)
+        if rc != 0:
+            raise SystemExit(f"kvq_probe_read failed ({rc})")
+
+    rows = []
+    for order, name in ((0, "strided"), (1, "scattered")):
+        for wgs in grids:
+            launch(wgs, order)
+            e0.record()
+            for _ in range(reps):
+                launch(wgs, order)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            rows.append({"order": name, "workgroups": wgs, "us": round(ms * 1e3, 1),
+                         "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    del buf
+    best = max(rows, key=lambda r: r["GBps"])
+    return {"GBps": best["GBps"], "best": best, "bytes_per_launch": nbytes,
+            "chunk_bytes": 1024, "all": rows,
+            "kernel": "kvq_probe_read_kernel (libkvq_probe.so): loads only, 8 chunks in "
+                      "flight per wavefront"}
 
 
 # ---------------------------------------------------------------------------
@@ -186,6 +286,7 @@ class Bench:
         self.calibrate = None
         self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)
         self.caches, self.k_new, self.v_new, self.q, self.out = [], [], [], [], []
+        self.k_prev, self.v_prev = [], []
         for layer in range(w.layers):
             kk, vv = [], []
             for r in range(b):
@@ -233,6 +334,12 @@ class Bench:
             nq = max(n_query, 1)   # new tokens per row and step
             self.k_new.append(torch.cat([k[-nq:] for k in kk]).contiguous())
             self.v_new.append(torch.cat([v[-nq:] for v in vv]).contiguous())
+            if not n_query and w.dtype in KIVI and int(lens.min()) >= 2:
+                # the token before the last: a step at length S - 1 rewrites
+                # it (the same values the prefill stored) and flushes the
+                # group that leaves the fp16 window at S
+                self.k_prev.append(torch.cat([k[-2:-1] for k in kk]).contiguous())
+                self.v_prev.append(torch.cat([v[-2:-1] for v in vv]).contiguous())
             if n_query:
                 self.q.append(inputs.gen_q(w, layer, device, 0, batch=b * n_query).reshape(
                     b, n_query, w.num_q_heads, 128).contiguous())
@@ -250,7 +357,22 @@ class Bench:
         else:
             self.ws = kvq.alloc_workspace(self.layout, b, self.max_len, device)
         self.scale = 1.0 / math.sqrt(128)
+        if self.k_prev:
+            self.lens_prev_t = torch.as_tensor(lens - 1, device=device)
+            self.out_prev = [torch.empty_like(o) for o in self.out]
         torch.cuda.synchronize()
+
+    def flush_step(self):
+        """A KIVI decode step at length S - 1 over all layers
+        (kvq_write_decode): it rewrites token S - 2 with the values the
+        prefill stored and flushes the group [nq(S) - 64, nq(S)) that leaves
+        the fp16 window at S, which the prefill already flushed with the same
+        codes, so the cache is unchanged.  Every 64th step of a row flushes
+        so; the other steps are the plain step."""
+        for layer in range(self.w.layers):
+            self.kvq.write_decode(self.caches[layer], self.k_prev[layer], self.v_prev[layer],
+                                  self.q[layer], self.table, self.lens_prev_t,
+                                  self.max_len - 1, self.scale, self.out_prev[layer], self.ws)
 
     def step(self, write=True, fused=True):
         """One decode step over all layers: append each row's new token and
@@ -337,6 +459,44 @@ def run(args):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
 
+    # KIVI: the step that flushes a group (one in 64), timed the same way
+    flush = None
+    if bench.k_prev and not args.separate:
+        fgraph = None
+        if not args.eager:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                bench.flush_step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            fgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(fgraph):
+                bench.flush_step()
+        for _ in range(max(args.warmup, 1)):
+            fgraph.replay() if fgraph is not None else bench.flush_step()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            fgraph.replay() if fgraph is not None else bench.flush_step()
+        stop.record()
+        torch.cuda.synchronize()
+        fms = start.elapsed_time(stop) / args.steps
+        # the flush step attends over S - 1 tokens (other outputs) and leaves
+        # the cache as it was: the plain step still gives the reference outputs
+        if any(torch.equal(a, b) for a, b in zip(bench.out_prev, ref)):
+            raise SystemExit("the flush step gave the plain step's outputs")
+        one()
+        torch.cuda.synchronize()
+        for o, r in zip(bench.out, ref):
+            if not torch.equal(o, r):
+                raise SystemExit("the flush step changed the cache")
+        flush = {"length": int(bench.max_len) - 1, "ms_per_step": round(fms, 5),
+                 "cycle_ms_per_step": round((63 * ms + fms) / 64, 5),
+                 "note": "kvq_write_decode at length S - 1 flushes the 64-token group "
+                         "leaving the fp16 window (one step in 64 does); cycle = 63 plain "
+                         "steps and one flush step, averaged"}
+
     # Decode-launch duration: one HIP event pair, on the stream the launches
     # run on, around the L decode launches of a step (one per layer, back to
     # back, the write launches left out), elapsed / L.  They run as the timed
@@ -394,6 +554,7 @@ def run(args):
                       "GBps_read_plus_write": round(2 * nbytes / (cms * 1e-3) / 1e9, 1)}
         del src, dst
     achieved = layer_bytes / (kern_ms * 1e-3) / 1e9
+    probe = None if args.no_probe else bandwidth_probe(args.probe_gib)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -405,6 +566,24 @@ def run(args):
         if (ent and t.get("kernel_source_hash") == kernel_source_hash()
                 and ent.get("split_tokens") == int(bench.layout.split_tokens)):
             traffic = ent.get("bytes_per_launch")
+
+    # rocprofv3 durations of this workload's decode and merge kernels
+    # (profiles/, taken under the same kernel sources and partition length)
+    profiled = None
+    if os.path.exists(TIMES_FILE) and not args.n_query:
+        with open(TIMES_FILE) as f:
+            t = json.load(f)
+        ent = t.get(w.name)
+        if (ent and t.get("kernel_source_hash") == kernel_source_hash()
+                and ent.get("split_tokens") == int(bench.layout.split_tokens)):
+            dec, mer = ent["decode_us"], ent.get("merge_us", 0.0)
+            profiled = {"decode_us": dec, "merge_us": mer,
+                        "frac_decode": round(layer_bytes / (dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "frac_decode_plus_merge": round(
+                            layer_bytes / ((dec + mer) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "launch_span_us": ent.get("launch_span_us"),
+                        "source": os.path.relpath(TIMES_FILE, ROOT),
+                        "command": ent.get("command")}
 
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -444,11 +623,18 @@ def run(args):
             "bytes_per_launch": layer_bytes,
             "avg_launch_us": round(kern_ms * 1e3, 3), "launches_timed": len(durs) * L,
             "timing": kernel_timing,
+            "probe_GBps": probe["GBps"] if probe else None,
+            "frac_of_probe": round(achieved / probe["GBps"], 4) if probe else None,
+            "profiled": profiled,
         },
         "cpu_baseline": cpu,
     }
     if copy_probe is not None:
         result["copy_probe"] = copy_probe
+    if probe is not None:
+        result["probe"] = probe
+    if flush is not None:
+        result["flush_step"] = flush
     if bench.calibrate is not None:
         result["calibrate"] = bench.calibrate
     print(json.dumps(result), flush=True)
@@ -471,7 +657,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a device copy of this many MiB (profiler yardstick)")
-    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="oracle processes (the GPU box's CPU share is 16)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the read-bandwidth probe")
+    ap.add_argument("--probe-gib", type=int, default=4,
+                    help="bytes the bandwidth probe reads per launch (GiB, a power of two)")
+    ap.add_argument("--probe", action="store_true",
+                    help="run only the read-bandwidth probe and print its JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
@@ -480,6 +673,9 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         raise SystemExit(2)
+    if args.probe:
+        print(json.dumps(bandwidth_probe(args.probe_gib)), flush=True)
+        return
     run(args)
 
 

@@ -69,5 +69,24 @@ def build_library(verbose: bool = False, out: str = LIB_PATH, defines=(),
     return out
 
 
+PROBE_SOURCE = "kvq_probe.hip"
+PROBE_PATH = os.path.join(PKG_DIR, "libkvq_probe.so")
+
+
+def build_probe(verbose: bool = False, out: str = PROBE_PATH) -> str:
+    """Compile the read-bandwidth probe (bench.py --probe) into its own
+    shared library; it is measurement tooling, not part of libkvq."""
+    hipcc = hipcc_path()
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", CSRC, "-x", "hip", "-shared",
+           os.path.join(CSRC, PROBE_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

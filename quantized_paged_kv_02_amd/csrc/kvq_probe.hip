@@ -1,0 +1,69 @@
+// Read-only HBM bandwidth probe (measurement tooling, built as its own
+// library libkvq_probe.so; not part of the libkvq ABI).
+//
+// It issues the decode kernel's access pattern without its arithmetic: every
+// wavefront load is one 16-byte buffer load per lane, i.e. one 1 KiB chunk
+// (an INT4 (block, head) code chunk, half an INT8 one), with the same
+// non-temporal cache policy, eight chunks in flight per wavefront.  Chunk
+// order: 0 = wavefront w takes chunks w, w + W, w + 2W, ... (W wavefronts in
+// the grid), 1 = the same indices sent through a bijection of the chunk
+// range (multiplication by an odd constant modulo a power of two), so
+// consecutive loads of a wavefront land far apart, as paged blocks do.  The
+// bytes a launch reads over its duration is the HBM read rate the chip
+// reaches with this pattern: the "achievable" denominator beside the
+// vendor's 8 TB/s.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.h"
+
+namespace {
+
+constexpr int kInFlight = 8;
+
+__global__ __launch_bounds__(256) void kvq_probe_read_kernel(const uint8_t *src,
+                                                             uint32_t chunk_mask,
+                                                             int random_order,
+                                                             uint32_t *sink) {
+  using namespace kvq;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const uint32_t waves = (gridDim.x * blockDim.x) >> 6;
+  const uint32_t n_chunks = chunk_mask + 1;
+  uint32_t acc = 0;
+  for (uint32_t c0 = wave; c0 < n_chunks; c0 += kInFlight * waves) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const uint32_t c = c0 + u * waves;
+      const uint32_t idx = random_order ? (c * 0x9E3779B1u) & chunk_mask : c;
+      // a chunk past the range reads through an empty resource: zeros
+      const rsrc_t r = make_rsrc(src + (size_t)idx * 1024, c < n_chunks ? 1024u : 0u);
+      v[u] = bld16(r, 16 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  // keeps every load live; the buffer is filled so that this never holds
+  if (acc == 0xFFFFFFFFu) sink[blockIdx.x] = acc;
+}
+
+}  // namespace
+
+// Read `bytes` (a power of two, at least 1 MiB, 1 KiB aligned) at the device
+// pointer `src` once with `workgroups` 256-thread workgroups on `stream`;
+// `sink` is a device uint32 array of `workgroups` entries that the kernel
+// may write.  Returns 0 on success, -1 for bad arguments, -6 if the launch
+// failed.
+extern "C" int kvq_probe_read(const void *src, size_t bytes, int workgroups, int random_order,
+                              uint32_t *sink, void *stream) {
+  if (!src || !sink || workgroups < 1 || bytes < (1u << 20) || (bytes & (bytes - 1)) != 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 1023u) != 0 || bytes / 1024 > (1ull << 30))
+    return -1;
+  const uint32_t mask = (uint32_t)(bytes / 1024 - 1);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kvq_probe_read_kernel, dim3(workgroups), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(src), mask,
+                     random_order, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}

@@ -3,9 +3,12 @@
 Two commands:
 
   python -m quantized_paged_kv_02_amd.profile_summary stats <dir> --command CMD --out FILE
+        [--workload NAME --times-out JSON --split-tokens N]
       Kernel durations from a ``rocprofv3 --kernel-trace --stats
       --output-format csv`` run (the ``*_kernel_trace.csv`` under <dir>):
-      calls, mean, median, min and max per kernel, written as markdown.
+      calls, mean, median, min and max per kernel, written as markdown,
+      and the decode launches bench.py's roofline times (decode kernel,
+      partition reduce, their span), also collected per workload in JSON.
 
   python -m quantized_paged_kv_02_amd.profile_summary traffic <fetch_dir> <write_dir>
         --workload NAME --command-fetch CMD --command-write CMD --out FILE
@@ -56,8 +59,45 @@ def _short(name: str) -> str:
     return name if len(name) <= 90 else name[:87] + "..."
 
 
-def stats(directory: str, command: str, out: str) -> None:
+def decode_times(rows):
+    """Durations (us) of the decode launches that bench.py's roofline times:
+    the kvq_paged_decode dispatches (the decode kernel dispatches with the
+    smallest grid: a decode step's kvq_write_decode adds flush workgroups
+    on KIVI caches) and the partition reduce dispatched right after each,
+    plus each such launch's span from the decode's start to the reduce's
+    end."""
+    rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    dec = [i for i, r in enumerate(rows) if "paged_decode" in r["Kernel_Name"]]
+    if not dec:
+        return None
+    grid = min(int(rows[i]["Grid_Size_X"]) for i in dec)
+    d_us, m_us, span = [], [], []
+    for i in dec:
+        r = rows[i]
+        if int(r["Grid_Size_X"]) != grid:
+            continue
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        d_us.append((t1 - t0) / 1000.0)
+        nxt = rows[i + 1] if i + 1 < len(rows) else None
+        if nxt is not None and "partition_reduce" in nxt["Kernel_Name"]:
+            m_us.append((int(nxt["End_Timestamp"]) - int(nxt["Start_Timestamp"])) / 1000.0)
+            span.append((int(nxt["End_Timestamp"]) - t0) / 1000.0)
+        else:
+            span.append((t1 - t0) / 1000.0)
+    out = {"decode_us": round(statistics.mean(d_us), 3),
+           "decode_median_us": round(statistics.median(d_us), 3),
+           "merge_us": round(statistics.mean(m_us), 3) if m_us else 0.0,
+           "merge_median_us": round(statistics.median(m_us), 3) if m_us else 0.0,
+           "launch_span_us": round(statistics.mean(span), 3),
+           "launch_span_median_us": round(statistics.median(span), 3),
+           "dispatches": len(d_us), "decode_grid": grid}
+    return out
+
+
+def stats(directory: str, command: str, out: str, workload: str | None = None,
+          times_out: str | None = None, split_tokens: int | None = None) -> None:
     rows = list(csv.DictReader(open(_find(directory, "kernel_trace.csv"))))
+    dt = decode_times(rows)
     per = {}
     for r in rows:
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
@@ -71,9 +111,32 @@ def stats(directory: str, command: str, out: str) -> None:
         lines.append(f"| `{_short(name)}` | {len(v)} | {statistics.mean(v):.2f} | "
                      f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                      f"{sum(v) / 1000:.3f} |")
+    if dt is not None:
+        lines += ["", "Decode launches as bench.py's roofline times them (kvq_paged_decode "
+                  f"dispatches, grid {dt['decode_grid']} workgroups, {dt['dispatches']} of "
+                  "them): decode kernel mean / median "
+                  f"{dt['decode_us']:.2f} / {dt['decode_median_us']:.2f} us, partition "
+                  f"reduce after it {dt['merge_us']:.2f} / {dt['merge_median_us']:.2f} us, "
+                  "launch span (decode start to reduce end) "
+                  f"{dt['launch_span_us']:.2f} / {dt['launch_span_median_us']:.2f} us."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
+    if times_out and workload and dt is not None:
+        data = json.load(open(times_out)) if os.path.exists(times_out) else {}
+        if data.get("kernel_source_hash") != kernel_source_hash():
+            data = {}
+        data["kernel_source_hash"] = kernel_source_hash()
+        data["note"] = ("rocprofv3 kernel-trace durations (us) of the decode launches bench.py "
+                        "times for its roofline (kvq_paged_decode: decode kernel, then the "
+                        "partition reduce when the launch is split), per workload")
+        data[workload] = {**dt, "split_tokens": split_tokens, "command": command,
+                          "summary": os.path.relpath(out, ROOT)}
+        with open(times_out, "w") as f:
+            json.dump(data, f, indent=1)
+            f.write("\n")
+        print(f"wrote {times_out}: {workload} decode {dt['decode_us']} us, merge "
+              f"{dt['merge_us']} us")
 
 
 def _counter(directory: str, counter: str):
@@ -128,6 +191,11 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--workload", default=None)
+    s.add_argument("--times-out", default=None,
+                   help="JSON file collecting decode / merge durations per workload")
+    s.add_argument("--split-tokens", type=int, default=None,
+                   help="the partition length the profiled launches used")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -140,7 +208,7 @@ def main(argv=None):
                    help="the partition length the profiled launches used")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        stats(a.dir, a.command, a.out)
+        stats(a.dir, a.command, a.out, a.workload, a.times_out, a.split_tokens)
     else:
         traffic(a.fetch_dir, a.write_dir, a.workload, a.copy_mib, a.command_fetch,
                 a.command_write, a.out, a.split_tokens)
