@@ -284,6 +284,7 @@ class Bench:
             self.layout.split_tokens = kvq.plan_split_tokens(self.layout, lens)
         b = w.batch
         self.calibrate = None
+        self.prefill_write = None
         self.ones_cu = torch.arange(b + 1, dtype=torch.int32, device=device)
         self.caches, self.k_new, self.v_new, self.q, self.out = [], [], [], [], []
         self.k_prev, self.v_prev = [], []
@@ -328,8 +329,31 @@ class Bench:
             n = (lens - 1).astype(np.int32)
             cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]).astype(np.int32),
                                  device=device)
-            kvq.write(cache, torch.cat(pre_k).contiguous(), torch.cat(pre_v).contiguous(), cu,
-                      self.table, torch.as_tensor(n, device=device), int(n.max()))
+            kpre, vpre = torch.cat(pre_k).contiguous(), torch.cat(pre_v).contiguous()
+            n_t = torch.as_tensor(n, device=device)
+            kvq.write(cache, kpre, vpre, cu, self.table, n_t, int(n.max()))
+            if layer == 0:
+                # time the prefill write of one layer: rewriting the same
+                # tokens stores the same codes, scales and ring values
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(3):
+                    kvq.write(cache, kpre, vpre, cu, self.table, n_t, int(n.max()))
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / 3
+                if w.dtype in KIVI:
+                    nbytes = metrics.kivi_write_bytes(w.dtype, n, w.num_kv_heads, w.residual_len)
+                else:
+                    nbytes = metrics.write_bytes(w.dtype, w.k_gran, w.v_gran, int(n.sum()),
+                                                 w.num_kv_heads)
+                self.prefill_write = {
+                    "call": "kvq_write of one layer's prefill (S - 1 tokens per row)",
+                    "tokens": int(n.sum()), "bytes": nbytes, "us": round(us, 2),
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del kpre, vpre
             self.caches.append(cache)
             nq = max(n_query, 1)   # new tokens per row and step
             self.k_new.append(torch.cat([k[-nq:] for k in kk]).contiguous())
@@ -637,6 +661,8 @@ def run(args):
         result["flush_step"] = flush
     if bench.calibrate is not None:
         result["calibrate"] = bench.calibrate
+    if bench.prefill_write is not None:
+        result["prefill_write"] = bench.prefill_write
     print(json.dumps(result), flush=True)
 
 

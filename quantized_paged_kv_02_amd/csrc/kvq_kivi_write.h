@@ -203,19 +203,20 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
       u32x2 out;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        float xv[16], sv[16], rv[16], qv[16];
+        float xv[16], sv[16], rv[16], zv[16];
+        uint32_t qv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = 32 * cb + 16 * d + e;
           xv[e] = (float)x[tt][c];
           sv[e] = sc[c];
           rv[e] = rc[c];
+          zv[e] = zs[c];
         }
-        rint_quotients(qv, xv, sv, rv);
+        kivi_codes<16, true>(qv, xv, sv, rv, zv, kQmax, 3u);
         uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          word |= affine_code(qv[e], sv[e], zs[32 * cb + 16 * d + e], kQmax) << (2 * e);
+        for (int e = 0; e < 16; ++e) word |= qv[e] << (2 * e);
         out[d] = word;
       }
       *reinterpret_cast<u32x2 *>(chunk + 128 * cb + 8 * (tt & 15)) = out;
@@ -224,23 +225,20 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * cb + 8 * d]);
-        float xv[8], sv[8], rv[8], qv[8];
+        float xv[8], sv[8], rv[8], zv[8];
+        uint32_t qv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = 32 * cb + 8 * d + e;
           xv[e] = (float)v[e];
           sv[e] = sc[c];
           rv[e] = rc[c];
+          zv[e] = AFF ? zs[c] : 0.0f;
         }
-        rint_quotients(qv, xv, sv, rv);
+        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax, 0xFu);
         uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = 32 * cb + 8 * d + e;
-          const uint32_t q = AFF ? affine_code(qv[e], sv[e], zs[c], kQmax)
-                                 : int_code(qv[e], sv[e], -8.0f, 7.0f) & 0xFu;
-          word |= q << (4 * e);
-        }
+        for (int e = 0; e < 8; ++e) word |= qv[e] << (4 * e);
         out[d] = word;
       }
       *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
@@ -303,20 +301,19 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
         const int pos = (e == 1) ? 2 : (e == 2 ? 1 : e);
-        float xv[8], sv[8], rv[8], qv[8];
+        float xv[8], sv[8], rv[8], zv[8];
+        uint32_t qv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int g = j >> 2;
           xv[j] = (float)x[tt][16 * j + m];
           sv[j] = sc[2 * tt + g];
           rv[j] = rc[2 * tt + g];
+          zv[j] = zs[2 * tt + g];
         }
-        rint_quotients(qv, xv, sv, rv);
+        kivi_codes<8, true>(qv, xv, sv, rv, zv, kQmax, 3u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t q = affine_code(qv[j], sv[j], zs[2 * tt + (j >> 2)], kQmax);
-          out[j >> 2] |= q << (8 * pos + 2 * (j & 3));
-        }
+        for (int j = 0; j < 8; ++j) out[j >> 2] |= qv[j] << (8 * pos + 2 * (j & 3));
       }
       *reinterpret_cast<u32x2 *>(chunk + 8 * u) = out;
     } else {
@@ -327,20 +324,20 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
         const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
         const float r0 = rc[2 * tt], r1 = rc[2 * tt + 1];
         const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
-        float xv[8], sv[8], rv[8], qv[8];
+        float xv[8], sv[8], rv[8], zv[8];
+        uint32_t qv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           xv[j] = (float)x[tt][16 * j + m];
           sv[j] = j < 4 ? s0 : s1;
           rv[j] = j < 4 ? r0 : r1;
+          zv[j] = j < 4 ? z0 : z1;
         }
-        rint_quotients(qv, xv, sv, rv);
+        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax, 0xFu);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t q = AFF ? affine_code(qv[j], sv[j], j < 4 ? z0 : z1, kQmax)
-                                 : int_code(qv[j], sv[j], -8.0f, 7.0f) & 0xFu;
           const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
-          out[j >> 1] |= q << (4 * p);
+          out[j >> 1] |= qv[j] << (4 * p);
         }
       }
       *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;

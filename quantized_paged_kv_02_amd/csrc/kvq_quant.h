@@ -37,43 +37,44 @@ __device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float 
   return (uint32_t)(int)y;
 }
 
-// q[i] = rintf(x[i] / s[i]), each quotient rounded as IEEE fp32 division
-// rounds it, for |x / s| <= 16, from r[i] = 1 / s[i] (correctly rounded).
-// Two roundings put a product x * r within |x / s| * 2^-23 <= 2^-19 of the
-// quotient, and the quotient's own rounding is at most 2^-20 there, so the
-// product is within 2^-18 of the rounded quotient (the test below may see
-// the product before its rounding: another 2^-20 at most).  Both round to
-// the same integer unless the product lies within 2^-17 of a half-integer
-// (or is not finite); if any lane of the wavefront has such a value, the
-// whole wavefront takes the divisions instead.  One multiply per value in
-// the common case, and the same integers as the division: the KIVI flush
-// quantizes with it (|x / s| <= qmax there; a zero scale gives code 0 after
-// this, whatever q holds).
-template <int N>
-__device__ __forceinline__ void rint_quotients(float (&q)[N], const float (&x)[N],
-                                               const float (&s)[N], const float (&r)[N]) {
+// KIVI group codes: round half to even of the IEEE fp32 quotient x / s, as
+// the oracle computes it, from r = 1 / s (correctly rounded) without a
+// division per value.  t = fma(x, r, M), M = 1.5 * 2^23, rounds the product
+// x * r to an integer n held in t's low mantissa bits (half to even: t's
+// unit in the last place is 1); rem = fma(x, r, -n) is the product's
+// distance to n.  For |x / s| <= 16 the product x * r is within
+// |x / s| 2^-23 <= 2^-19 of the quotient and the quotient's own rounding
+// is at most 2^-20, so the two round to the same integer unless the
+// product lies within 2^-18 of a half-integer; the test |rem| < 1/2 - 2^-17
+// leaves a margin for rem's own rounding.  If any lane of the wavefront
+// fails it (or is not finite), the wavefront divides instead.  Codes come
+// from t's bits: symmetric, the two's-complement low bits of n (a group's
+// own scale keeps |n| <= qmax); affine, n + z clamped to [0, qmax].  A zero
+// scale (r = 0) gives n = 0, and its group's z is 0.
+template <int N, bool AFF>
+__device__ __forceinline__ void kivi_codes(uint32_t (&code)[N], const float (&x)[N],
+                                           const float (&s)[N], const float (&r)[N],
+                                           const float (&z)[N], float qmax, uint32_t mask) {
+  constexpr float M = 12582912.0f;  // 1.5 * 2^23
+  float t[N];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float y = x[i] * r[i];
-    const float f = y - floorf(y);
-    near |= !(fabsf(f - 0.5f) > 0x1p-17f);
-    q[i] = rintf(y);
+    t[i] = __builtin_fmaf(x[i], r[i], M);
+    const float n = t[i] - M;
+    const float rem = __builtin_fmaf(x[i], r[i], -n);
+    near |= !(fabsf(rem) < 0.5f - 0x1p-17f);
   }
   if (__any(near)) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) q[i] = rintf(x[i] / s[i]);
+    for (int i = 0; i < N; ++i) t[i] = (s[i] != 0.0f ? rintf(x[i] / s[i]) : 0.0f) + M;
   }
-}
-// Codes from rounded quotients: clamp(q, lo, hi) (symmetric) and clamp(q +
-// z, 0, qmax) (affine), 0 for a zero scale.
-__device__ __forceinline__ uint32_t int_code(float q, float s, float lo, float hi) {
-  if (s == 0.0f) return 0u;
-  return (uint32_t)(int)fminf(fmaxf(q, lo), hi);
-}
-__device__ __forceinline__ uint32_t affine_code(float q, float s, float z, float qmax) {
-  if (s == 0.0f) return 0u;
-  return (uint32_t)(int)fminf(fmaxf(q + z, 0.0f), qmax);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float v = t[i];
+    if constexpr (AFF) v = fminf(fmaxf(v + z[i], M), M + qmax);
+    code[i] = __builtin_bit_cast(uint32_t, v) & mask;
+  }
 }
 
 // x / s clamped to the format's finite range (448 E4M3, 57344 E5M2).

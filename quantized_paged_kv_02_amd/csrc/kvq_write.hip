@@ -57,6 +57,191 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
   }
 }
 
+// Codes of 8 values under their scales (the rule of quantize_pair: round
+// half to even of the IEEE quotient x / s; FP8 clamped to the format's range
+// then converted by the hardware, round to nearest even), byte i = value i.
+// INT8 takes the product x * r, r = 1 / s correctly rounded, clamped to
+// +-129: for |x / s| <= 129 it lies within 129 * 2^-23 < 2^-16 of the
+// quotient, whose own rounding is at most 2^-17, so both round to the same
+// integer unless the product is within 2^-15 of a half-integer (beyond
+// +-129 both clamp alike); a wavefront with such a value, or with a scale
+// whose reciprocal is not finite, divides instead.  A zero scale gives
+// r = 0 and code 0, as the division rule does.
+template <int DT>
+__device__ __forceinline__ u32x2 quantize8(const float (&x)[8], const float (&s)[8]) {
+  u32x2 w;
+  if constexpr (DT == kInt8) {
+    float q[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = s[i] != 0.0f ? 1.0f / s[i] : 0.0f;
+      const float p = fminf(fmaxf(x[i] * r, -129.0f), 129.0f);
+      q[i] = rintf(p);
+      near |= !(fabsf(p - q[i]) < 0.5f - 0x1p-14f) || !(fabsf(r) < 0x1p127f);
+    }
+    if (__any(near)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = s[i] != 0.0f ? rintf(x[i] / s[i]) : 0.0f;
+    }
+#pragma unroll
+    for (int hw = 0; hw < 2; ++hw) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        word |= ((uint32_t)(int)fminf(fmaxf(q[4 * hw + e], -128.0f), 127.0f) & 0xFFu) << (8 * e);
+      w[hw] = word;
+    }
+  } else {
+#pragma unroll
+    for (int hw = 0; hw < 2; ++hw) {
+      const int i = 4 * hw;
+      constexpr float top = code_top<DT>();
+      const float y0 = fp8_prescale(x[i], s[i], top), y1 = fp8_prescale(x[i + 1], s[i + 1], top);
+      const float y2 = fp8_prescale(x[i + 2], s[i + 2], top);
+      const float y3 = fp8_prescale(x[i + 3], s[i + 3], top);
+      int pk;
+      if constexpr (DT == kFp8) {
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
+      } else {
+        pk = __builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, pk, true);
+      }
+      w[hw] = (uint32_t)pk;
+    }
+  }
+  return w;
+}
+
+// INT8 / FP8 bulk write (prefill): one 256-thread workgroup per run of
+// kWriteBlocks 16-token blocks of a row and one KV head, for the blocks'
+// new tokens.  Thread t takes channels 8 (t % 16) .. + 7 of token slot
+// t / 16 of every block (one 16-byte load of K and one of V per block, all
+// issued first); a per-token scale is the maximum over the 16 threads of
+// the slot (shuffles within 16 lanes).  Block by block, the codes go to LDS
+// in the cache's byte order, then every thread stores one 16-byte unit of
+// the (block, head) chunk (threads 0..127 K, 128..255 V): a K unit is 16
+// channels of one token, a V unit 4 channels of 4 tokens, stored whole when
+// all its tokens are new and byte by byte otherwise (the tokens already in
+// the block keep their codes).
+#ifndef KVQ_WRITE_BLOCKS
+#define KVQ_WRITE_BLOCKS 4
+#endif
+constexpr int kWriteBlocks = KVQ_WRITE_BLOCKS;
+
+template <int DT>
+__global__ __launch_bounds__(256) void kvq_write_q8_block_kernel(WriteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[2][2048];  // K, V chunks
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
+  const int s_new = a.seq_lens[b];
+  const int s_old = s_new - n_new;
+  const int lb0 = s_old / kBlock + (int)blockIdx.x * kWriteBlocks;  // first logical block
+  if (n_new <= 0 || lb0 * kBlock >= s_new) return;
+  const int slot = tid >> 4, k8 = tid & 15;
+  // loads of every block first (tokens past the write read nothing)
+  u32x4 rk[kWriteBlocks], rv[kWriteBlocks];
+  int phys[kWriteBlocks];
+#pragma unroll
+  for (int j = 0; j < kWriteBlocks; ++j) {
+    const int lb = lb0 + j;
+    const int pos = lb * kBlock + slot;
+    rk[j] = rv[j] = u32x4{0u, 0u, 0u, 0u};
+    phys[j] = 0;
+    if (lb * kBlock < s_new) {
+      phys[j] = a.block_tables[(size_t)b * a.max_blocks_per_seq + lb];
+      if (pos >= s_old && pos < s_new) {
+        const size_t src =
+            ((size_t)(c_begin + pos - s_old) * a.num_kv_heads + h) * kHeadDim + 8 * k8;
+        rk[j] = ld16(a.k_new + src);
+        rv[j] = ld16(a.v_new + src);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kWriteBlocks; ++j) {
+    const int lb = lb0 + j;
+    if (lb * kBlock >= s_new) break;  // uniform
+    const int t_lo = max(lb * kBlock, s_old), t_hi = min(lb * kBlock + kBlock, s_new);
+    const bool live = lb * kBlock + slot >= t_lo && lb * kBlock + slot < t_hi;
+    const size_t chunk = (size_t)phys[j] * a.num_kv_heads + h;
+    if (j > 0) __syncthreads();  // the previous block's units are stored
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const u32x4 raw = which ? rv[j] : rk[j];
+      const int gran = which ? a.v_gran : a.k_gran;
+      const float *scales = which ? a.v_scales : a.k_scales;
+      float x[8], sc[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = half_bits_to_float(raw[e] & 0xFFFFu);
+        x[2 * e + 1] = half_bits_to_float(raw[e] >> 16);
+      }
+      if (gran == kPerToken) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+        const float st = m / code_top<DT>();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = st;
+        if (live && k8 == 0) const_cast<float *>(scales)[chunk * kBlock + slot] = st;
+      } else if (gran == kPerTensor || gran == kPerHead) {
+        const float st = scales[gran == kPerHead ? h : 0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = st;
+      } else {
+        const f32x4 s0 = ld16f(scales + h * kHeadDim + 8 * k8);
+        const f32x4 s1 = ld16f(scales + h * kHeadDim + 8 * k8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[e] = s0[e];
+          sc[4 + e] = s1[e];
+        }
+      }
+      const u32x2 q = quantize8<DT>(x, sc);
+      if (which == 0) {
+        // K: channels 8 k8 .. + 7 of the slot are 8 consecutive bytes
+        *reinterpret_cast<u32x2 *>(&codes[0][1024 * ((k8 >> 1) & 1) + 256 * (k8 >> 2) +
+                                             16 * slot + 8 * (k8 & 1)]) = q;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          codes[1][v8_offset(slot, 8 * k8 + e)] = (uint8_t)(q[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+    __syncthreads();
+    const int u = tid & 127;
+    if (tid < 128) {
+      // K unit u: token slot u % 16
+      const int upos = lb * kBlock + (u & 15);
+      if (upos >= t_lo && upos < t_hi)
+        *reinterpret_cast<u32x4 *>(a.k_codes + chunk * 2048 + 16 * u) =
+            *reinterpret_cast<const u32x4 *>(&codes[0][16 * u]);
+    } else {
+      // V unit u: slots 4 ((u / 16) % 4) .. + 3, byte 4 i + e = slot e
+      const int q0 = lb * kBlock + 4 * ((u >> 4) & 3);
+      uint8_t *dst = a.v_codes + chunk * 2048 + 16 * u;
+      if (q0 >= t_lo && q0 + 3 < t_hi) {
+        *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(&codes[1][16 * u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (q0 + e >= t_lo && q0 + e < t_hi) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[4 * i + e] = codes[1][16 * u + 4 * i + e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // FP16 (unquantized) cache: the same scatter with the values stored as they
 // are, in the 4 KiB-per-(block, head) operand layout of kvq_quant.h.
 __global__ __launch_bounds__(64) void kvq_write_f16_kernel(WriteArgs a) {
@@ -86,8 +271,15 @@ __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
   int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// Workgroup x appends the row's new token n_new - 1 - x: a row keeps at
+// most ring - 1 tokens in fp16 (S - nq(S) < R + G), so only the last
+// min(n_new, ring) new tokens can land in the ring.
 __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
-  append_token(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+  int c_begin, n_new;
+  new_tokens(a, blockIdx.z, c_begin, n_new);
+  const int i = n_new - 1 - (int)blockIdx.x;
+  if (i < 0) return;
+  append_token(a, i, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
 // Flush and append in one launch: workgroups x < 2*groups flush, the rest
@@ -107,6 +299,20 @@ __global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a,
 
 hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new,
                            hipStream_t stream) {
+  if (max_new > 1) {
+    // blocks a run of n tokens can touch: floor((n + 14) / 16) + 1
+    const int blocks = (max_new + 14) / kBlock + 1;
+    const dim3 grid((blocks + kWriteBlocks - 1) / kWriteBlocks, a.num_kv_heads, batch);
+    if (dtype == kFp8) {
+      hipLaunchKernelGGL(kvq_write_q8_block_kernel<kFp8>, grid, dim3(256), 0, stream, a);
+    } else if (dtype == kFp8E5M2) {
+      hipLaunchKernelGGL(kvq_write_q8_block_kernel<kFp8E5M2>, grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(kvq_write_q8_block_kernel<kInt8>, grid, dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
+  // one token per row (a decode step written apart from its decode)
   const dim3 grid(max_new, a.num_kv_heads, batch);
   if (dtype == kFp8) {
     hipLaunchKernelGGL(kvq_write_q8_kernel<kFp8>, grid, dim3(64), 0, stream, a);
@@ -152,7 +358,8 @@ hipError_t launch_write_int4(const WriteArgs &a, int dtype, int batch, int max_n
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kvq_int4_append_kernel, dim3(max_new, a.num_kv_heads, batch), dim3(64),
+  hipLaunchKernelGGL(kvq_int4_append_kernel,
+                     dim3(max_new < a.ring ? max_new : a.ring, a.num_kv_heads, batch), dim3(64),
                      0, stream, a);
   return hipGetLastError();
 }

@@ -85,3 +85,22 @@ def write_bytes(dtype: str, k_gran: str, v_gran: str, n_new: int, num_kv_heads: 
         if gran == "token":
             total += n_new * hkv * 4
     return total
+
+
+def kivi_write_bytes(dtype: str, lens, num_kv_heads: int, residual: int = 128) -> int:
+    """Bytes of a KIVI kvq_write that grows empty rows to lengths ``lens``:
+    every new token's fp16 K and V read once; the INT4 (2-bit) codes, scales
+    and zero points of the groups the write flushes (those below nq(S + 1):
+    groups leave the window one token early) and the fp16 ring tokens
+    written."""
+    hkv, d = num_kv_heads, HEAD_DIM
+    total = 0
+    for s in (int(x) for x in lens):
+        nq = kivi_quantized_len(s + 1, residual)
+        total += s * hkv * d * 2 * 2                      # K and V read
+        total += hkv * nq * d // (2 if dtype == "int2-affine" else 1)   # codes
+        total += hkv * (nq // GROUP) * d * 4 + hkv * nq * 2 * 4         # scales
+        if dtype != "int4":
+            total += hkv * (nq // GROUP) * d + hkv * nq * 2             # zero points
+        total += hkv * (s - kivi_quantized_len(s, residual)) * d * 2 * 2  # ring
+    return total
