@@ -209,12 +209,16 @@ def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
 # Achievable read bandwidth: the probe of libkvq_probe.so
 # ---------------------------------------------------------------------------
 
-def bandwidth_probe(gib: int = 4, reps: int = 5):
-    """Read ``gib`` GiB in 1 KiB chunks (one 16-byte buffer load per lane,
-    the decode's granule and cache policy) with several grid sizes, in
-    wavefront-strided and in scattered chunk order; each configuration is
-    launched back to back ``reps`` times between one HIP event pair.
-    Returns the best rate (GB/s, 1e9 bytes) and every configuration's."""
+def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048)):
+    """Read ``gib`` GiB (a power of two) per launch in 1 KiB chunks (one
+    16-byte buffer load per lane, the decode's granule and cache policy)
+    with several grid sizes, in wavefront-strided and in scattered chunk
+    order; each configuration is launched back to back ``reps`` times
+    between one HIP event pair, each launch on another slice of a buffer of
+    at least 2 GiB (so a launch smaller than the 256 MB Infinity Cache does
+    not read what the previous one left there, as the decode's layers do
+    not).  Returns the best rate (GB/s, 1e9 bytes) and every
+    configuration's."""
     import ctypes
     import torch
     if not os.path.exists(PROBE_LIB):
@@ -224,28 +228,29 @@ def bandwidth_probe(gib: int = 4, reps: int = 5):
     lib.kvq_probe_read.restype = ctypes.c_int
     lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p, ctypes.c_void_p]
-    nbytes = gib << 30
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    nbytes = int(gib * (1 << 30))
+    slices = max(1, (2 << 30) // nbytes)
+    reps = max(reps, min(slices, 64))
+    buf = torch.empty(nbytes * slices, dtype=torch.uint8, device="cuda")
     buf.fill_(0x5A)          # every dword xors to 0: the sink is never written
-    grids = (256, 512, 1024, 2048)
     sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
 
-    def launch(wgs, order):
-        rc = lib.kvq_probe_read(buf.data_ptr(), nbytes, wgs, order, sink.data_ptr(),
-                                stream.cuda_stream)
+    def launch(wgs, order, i=0):
+        rc = lib.kvq_probe_read(buf.data_ptr() + (i % slices) * nbytes, nbytes, wgs, order,
+                                sink.data_ptr(), stream.cuda_stream)
         if rc != 0:
             raise SystemExit(f"kvq_probe_read failed ({rc})")
 
     rows = []
     for order, name in ((0, "strided"), (1, "scattered")):
         for wgs in grids:
-            launch(wgs, order)
+            launch(wgs, order, reps - 1)
             e0.record()
-            for _ in range(reps):
-                launch(wgs, order)
+            for i in range(reps):
+                launch(wgs, order, i)
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
@@ -253,7 +258,7 @@ def bandwidth_probe(gib: int = 4, reps: int = 5):
                          "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
     del buf
     best = max(rows, key=lambda r: r["GBps"])
-    return {"GBps": best["GBps"], "best": best, "bytes_per_launch": nbytes,
+    return {"GBps": best["GBps"], "best": best, "bytes_per_launch": nbytes, "slices": slices,
             "chunk_bytes": 1024, "all": rows,
             "kernel": "kvq_probe_read_kernel (libkvq_probe.so): loads only, 8 chunks in "
                       "flight per wavefront"}
@@ -264,7 +269,8 @@ def bandwidth_probe(gib: int = 4, reps: int = 5):
 # ---------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, w: inputs.Workload, device="cuda", n_query: int = 0):
+    def __init__(self, w: inputs.Workload, device="cuda", n_query: int = 0,
+                 partition: str = "auto"):
         import torch
         from quantized_paged_kv_02_amd import kvq
         self.torch, self.kvq, self.w = torch, kvq, w
@@ -282,6 +288,10 @@ class Bench:
         # plan, which counts the queries
         if not n_query:
             self.layout.split_tokens = kvq.plan_split_tokens(self.layout, lens)
+        if partition == "auto":
+            self.layout.partition = kvq.plan_partition(self.layout, lens)
+        else:
+            self.layout.partition = kvq.PARTITIONS[partition]
         b = w.batch
         self.calibrate = None
         self.prefill_write = None
@@ -435,7 +445,7 @@ def run(args):
         cpu = cpu_baseline(w, inputs.seq_lens(w), workers=args.cpu_workers)
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    bench = Bench(w, n_query=args.n_query)
+    bench = Bench(w, n_query=args.n_query, partition=args.partition)
     b = w.batch
     L = w.layers
     layer_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, bench.lens,
@@ -580,6 +590,7 @@ def run(args):
     achieved = layer_bytes / (kern_ms * 1e-3) / 1e9
     probe = None if args.no_probe else bandwidth_probe(args.probe_gib)
 
+    part_name = "balanced" if bench.layout.partition else "per-row"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -588,7 +599,8 @@ def run(args):
         # counters taken with other kernels or another partition length
         # describe other launches
         if (ent and t.get("kernel_source_hash") == kernel_source_hash()
-                and ent.get("split_tokens") == int(bench.layout.split_tokens)):
+                and ent.get("split_tokens") == int(bench.layout.split_tokens)
+                and ent.get("partition", "per-row") == part_name):
             traffic = ent.get("bytes_per_launch")
 
     # rocprofv3 durations of this workload's decode and merge kernels
@@ -599,7 +611,8 @@ def run(args):
             t = json.load(f)
         ent = t.get(w.name)
         if (ent and t.get("kernel_source_hash") == kernel_source_hash()
-                and ent.get("split_tokens") == int(bench.layout.split_tokens)):
+                and ent.get("split_tokens") == int(bench.layout.split_tokens)
+                and ent.get("partition", "per-row") == part_name):
             dec, mer = ent["decode_us"], ent.get("merge_us", 0.0)
             profiled = {"decode_us": dec, "merge_us": mer,
                         "frac_decode": round(layer_bytes / (dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -638,6 +651,7 @@ def run(args):
                      else "per layer: kvq_write_decode (1 token/row appended, then decoded)"),
             "launch": "hip graph" if graph is not None else "eager",
             "split_tokens": int(bench.layout.split_tokens),
+            "partition": "balanced" if bench.layout.partition else "per-row",
             "algorithmic_bytes_per_step": step_bytes,
         },
         "roofline": {
@@ -685,9 +699,11 @@ def main():
                     help="also time a device copy of this many MiB (profiler yardstick)")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
                     help="oracle processes (the GPU box's CPU share is 16)")
+    ap.add_argument("--partition", default="auto", choices=["auto", "per-row", "balanced"],
+                    help="decode partitions: the host plan's choice (auto) or a forced mode")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the read-bandwidth probe")
-    ap.add_argument("--probe-gib", type=int, default=4,
+    ap.add_argument("--probe-gib", type=float, default=4,
                     help="bytes the bandwidth probe reads per launch (GiB, a power of two)")
     ap.add_argument("--probe", action="store_true",
                     help="run only the read-bandwidth probe and print its JSON")

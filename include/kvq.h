@@ -186,6 +186,23 @@ typedef enum kvq_granularity {
   KVQ_PER_TOKEN = 3
 } kvq_granularity;
 
+/* How a decode launch divides the work among its workgroups.
+ *  KVQ_PARTITION_PER_ROW: every row is cut into partitions of split_tokens
+ *    tokens; a workgroup streams one partition of one (row, KV head).
+ *  KVQ_PARTITION_BALANCED: the blocks of all rows of a KV head, laid end to
+ *    end in row order, are cut into one equal range per workgroup (one
+ *    workgroup per CU: max(1, 256 / num_kv_heads) per KV head), so rows of
+ *    unequal length leave no workgroup short of work ([oh-bug] section
+ *    "为什么长上下文更需要 KV Cache Quantization": each step streams each
+ *    row's whole history).  A range that crosses rows leaves one partial per
+ *    row segment; the merge launch always runs.  INT8, FP8 and FP16 caches,
+ *    batch <= 256; split_tokens is unused.  Results equal the per-row
+ *    partitions' up to the order of the fp32 sums. */
+typedef enum kvq_partition {
+  KVQ_PARTITION_PER_ROW = 0,
+  KVQ_PARTITION_BALANCED = 1
+} kvq_partition;
+
 /* Shape and quantization scheme of one layer's cache (host struct). */
 typedef struct kvq_layout {
   uint32_t struct_size;       /* sizeof(kvq_layout)                          */
@@ -203,6 +220,8 @@ typedef struct kvq_layout {
   int32_t split_tokens;       /* decode partition length in tokens; 0 picks
                                  one from the grid size.  Multiple of 16
                                  (INT4: of 64).                              */
+  int32_t partition;          /* kvq_partition: how a decode launch divides
+                                 the rows among workgroups                  */
 } kvq_layout;
 
 /* Device buffers of one layer's cache (host struct of device pointers). */
@@ -355,6 +374,19 @@ kvq_status kvq_write_decode_noalloc(const kvq_layout *layout, const kvq_cache *c
  * errors as kvq_validate).  Host only, no HIP call. */
 int32_t kvq_plan_split_tokens(const kvq_layout *layout, const int32_t *host_seq_lens,
                               int32_t batch);
+
+/* The partition mode (kvq_partition) for a batch whose row lengths the
+ * caller knows on the host, for the layout as given (its split_tokens, or
+ * the automatic plan's when 0): KVQ_PARTITION_BALANCED when the per-row
+ * partitions fit in one round of workgroups (one per CU) and their longest
+ * workgroup streams more than 1.25 times the mean workgroup's blocks (rows
+ * unequal enough that its tail outweighs the balanced launch's merge and
+ * second segments); else KVQ_PARTITION_PER_ROW (always for KIVI caches,
+ * batch 0 or more than 256 rows).  Set layout->partition to it before sizing the workspace.
+ * Returns the mode (>= 0) or a negative kvq_status (as
+ * kvq_plan_split_tokens).  Host only, no HIP call. */
+int32_t kvq_plan_partition(const kvq_layout *layout, const int32_t *host_seq_lens,
+                           int32_t batch);
 
 /* Host-side check of block tables and row lengths, on HOST copies (the
  * entry points cannot check device data before launching; a block id out

@@ -84,8 +84,15 @@ struct DecodeArgs {
   int32_t max_seq_len;      // the host's bound; longer rows get NaN outputs
   int32_t part_blocks;      // blocks per main partition
   int32_t num_parts;        // main partitions in the grid
-  int32_t slots;            // partial slots per (b, hq) = num_parts;
-                            // 1 = the decode kernel writes out directly
+  int32_t slots;            // partial slots per (b, hq) = num_parts (balanced:
+                            // wg_per_head); 1 = the decode kernel writes out
+                            // directly
+  // Balanced partitions (INT8 / FP8 / FP16, batch <= kMaxBalancedRows): the
+  // rows' blocks of each KV head, concatenated, are cut into wg_per_head
+  // equal ranges, one per workgroup; a workgroup writes one partial per row
+  // segment of its range (see decode_balanced in kvq_decode.hip).
+  int32_t balanced;
+  int32_t wg_per_head;
   int32_t ring;             // INT4 ring slots
   int32_t residual;         // INT4 residual length
   int32_t k_head_stride;    // 0 for a per-tensor K scale, 1 per head
@@ -96,6 +103,8 @@ struct DecodeArgs {
   int32_t xcd_heads;
   float qk_scale;           // softmax_scale * log2(e)
 };
+
+constexpr int kMaxBalancedRows = 256;
 
 // Kernel-side scale kinds for the decode templates.
 int decode_scale_kind(int granularity);

@@ -464,9 +464,12 @@ __device__ __forceinline__ void load_q(u32x4 (&qr)[4], const DecodeArgs &a, int 
   }
 }
 
+// Blocks [blk0, blk1) of row b (a partition, or a balanced launch's segment
+// of the row).  use_pre: the first 256 block ids arrive prefetched (pre_id).
 template <int DT, int KS, int VS>
-__device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h, int p,
-                          int seq_len, int wave, int lane, int tid, int pre_id) {
+__device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
+                          int blk0, int blk1, int seq_len, int wave, int lane, int tid,
+                          int pre_id, bool use_pre) {
   const int n = lane & 15, qd = lane >> 4;
   u32x4 qr[4];
   load_q(qr, a, b, h, n, qd);
@@ -504,13 +507,10 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     if constexpr (KS == kUniform) kmul *= a.k_scales[h * a.k_head_stride];
   }
 
-  const int n_blocks = (seq_len + kBlock - 1) / kBlock;
-  const int blk0 = p * a.part_blocks;
-  const int blk1 = min(n_blocks, blk0 + a.part_blocks);
   const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
   for (int c0 = blk0; c0 < blk1; c0 += kIdChunk) {
     const int c1 = min(blk1, c0 + kIdChunk);
-    stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
+    stage_ids(sh, bt, c0, c1, tid, pre_id, use_pre && c0 == blk0);
     const int npairs = (c1 - c0 + 1) / 2;
     // Pairs wholly visible to every column run unmasked.  The rest are
     // masked per column: the row's partial block, a chunk's odd last block
@@ -1617,6 +1617,44 @@ __device__ __forceinline__ WriteArgs step_write_args(const DecodeArgs &a) {
   return w;
 }
 
+// Prefix sums of the rows' block counts, for the balanced partitions:
+// pre[0] = 0, pre[b + 1] = blocks of rows 0 .. b.  A row of length <= 0 or
+// above the host's max_seq_len counts no blocks (no workgroup streams it;
+// the merge gives it zeros or NaN).  All 256 threads of the workgroup call
+// it (batch <= 256); it ends with a barrier.
+__device__ void row_block_prefix(const DecodeArgs &a, int *pre, int tid) {
+  int x = 0;
+  if (tid < a.batch) {
+    const int s = a.seq_lens[tid];
+    x = (s > 0 && s <= a.max_seq_len) ? (s + kBlock - 1) / kBlock : 0;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) pre[kMaxBalancedRows + 1 + wave] = x;  // wave totals
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += pre[kMaxBalancedRows + 1 + w];
+  pre[tid + 1] = x;
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+}
+
+// The balanced range of workgroup w: blocks [start, end) of the
+// concatenation, range = ceil(total / wg_per_head) blocks per workgroup.
+struct BalancedRange {
+  int range, start, end;
+};
+__device__ __forceinline__ BalancedRange balanced_range(const DecodeArgs &a, const int *pre,
+                                                        int w) {
+  const int total = pre[a.batch];
+  const int range = max(1, (total + a.wg_per_head - 1) / a.wg_per_head);
+  const int start = min(total, w * range);
+  return {range, start, min(total, start + range)};
+}
+
 // out rows of (row b, KV head h): column hn of this thread (tid / 16), its
 // eight channels 8 (tid % 16) ..
 __device__ __forceinline__ float *out_cols(const DecodeArgs &a, int b, int h, int tid) {
@@ -1741,9 +1779,72 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    stream_q8<DT, KS, VS>(st, a, sh, b, h, p, seq_len, wave, lane, tid, pre_id);
+    const int blk0 = p * a.part_blocks;
+    const int blk1 = min((seq_len + kBlock - 1) / kBlock, blk0 + a.part_blocks);
+    stream_q8<DT, KS, VS>(st, a, sh, b, h, blk0, blk1, seq_len, wave, lane, tid, pre_id, true);
   }
   merge_and_store(a, sh, st, b, h, p, direct, wave, lane, tid);
+}
+
+// Balanced partitions (INT8 / FP8 / FP16): workgroup i takes KV head
+// i % H and the range w = i / H of that head's blocks, the rows'
+// blocks laid end to end in row order ([oh-bug] "KV Cache Quantization 生产实战",
+// section "为什么长上下文更需要 KV Cache Quantization": every step streams
+// each row's whole history, so ragged rows leave short workgroups idle when
+// each row is split on its own).  The range crosses row boundaries; each
+// row segment is streamed as a partition is (the row's own query group,
+// online softmax, LDS merge of the four waves) and leaves one partial in
+// slot w - floor(first block of the row / range) of the row, which the
+// merge finds from the same prefix sums.  A decode step's new token is
+// appended by the workgroup whose segment holds the row's last block.
+template <int DT, int KS, int VS>
+__device__ void decode_balanced(const DecodeArgs &a, SharedLds &sh, int *pre) {
+  const int i = blockIdx.x;
+  int h, w;
+  if (a.xcd_heads) {
+    // all heads of range w on one XCD (workgroup i runs on XCD i % 8), as
+    // wg_coord deals them: neighbouring heads share lines of the scale rows
+    const int j = i >> 3;
+    h = j % a.num_kv_heads;
+    w = (j / a.num_kv_heads) * 8 + (i & 7);
+  } else {
+    h = i % a.num_kv_heads;
+    w = i / a.num_kv_heads;
+  }
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  row_block_prefix(a, pre, tid);
+  if (w >= a.wg_per_head) return;  // padding of the XCD-dealt grid
+  const BalancedRange r = balanced_range(a, pre, w);
+  if (r.start >= r.end) return;
+  // first row whose blocks reach past start (binary search over pre)
+  int lo = 0, hi = a.batch;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid + 1] <= r.start) lo = mid + 1;
+    else hi = mid;
+  }
+  for (int b = lo; b < a.batch && pre[b] < r.end; ++b) {
+    const int nb = pre[b + 1] - pre[b];
+    if (nb == 0) continue;
+    const int blk0 = max(r.start, pre[b]) - pre[b];
+    const int blk1 = min(r.end, pre[b + 1]) - pre[b];
+    const int seq_len = a.seq_lens[b];
+    Softmax st;
+    softmax_init(st);
+    if (a.k_new != nullptr && blk1 == nb) {
+      // this segment holds the row's last block: store the new token first
+      if constexpr (DT == kFp16) {
+        append_token_f16(a, b, h, seq_len, wave, lane);
+      } else {
+        append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    stream_q8<DT, KS, VS>(st, a, sh, b, h, blk0, blk1, seq_len, wave, lane, tid, 0, false);
+    merge_and_store(a, sh, st, b, h, w - pre[b] / r.range, false, wave, lane, tid);
+  }
 }
 
 // INT8 / FP8 / FP16 and INT4 caches get separate kernels so that each is
@@ -1752,6 +1853,11 @@ template <int DT, int KS, int VS>
 __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, KS, VS)) void kvq_paged_decode_kernel(
     DecodeArgs a) {
   __shared__ SharedLds sh;
+  if (a.balanced) {
+    __shared__ int pre[kMaxBalancedRows + 1 + kWaves];
+    decode_balanced<DT, KS, VS>(a, sh, pre);
+    return;
+  }
   decode_workgroup<DT, KS, VS, false>(a, sh);
 }
 
@@ -1778,6 +1884,17 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
   const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, query, hq) row
   const int c4 = threadIdx.x & 31;
   const int b = gid / (a.num_q_heads * a.n_query);
+  // balanced partitions: the row's partials are those of the ranges its
+  // blocks meet (the decode kernel's prefix sums, recomputed here)
+  __shared__ int pre[kMaxBalancedRows + 1 + kWaves];
+  int bal_total = 0;
+  if (a.balanced) {
+    row_block_prefix(a, pre, threadIdx.x);
+    if (b < a.batch && pre[b + 1] > pre[b]) {
+      const int range = balanced_range(a, pre, 0).range;
+      bal_total = (pre[b + 1] - 1) / range - pre[b] / range + 1;
+    }
+  }
   if (b >= a.batch) return;
   const size_t base = (size_t)gid * a.slots;
   float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
@@ -1800,7 +1917,9 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
         *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
         return;
       }
-      if (is_int4) {
+      if (a.balanced) {
+        total = bal_total;
+      } else if (is_int4) {
         const int nq = kivi_quantized_len(seq_len, a.residual);
         total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
       } else {
@@ -1880,7 +1999,11 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   const long pairs8 = ((long)a.num_parts * batch + 7) / 8 * 8;
   // a KIVI decode step: its flush workgroups (K and V of every (row, head))
   const long flush = is_kivi(dtype) && a.k_new != nullptr ? 2L * batch * a.num_kv_heads : 0;
-  const dim3 grid((unsigned)(pairs8 * a.num_kv_heads + flush));
+  // balanced: the ranges of every head, padded to a multiple of 8 ranges
+  // when the heads of a range are dealt to one XCD
+  const long bal = a.xcd_heads ? ((long)a.wg_per_head + 7) / 8 * 8 * a.num_kv_heads
+                               : (long)a.wg_per_head * a.num_kv_heads;
+  const dim3 grid(a.balanced ? (unsigned)bal : (unsigned)(pairs8 * a.num_kv_heads + flush));
   // the compact INT4 layout holds one query token's four heads per block
   if (dtype == kInt4 && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, true>), grid, dim3(kThreads), 0,
@@ -1908,7 +2031,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
     launch_k<kInt8>(a, k_kind, v_kind, grid, stream);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.slots == 1) return e;
+  if (e != hipSuccess || (a.slots == 1 && !a.balanced)) return e;
   const int rows = batch * a.n_query * a.num_q_heads;
   hipLaunchKernelGGL(kvq_partition_reduce_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, a,
                      is_kivi(dtype) ? 1 : 0);

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2, INT2_AFFINE = 1, 2, 3, 4, 5, 6, 7
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
+PARTITION_PER_ROW, PARTITION_BALANCED = 0, 1
+PARTITIONS = {"per-row": PARTITION_PER_ROW, "balanced": PARTITION_BALANCED}
 DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16,
           "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2, "int2-affine": INT2_AFFINE}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
@@ -33,7 +35,8 @@ EXPORTED = ("kvq_status_str", "kvq_validate", "kvq_decode_workspace_bytes",
             "kvq_write", "kvq_paged_decode", "kvq_write_decode",
             "kvq_calibrate_workspace_bytes", "kvq_calibrate",
             "kvq_paged_decode_mq_workspace_bytes", "kvq_paged_decode_mq",
-            "kvq_plan_split_tokens", "kvq_check_tables", "kvq_write_decode_noalloc")
+            "kvq_plan_split_tokens", "kvq_check_tables", "kvq_write_decode_noalloc",
+            "kvq_plan_partition")
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -52,6 +55,7 @@ class Layout(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("split_tokens", ctypes.c_int32),
+        ("partition", ctypes.c_int32),
     ]
 
 
@@ -98,6 +102,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_write_decode_noalloc.restype = I32
     lib.kvq_write_decode_noalloc.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P,
                                              P, P, P, P, I32, I32, ctypes.c_float, P, P]
+    lib.kvq_plan_partition.restype = I32
+    lib.kvq_plan_partition.argtypes = [ctypes.POINTER(Layout), P, I32]
     lib.kvq_plan_split_tokens.restype = I32
     lib.kvq_plan_split_tokens.argtypes = [ctypes.POINTER(Layout), P, I32]
     lib.kvq_paged_decode_mq_workspace_bytes.restype = SZ
@@ -121,10 +127,10 @@ LIB = _load()
 def make_layout(dtype: str, k_gran: str, v_gran: str, num_q_heads: int, num_kv_heads: int,
                 num_blocks: int, max_blocks_per_seq: int, split_tokens: int = 0,
                 residual_len: int = 128, group_size: int = 64, head_dim: int = 128,
-                block_size: int = 16) -> Layout:
+                block_size: int = 16, partition: str = "per-row") -> Layout:
     return Layout(ctypes.sizeof(Layout), DTYPES[dtype], GRANS[k_gran], GRANS[v_gran],
                   group_size, residual_len, block_size, num_q_heads, num_kv_heads, head_dim,
-                  num_blocks, max_blocks_per_seq, split_tokens)
+                  num_blocks, max_blocks_per_seq, split_tokens, PARTITIONS[partition])
 
 
 def _ptr(t) -> int | None:
@@ -420,3 +426,15 @@ def check_tables(layout: Layout, host_block_tables, host_seq_lens, max_seq_len: 
                               lens.ctypes.data if batch else None, batch, int(max_seq_len),
                               ctypes.byref(bad))
     return int(st), int(bad.value)
+
+
+def plan_partition(layout: Layout, host_seq_lens) -> int:
+    """kvq_plan_partition: PARTITION_PER_ROW or PARTITION_BALANCED for these
+    host-known row lengths (see kvq.h); raises on error."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(host_seq_lens, dtype=np.int32))
+    r = LIB.kvq_plan_partition(ctypes.byref(layout),
+                               lens.ctypes.data if lens.size else None, int(lens.size))
+    if r < 0:
+        raise KvqError(r, "kvq_plan_partition")
+    return int(r)

@@ -95,7 +95,8 @@ def decode_times(rows):
 
 
 def stats(directory: str, command: str, out: str, workload: str | None = None,
-          times_out: str | None = None, split_tokens: int | None = None) -> None:
+          times_out: str | None = None, split_tokens: int | None = None,
+          partition: str = "per-row") -> None:
     rows = list(csv.DictReader(open(_find(directory, "kernel_trace.csv"))))
     dt = decode_times(rows)
     per = {}
@@ -130,8 +131,8 @@ def stats(directory: str, command: str, out: str, workload: str | None = None,
         data["note"] = ("rocprofv3 kernel-trace durations (us) of the decode launches bench.py "
                         "times for its roofline (kvq_paged_decode: decode kernel, then the "
                         "partition reduce when the launch is split), per workload")
-        data[workload] = {**dt, "split_tokens": split_tokens, "command": command,
-                          "summary": os.path.relpath(out, ROOT)}
+        data[workload] = {**dt, "split_tokens": split_tokens, "partition": partition,
+                          "command": command, "summary": os.path.relpath(out, ROOT)}
         with open(times_out, "w") as f:
             json.dump(data, f, indent=1)
             f.write("\n")
@@ -157,7 +158,8 @@ def _per_launch(rows, copy_bytes_kib: float):
 
 
 def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fetch: str,
-            cmd_write: str, out: str, split_tokens: int | None = None) -> None:
+            cmd_write: str, out: str, split_tokens: int | None = None,
+            partition: str = "per-row") -> None:
     copy_kib = copy_mib * 1024.0
     rd, rf, n_rd = _per_launch(_counter(fetch_dir, "FETCH_SIZE"), copy_kib)
     wr, wf, n_wr = _per_launch(_counter(write_dir, "WRITE_SIZE"), copy_kib)
@@ -174,7 +176,7 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fe
         "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
         "fetch_scale": round(rf, 4), "write_scale": round(wf, 4),
         "dispatches": [n_rd, n_wr], "command_fetch": cmd_fetch, "command_write": cmd_write,
-        "split_tokens": split_tokens,
+        "split_tokens": split_tokens, "partition": partition,
     }
     with open(out, "w") as f:
         json.dump(data, f, indent=1)
@@ -196,6 +198,7 @@ def main(argv=None):
                    help="JSON file collecting decode / merge durations per workload")
     s.add_argument("--split-tokens", type=int, default=None,
                    help="the partition length the profiled launches used")
+    s.add_argument("--partition", default="per-row", choices=["per-row", "balanced"])
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -206,12 +209,13 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     t.add_argument("--split-tokens", type=int, default=None,
                    help="the partition length the profiled launches used")
+    t.add_argument("--partition", default="per-row", choices=["per-row", "balanced"])
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        stats(a.dir, a.command, a.out, a.workload, a.times_out, a.split_tokens)
+        stats(a.dir, a.command, a.out, a.workload, a.times_out, a.split_tokens, a.partition)
     else:
         traffic(a.fetch_dir, a.write_dir, a.workload, a.copy_mib, a.command_fetch,
-                a.command_write, a.out, a.split_tokens)
+                a.command_write, a.out, a.split_tokens, a.partition)
 
 
 if __name__ == "__main__":

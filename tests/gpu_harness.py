@@ -68,7 +68,7 @@ def fill_garbage(cache):
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
              table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
-             n_query=0, host_plan=False, device="cuda"):
+             n_query=0, host_plan=False, partition="per-row", device="cuda"):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
@@ -84,9 +84,10 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         nb = int(table.max()) + 1
     mbs = table.shape[1]
     layout = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads, w.num_kv_heads,
-                             nb, mbs, split_tokens, w.residual_len)
+                             nb, mbs, split_tokens, w.residual_len, partition=partition)
     if host_plan:
         layout.split_tokens = kvq.plan_split_tokens(layout, lens)
+        layout.partition = kvq.plan_partition(layout, lens)
     ks, vs = [], []
     for r in range(b):
         k, v = inputs.gen_kv(w, layer, r, int(lens[r]), device, seed)

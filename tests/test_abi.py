@@ -34,8 +34,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_sizes_match_header():
-    # kvq_layout: 1 uint32 + 12 int32; kvq_cache: 6 pointers + int32 (+pad)
-    assert ctypes.sizeof(kvq.Layout) == 52
+    # kvq_layout: 1 uint32 + 13 int32; kvq_cache: 6 pointers + int32 (+pad)
+    assert ctypes.sizeof(kvq.Layout) == 56
     assert ctypes.sizeof(kvq.Cache) == 56
 
 
@@ -420,3 +420,21 @@ def test_noalloc_rejects_oversized_partials_before_any_hip_call():
     assert kvq.LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(_cache()), FAKE,
                                             FAKE, FAKE, FAKE, FAKE, 0, 2048, 0.1, FAKE,
                                             None) == OK
+
+
+def test_balanced_partition_rules():
+    assert kvq.validate(_layout(partition=1), _cache(), 256, 100) == OK
+    assert kvq.validate(_layout(partition=1), _cache(), 257, 100) == UNS     # > 256 rows
+    assert kvq.validate(_layout(partition=2), _cache(), 2, 100) == INV
+    lay4 = kvq.make_layout("int4", "channel", "token", 8, 2, 64, 16, partition="balanced")
+    assert kvq.validate(lay4, _cache(int4=True), 2, 100) == UNS              # KIVI caches
+    # the plan: ragged rows that fit one round go balanced; KIVI never
+    lay = kvq.make_layout("fp8", "head", "head", 32, 8, 20000, 1024)
+    lens = [1024, 16384] + [2000] * 30
+    assert kvq.plan_partition(lay, lens) == kvq.PARTITION_BALANCED
+    lay4 = kvq.make_layout("int4", "channel", "token", 32, 8, 20000, 1024)
+    assert kvq.plan_partition(lay4, lens) == kvq.PARTITION_PER_ROW
+    # short rows (several rounds of per-row workgroups) stay per row
+    lay2 = kvq.make_layout("int8", "token", "token", 32, 32, 512, 128)
+    assert kvq.plan_partition(lay2, [2048] * 4) == kvq.PARTITION_PER_ROW
+    assert kvq.plan_partition(lay2, []) == kvq.PARTITION_PER_ROW

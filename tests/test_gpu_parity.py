@@ -236,3 +236,41 @@ def test_planned_split_on_ragged_rows(dtype, kg, vg):
     split = kvq.plan_split_tokens(lay, lens)
     res = run_case(w, lens, split_tokens=split, table=table)
     check_rows(res)
+
+
+# --- balanced partitions (the rows of a KV head cut into equal block ranges)
+
+BAL_LENS = [1, 0, 300, 1000, 17, 64, 2000, 5]
+
+
+@pytest.mark.parametrize("dtype,kg,vg,table", [("int8", "token", "token", "identity"),
+                                               ("fp8", "head", "head", "shuffled"),
+                                               ("fp8e5m2", "channel", "token", "shuffled"),
+                                               ("int8", "channel", "tensor", "shuffled"),
+                                               ("fp16", "none", "none", "shuffled")])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("hkv", [2, 8])
+def test_balanced_partitions(dtype, kg, vg, table, fused, hkv):
+    # 2 KV heads: 128 ranges per head of one or two blocks, so rows span many
+    # workgroups and many ranges hold several rows; 8 KV heads: 32 per head
+    w = _small(dtype, kg, vg, hq=2 * hkv, hkv=hkv, table=table)
+    res = run_case(w, BAL_LENS, partition="balanced", fused=fused, decode_twice=True)
+    check_rows(res, rows=[r for r, s in enumerate(BAL_LENS) if s > 0])
+    assert np.all(res.out[1] == 0)
+    assert np.array_equal(res.out, res.out2)
+
+
+def test_balanced_matches_per_row_closely():
+    # the same attention; the partitions' running maxima differ, so the
+    # softmax weights round to fp16 differently (2^-11 relative each)
+    w = _small("int8", "token", "token", hq=16, hkv=4, table="shuffled")
+    a = run_case(w, BAL_LENS, partition="balanced", split_tokens=0)
+    b = run_case(w, BAL_LENS, partition="per-row", split_tokens=64)
+    assert np.allclose(a.out, b.out, atol=1e-3, rtol=1e-3)
+
+
+@pytest.mark.parametrize("n_query", [2, 4])
+def test_balanced_multi_query(n_query):
+    w = _small("int8", "token", "token", hq=8, hkv=2, table="shuffled")
+    res = run_case(w, [3, 1000, 40, 1], partition="balanced", n_query=n_query)
+    check_rows(res)
