@@ -209,7 +209,8 @@ def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
 # Achievable read bandwidth: the probe of libkvq_probe.so
 # ---------------------------------------------------------------------------
 
-def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048)):
+def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(128, 256, 512, 1024, 2048),
+                    threads: int = 256):
     """Read ``gib`` GiB (a power of two) per launch in 1 KiB chunks (one
     16-byte buffer load per lane, the decode's granule and cache policy)
     with several grid sizes, in wavefront-strided and in scattered chunk
@@ -227,7 +228,7 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048))
     lib = ctypes.CDLL(PROBE_LIB)
     lib.kvq_probe_read.restype = ctypes.c_int
     lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_void_p, ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     nbytes = int(gib * (1 << 30))
     slices = max(1, (2 << 30) // nbytes)
     reps = max(reps, min(slices, 64))
@@ -239,8 +240,8 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048))
     e1 = torch.cuda.Event(enable_timing=True)
 
     def launch(wgs, order, i=0):
-        rc = lib.kvq_probe_read(buf.data_ptr() + (i % slices) * nbytes, nbytes, wgs, order,
-                                sink.data_ptr(), stream.cuda_stream)
+        rc = lib.kvq_probe_read(buf.data_ptr() + (i % slices) * nbytes, nbytes, wgs, threads,
+                                order, sink.data_ptr(), stream.cuda_stream)
         if rc != 0:
             raise SystemExit(f"kvq_probe_read failed ({rc})")
 
@@ -254,7 +255,8 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048))
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            rows.append({"order": name, "workgroups": wgs, "us": round(ms * 1e3, 1),
+            rows.append({"order": name, "workgroups": wgs, "threads": threads,
+                         "us": round(ms * 1e3, 1),
                          "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
     del buf
     best = max(rows, key=lambda r: r["GBps"])
@@ -262,6 +264,21 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(256, 512, 1024, 2048))
             "chunk_bytes": 1024, "all": rows,
             "kernel": "kvq_probe_read_kernel (libkvq_probe.so): loads only, 8 chunks in "
                       "flight per wavefront"}
+
+
+def launch_floor(layer_bytes: int):
+    """The loads-only probe at the size of one decode launch (the largest
+    power of two not above its bytes, fresh data each launch): how long a
+    kernel that only reads that much takes, the floor of the launch."""
+    p2 = 1 << (int(layer_bytes).bit_length() - 1)
+    if p2 < (1 << 20) or p2 > (1 << 30):
+        return None
+    r = bandwidth_probe(p2 / (1 << 30), reps=32)
+    best = r["best"]
+    return {"bytes": p2, "us": best["us"], "GBps": best["GBps"],
+            "frac_of_peak": round(best["GBps"] / HBM_PEAK_GBS, 4),
+            "launch_floor_us": round(layer_bytes / (best["GBps"] * 1e9) * 1e6, 2),
+            "config": {k: best[k] for k in ("order", "workgroups", "threads")}}
 
 
 # ---------------------------------------------------------------------------
@@ -589,6 +606,7 @@ def run(args):
         del src, dst
     achieved = layer_bytes / (kern_ms * 1e-3) / 1e9
     probe = None if args.no_probe else bandwidth_probe(args.probe_gib)
+    floor = None if args.no_probe else launch_floor(layer_bytes)
 
     part_name = "balanced" if bench.layout.partition else "per-row"
     traffic = None
@@ -663,6 +681,7 @@ def run(args):
             "timing": kernel_timing,
             "probe_GBps": probe["GBps"] if probe else None,
             "frac_of_probe": round(achieved / probe["GBps"], 4) if probe else None,
+            "launch_size_probe": floor,
             "profiled": profiled,
         },
         "cpu_baseline": cpu,
@@ -705,6 +724,8 @@ def main():
                     help="skip the read-bandwidth probe")
     ap.add_argument("--probe-gib", type=float, default=4,
                     help="bytes the bandwidth probe reads per launch (GiB, a power of two)")
+    ap.add_argument("--probe-threads", type=int, default=256,
+                    help="threads per workgroup of the probe (--probe)")
     ap.add_argument("--probe", action="store_true",
                     help="run only the read-bandwidth probe and print its JSON")
     args = ap.parse_args()
@@ -716,7 +737,8 @@ def main():
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         raise SystemExit(2)
     if args.probe:
-        print(json.dumps(bandwidth_probe(args.probe_gib)), flush=True)
+        print(json.dumps(bandwidth_probe(args.probe_gib, threads=args.probe_threads)),
+              flush=True)
         return
     run(args)
 

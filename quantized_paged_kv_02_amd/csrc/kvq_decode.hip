@@ -1883,27 +1883,13 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
   constexpr int kUnroll = 8;
   const int gid = blockIdx.x * 8 + (threadIdx.x >> 5);   // (b, query, hq) row
   const int c4 = threadIdx.x & 31;
+  const int rows = a.batch * a.n_query * a.num_q_heads;
+  const bool live = gid < rows;
   const int b = gid / (a.num_q_heads * a.n_query);
-  // balanced partitions: the row's partials are those of the ranges its
-  // blocks meet (the decode kernel's prefix sums, recomputed here)
-  __shared__ int pre[kMaxBalancedRows + 1 + kWaves];
-  int bal_total = 0;
-  if (a.balanced) {
-    row_block_prefix(a, pre, threadIdx.x);
-    if (b < a.batch && pre[b + 1] > pre[b]) {
-      const int range = balanced_range(a, pre, 0).range;
-      bal_total = (pre[b + 1] - 1) / range - pre[b] / range + 1;
-    }
-  }
-  if (b >= a.batch) return;
-  const size_t base = (size_t)gid * a.slots;
-  float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
-  float big = kNegInf, lt = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int total = kUnroll;  // known once the row length has arrived
-  for (int p0 = 0; p0 < total; p0 += kUnroll) {
-    float mv[kUnroll], lv[kUnroll];
-    f32x4 ov[kUnroll];
+  const size_t base = (size_t)(live ? gid : rows - 1) * a.slots;
+  float mv[kUnroll], lv[kUnroll];
+  f32x4 ov[kUnroll];
+  auto load_chunk = [&](int p0) {
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const size_t slot = base + min(p0 + i, a.slots - 1);
@@ -1911,28 +1897,48 @@ __global__ __launch_bounds__(256) void kvq_partition_reduce_kernel(DecodeArgs a,
       lv[i] = a.ws_l[slot];
       ov[i] = *reinterpret_cast<const f32x4 *>(a.ws_o + slot * kHeadDim + 4 * c4);
     }
-    if (p0 == 0) {
-      const int seq_len = a.seq_lens[b];
-      if (seq_len <= 0) {
-        *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
-        return;
-      }
-      if (a.balanced) {
-        total = bal_total;
-      } else if (is_int4) {
-        const int nq = kivi_quantized_len(seq_len, a.residual);
-        total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
-      } else {
-        total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
-      }
-      if (seq_len > a.max_seq_len) {
-        // the row is longer than the host's max_seq_len: NaN, not a
-        // partial answer
-        const float nan = __builtin_nanf("");
-        *reinterpret_cast<f32x4 *>(out) = f32x4{nan, nan, nan, nan};
-        return;
-      }
+  };
+  // the first chunk is in flight while the row length (and, for balanced
+  // partitions, the rows' block prefix sums) arrive
+  load_chunk(0);
+  // balanced partitions: the row's partials are those of the ranges its
+  // blocks meet (the decode kernel's prefix sums, recomputed here)
+  __shared__ int pre[kMaxBalancedRows + 1 + kWaves];
+  int bal_total = 0;
+  if (a.balanced) {
+    row_block_prefix(a, pre, threadIdx.x);
+    if (live && pre[b + 1] > pre[b]) {
+      const int range = balanced_range(a, pre, 0).range;
+      bal_total = (pre[b + 1] - 1) / range - pre[b] / range + 1;
     }
+  }
+  if (!live) return;
+  float *out = a.out + (size_t)gid * kHeadDim + 4 * c4;
+  const int seq_len = a.seq_lens[b];
+  if (seq_len <= 0) {
+    *reinterpret_cast<f32x4 *>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (seq_len > a.max_seq_len) {
+    // the row is longer than the host's max_seq_len: NaN, not a partial
+    // answer
+    const float nan = __builtin_nanf("");
+    *reinterpret_cast<f32x4 *>(out) = f32x4{nan, nan, nan, nan};
+    return;
+  }
+  int total;
+  if (a.balanced) {
+    total = bal_total;
+  } else if (is_int4) {
+    const int nq = kivi_quantized_len(seq_len, a.residual);
+    total = max(1, (nq / kBlock + a.part_blocks - 1) / a.part_blocks);
+  } else {
+    total = ((seq_len + kBlock - 1) / kBlock + a.part_blocks - 1) / a.part_blocks;
+  }
+  float big = kNegInf, lt = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < total; p0 += kUnroll) {
+    if (p0 > 0) load_chunk(p0);
     float cm = big;
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) cm = p0 + i < total ? fmaxf(cm, mv[i]) : cm;

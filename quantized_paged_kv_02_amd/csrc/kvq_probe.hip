@@ -21,7 +21,7 @@ namespace {
 
 constexpr int kInFlight = 8;
 
-__global__ __launch_bounds__(256) void kvq_probe_read_kernel(const uint8_t *src,
+__global__ __launch_bounds__(1024) void kvq_probe_read_kernel(const uint8_t *src,
                                                              uint32_t chunk_mask,
                                                              int random_order,
                                                              uint32_t *sink) {
@@ -51,18 +51,19 @@ __global__ __launch_bounds__(256) void kvq_probe_read_kernel(const uint8_t *src,
 }  // namespace
 
 // Read `bytes` (a power of two, at least 1 MiB, 1 KiB aligned) at the device
-// pointer `src` once with `workgroups` 256-thread workgroups on `stream`;
-// `sink` is a device uint32 array of `workgroups` entries that the kernel
-// may write.  Returns 0 on success, -1 for bad arguments, -6 if the launch
-// failed.
-extern "C" int kvq_probe_read(const void *src, size_t bytes, int workgroups, int random_order,
-                              uint32_t *sink, void *stream) {
+// pointer `src` once with `workgroups` workgroups of `threads` threads (64,
+// 128, ..., 1024) on `stream`; `sink` is a device uint32 array of
+// `workgroups` entries that the kernel may write.  Returns 0 on success, -1
+// for bad arguments, -6 if the launch failed.
+extern "C" int kvq_probe_read(const void *src, size_t bytes, int workgroups, int threads,
+                              int random_order, uint32_t *sink, void *stream) {
   if (!src || !sink || workgroups < 1 || bytes < (1u << 20) || (bytes & (bytes - 1)) != 0 ||
-      (reinterpret_cast<uintptr_t>(src) & 1023u) != 0 || bytes / 1024 > (1ull << 30))
+      (reinterpret_cast<uintptr_t>(src) & 1023u) != 0 || bytes / 1024 > (1ull << 30) ||
+      threads < 64 || threads > 1024 || threads % 64 != 0)
     return -1;
   const uint32_t mask = (uint32_t)(bytes / 1024 - 1);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kvq_probe_read_kernel, dim3(workgroups), dim3(256), 0,
+  hipLaunchKernelGGL(kvq_probe_read_kernel, dim3(workgroups), dim3(threads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(src), mask,
                      random_order, sink);
   return hipGetLastError() == hipSuccess ? 0 : -6;
