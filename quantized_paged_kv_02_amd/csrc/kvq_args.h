@@ -106,8 +106,11 @@ struct DecodeArgs {
 
 constexpr int kMaxBalancedRows = 256;
 
-// Kernel-side scale kinds for the decode templates.
-int decode_scale_kind(int granularity);
+// Kernel-side scale kind of a kvq_granularity (0 tensor, 1 head, 2
+// channel, 3 token).
+constexpr int decode_scale_kind(int granularity) {
+  return granularity == 2 ? kChannel : (granularity == 3 ? kToken : kUniform);
+}
 
 // Static-scale calibration (kvq_calibrate).  Granularities are kvq_granularity
 // values; a null scale array is not calibrated (per-token granularity).

@@ -1991,13 +1991,6 @@ void launch_k(const DecodeArgs &a, int k_kind, int v_kind, dim3 grid, hipStream_
 
 }  // namespace
 
-int decode_scale_kind(int granularity) {
-  // kvq_granularity: 0 tensor, 1 head, 2 channel, 3 token
-  if (granularity == 2) return kChannel;
-  if (granularity == 3) return kToken;
-  return kUniform;
-}
-
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind, int batch,
                          hipStream_t stream) {
   // one workgroup per (partition, KV head, row), ordered for the XCDs by

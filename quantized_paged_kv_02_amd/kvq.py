@@ -77,47 +77,43 @@ class KvqError(RuntimeError):
         self.status = status
 
 
-def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+def _signatures():
+    """(name, restype, argtypes) of every C entry point."""
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    L, C = ctypes.POINTER(Layout), ctypes.POINTER(Cache)
+    return [
+        ("kvq_status_str", ctypes.c_char_p, [I32]),
+        ("kvq_validate", I32, [L, C, I32, I32]),
+        ("kvq_decode_workspace_bytes", SZ, [L, I32, I32]),
+        ("kvq_write", I32, [L, C, P, P, P, P, P, I32, I32, I32, P]),
+        ("kvq_paged_decode", I32, [L, C, P, P, P, I32, I32, F, P, P, SZ, P]),
+        ("kvq_write_decode", I32, [L, C, P, P, P, P, P, I32, I32, F, P, P, SZ, P]),
+        ("kvq_write_decode_noalloc", I32, [L, C, P, P, P, P, P, I32, I32, F, P, P]),
+        ("kvq_plan_partition", I32, [L, P, I32]),
+        ("kvq_plan_split_tokens", I32, [L, P, I32]),
+        ("kvq_paged_decode_mq_workspace_bytes", SZ, [L, I32, I32, I32]),
+        ("kvq_paged_decode_mq", I32, [L, C, P, I32, P, P, I32, I32, F, P, P, SZ, P]),
+        ("kvq_check_tables", I32, [L, P, P, I32, I32, ctypes.POINTER(I32)]),
+        ("kvq_calibrate_workspace_bytes", SZ, [L, I32]),
+        ("kvq_calibrate", I32, [L, P, P, I32, P, P, I32, P, SZ, P]),
+    ]
+
+
+def _load(path: str = LIB_PATH, strict: bool = True) -> ctypes.CDLL:
+    """Load the library at ``path`` and declare every entry point's C
+    signature.  strict=False skips entry points the library lacks (a
+    host-only test build)."""
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with "
             "`python -m quantized_paged_kv_02_amd.build` (there is no fallback)")
     lib = ctypes.CDLL(path)
-    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    lib.kvq_status_str.restype = ctypes.c_char_p
-    lib.kvq_status_str.argtypes = [I32]
-    lib.kvq_validate.restype = I32
-    lib.kvq_validate.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), I32, I32]
-    lib.kvq_decode_workspace_bytes.restype = SZ
-    lib.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32, I32]
-    lib.kvq_write.restype = I32
-    lib.kvq_write.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P, P,
-                              I32, I32, I32, P]
-    lib.kvq_paged_decode.restype = I32
-    lib.kvq_paged_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P,
-                                     I32, I32, ctypes.c_float, P, P, SZ, P]
-    lib.kvq_write_decode.restype = I32
-    lib.kvq_write_decode.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, P, P, P,
-                                     P, I32, I32, ctypes.c_float, P, P, SZ, P]
-    lib.kvq_write_decode_noalloc.restype = I32
-    lib.kvq_write_decode_noalloc.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P,
-                                             P, P, P, P, I32, I32, ctypes.c_float, P, P]
-    lib.kvq_plan_partition.restype = I32
-    lib.kvq_plan_partition.argtypes = [ctypes.POINTER(Layout), P, I32]
-    lib.kvq_plan_split_tokens.restype = I32
-    lib.kvq_plan_split_tokens.argtypes = [ctypes.POINTER(Layout), P, I32]
-    lib.kvq_paged_decode_mq_workspace_bytes.restype = SZ
-    lib.kvq_paged_decode_mq_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32, I32, I32]
-    lib.kvq_paged_decode_mq.restype = I32
-    lib.kvq_paged_decode_mq.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Cache), P, I32,
-                                        P, P, I32, I32, ctypes.c_float, P, P, SZ, P]
-    lib.kvq_check_tables.restype = I32
-    lib.kvq_check_tables.argtypes = [ctypes.POINTER(Layout), P, P, I32, I32,
-                                     ctypes.POINTER(I32)]
-    lib.kvq_calibrate_workspace_bytes.restype = SZ
-    lib.kvq_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(Layout), I32]
-    lib.kvq_calibrate.restype = I32
-    lib.kvq_calibrate.argtypes = [ctypes.POINTER(Layout), P, P, I32, P, P, I32, P, SZ, P]
+    for name, res, args in _signatures():
+        if not strict and not hasattr(lib, name):
+            continue
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
     return lib
 
 
