@@ -134,9 +134,10 @@
  * query per row (kvq_paged_decode_mq takes n_query = 1 only).
  *   k_codes : uint8 [NB][H][512]; (slot s, channel c) at byte
  *             128*(c>>5) + 8*s + ((c&31)>>2), bits 2*(c&3).
- *   v_codes : uint8 [NB][H][512]; with j = c>>4, e = s&3 and
- *             pos(e) = 0, 2, 1, 3 for e = 0..3: byte
- *             8*((c&15) + 16*(s>>2)) + 4*(j>>2) + pos(e), bits 2*(j&3).
+ *   v_codes : uint8 [NB][H][512]; with j = c>>4, e = s&3: byte
+ *             8*((c&15) + 16*(s>>2)) + 4*((j&3)>>1) + 2*(j&1) + (e>>1),
+ *             bits 2*(j>>2) + 4*(e&1) (a byte holds two consecutive tokens
+ *             of two tiles, which the decode converts as FP4 nibbles).
  *
  * ---- FP16 (unquantized) layout: fp16 [NB][H][2048] for each of K and V ----
  * The baseline the quantized formats are measured against ([intelli] §5:

@@ -1127,15 +1127,16 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[4], con
 }
 
 // ---------------------------------------------------------------------------
-// 2-bit affine KIVI on the compact layout.  Key codes: a dword holds 16
-// channels (2 bits each); masking one 2-bit field per fp16 half under the
-// exponent of 1024, less 1024, gives 4^k u for fields k = 0..3 of bytes 0
-// and 2 (and of bytes 1 and 3 after a shift by 8), so one dword yields two
-// operands of 8 channels: slots (2k, 2k+1) hold channels (k, k+8) or
-// (4+k, 12+k), weight 4^-k folded into q'.  Value codes are stored by token
-// (byte order t0, t2, t1, t3; four tiles per byte), so the same masks give
-// tile k's pairs (t0, t1) and (t2, t3), less 1024 exactly: a tile carries
-// the factor 4^k, removed at the end.
+// 2-bit affine KIVI on the compact layout.  A code u in the low two bits
+// of a nibble (00uu) is the OCP FP4 (E2M1) value u / 2 exactly, so a dword
+// masked with 0x33333333 (fields 0 and 2 of every byte), or shifted right by
+// 2 and masked (fields 1 and 3), becomes exact fp16 codes one byte -- two
+// codes -- per hardware FP4 conversion (scale 2).  Key codes: byte b of a
+// lane's dword w holds channels 16w + 4b + f at bits 2f, so the operand of
+// (w, field parity h) holds channels 16w + 4b + h and 16w + 4b + h + 2 in
+// slots 2b, 2b + 1.  Value codes are stored so that each byte holds two
+// consecutive tokens of two tiles (the layout in kvq.h): one conversion
+// gives a tile's two tokens, four give its operand of a block pair.
 // ---------------------------------------------------------------------------
 struct Group2C {
   u32x2 k[4];   // block u: codes of channels 32qd..32qd+31, token l%16
@@ -1151,11 +1152,11 @@ __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
                             __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
 }
 
-// Channel (within its 32) of the first of lane l's two q' channels: chunk
-// J = (l/4)%4, pair i = l%4 -> 16(J/2) + 4(J%2) + i; the second is +8.
+// Channel (within its 32) of the first of lane l's two q' channels: operand
+// J = (l/4)%4, slot pair i = l%4 -> 16(J/2) + 4i + J%2; the second is + 2.
 __device__ __forceinline__ int k2_chan(int lane) {
   const int J = (lane >> 2) & 3, i = lane & 3;
-  return 16 * (J >> 1) + 4 * (J & 1) + i;
+  return 16 * (J >> 1) + 4 * i + (J & 1);
 }
 
 __device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, const int (&ph)[4],
@@ -1171,7 +1172,7 @@ __device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, co
   const float *krow = a.k_scales + ((size_t)pm * H + h) * kRow;
   const int c = k2_chan(lane);
   t.ks[0] = krow[c];
-  t.ks[1] = krow[c + 8];
+  t.ks[1] = krow[c + 2];
   const float *vsp = a.v_scales + ((size_t)pv * H + h) * kRow + 8 * (lane >> 4);
   t.vsa = ld16f(vsp);
   t.vsb = ld16f(vsp + 4);
@@ -1180,33 +1181,34 @@ __device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, co
   t.zw = reinterpret_cast<const uint32_t *>(zrow)[n & 7];
 }
 
-// The four fp16 pairs of 2-bit fields k = 0..3 of bytes 0 and 2 of x:
-// 4^k u, exact (the splice gives 1024 + 4^k u; the 1024, large next to the
-// codes' range, is removed here rather than from the fp32 score sums).
-__device__ __forceinline__ f16x8 uint2x8_to_f16(uint32_t x) {
-  const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
-  const u32x4 r = {as_u32(as_f16x2((x & 0x00030003u) | 0x64006400u) + m1024),
-                   as_u32(as_f16x2((x & 0x000C000Cu) | 0x64006400u) + m1024),
-                   as_u32(as_f16x2((x & 0x00300030u) | 0x64006400u) + m1024),
-                   as_u32(as_f16x2((x & 0x00C000C0u) | 0x64006400u) + m1024)};
-  return u4_to_f16x8(r);
+// Bytes B0 and B0 + 1 of a masked dword (two 2-bit codes in the low bits
+// of each nibble) as four exact fp16 codes: byte B0's low then high nibble,
+// then byte B0 + 1's.
+template <int B0>
+__device__ __forceinline__ f16x4 uint2_bytes(uint32_t y) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0 + 1);
+  return f16x4{a.x, a.y, b.x, b.y};
 }
+__device__ __forceinline__ f16x8 uint2_operand(uint32_t y) {
+  return cat(uint2_bytes<0>(y), uint2_bytes<2>(y));
+}
+constexpr uint32_t kFields02 = 0x33333333u;  // fields 0 and 2 of every byte
 
-// Key offset operand of chunk J: 4^k z for slots (2k, 2k+1) = channels
-// (c0 + k, c0 + k + 8), c0 = 16(J/2) + 4(J%2); zero-point dwords (channels
-// 4i .. 4i+3 in dword i) come by row broadcast.
+// Key offset operand J: the zero points z of slots (2i, 2i+1) = channels
+// 16(J/2) + 4i + J%2 and + 2, exact (a byte z < 16 read as an E4M3 byte is
+// z / 512); zero-point dword d holds channels 4d .. 4d+3 and comes by row
+// broadcast.
 template <int J>
 __device__ __forceinline__ f16x8 zp2_key_offsets(uint32_t zw) {
-  constexpr int lo = 4 * (J >> 1) + (J & 1);
-  const uint32_t dl = row_bcast<lo>(zw), dh = row_bcast<lo + 2>(zw);
-  u32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t sel = (uint32_t)k | 0x0C00u | ((uint32_t)(4 + k) << 16) | 0x0C000000u;
-    const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
-    r[k] = as_u32(as_f16x2((__builtin_amdgcn_perm(dh, dl, sel) << (2 * k)) | 0x64006400u) +
-                  m1024);
-  }
+  constexpr uint32_t sel = (J & 1) ? 0x0C0C0301u : 0x0C0C0200u;  // bytes J%2, J%2+2
+  const uint32_t d0 = row_bcast<4 * (J >> 1) + 0>(zw), d1 = row_bcast<4 * (J >> 1) + 1>(zw);
+  const uint32_t d2 = row_bcast<4 * (J >> 1) + 2>(zw), d3 = row_bcast<4 * (J >> 1) + 3>(zw);
+  const u32x4 r = {
+      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d0, d0, sel), 512.0f, false)),
+      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d1, d1, sel), 512.0f, false)),
+      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d2, d2, sel), 512.0f, false)),
+      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d3, d3, sel), 512.0f, false))};
   return u4_to_f16x8(r);
 }
 
@@ -1225,29 +1227,28 @@ __device__ __forceinline__ f16x8 zp2_value_points(uint32_t zw) {
   return u4_to_f16x8(r);
 }
 
-// Value product of block pair PR: tile j = 4jh + k from the masks of field
-// k over each block's dword jh (and the dword shifted by 8), less 1024
-// exactly (the codes' range 0..3 is small next to the splice's 1024, which
-// would otherwise cost the fp32 sums their low bits).  vb[2 + g] takes the
-// weights times the zero points.
+// Value product of block pair PR.  Tile j (jj = j % 4) is in dword jj / 2
+// of each block, bytes 2(jj % 2) and 2(jj % 2) + 1 (tokens 0, 1 and 2, 3),
+// among fields 0 and 2 for tiles 0..3 and fields 1 and 3 for tiles 4..7.
+// vb[2 + g] takes the weights times the zero points.
 template <int PR>
 __device__ __forceinline__ void value_pair2c(Softmax &st, f32x4 (&vb)[4], const Group2C &t,
                                              const f16x8 &pb0, const f16x8 &pb1) {
-  const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+  uint32_t y[2][2][2];  // [block of the pair][dword][field parity]
 #pragma unroll
-  for (int jh = 0; jh < 2; ++jh) {
-    const uint32_t m0 = t.v[2 * PR][jh], m1 = t.v[2 * PR + 1][jh];
-    const uint32_t n0 = m0 >> 8, n1 = m1 >> 8;
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t mask = 0x00030003u << (2 * k);
-      const u32x4 r = {as_u32(as_f16x2((m0 & mask) | 0x64006400u) + m1024),
-                       as_u32(as_f16x2((n0 & mask) | 0x64006400u) + m1024),
-                       as_u32(as_f16x2((m1 & mask) | 0x64006400u) + m1024),
-                       as_u32(as_f16x2((n1 & mask) | 0x64006400u) + m1024)};
-      const int j = 4 * jh + k;
-      st.o[j] = mfma32(u4_to_f16x8(r), jh ? pb1 : pb0, st.o[j]);
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t x = t.v[2 * PR + u][w];
+      y[u][w][0] = x & kFields02;
+      y[u][w][1] = (x >> 2) & kFields02;
     }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int jj = j & 3, w = jj >> 1, hf = j >> 2;
+    const f16x8 av = (jj & 1) ? cat(uint2_bytes<2>(y[0][w][hf]), uint2_bytes<2>(y[1][w][hf]))
+                              : cat(uint2_bytes<0>(y[0][w][hf]), uint2_bytes<0>(y[1][w][hf]));
+    st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
   }
   vb[2] = mfma32(zp2_value_points<PR, 0>(t.zw), pb0, vb[2]);
   vb[3] = mfma32(zp2_value_points<PR, 1>(t.zw), pb1, vb[3]);
@@ -1274,8 +1275,9 @@ __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], con
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[u] = mfma32(uint2x8_to_f16(t.k[u][w]), bq[2 * w], acc[u]);
-      acc[u] = mfma32(uint2x8_to_f16(t.k[u][w] >> 8), bq[2 * w + 1], acc[u]);
+      const uint32_t x = t.k[u][w];
+      acc[u] = mfma32(uint2_operand(x & kFields02), bq[2 * w], acc[u]);
+      acc[u] = mfma32(uint2_operand((x >> 2) & kFields02), bq[2 * w + 1], acc[u]);
     }
   }
   ac = mfma32(zp2_key_offsets<0>(t.zw), bq[0], ac);
@@ -1288,8 +1290,7 @@ __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], con
   for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
   softmax_update_c(st, vb, s, p);
-  // weights times the V scales of this lane's tokens (channel groups 0, 1);
-  // the value codes carry their per-tile factor, not a per-token one
+  // weights times the V scales of this lane's tokens (channel groups 0, 1)
   const uint32_t d0[2] = {pack_rne(p[0] * t.vsa[0], p[1] * t.vsa[2]),
                           pack_rne(p[2] * t.vsb[0], p[3] * t.vsb[2])};
   const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
@@ -1313,13 +1314,11 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
   constexpr bool AFF = DT != kInt4;
   float qv[4][2];
   if constexpr (DT == kInt2Affine) {
-    // the pair's 2-bit field k = lane % 4 carries 4^k x code: q' / 4^k
     const int c = 32 * qd + k2_chan(lane);
-    const float f = 1.0f / (float)(1 << (2 * (lane & 3)));
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
-      qv[hh][0] = (float)sh.s.q[hh][c] * f;
-      qv[hh][1] = (float)sh.s.q[hh][c + 8] * f;
+      qv[hh][0] = (float)sh.s.q[hh][c];
+      qv[hh][1] = (float)sh.s.q[hh][c + 2];
     }
   } else {
     const int2 ko = koff_pair(lane);
@@ -1375,11 +1374,9 @@ __device__ void stream_int4c(Softmax &st, const DecodeArgs &a, SharedLds &sh, in
     pipeline<Unit>(cnt, load, compute);
   }
   if constexpr (DT == kInt2Affine) {
-    // tile j = 4g + k: remove the factor 4^k, then the zero points of
-    // channel group g
+    // tile j: remove the zero points of its channel group j / 4
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st.o[j] = st.o[j] * (1.0f / (float)(1 << (2 * (j & 3)))) - vb[2 + (j >> 2)];
+    for (int j = 0; j < 8; ++j) st.o[j] -= vb[2 + (j >> 2)];
   } else {
     // the value bias of each channel group, once into its four tiles
 #pragma unroll

@@ -295,12 +295,12 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
     const int m = u & 15, quad = u >> 4;
     uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * kChunk;
     if constexpr (TWO) {
-      // 2-bit: dword j>>2, byte pos(e) = 0, 2, 1, 3 of token e, bits 2(j&3)
+      // 2-bit: tile j, token e at dword (j % 4) / 2, byte 2 (j % 2) + e / 2,
+      // bits 2 (j / 4) + 4 (e % 2)
       u32x2 out = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
-        const int pos = (e == 1) ? 2 : (e == 2 ? 1 : e);
         float xv[8], sv[8], rv[8], zv[8];
         uint32_t qv[8];
 #pragma unroll
@@ -313,7 +313,8 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
         }
         kivi_codes<8, true>(qv, xv, sv, rv, zv, kQmax, 3u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j >> 2] |= qv[j] << (8 * pos + 2 * (j & 3));
+        for (int j = 0; j < 8; ++j)
+          out[(j & 3) >> 1] |= qv[j] << (8 * (2 * (j & 1) + (e >> 1)) + 2 * (j >> 2) + 4 * (e & 1));
       }
       *reinterpret_cast<u32x2 *>(chunk + 8 * u) = out;
     } else {

@@ -34,9 +34,10 @@ V16_OFF = (1024 * (C_IDX >> 5) + 256 * (S_IDX >> 2) + 16 * (C_IDX & 15)
 # 2-bit chunks (512 bytes per (block, head)): byte offset and bit position
 K2_BYTE = 128 * (C_IDX >> 5) + 8 * S_IDX + ((C_IDX & 31) >> 2)
 K2_BIT = np.broadcast_to(2 * (C_IDX & 3), (16, 128))
-_POS = np.array([0, 2, 1, 3])[S_IDX & 3]
-V2_BYTE = 8 * ((C_IDX & 15) + 16 * (S_IDX >> 2)) + 4 * ((C_IDX >> 4) >> 2) + _POS
-V2_BIT = np.broadcast_to(2 * ((C_IDX >> 4) & 3), (16, 128))
+_J2 = C_IDX >> 4
+V2_BYTE = (8 * ((C_IDX & 15) + 16 * (S_IDX >> 2)) + 4 * ((_J2 & 3) >> 1) + 2 * (_J2 & 1)
+           + ((S_IDX & 3) >> 1))
+V2_BIT = 2 * (_J2 >> 2) + 4 * (S_IDX & 1)
 assert sorted((4 * K2_BYTE + K2_BIT // 2).ravel().tolist()) == list(range(2048))
 assert sorted((4 * V2_BYTE + V2_BIT // 2).ravel().tolist()) == list(range(2048))
 
