@@ -130,8 +130,8 @@
  * 2-bit entry of [oh-bug] section "KV Cache 的基本内存模型" (0.25 byte per
  * value) and KIVI's asymmetric 2-bit scheme named in its references.
  * Groups, residual window, ring and the 40-float scale / zero-point rows
- * are those of KVQ_INT4_AFFINE.  Query groups Hq / H of at most 4, one
- * query per row (kvq_paged_decode_mq takes n_query = 1 only).
+ * are those of KVQ_INT4_AFFINE.  Query groups and query counts as for the
+ * other formats (n_query * Hq / H <= 16).
  *   k_codes : uint8 [NB][H][512]; (slot s, channel c) at byte
  *             128*(c>>5) + 8*s + ((c&31)>>2), bits 2*(c&3).
  *   v_codes : uint8 [NB][H][512]; with j = c>>4, e = s&3: byte

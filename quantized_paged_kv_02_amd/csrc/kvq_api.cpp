@@ -59,9 +59,6 @@ kvq_status check_layout(const kvq_layout *L) {
   if (L->head_dim != kHeadDim || L->block_size != kBlock) return KVQ_ERR_UNSUPPORTED;
   if (L->num_q_heads / L->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
   if (kivi(L)) {
-    // 2-bit decode is built for query groups of at most four
-    if (L->dtype == KVQ_INT2_AFFINE && L->num_q_heads / L->num_kv_heads > 4)
-      return KVQ_ERR_UNSUPPORTED;
     if (L->k_gran != KVQ_PER_CHANNEL || L->v_gran != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
     if (L->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
     if (L->residual_len < kGroup || L->residual_len % kGroup != 0) return KVQ_ERR_UNSUPPORTED;
@@ -558,7 +555,6 @@ static kvq_status check_mq(const kvq_layout *layout, int32_t n_query) {
   const kvq_status st = check_layout(layout);
   if (st != KVQ_OK) return st;
   if (n_query < 1) return KVQ_ERR_INVALID_ARG;
-  if (layout->dtype == KVQ_INT2_AFFINE && n_query > 1) return KVQ_ERR_UNSUPPORTED;
   if ((int64_t)n_query * (layout->num_q_heads / layout->num_kv_heads) > 16)
     return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;

@@ -55,6 +55,8 @@
 // enter through offset and bias operands of the matrix products).  Several
 // query tokens per row use the score product's columns for (query, head)
 // pairs and mask the last block pairs per column.
+#include <type_traits>
+
 #include "kvq_args.h"
 #include "kvq_device.h"
 #include "kvq_kivi_write.h"
@@ -920,10 +922,195 @@ __device__ __forceinline__ void compute_group4(Softmax &st, f32x4 (&vb)[2], cons
   }
 }
 
-template <bool AFF>
+// ---------------------------------------------------------------------------
+// 2-bit affine KIVI on the generic layout (more than four query heads per KV
+// head, or several queries per row): the 16 score columns hold (query,
+// head) pairs; q' = q s_c is split into fp16 hi and lo products as for
+// INT4.  Codes are converted as FP4 nibbles (see the compact 2-bit path
+// below) and the zero points subtracted exactly in fp16 before the key
+// products; the value zero points go to a per-channel-group accumulator.
+// ---------------------------------------------------------------------------
+struct Group2 {
+  u32x2 k[4];   // block u: codes of channels 32qd..32qd+31, token l%16
+  u32x2 v[4];   // block u: tokens 4qd..4qd+3 of channels 16j + l%16
+  float ks[2];  // as Group4: K scales of channels 8(l/4) + koff_pair(l)
+  float vs[2];  // V scales (channel groups 0, 1) of token l of the group
+  uint32_t kz;  // zero points of those K channels (bytes 0, 1)
+  uint32_t vz;  // zero points of those V scales (bytes 0, 1)
+  __device__ explicit Group2(int = 0) {}
+};
+
+__device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
+}
+
+// 2-bit codes as FP4: a code u in the low two bits of a nibble (00uu) is
+// the OCP FP4 (E2M1) value u / 2 exactly, so a dword masked with kFields02
+// (fields 0 and 2 of every byte), or shifted right by 2 and masked (fields
+// 1 and 3), converts to exact fp16 codes one byte -- two codes -- per
+// hardware FP4 conversion (scale 2).
+// Bytes B0 and B0 + 1 of a masked dword (two 2-bit codes in the low bits
+// of each nibble) as four exact fp16 codes: byte B0's low then high nibble,
+// then byte B0 + 1's.
+template <int B0>
+__device__ __forceinline__ f16x4 uint2_bytes(uint32_t y) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0 + 1);
+  return f16x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ f16x8 uint2_operand(uint32_t y) {
+  return cat(uint2_bytes<0>(y), uint2_bytes<2>(y));
+}
+constexpr uint32_t kFields02 = 0x33333333u;  // fields 0 and 2 of every byte
+
+// pm, pz as for load_group4 (the scale and zero-point rows are those of the
+// affine INT4 layout).
+__device__ __forceinline__ void load_group2(Group2 &t, const DecodeArgs &a, const int (&ph)[4],
+                                            int pm, int pz, int h, int lane) {
+  constexpr int kRow = 40;
+  const int H = a.num_kv_heads;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t chunk = (size_t)ph[u] * H + h;
+    t.k[u] = bld8(make_rsrc(a.k_codes + chunk * 512, 512), 8 * lane);
+    t.v[u] = bld8(make_rsrc(a.v_codes + chunk * 512, 512), 8 * lane);
+  }
+  const size_t chunk = (size_t)pm * H + h;
+  const int2 ko = koff_pair(lane);
+  const float *krow = a.k_scales + chunk * kRow;
+  const float *vrow = a.v_scales + chunk * kRow;
+  const float *ksp = krow + 8 * ((lane >> 2) & 3);
+  const float2 vs = *reinterpret_cast<const float2 *>(vrow + 2 * (lane & 15));
+  t.ks[0] = ksp[ko.x];
+  t.ks[1] = ksp[ko.y];
+  t.vs[0] = vs.x;
+  t.vs[1] = vs.y;
+  const uint8_t *kzp = reinterpret_cast<const uint8_t *>(krow + 32) + 8 * ((lane >> 2) & 3);
+  t.kz = (uint32_t)kzp[ko.x] | ((uint32_t)kzp[ko.y] << 8);
+  const float *zrow = a.v_scales + ((size_t)pz * H + h) * kRow;
+  t.vz = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(zrow + 32) +
+                                             8 * (lane >> 4) + 2 * (lane & 3));
+}
+
+// Element (or float) e of the operand of key chunk J: channel (within the
+// 16 of dword J / 2) 4(e/2) + J%2 + 2(e%2).
+template <int J>
+__device__ __forceinline__ int k2g_idx(int e) {
+  return 4 * (e >> 1) + (J & 1) + 2 * (e & 1);
+}
+
+__device__ __forceinline__ void compute_group2(Softmax &st, f32x4 (&vb)[2], const Group2 &t,
+                                               const f16 *qs, float *scl, float qk_scale,
+                                               int lane, int n, int qd) {
+  // stage the group's scales and zero points in this wave's LDS slot
+  {
+    const int2 ko = koff_pair(lane);
+    scl[8 * (lane >> 2) + ko.x] = t.ks[0];
+    scl[8 * (lane >> 2) + ko.y] = t.ks[1];
+    scl[256 + 8 * (lane >> 2) + ko.x] = (float)(t.kz & 0xFFu);
+    scl[256 + 8 * (lane >> 2) + ko.y] = (float)(t.kz >> 8);
+    *reinterpret_cast<float2 *>(scl + 384 + 2 * lane) =
+        float2{(float)(t.vz & 0xFFu), (float)(t.vz >> 8)};
+  }
+  *reinterpret_cast<float2 *>(scl + 128 + 2 * lane) = float2{t.vs[0], t.vs[1]};
+  f32x4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto chunk = [&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    const int base = 32 * qd + 16 * (J >> 1);  // the 16 channels of dword J / 2
+    const f16x8 q0 = *reinterpret_cast<const f16x8 *>(qs + n * kQRow + base);
+    const f16x8 q1 = *reinterpret_cast<const f16x8 *>(qs + n * kQRow + base + 8);
+    float sv[16], zv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(scl + base + 4 * i);
+      const f32x4 z = *reinterpret_cast<const f32x4 *>(scl + 256 + base + 4 * i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sv[4 * i + c] = a[c];
+        zv[4 * i + c] = z[c];
+      }
+    }
+    uint32_t hi[4], lo[4], zs[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int c0 = k2g_idx<J>(2 * e2), c1 = k2g_idx<J>(2 * e2 + 1);
+      const float x0 = (float)(c0 < 8 ? q0[c0] : q1[c0 - 8]) * sv[c0];
+      const float x1 = (float)(c1 < 8 ? q0[c1] : q1[c1 - 8]) * sv[c1];
+      split_hi_lo(x0, x1, hi[e2], lo[e2]);
+      zs[e2] = pack_rtz(-zv[c0], -zv[c1]);  // small integers: exact
+    }
+    const f16x8 bhi = pairs_to_f16x8(hi), blo = pairs_to_f16x8(lo);
+    const f16x8 zsub = pairs_to_f16x8(zs);
+    f16x8 av[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t x = t.k[u][J >> 1];
+      av[u] = uint2_operand((J & 1) ? ((x >> 2) & kFields02) : (x & kFields02)) + zsub;
+      acc[u] = mfma32(av[u], bhi, acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = mfma32(av[u], blo, acc[u]);
+  };
+  chunk(std::integral_constant<int, 0>{});
+  chunk(std::integral_constant<int, 1>{});
+  chunk(std::integral_constant<int, 2>{});
+  chunk(std::integral_constant<int, 3>{});
+  f32x4 pg[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] *= qk_scale;
+  softmax_update4(st, vb, acc, pg);
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {
+    const f32x4 &p0 = pg[2 * pr], &p1 = pg[2 * pr + 1];
+    const float *vsp = scl + 128 + 2 * (32 * pr + 4 * qd);
+    const f32x4 va0 = *reinterpret_cast<const f32x4 *>(vsp);        // tokens 0,1 of b0
+    const f32x4 va1 = *reinterpret_cast<const f32x4 *>(vsp + 4);    // tokens 2,3 of b0
+    const f32x4 vb0 = *reinterpret_cast<const f32x4 *>(vsp + 32);   // tokens 0,1 of b1
+    const f32x4 vb1 = *reinterpret_cast<const f32x4 *>(vsp + 36);   // tokens 2,3 of b1
+    const f32x4 g0a = {va0[0], va0[2], va1[0], va1[2]}, g1a = {va0[1], va0[3], va1[1], va1[3]};
+    const f32x4 g0b = {vb0[0], vb0[2], vb1[0], vb1[2]}, g1b = {vb0[1], vb0[3], vb1[1], vb1[3]};
+    const f16x8 pb0 = p_operand(p0 * g0a, p1 * g0b);
+    const f16x8 pb1 = p_operand(p0 * g1a, p1 * g1b);
+    // the value zero points of the slots' tokens, negated, per channel group
+    const float *zp = scl + 384 + 2 * (32 * pr + 4 * qd);
+    const f32x4 za0 = *reinterpret_cast<const f32x4 *>(zp);
+    const f32x4 za1 = *reinterpret_cast<const f32x4 *>(zp + 4);
+    const f32x4 zb0 = *reinterpret_cast<const f32x4 *>(zp + 32);
+    const f32x4 zb1 = *reinterpret_cast<const f32x4 *>(zp + 36);
+    const f16x8 nz0 = {(f16)-za0[0], (f16)-za0[2], (f16)-za1[0], (f16)-za1[2],
+                       (f16)-zb0[0], (f16)-zb0[2], (f16)-zb1[0], (f16)-zb1[2]};
+    const f16x8 nz1 = {(f16)-za0[1], (f16)-za0[3], (f16)-za1[1], (f16)-za1[3],
+                       (f16)-zb0[1], (f16)-zb0[3], (f16)-zb1[1], (f16)-zb1[3]};
+    uint32_t y[2][2][2];  // [block of the pair][dword][field parity]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t x = t.v[2 * pr + u][w];
+        y[u][w][0] = x & kFields02;
+        y[u][w][1] = (x >> 2) & kFields02;
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = j & 3, w = jj >> 1, hf = j >> 2;
+      const f16x8 av = (jj & 1) ? cat(uint2_bytes<2>(y[0][w][hf]), uint2_bytes<2>(y[1][w][hf]))
+                                : cat(uint2_bytes<0>(y[0][w][hf]), uint2_bytes<0>(y[1][w][hf]));
+      st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
+    }
+    vb[0] = mfma32(nz0, pb0, vb[0]);
+    vb[1] = mfma32(nz1, pb1, vb[1]);
+  }
+}
+
+// DT: kInt4, kInt4Affine or kInt2Affine on the generic layout
+template <int DT>
 __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b, int h,
                             int p, int seq_len, int wave, int lane, int tid, u32x4 qrow,
                             int pre_id) {
+  constexpr bool AFF = DT != kInt4;
   const int n = lane & 15, qd = lane >> 4;
   // the group's queries (fp16, zero rows past the group) stay in LDS and are
   // re-read per channel chunk, which keeps them out of the register budget
@@ -940,20 +1127,30 @@ __device__ void stream_int4(Softmax &st, const DecodeArgs &a, SharedLds &sh, int
     stage_ids(sh, bt, c0, c1, tid, pre_id, c0 == blk0);
     const int ngroups = (c1 - c0) / 4;
     const int cnt = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    auto load = [&](Group4 &t, int k) {
+    using Unit = typename std::conditional<DT == kInt2Affine, Group2, Group4>::type;
+    auto load = [&](Unit &t, int k) {
       const int j0 = 4 * (wave + kWaves * k);
       const int ph[4] = {uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]),
                          uniform(sh.s.ids[j0 + 2]), uniform(sh.s.ids[j0 + 3])};
       // a per-lane LDS read: selecting among ph[] per lane would become a
       // private-array access, whose scratch load joins the in-order vmcnt
       // queue and makes every group wait for all loads in flight
-      load_group4<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + ((lane & 15) >> 2)],
-                       h, lane);
+      if constexpr (DT == kInt2Affine) {
+        load_group2(t, a, ph, sh.s.ids[j0 + (lane >> 4)], sh.s.ids[j0 + ((lane & 15) >> 2)], h,
+                    lane);
+      } else {
+        load_group4<AFF>(t, a, ph, sh.s.ids[j0 + (lane >> 4)],
+                         sh.s.ids[j0 + ((lane & 15) >> 2)], h, lane);
+      }
     };
-    auto compute = [&](Group4 &t, int) {
-      compute_group4<AFF>(st, vb, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
+    auto compute = [&](Unit &t, int) {
+      if constexpr (DT == kInt2Affine) {
+        compute_group2(st, vb, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
+      } else {
+        compute_group4<AFF>(st, vb, t, &sh.s.q[0][0], scl, a.qk_scale, lane, n, qd);
+      }
     };
-    pipeline<Group4>(cnt, load, compute);
+    pipeline<Unit>(cnt, load, compute);
   }
   // the value bias of each channel group, once into its four tiles
 #pragma unroll
@@ -1127,14 +1324,11 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[4], con
 }
 
 // ---------------------------------------------------------------------------
-// 2-bit affine KIVI on the compact layout.  A code u in the low two bits
-// of a nibble (00uu) is the OCP FP4 (E2M1) value u / 2 exactly, so a dword
-// masked with 0x33333333 (fields 0 and 2 of every byte), or shifted right by
-// 2 and masked (fields 1 and 3), becomes exact fp16 codes one byte -- two
-// codes -- per hardware FP4 conversion (scale 2).  Key codes: byte b of a
-// lane's dword w holds channels 16w + 4b + f at bits 2f, so the operand of
-// (w, field parity h) holds channels 16w + 4b + h and 16w + 4b + h + 2 in
-// slots 2b, 2b + 1.  Value codes are stored so that each byte holds two
+// 2-bit affine KIVI on the compact layout, codes converted as FP4 nibbles
+// (uint2_bytes above).  Key codes: byte b of a lane's dword w holds
+// channels 16w + 4b + f at bits 2f, so the operand of (w, field parity h)
+// holds channels 16w + 4b + h and 16w + 4b + h + 2 in slots 2b, 2b + 1.
+// Value codes are stored so that each byte holds two
 // consecutive tokens of two tiles (the layout in kvq.h): one conversion
 // gives a tile's two tokens, four give its operand of a block pair.
 // ---------------------------------------------------------------------------
@@ -1146,11 +1340,6 @@ struct Group2C {
   uint32_t zw;  // as Group4C
   __device__ explicit Group2C(int = 0) {}
 };
-
-__device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2,
-                            __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamPolicy));
-}
 
 // Channel (within its 32) of the first of lane l's two q' channels: operand
 // J = (l/4)%4, slot pair i = l%4 -> 16(J/2) + 4i + J%2; the second is + 2.
@@ -1180,20 +1369,6 @@ __device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, co
   const float *zrow = (n < 8 ? a.k_scales : a.v_scales) + ((size_t)pm * H + h) * kRow + 32;
   t.zw = reinterpret_cast<const uint32_t *>(zrow)[n & 7];
 }
-
-// Bytes B0 and B0 + 1 of a masked dword (two 2-bit codes in the low bits
-// of each nibble) as four exact fp16 codes: byte B0's low then high nibble,
-// then byte B0 + 1's.
-template <int B0>
-__device__ __forceinline__ f16x4 uint2_bytes(uint32_t y) {
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 2.0f, B0 + 1);
-  return f16x4{a.x, a.y, b.x, b.y};
-}
-__device__ __forceinline__ f16x8 uint2_operand(uint32_t y) {
-  return cat(uint2_bytes<0>(y), uint2_bytes<2>(y));
-}
-constexpr uint32_t kFields02 = 0x33333333u;  // fields 0 and 2 of every byte
 
 // Key offset operand J: the zero points z of slots (2i, 2i+1) = channels
 // 16(J/2) + 4i + J%2 and + 2, exact (a byte z < 16 read as an E4M3 byte is
@@ -1759,7 +1934,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
       stream_int4c<DT>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
     } else {
-      stream_int4<DT == kInt4Affine>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
+      stream_int4<DT>(st, a, sh, b, h, p, seq_len, wave, lane, tid, qrow, pre_id);
       if (p == n_main - 1 && seq_len > nq) stream_ring(st, a, b, h, seq_len, wave, lane);
     }
   } else {
@@ -1863,7 +2038,6 @@ template <int DT, bool G4>
 __global__ __launch_bounds__(kThreads, decode_wg_per_cu(DT, kChannel, kToken)) void kvq_paged_decode_int4_kernel(
     DecodeArgs a) {
   static_assert(is_kivi(DT), "KIVI-grouped INT4 caches only");
-  static_assert(DT != kInt2Affine || G4, "2-bit codes: compact layout only");
   __shared__ SharedLds sh;
   decode_workgroup<DT, kChannel, kToken, G4>(a, sh);
 }
@@ -2007,8 +2181,11 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
   } else if (dtype == kInt4) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4, false>), grid, dim3(kThreads), 0,
                        stream, a);
-  } else if (dtype == kInt2Affine) {  // the host admits g <= 4, one query
+  } else if (dtype == kInt2Affine && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt2Affine, true>), grid, dim3(kThreads),
+                       0, stream, a);
+  } else if (dtype == kInt2Affine) {
+    hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt2Affine, false>), grid, dim3(kThreads),
                        0, stream, a);
   } else if (dtype == kInt4Affine && a.group <= 4 && a.n_query == 1) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, true>), grid, dim3(kThreads),

@@ -290,11 +290,15 @@ def test_int2_affine_rules():
     base = dict(dtype=7, k_gran=2, v_gran=3, residual_len=128, group_size=64)
     assert kvq.validate(_layout(**base), _cache(int4=True), 2, 100) == OK         # g = 4
     assert kvq.validate(_layout(**{**base, "num_q_heads": 16}), _cache(int4=True), 2,
-                        100) == UNS                                              # g = 8
+                        100) == OK                                               # g = 8
+    assert kvq.validate(_layout(**{**base, "num_q_heads": 64}), _cache(int4=True), 2,
+                        100) == UNS                                              # g = 32
     assert kvq.validate(_layout(**{**base, "k_gran": 3}), _cache(int4=True), 2, 100) == UNS
     assert kvq.validate(_layout(**base), _cache(int4=False), 2, 100) == INV
-    assert _decode_mq(_layout(**base), _cache(int4=True), nq=2) == UNS
-    assert kvq.paged_decode_mq_workspace_bytes(_layout(**base), 2, 2, 1000) == 0
+    assert _decode_mq(_layout(**base), _cache(int4=True), nq=2, batch=0) == OK
+    assert _decode_mq(_layout(**base), _cache(int4=True), nq=5) == UNS         # 20 columns
+    assert kvq.paged_decode_mq_workspace_bytes(_layout(**base, split_tokens=64), 2, 2,
+                                               1000) > 0
     assert _calibrate(_layout(**base)) == UNS
 
 

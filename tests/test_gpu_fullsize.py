@@ -86,3 +86,13 @@ def test_fullsize_int4_query_groups(hq):
     w = inputs.scaled_down(W["kivi-int4"], name=f"kivi-int4-g{hq // 8}", num_q_heads=hq,
                            batch=4)
     _run_layers(w, inputs.seq_lens(w), fused=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("hq", [32, 64, 128])
+def test_fullsize_int2_query_groups(hq):
+    """2-bit affine groups at the KIVI shape (32768 tokens, 8 KV heads) with
+    query groups 4 (compact layout), 8 and 16 (generic layout)."""
+    w = inputs.scaled_down(W["kivi-int2-affine"], name=f"kivi-int2-g{hq // 8}",
+                           num_q_heads=hq, batch=4)
+    _run_layers(w, inputs.seq_lens(w), fused=True)

@@ -24,7 +24,7 @@ def _w(dtype, kg, vg, hq, hkv, table="shuffled"):
 
 FORMATS = [("int8", "token", "token"), ("fp8", "head", "head"), ("fp16", "none", "none"),
            ("fp8e5m2", "channel", "token"), ("int4", "channel", "token"),
-           ("int4-affine", "channel", "token")]
+           ("int4-affine", "channel", "token"), ("int2-affine", "channel", "token")]
 
 
 @pytest.mark.parametrize("dtype,kg,vg", FORMATS)

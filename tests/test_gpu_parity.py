@@ -188,7 +188,8 @@ def test_int4_affine_residual_64_and_constant_groups():
     check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))
 
 
-# --- 2-bit affine KIVI groups (query groups of at most four)
+# --- 2-bit affine KIVI groups (compact path for query groups of at most
+# four, generic path above)
 
 def _two_bit(**kw):
     kw.setdefault("channel_outliers", (8, 10.0, "k"))
@@ -207,9 +208,14 @@ def test_int2_affine(lens, split):
     assert np.array_equal(res.out, res.out2)
 
 
-@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (4, 1)])
-def test_int2_affine_group_sizes(hq, hkv):
-    check_rows(run_case(_two_bit(hq=hq, hkv=hkv), [300, 700, 192], split_tokens=128))
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (4, 1), (16, 2), (32, 2), (12, 3),
+                                    (64, 8), (16, 1)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_int2_affine_group_sizes(hq, hkv, fused):
+    res = run_case(_two_bit(hq=hq, hkv=hkv, table="shuffled"), [300, 700, 192, 65],
+                   split_tokens=128, fused=fused, decode_twice=True)
+    check_rows(res)
+    assert np.array_equal(res.out, res.out2)
 
 
 @pytest.mark.parametrize("chunks", [3, 7])
