@@ -266,6 +266,58 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(128, 256, 512, 1024, 2
                       "flight per wavefront"}
 
 
+def write_probe(read_bytes: int, reps: int = 5, grids=(256, 512, 1024, 2048, 4096),
+                threads: int = 256):
+    """The read-and-write probe of libkvq_probe.so: read ``read_bytes`` (a
+    power of two) in 1 KiB chunks and write half as many bytes in 512-byte
+    runs, the bulk write's 2 : 1 mix of fp16 in and one-byte codes out, at
+    several grid sizes, each launch on fresh source and destination slices.
+    Returns the best rate over the bytes read plus written (GB/s)."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build it with "
+                         "`python -m quantized_paged_kv_02_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.kvq_probe_rw.restype = ctypes.c_int
+    lib.kvq_probe_rw.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    slices = max(2, (2 << 30) // read_bytes)
+    src = torch.empty(read_bytes * slices, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(read_bytes // 2 * slices, dtype=torch.uint8, device="cuda")
+    src.fill_(0x3C)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def launch(wgs, i):
+        rc = lib.kvq_probe_rw(src.data_ptr() + (i % slices) * read_bytes, read_bytes,
+                              dst.data_ptr() + (i % slices) * (read_bytes // 2), wgs, threads,
+                              stream.cuda_stream)
+        if rc != 0:
+            raise SystemExit(f"kvq_probe_rw failed ({rc})")
+
+    rows = []
+    for wgs in grids:
+        launch(wgs, reps - 1)
+        e0.record()
+        for i in range(reps):
+            launch(wgs, i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        moved = read_bytes + read_bytes // 2
+        rows.append({"workgroups": wgs, "threads": threads, "us": round(ms * 1e3, 1),
+                     "GBps": round(moved / (ms * 1e-3) / 1e9, 1)})
+    del src, dst
+    best = max(rows, key=lambda r: r["GBps"])
+    return {"GBps": best["GBps"], "frac_of_peak": round(best["GBps"] / HBM_PEAK_GBS, 4),
+            "bytes_read": read_bytes, "bytes_written": read_bytes // 2, "best": best,
+            "all": rows,
+            "kernel": "kvq_probe_rw_kernel (libkvq_probe.so): 16-byte loads, 8-byte "
+                      "stores, 8 chunks in flight per wavefront"}
+
+
 def launch_floor(layer_bytes: int):
     """The loads-only probe at the size of one decode launch (the largest
     power of two not above its bytes, fresh data each launch): how long a

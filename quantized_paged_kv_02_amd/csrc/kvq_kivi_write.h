@@ -98,7 +98,22 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
 
   const size_t ring_row = (size_t)b * H + h;
   const uint16_t *fresh = is_v ? a.v_new : a.k_new;
-  if (!is_v) {
+  if (t0 >= s_old) {
+    // every token of the group is new (a prefill write): K and V alike in
+    // 16-byte units (token, 8 channels), all four loads of a thread first
+    u32x4 g[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + 256 * k;
+      g[k] = ld16(fresh + ((size_t)(c_begin + t0 + (e >> 4) - s_old) * H + h) * kHeadDim +
+                  (e & 15) * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + 256 * k;
+      *reinterpret_cast<u32x4 *>(&x[e >> 4][(e & 15) * 8]) = g[k];
+    }
+  } else if (!is_v) {
     // K: 16-byte units (token, 8 channels); ring rows are contiguous
     for (int e = tid; e < kGroup * 16; e += 256) {
       const int tt = e >> 4, c8 = (e & 15) * 8;

@@ -15,7 +15,7 @@
 
 namespace kvq {
 
-constexpr int kPerTensor = 0, kPerHead = 1, kPerToken = 3;
+constexpr int kPerTensor = 0, kPerHead = 1, kPerChannel = 2, kPerToken = 3;
 
 // Byte offset of (slot s, channel c) inside an INT8/FP8 (block, head) chunk.
 __device__ __forceinline__ int k8_offset(int s, int c) {

@@ -58,77 +58,114 @@ __global__ __launch_bounds__(64) void kvq_write_q8_kernel(WriteArgs a) {
 }
 
 // Codes of 8 values under their scales (the rule of quantize_pair: round
-// half to even of the IEEE quotient x / s; FP8 clamped to the format's range
-// then converted by the hardware, round to nearest even), byte i = value i.
-// INT8 takes the product x * r, r = 1 / s correctly rounded, clamped to
-// +-129: for |x / s| <= 129 it lies within 129 * 2^-23 < 2^-16 of the
-// quotient, whose own rounding is at most 2^-17, so both round to the same
-// integer unless the product is within 2^-15 of a half-integer (beyond
-// +-129 both clamp alike); a wavefront with such a value, or with a scale
-// whose reciprocal is not finite, divides instead.  A zero scale gives
-// r = 0 and code 0, as the division rule does.
+// half to even of the IEEE quotient x / s, INT8 clamped to [-128, 127]; FP8
+// clamped to the format's range then converted by the hardware, round to
+// nearest even), byte i = value i, from r = 1 / s (correctly rounded; 0 for
+// a zero scale) instead of a division per value.  The product p = x * r is
+// within 2^-23 |x / s| of the quotient, whose own rounding is at most
+// 2^-24 |x / s|.
+// INT8: p clamped to [-128, 127] and rounded half to even by adding
+// M = 1.5 * 2^23 (the integer lands in the low mantissa bits, whose byte is
+// the two's-complement code).  For |x / s| <= 129 the two quotients differ
+// by less than 2^-16, so they round alike unless p lies within 2^-14 of a
+// half-integer; beyond that range both clamp to the same end code.
+// FP8: the codes of p (1 - 2^-20) and p (1 + 2^-20), clamped, bracket both
+// quotients, and rounding is monotonic: when the two codes agree, both
+// quotients take that code.
+// A wavefront with a value outside these windows, or with a scale whose
+// reciprocal is not finite (FP8: or zero), divides instead.
 template <int DT>
-__device__ __forceinline__ u32x2 quantize8(const float (&x)[8], const float (&s)[8]) {
+__device__ __forceinline__ u32x2 quantize8(const float (&x)[8], const float (&s)[8],
+                                           const float (&r)[8]) {
   u32x2 w;
+  bool near = false;
   if constexpr (DT == kInt8) {
-    float q[8];
-    bool near = false;
+    constexpr float M = 12582912.0f;  // 1.5 * 2^23
+    float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float r = s[i] != 0.0f ? 1.0f / s[i] : 0.0f;
-      const float p = fminf(fmaxf(x[i] * r, -129.0f), 129.0f);
-      q[i] = rintf(p);
-      near |= !(fabsf(p - q[i]) < 0.5f - 0x1p-14f) || !(fabsf(r) < 0x1p127f);
+      const float p = fminf(fmaxf(x[i] * r[i], -128.0f), 127.0f);
+      t[i] = p + M;
+      near |= !(fabsf(p - (t[i] - M)) < 0.5f - 0x1p-14f) || !(fabsf(r[i]) < 0x1p127f);
     }
     if (__any(near)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = s[i] != 0.0f ? rintf(x[i] / s[i]) : 0.0f;
+      for (int i = 0; i < 8; ++i)
+        t[i] = (s[i] != 0.0f ? fminf(fmaxf(rintf(x[i] / s[i]), -128.0f), 127.0f) : 0.0f) + M;
     }
 #pragma unroll
     for (int hw = 0; hw < 2; ++hw) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        word |= ((uint32_t)(int)fminf(fmaxf(q[4 * hw + e], -128.0f), 127.0f) & 0xFFu) << (8 * e);
-      w[hw] = word;
+      const uint32_t *b = reinterpret_cast<const uint32_t *>(t + 4 * hw);
+      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // bytes n0, n1
+      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);  // bytes n2, n3
+      w[hw] = lo | hi;
     }
   } else {
-#pragma unroll
-    for (int hw = 0; hw < 2; ++hw) {
-      const int i = 4 * hw;
-      constexpr float top = code_top<DT>();
-      const float y0 = fp8_prescale(x[i], s[i], top), y1 = fp8_prescale(x[i + 1], s[i + 1], top);
-      const float y2 = fp8_prescale(x[i + 2], s[i + 2], top);
-      const float y3 = fp8_prescale(x[i + 3], s[i + 3], top);
+    constexpr float top = code_top<DT>();
+    auto clamp = [](float v) { return fminf(fmaxf(v, -top), top); };
+    auto cvt4 = [](const float (&v)[4]) {
       int pk;
       if constexpr (DT == kFp8) {
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
       } else {
-        pk = __builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
-        pk = __builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, pk, true);
+        pk = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], pk, true);
       }
-      w[hw] = (uint32_t)pk;
+      return (uint32_t)pk;
+    };
+#pragma unroll
+    for (int hw = 0; hw < 2; ++hw) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * hw + e;
+        const float p = x[i] * r[i];
+        lo[e] = clamp(p * (1.0f - 0x1p-20f));
+        hi[e] = clamp(p * (1.0f + 0x1p-20f));
+        // a zero scale codes +0, which -0 * 0 would not give
+        near |= !(fabsf(r[i]) < 0x1p127f) || r[i] == 0.0f;
+      }
+      w[hw] = cvt4(lo);
+      near |= w[hw] != cvt4(hi);
+    }
+    if (__any(near)) {
+#pragma unroll
+      for (int hw = 0; hw < 2; ++hw) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fp8_prescale(x[4 * hw + e], s[4 * hw + e], top);
+        w[hw] = cvt4(y);
+      }
     }
   }
   return w;
 }
+
+// Maximum over the 16 lanes of a row (every lane gets it): quad swaps, then
+// rotations by 4 and 8 within the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(0.0f, v));  // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(0.0f, v));  // quad_perm [2, 3, 0, 1]
+  return bank_max(v);
+}
+
+// 1 / s, correctly rounded, and 0 for a zero scale
+__device__ __forceinline__ float recip_or_zero(float s) { return s != 0.0f ? 1.0f / s : 0.0f; }
 
 // INT8 / FP8 bulk write (prefill): one 256-thread workgroup per run of
 // kWriteBlocks 16-token blocks of a row and one KV head, for the blocks'
 // new tokens.  Thread t takes channels 8 (t % 16) .. + 7 of token slot
 // t / 16 of every block (one 16-byte load of K and one of V per block, all
 // issued first); a per-token scale is the maximum over the 16 threads of
-// the slot (shuffles within 16 lanes).  Block by block, the codes go to LDS
-// in the cache's byte order, then every thread stores one 16-byte unit of
-// the (block, head) chunk (threads 0..127 K, 128..255 V): a K unit is 16
+// the slot (DPP within the 16-lane row); static scales and their
+// reciprocals are taken once per workgroup.  Block by block, the codes go to
+// LDS in the cache's byte order, then every thread stores one 16-byte unit
+// of the (block, head) chunk (threads 0..127 K, 128..255 V): a K unit is 16
 // channels of one token, a V unit 4 channels of 4 tokens, stored whole when
 // all its tokens are new and byte by byte otherwise (the tokens already in
 // the block keep their codes).
-#ifndef KVQ_WRITE_BLOCKS
-#define KVQ_WRITE_BLOCKS 4
-#endif
-constexpr int kWriteBlocks = KVQ_WRITE_BLOCKS;
+constexpr int kWriteBlocks = 4;
 
 template <int DT>
 __global__ __launch_bounds__(256) void kvq_write_q8_block_kernel(WriteArgs a) {
@@ -162,6 +199,33 @@ __global__ __launch_bounds__(256) void kvq_write_q8_block_kernel(WriteArgs a) {
       }
     }
   }
+  // static scales of this thread's channels and their reciprocals (per
+  // token: set per block below)
+  float ss[2][8], sr[2][8];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const int gran = which ? a.v_gran : a.k_gran;
+    const float *scales = which ? a.v_scales : a.k_scales;
+    if (gran == kPerChannel) {
+      const f32x4 s0 = ld16f(scales + h * kHeadDim + 8 * k8);
+      const f32x4 s1 = ld16f(scales + h * kHeadDim + 8 * k8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss[which][e] = s0[e];
+        ss[which][4 + e] = s1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sr[which][e] = recip_or_zero(ss[which][e]);
+    } else {
+      const float st = gran == kPerToken ? 0.0f : scales[gran == kPerHead ? h : 0];
+      const float rt = recip_or_zero(st);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss[which][e] = st;
+        sr[which][e] = rt;
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kWriteBlocks; ++j) {
     const int lb = lb0 + j;
@@ -173,38 +237,28 @@ __global__ __launch_bounds__(256) void kvq_write_q8_block_kernel(WriteArgs a) {
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const u32x4 raw = which ? rv[j] : rk[j];
-      const int gran = which ? a.v_gran : a.k_gran;
-      const float *scales = which ? a.v_scales : a.k_scales;
-      float x[8], sc[8];
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[2 * e] = half_bits_to_float(raw[e] & 0xFFFFu);
         x[2 * e + 1] = half_bits_to_float(raw[e] >> 16);
       }
-      if (gran == kPerToken) {
+      u32x2 q;
+      if ((which ? a.v_gran : a.k_gran) == kPerToken) {
         float m = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+        m = row16_max(m);
         const float st = m / code_top<DT>();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = st;
-        if (live && k8 == 0) const_cast<float *>(scales)[chunk * kBlock + slot] = st;
-      } else if (gran == kPerTensor || gran == kPerHead) {
-        const float st = scales[gran == kPerHead ? h : 0];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = st;
+        const float rt = recip_or_zero(st);
+        const float sc[8] = {st, st, st, st, st, st, st, st};
+        const float rc[8] = {rt, rt, rt, rt, rt, rt, rt, rt};
+        q = quantize8<DT>(x, sc, rc);
+        if (live && k8 == 0)
+          (which ? a.v_scales : a.k_scales)[chunk * kBlock + slot] = st;
       } else {
-        const f32x4 s0 = ld16f(scales + h * kHeadDim + 8 * k8);
-        const f32x4 s1 = ld16f(scales + h * kHeadDim + 8 * k8 + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc[e] = s0[e];
-          sc[4 + e] = s1[e];
-        }
+        q = quantize8<DT>(x, ss[which], sr[which]);
       }
-      const u32x2 q = quantize8<DT>(x, sc);
       if (which == 0) {
         // K: channels 8 k8 .. + 7 of the slot are 8 consecutive bytes
         *reinterpret_cast<u32x2 *>(&codes[0][1024 * ((k8 >> 1) & 1) + 256 * (k8 >> 2) +
