@@ -72,10 +72,15 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
   __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
   __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
   __shared__ float partn[AFF ? 4 : 1][kHeadDim];  // K affine: channel minima
-  __shared__ float sc[kHeadDim];        // K: [128] channel scales; V: [64][2] token scales
-  __shared__ float rc[kHeadDim];        // 1 / sc
-  __shared__ float zs[AFF ? kHeadDim : 1];  // affine zero points, as sc
   __shared__ int phys_s[4];
+  // Scales, their reciprocals and (affine) kRoundAddend + zero points, K:
+  // [128] per channel, V: [64][2] per token and channel group.  They reuse
+  // part's rows: a K thread writes its channel's entries after reading that
+  // channel's partial maxima, and no other thread reads them before the
+  // next barrier (the smaller footprint keeps 7 affine workgroups per CU).
+  float *const sc = part[0];
+  float *const rc = part[1];
+  float *const zs = part[2];
 
   const int gs = bx >> 1;
   const bool is_v = (bx & 1) != 0;
@@ -167,26 +172,24 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
     // K scales: max over the group's 64 tokens of |K[:, c]| / 7 (affine: the
     // channel's minimum and maximum, each starting from 0)
     {
+      // maxima and minima of fp16 values are exact in packed fp16
       const int cp = tid & 63, qq = tid >> 6;
-      float m0 = 0.0f, m1 = 0.0f, n0 = 0.0f, n1 = 0.0f;
-#pragma unroll 4
+      f16x2 m = {(f16)0.0f, (f16)0.0f}, n = m;
+#pragma unroll
       for (int i = 0; i < 16; ++i) {
         const f16x2 v = *reinterpret_cast<const f16x2 *>(&x[16 * qq + i][2 * cp]);
         if constexpr (AFF) {
-          m0 = fmaxf(m0, (float)v.x);
-          m1 = fmaxf(m1, (float)v.y);
-          n0 = fminf(n0, (float)v.x);
-          n1 = fminf(n1, (float)v.y);
+          m = __builtin_elementwise_max(m, v);
+          n = __builtin_elementwise_min(n, v);
         } else {
-          m0 = fmaxf(m0, fabsf((float)v.x));
-          m1 = fmaxf(m1, fabsf((float)v.y));
+          m = __builtin_elementwise_max(m, __builtin_elementwise_abs(v));
         }
       }
-      part[qq][2 * cp] = m0;
-      part[qq][2 * cp + 1] = m1;
+      part[qq][2 * cp] = (float)m.x;
+      part[qq][2 * cp + 1] = (float)m.y;
       if constexpr (AFF) {
-        partn[qq][2 * cp] = n0;
-        partn[qq][2 * cp + 1] = n1;
+        partn[qq][2 * cp] = (float)n.x;
+        partn[qq][2 * cp + 1] = (float)n.y;
       }
     }
     __syncthreads();
@@ -199,7 +202,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
         const float2 sz = affine_params(mn, mx, kQmax);
         sc[tid] = sz.x;
         rc[tid] = recip(sz.x);
-        zs[tid] = sz.y;
+        zs[tid] = kRoundAddend + sz.y;
         row[tid & 31] = sz.x;
         reinterpret_cast<uint8_t *>(row + 32)[tid & 31] = (uint8_t)(int)sz.y;
       } else {
@@ -248,7 +251,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
           xv[e] = (float)v[e];
           sv[e] = sc[c];
           rv[e] = rc[c];
-          zv[e] = AFF ? zs[c] : 0.0f;
+          zv[e] = AFF ? zs[c] : kRoundAddend;
         }
         kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax, 0xFu);
         uint32_t word = 0;
@@ -263,20 +266,22 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
     // (affine: the half's minimum and maximum, each starting from 0)
     {
       const int tt = tid >> 2, qq = tid & 3;
-      float m = 0.0f, mn = 0.0f;
+      f16x2 m2 = {(f16)0.0f, (f16)0.0f}, n2 = m2;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const f16x8 v = *reinterpret_cast<const f16x8 *>(&x[tt][32 * qq + 8 * d]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 8; e += 2) {
+          const f16x2 w = {v[e], v[e + 1]};
           if constexpr (AFF) {
-            m = fmaxf(m, (float)v[e]);
-            mn = fminf(mn, (float)v[e]);
+            m2 = __builtin_elementwise_max(m2, w);
+            n2 = __builtin_elementwise_min(n2, w);
           } else {
-            m = fmaxf(m, fabsf((float)v[e]));
+            m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(w));
           }
         }
       }
+      float m = fmaxf((float)m2.x, (float)m2.y), mn = fminf((float)n2.x, (float)n2.y);
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       if constexpr (AFF) mn = fminf(mn, __shfl_xor(mn, 1, 64));
       if ((qq & 1) == 0) {
@@ -286,7 +291,7 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
           const float2 sz = affine_params(mn, m, kQmax);
           sc[2 * tt + (qq >> 1)] = sz.x;
           rc[2 * tt + (qq >> 1)] = recip(sz.x);
-          zs[2 * tt + (qq >> 1)] = sz.y;
+          zs[2 * tt + (qq >> 1)] = kRoundAddend + sz.y;
           row[k] = sz.x;
           // zero points group-transposed: token 16b + 4u + e of the group
           // goes to the row of the group's block u, byte 8b + 2e + g
@@ -339,7 +344,8 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
         const int tt = 16 * ub + 4 * quad + e;
         const float s0 = sc[2 * tt], s1 = sc[2 * tt + 1];
         const float r0 = rc[2 * tt], r1 = rc[2 * tt + 1];
-        const float z0 = AFF ? zs[2 * tt] : 0.0f, z1 = AFF ? zs[2 * tt + 1] : 0.0f;
+        const float z0 = AFF ? zs[2 * tt] : kRoundAddend;
+        const float z1 = AFF ? zs[2 * tt + 1] : kRoundAddend;
         float xv[8], sv[8], rv[8], zv[8];
         uint32_t qv[8];
 #pragma unroll

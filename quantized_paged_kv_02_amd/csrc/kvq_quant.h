@@ -39,40 +39,42 @@ __device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float 
 
 // KIVI group codes: round half to even of the IEEE fp32 quotient x / s, as
 // the oracle computes it, from r = 1 / s (correctly rounded) without a
-// division per value.  t = fma(x, r, M), M = 1.5 * 2^23, rounds the product
-// x * r to an integer n held in t's low mantissa bits (half to even: t's
-// unit in the last place is 1); rem = fma(x, r, -n) is the product's
-// distance to n.  For |x / s| <= 16 the product x * r is within
-// |x / s| 2^-23 <= 2^-19 of the quotient and the quotient's own rounding
-// is at most 2^-20, so the two round to the same integer unless the
-// product lies within 2^-18 of a half-integer; the test |rem| < 1/2 - 2^-17
-// leaves a margin for rem's own rounding.  If any lane of the wavefront
-// fails it (or is not finite), the wavefront divides instead.  Codes come
-// from t's bits: symmetric, the two's-complement low bits of n (a group's
-// own scale keeps |n| <= qmax); affine, n + z clamped to [0, qmax].  A zero
-// scale (r = 0) gives n = 0, and its group's z is 0.
+// division per value.  zm = M + z with M = 1.5 * 2^23 and z the affine zero
+// point (0 for symmetric codes; M + z is exact).  t = fma(x, r, zm) rounds
+// the product x * r to an integer n and adds it to zm, all in t's low
+// mantissa bits (half to even: t's unit in the last place is 1);
+// rem = fma(x, r, -n) is the product's distance to n.  For |x / s| <= 16
+// the product x * r is within |x / s| 2^-23 <= 2^-19 of the quotient and
+// the quotient's own rounding is at most 2^-20, so the two round to the same
+// integer unless the product lies within 2^-18 of a half-integer; the test
+// |rem| < 1/2 - 2^-17 leaves a margin for rem's own rounding.  If any lane
+// of the wavefront fails it (or is not finite), the wavefront divides
+// instead.  Codes come from t's bits: symmetric, the two's-complement low
+// bits of n (a group's own scale keeps |n| <= qmax); affine, n + z clamped
+// to [0, qmax].  A zero scale (r = 0) gives n = 0, and its group's z is 0.
+constexpr float kRoundAddend = 12582912.0f;  // 1.5 * 2^23
 template <int N, bool AFF>
 __device__ __forceinline__ void kivi_codes(uint32_t (&code)[N], const float (&x)[N],
                                            const float (&s)[N], const float (&r)[N],
-                                           const float (&z)[N], float qmax, uint32_t mask) {
-  constexpr float M = 12582912.0f;  // 1.5 * 2^23
+                                           const float (&zm)[N], float qmax, uint32_t mask) {
+  constexpr float M = kRoundAddend;
   float t[N];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    t[i] = __builtin_fmaf(x[i], r[i], M);
-    const float n = t[i] - M;
+    t[i] = __builtin_fmaf(x[i], r[i], zm[i]);
+    const float n = t[i] - zm[i];
     const float rem = __builtin_fmaf(x[i], r[i], -n);
     near |= !(fabsf(rem) < 0.5f - 0x1p-17f);
   }
   if (__any(near)) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) t[i] = (s[i] != 0.0f ? rintf(x[i] / s[i]) : 0.0f) + M;
+    for (int i = 0; i < N; ++i) t[i] = (s[i] != 0.0f ? rintf(x[i] / s[i]) : 0.0f) + zm[i];
   }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     float v = t[i];
-    if constexpr (AFF) v = fminf(fmaxf(v + z[i], M), M + qmax);
+    if constexpr (AFF) v = fminf(fmaxf(v, M), M + qmax);
     code[i] = __builtin_bit_cast(uint32_t, v) & mask;
   }
 }
