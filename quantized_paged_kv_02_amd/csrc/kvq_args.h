@@ -25,7 +25,9 @@ enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
 // dtype and K / V scale kinds: the kernel's register bound and the partition
 // plan's round size.  INT4, FP16 (twice the bytes in flight per unit) and
 // FP8 (E4M3 or E5M2) with per-token V and non-uniform K scales need the
-// larger per-wave register budget of two per CU.
+// larger per-wave register budget of two per CU.  (The compact 2-bit kernel
+// fits three per CU in registers and LDS, but on the KIVI shape six
+// partitions per row at three per CU ran 3 % slower than four at two.)
 constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
   return (is_kivi(dtype) || dtype == kFp16) ? 2
          : ((dtype == kFp8 || dtype == kFp8E5M2) && v_kind == kToken && k_kind != kUniform) ? 2

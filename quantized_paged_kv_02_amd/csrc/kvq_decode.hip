@@ -106,9 +106,10 @@ struct MergeLds {
   float l[kWaves][16];
   float o[kWaves][16][kMergeRow];
 };
-union SharedLds {
+union alignas(16) SharedLds {
   StreamLds s;
   MergeLds g;
+  FlushLds<true> f;  // a KIVI step's flush workgroups (FlushLds<false> is smaller)
 };
 
 __device__ __forceinline__ void softmax_init(Softmax &st) {
@@ -1852,7 +1853,8 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
       // a row longer than the launch covers (above the host's max_seq_len)
       // is left as it is, as its decode workgroups leave it
       if (fb < a.batch && a.seq_lens[fb] <= a.max_seq_len)
-        int4_flush<DT>(step_write_args(a), f & 1, r - fb * a.num_kv_heads, fb);
+        int4_flush<DT>(step_write_args(a), f & 1, r - fb * a.num_kv_heads, fb,
+                       *reinterpret_cast<FlushLds<DT != kInt4> *>(&sh.f));
       return;
     }
   }

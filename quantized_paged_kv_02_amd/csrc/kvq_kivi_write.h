@@ -48,6 +48,17 @@ __device__ __forceinline__ int kivi_len(int s, int residual) {
 // floats per (block, head), the last 32 bytes holding the zero points.
 constexpr int kFlushRow = kHeadDim + 8;  // padded LDS row (fp16)
 
+// A flush workgroup's LDS (AFF: affine, with the channel minima).  The
+// decode kernel's flush workgroups lay it over the LDS the decode
+// workgroups use for streaming and merging.
+template <bool AFF>
+struct alignas(16) FlushLds {
+  f16 x[kGroup][kFlushRow];
+  float part[4][kHeadDim];              // K: channel maxima of four 16-token slices
+  float partn[AFF ? 4 : 1][kHeadDim];   // K affine: channel minima
+  int phys[4];
+};
+
 // Affine parameters of a group with minimum lo <= 0 <= maximum hi, codes
 // 0 .. qmax.
 __device__ __forceinline__ float2 affine_params(float lo, float hi, float qmax) {
@@ -63,16 +74,17 @@ __device__ __forceinline__ float recip(float s) { return s > 0.0f ? 1.0f / s : 0
 // chunks, the code layouts of kvq.h).  bx = 2 x (the call's g-th group of
 // row b) + (0: K, 1: V); h: KV head.
 template <int DT>
-__device__ void int4_flush(const WriteArgs &a, int bx, int h, int b) {
+__device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
+                           FlushLds<DT != kInt4> &lds) {
   constexpr bool AFF = DT != kInt4;
   constexpr bool TWO = DT == kInt2Affine;
   constexpr float kQmax = TWO ? 3.0f : 15.0f;
   constexpr int kChunk = kivi_chunk_bytes(DT);
   constexpr int kRow = AFF ? 40 : 32;   // floats per (block, head) scale row
-  __shared__ __attribute__((aligned(16))) f16 x[kGroup][kFlushRow];
-  __shared__ float part[4][kHeadDim];   // K: channel maxima of four 16-token slices
-  __shared__ float partn[AFF ? 4 : 1][kHeadDim];  // K affine: channel minima
-  __shared__ int phys_s[4];
+  auto &x = lds.x;
+  auto &part = lds.part;
+  auto &partn = lds.partn;
+  int *const phys_s = lds.phys;
   // Scales, their reciprocals and (affine) kRoundAddend + zero points, K:
   // [128] per channel, V: [64][2] per token and channel group.  They reuse
   // part's rows: a K thread writes its channel's entries after reading that

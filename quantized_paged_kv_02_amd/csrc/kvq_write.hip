@@ -322,7 +322,8 @@ __global__ __launch_bounds__(64) void kvq_write_f16_kernel(WriteArgs a) {
 
 template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
-  int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ __attribute__((aligned(16))) FlushLds<DT != kInt4> lds;
+  int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Workgroup x appends the row's new token n_new - 1 - x: a row keeps at
@@ -342,8 +343,9 @@ __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
 // from the ring, so its ring slot is never one of them.
 template <int DT>
 __global__ __launch_bounds__(256) void kvq_int4_flush_append_kernel(WriteArgs a, int groups) {
+  __shared__ __attribute__((aligned(16))) FlushLds<DT != kInt4> lds;
   if ((int)blockIdx.x < 2 * groups) {
-    int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
   } else if (threadIdx.x < 64) {
     append_token(a, blockIdx.x - 2 * groups, blockIdx.y, blockIdx.z, threadIdx.x);
   }
