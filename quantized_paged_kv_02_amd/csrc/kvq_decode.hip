@@ -618,7 +618,8 @@ __device__ __forceinline__ f16x8 uint4x8_to_f16_koff(uint32_t x) {
 template <int K>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
   static_assert(K >= 0 && K < 16, "lane within a row");
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + K, 0xF, 0xF, false);
+  // every lane's source is valid: no old value to merge
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + K, 0xF, 0xF, true);
 }
 
 // Offset operand of the affine key conversion for the channels 8j..8j+7 of
@@ -1371,35 +1372,35 @@ __device__ __forceinline__ void load_group2c(Group2C &t, const DecodeArgs &a, co
   t.zw = reinterpret_cast<const uint32_t *>(zrow)[n & 7];
 }
 
+// The zero-point bytes of this lane's dword zw (see Group4C) as fp16 pairs,
+// exact (a byte z < 16 read as an E4M3 byte is z / 512): z[0] = bytes 0
+// and 2, z[1] = bytes 1 and 3.  K dwords (lanes n < 8) hold channels
+// 4n .. 4n+3; V dwords (lanes 8 + w) hold tokens 2(w%2), 2(w%2)+1 of block
+// w/2 for channel groups 0, 1 (the group-transposed rows).  Converted once
+// per group; the operands below are row broadcasts of them.
+__device__ __forceinline__ void zp2_pairs(uint32_t zw, uint32_t (&z)[2]) {
+  z[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+      __builtin_amdgcn_perm(zw, zw, 0x0C0C0200u), 512.0f, false));
+  z[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+      __builtin_amdgcn_perm(zw, zw, 0x0C0C0301u), 512.0f, false));
+}
+
 // Key offset operand J: the zero points z of slots (2i, 2i+1) = channels
-// 16(J/2) + 4i + J%2 and + 2, exact (a byte z < 16 read as an E4M3 byte is
-// z / 512); zero-point dword d holds channels 4d .. 4d+3 and comes by row
-// broadcast.
+// 16(J/2) + 4i + J%2 and + 2, i.e. pair J%2 of K dword 4(J/2) + i.
 template <int J>
-__device__ __forceinline__ f16x8 zp2_key_offsets(uint32_t zw) {
-  constexpr uint32_t sel = (J & 1) ? 0x0C0C0301u : 0x0C0C0200u;  // bytes J%2, J%2+2
-  const uint32_t d0 = row_bcast<4 * (J >> 1) + 0>(zw), d1 = row_bcast<4 * (J >> 1) + 1>(zw);
-  const uint32_t d2 = row_bcast<4 * (J >> 1) + 2>(zw), d3 = row_bcast<4 * (J >> 1) + 3>(zw);
-  const u32x4 r = {
-      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d0, d0, sel), 512.0f, false)),
-      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d1, d1, sel), 512.0f, false)),
-      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d2, d2, sel), 512.0f, false)),
-      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(d3, d3, sel), 512.0f, false))};
+__device__ __forceinline__ f16x8 zp2_key_offsets(const uint32_t (&z)[2]) {
+  const u32x4 r = {row_bcast<4 * (J >> 1) + 0>(z[J & 1]), row_bcast<4 * (J >> 1) + 1>(z[J & 1]),
+                   row_bcast<4 * (J >> 1) + 2>(z[J & 1]), row_bcast<4 * (J >> 1) + 3>(z[J & 1])};
   return u4_to_f16x8(r);
 }
 
 // Zero points (as fp16, exact) of the slots of block pair PR for channel
-// group G: tokens 0..3 of block 2PR, then of block 2PR+1.
+// group G: tokens 0..3 of block 2PR, then of block 2PR+1 (pair G of V
+// dwords 4PR .. 4PR+3).
 template <int PR, int G>
-__device__ __forceinline__ f16x8 zp2_value_points(uint32_t zw) {
-  constexpr uint32_t sel = G ? 0x0C0C0301u : 0x0C0C0200u;  // bytes g, 2 + g -> bytes 0, 1
-  u32x4 r;
-  const uint32_t w0 = row_bcast<8 + 4 * PR>(zw), w1 = row_bcast<9 + 4 * PR>(zw);
-  const uint32_t w2 = row_bcast<10 + 4 * PR>(zw), w3 = row_bcast<11 + 4 * PR>(zw);
-  r[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w0, w0, sel), 512.0f, false));
-  r[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w1, w1, sel), 512.0f, false));
-  r[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w2, w2, sel), 512.0f, false));
-  r[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w3, w3, sel), 512.0f, false));
+__device__ __forceinline__ f16x8 zp2_value_points(const uint32_t (&z)[2]) {
+  const u32x4 r = {row_bcast<8 + 4 * PR>(z[G]), row_bcast<9 + 4 * PR>(z[G]),
+                   row_bcast<10 + 4 * PR>(z[G]), row_bcast<11 + 4 * PR>(z[G])};
   return u4_to_f16x8(r);
 }
 
@@ -1409,7 +1410,8 @@ __device__ __forceinline__ f16x8 zp2_value_points(uint32_t zw) {
 // vb[2 + g] takes the weights times the zero points.
 template <int PR>
 __device__ __forceinline__ void value_pair2c(Softmax &st, f32x4 (&vb)[4], const Group2C &t,
-                                             const f16x8 &pb0, const f16x8 &pb1) {
+                                             const uint32_t (&z)[2], const f16x8 &pb0,
+                                             const f16x8 &pb1) {
   uint32_t y[2][2][2];  // [block of the pair][dword][field parity]
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -1426,8 +1428,8 @@ __device__ __forceinline__ void value_pair2c(Softmax &st, f32x4 (&vb)[4], const 
                               : cat(uint2_bytes<0>(y[0][w][hf]), uint2_bytes<0>(y[1][w][hf]));
     st.o[j] = mfma32(av, j < 4 ? pb0 : pb1, st.o[j]);
   }
-  vb[2] = mfma32(zp2_value_points<PR, 0>(t.zw), pb0, vb[2]);
-  vb[3] = mfma32(zp2_value_points<PR, 1>(t.zw), pb1, vb[3]);
+  vb[2] = mfma32(zp2_value_points<PR, 0>(z), pb0, vb[2]);
+  vb[3] = mfma32(zp2_value_points<PR, 1>(z), pb1, vb[3]);
 }
 
 __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], const Group2C &t,
@@ -1456,10 +1458,12 @@ __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], con
       acc[u] = mfma32(uint2_operand((x >> 2) & kFields02), bq[2 * w + 1], acc[u]);
     }
   }
-  ac = mfma32(zp2_key_offsets<0>(t.zw), bq[0], ac);
-  ac = mfma32(zp2_key_offsets<1>(t.zw), bq[1], ac);
-  ac = mfma32(zp2_key_offsets<2>(t.zw), bq[2], ac);
-  ac = mfma32(zp2_key_offsets<3>(t.zw), bq[3], ac);
+  uint32_t z[2];
+  zp2_pairs(t.zw, z);
+  ac = mfma32(zp2_key_offsets<0>(z), bq[0], ac);
+  ac = mfma32(zp2_key_offsets<1>(z), bq[1], ac);
+  ac = mfma32(zp2_key_offsets<2>(z), bq[2], ac);
+  ac = mfma32(zp2_key_offsets<3>(z), bq[3], ac);
   const float off = all_banks(ac[0]);
   f32x4 s = pack_scores(acc);
 #pragma unroll
@@ -1471,8 +1475,8 @@ __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], con
                           pack_rne(p[2] * t.vsb[0], p[3] * t.vsb[2])};
   const uint32_t d1[2] = {pack_rne(p[0] * t.vsa[1], p[1] * t.vsa[3]),
                           pack_rne(p[2] * t.vsb[1], p[3] * t.vsb[3])};
-  value_pair2c<0>(st, vb, t, p_operand_c<0>(d0), p_operand_c<0>(d1));
-  value_pair2c<1>(st, vb, t, p_operand_c<1>(d0), p_operand_c<1>(d1));
+  value_pair2c<0>(st, vb, t, z, p_operand_c<0>(d0), p_operand_c<0>(d1));
+  value_pair2c<1>(st, vb, t, z, p_operand_c<1>(d0), p_operand_c<1>(d1));
 }
 
 template <int DT> struct CompactUnit { using T = Group4C; };
