@@ -339,7 +339,7 @@ def launch_floor(layer_bytes: int):
 
 class Bench:
     def __init__(self, w: inputs.Workload, device="cuda", n_query: int = 0,
-                 partition: str = "auto"):
+                 partition: str = "auto", with_probe: bool = True):
         import torch
         from quantized_paged_kv_02_amd import kvq
         self.torch, self.kvq, self.w = torch, kvq, w
@@ -432,6 +432,16 @@ class Bench:
                     "tokens": int(n.sum()), "bytes": nbytes, "us": round(us, 2),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                if with_probe:
+                    # the read-and-write probe at the prefill's read size
+                    # (largest power of two): the achievable 2 : 1 rate
+                    rd = int(n.sum()) * w.num_kv_heads * 128 * 2 * 2
+                    p2 = 1 << (rd.bit_length() - 1)
+                    if (1 << 20) <= p2 <= (1 << 30):
+                        wp = write_probe(p2)
+                        self.prefill_write["write_probe_GBps"] = wp["GBps"]
+                        self.prefill_write["frac_of_write_probe"] = round(
+                            nbytes / (us * 1e-6) / 1e9 / wp["GBps"], 4)
             del kpre, vpre
             self.caches.append(cache)
             nq = max(n_query, 1)   # new tokens per row and step
@@ -514,7 +524,8 @@ def run(args):
         cpu = cpu_baseline(w, inputs.seq_lens(w), workers=args.cpu_workers)
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    bench = Bench(w, n_query=args.n_query, partition=args.partition)
+    bench = Bench(w, n_query=args.n_query, partition=args.partition,
+                  with_probe=not args.no_probe)
     b = w.batch
     L = w.layers
     layer_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, bench.lens,

@@ -609,8 +609,8 @@ __device__ __forceinline__ f16x8 uint4x8_to_f16_koff(uint32_t x) {
   const uint32_t lo = x & 0x0F0F0F0Fu;
   const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // nibbles 0, 2
   const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // nibbles 4, 6
-  const f16x2 b = as_f16x2((x & 0x00F000F0u) | 0x64006400u);                     // nibbles 1, 5
-  const f16x2 d = as_f16x2(((x >> 8) & 0x00F000F0u) | 0x64006400u);              // nibbles 3, 7
+  const f16x2 b = as_f16x2(and_or(x, 0x00F000F0u, 0x64006400u));               // nibbles 1, 5
+  const f16x2 d = as_f16x2(and_or(x >> 8, 0x00F000F0u, 0x64006400u));          // nibbles 3, 7
   return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
@@ -785,10 +785,10 @@ __device__ __forceinline__ f16x8 uint4x8_minus_zp(uint32_t x, const uint32_t (&s
   const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
   const uint32_t y = x >> 8;
   uint32_t r[4];
-  r[0] = as_u32(as_f16x2((x & 0x000F000Fu) | 0x64006400u) + as_f16x2(sub[0]));
-  r[1] = as_u32(as_f16x2((x & 0x00F000F0u) | 0x64006400u) * sixteenth + as_f16x2(sub[1]));
-  r[2] = as_u32(as_f16x2((y & 0x000F000Fu) | 0x64006400u) + as_f16x2(sub[2]));
-  r[3] = as_u32(as_f16x2((y & 0x00F000F0u) | 0x64006400u) * sixteenth + as_f16x2(sub[3]));
+  r[0] = as_u32(as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) + as_f16x2(sub[0]));
+  r[1] = as_u32(as_f16x2(and_or(x, 0x00F000F0u, 0x64006400u)) * sixteenth + as_f16x2(sub[1]));
+  r[2] = as_u32(as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) + as_f16x2(sub[2]));
+  r[3] = as_u32(as_f16x2(and_or(y, 0x00F000F0u, 0x64006400u)) * sixteenth + as_f16x2(sub[3]));
   return pairs_to_f16x8(r);
 }
 
@@ -797,8 +797,8 @@ __device__ __forceinline__ f16x8 uint4x8_minus_zp(uint32_t x, const uint32_t (&s
 // product, with the zero points.
 __device__ __forceinline__ f16x8 uint4x8_to_f16_biased(uint32_t x) {
   const uint32_t y = x >> 8;
-  const uint32_t r[4] = {(x & 0x000F000Fu) | 0x64006400u, (x & 0x00F000F0u) | 0x64006400u,
-                         (y & 0x000F000Fu) | 0x64006400u, (y & 0x00F000F0u) | 0x64006400u};
+  const uint32_t r[4] = {and_or(x, 0x000F000Fu, 0x64006400u), and_or(x, 0x00F000F0u, 0x64006400u),
+                         and_or(y, 0x000F000Fu, 0x64006400u), and_or(y, 0x00F000F0u, 0x64006400u)};
   return pairs_to_f16x8(r);
 }
 

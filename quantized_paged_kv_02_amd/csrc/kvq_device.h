@@ -65,6 +65,13 @@ __device__ __forceinline__ uint32_t bsel(uint32_t x, uint32_t m, uint32_t c) {
   return ((x ^ c) & m) | (c & ~m);
 }
 
+// (x & m) | c as one three-input bit operation (gfx950 v_bitop3_b32: bit i
+// of the table is the result for inputs (x, m, c) = bits 2, 1, 0 of i).
+// Written out, the compiler emits an AND and an OR with literal operands.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  return (uint32_t)__builtin_amdgcn_bitop3_b32(x, m, c, 0xEA);
+}
+
 __device__ __forceinline__ void int4x8_to_f16_pairs(uint32_t x, uint32_t out[4]) {
   const f16x2 sub = {(f16)-1032.0f, (f16)-1032.0f};
   const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
