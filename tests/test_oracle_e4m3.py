@@ -105,3 +105,30 @@ def test_quantize_e4m3_lossless_and_saturating():
     assert c2.tolist() == [0x7E, 0xFE, 0x7E]
     # zero scale gives +0 codes
     assert oracle.quantize_e4m3(np.zeros(4, np.float32), np.float32(0)).tolist() == [0] * 4
+
+
+def test_dequantize_fp8_branches():
+    """oracle.dequantize reads E4M3 / E5M2 codes through the format's own
+    values times the scale (fp64): fixed points of each format, per-row
+    scales broadcast, and a quantize / dequantize round trip within half a
+    unit in the last place of the format (E4M3 3 mantissa bits, E5M2 2)."""
+    codes = np.array([[0x38, 0x7E, 0x01, 0x80], [0xB8, 0xFE, 0x08, 0x00]], np.uint8)
+    s = np.array([[2.0], [0.5]])
+    got = oracle.dequantize(codes, s, "fp8")
+    want = np.array([[2.0, 896.0, 2.0 ** -8, 0.0], [-0.5, -224.0, 2.0 ** -7, 0.0]])
+    assert np.array_equal(got, want) and np.signbit(got[0, 3])
+    codes5 = np.array([[0x3C, 0x7B, 0x01, 0xBC]], np.uint8)
+    got5 = oracle.dequantize(codes5, np.array([[4.0]]), "fp8e5m2")
+    assert np.array_equal(got5, [[4.0, 4 * 57344.0, 4 * 2.0 ** -16, -4.0]])
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 128)).astype(np.float16)
+    for dtype, mant in (("fp8", 3), ("fp8e5m2", 2)):
+        q, sc = oracle.quantize_per_token(x, dtype)
+        xh = oracle.dequantize(q, sc[:, None], dtype)
+        xs = x.astype(np.float64) / sc[:, None].astype(np.float64)
+        # normal range: relative half-ulp; near zero: half the smallest step;
+        # plus the fp32 rounding of the quotient (relative 2^-24)
+        tiny = 2.0 ** (-9 if dtype == "fp8" else -16)
+        bound = np.maximum(np.abs(xs) * 2.0 ** -(mant + 1), tiny / 2) * sc[:, None]
+        bound += np.abs(x.astype(np.float64)) * 2.0 ** -23
+        assert np.all(np.abs(xh - x.astype(np.float64)) <= bound)
