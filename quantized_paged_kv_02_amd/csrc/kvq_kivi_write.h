@@ -243,11 +243,14 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
           rv[e] = rc[c];
           zv[e] = zs[c];
         }
-        kivi_codes<16, true>(qv, xv, sv, rv, zv, kQmax, 3u);
-        uint32_t word = 0;
+        kivi_codes<16, true>(qv, xv, sv, rv, zv, kQmax);
+        // byte k of a_f: the code of channel 4k + f (affine codes fill
+        // their bytes' low bits exactly)
+        uint32_t af[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) word |= qv[e] << (2 * e);
-        out[d] = word;
+        for (int f = 0; f < 4; ++f)
+          af[f] = byte_pair<0>(qv[f], qv[4 + f]) | byte_pair<2>(qv[8 + f], qv[12 + f]);
+        out[d] = af[0] | (af[1] << 2) | (af[2] << 4) | (af[3] << 6);
       }
       *reinterpret_cast<u32x2 *>(chunk + 128 * cb + 8 * (tt & 15)) = out;
     } else {
@@ -265,11 +268,11 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
           rv[e] = rc[c];
           zv[e] = AFF ? zs[c] : kRoundAddend;
         }
-        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax, 0xFu);
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) word |= qv[e] << (4 * e);
-        out[d] = word;
+        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax);
+        // byte k: channel 2k in the low nibble, 2k + 1 in the high one
+        const uint32_t lo = byte_pair<0>(qv[0], qv[2]) | byte_pair<2>(qv[4], qv[6]);
+        const uint32_t hi = byte_pair<0>(qv[1], qv[3]) | byte_pair<2>(qv[5], qv[7]);
+        out[d] = AFF ? lo | (hi << 4) : nibbles_of(lo, hi);
       }
       *reinterpret_cast<u32x4 *>(chunk + 256 * cb + 16 * (tt & 15)) = out;
     }
@@ -328,8 +331,9 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
     uint8_t *chunk = a.v_codes + ((size_t)phys_s[ub] * H + h) * kChunk;
     if constexpr (TWO) {
       // 2-bit: tile j, token e at dword (j % 4) / 2, byte 2 (j % 2) + e / 2,
-      // bits 2 (j / 4) + 4 (e % 2)
-      u32x2 out = {0u, 0u};
+      // bits 2 (j / 4) + 4 (e % 2).  pf[w][g][h]: the codes of dword w with
+      // j / 4 = g and e % 2 = h, each in the low bits of its byte
+      uint32_t pf[2][2][2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
@@ -343,14 +347,30 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
           rv[j] = rc[2 * tt + g];
           zv[j] = zs[2 * tt + g];
         }
-        kivi_codes<8, true>(qv, xv, sv, rv, zv, kQmax, 3u);
+        kivi_codes<8, true>(qv, xv, sv, rv, zv, kQmax);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          out[(j & 3) >> 1] |= qv[j] << (8 * (2 * (j & 1) + (e >> 1)) + 2 * (j >> 2) + 4 * (e & 1));
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            // tiles 4g + 2w (bytes e / 2) and 4g + 2w + 1 (bytes 2 + e / 2)
+            const uint32_t v = (e >> 1) ? byte_spread<1>(qv[4 * g + 2 * w], qv[4 * g + 2 * w + 1])
+                                        : byte_spread<0>(qv[4 * g + 2 * w], qv[4 * g + 2 * w + 1]);
+            if (e < 2) {
+              pf[w][g][e & 1] = v;
+            } else {
+              pf[w][g][e & 1] |= v;
+            }
+          }
       }
+      u32x2 out;
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+        out[w] = pf[w][0][0] | (pf[w][1][0] << 2) | (pf[w][0][1] << 4) | (pf[w][1][1] << 6);
       *reinterpret_cast<u32x2 *>(chunk + 8 * u) = out;
     } else {
-      u32x4 out = {0u, 0u, 0u, 0u};
+      // dword w (tiles 2w, 2w + 1): byte k low nibble = tile 2w + k % 2 of
+      // token k / 2, high nibble = the same tile of token 2 + k / 2
+      uint32_t lo[4], hi[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tt = 16 * ub + 4 * quad + e;
@@ -367,13 +387,22 @@ __device__ void int4_flush(const WriteArgs &a, int bx, int h, int b,
           rv[j] = j < 4 ? r0 : r1;
           zv[j] = j < 4 ? z0 : z1;
         }
-        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax, 0xFu);
+        kivi_codes<8, AFF>(qv, xv, sv, rv, zv, kQmax);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = 2 * (j & 1) + (e >> 1) + 4 * (e & 1);
-          out[j >> 1] |= qv[j] << (4 * p);
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = (e & 1) ? byte_pair<2>(qv[2 * w], qv[2 * w + 1])
+                                     : byte_pair<0>(qv[2 * w], qv[2 * w + 1]);
+          uint32_t &dst = (e >> 1) ? hi[w] : lo[w];
+          if (e & 1) {
+            dst |= v;
+          } else {
+            dst = v;
+          }
         }
       }
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) out[w] = AFF ? lo[w] | (hi[w] << 4) : nibbles_of(lo[w], hi[w]);
       *reinterpret_cast<u32x4 *>(chunk + 16 * u) = out;
     }
   }

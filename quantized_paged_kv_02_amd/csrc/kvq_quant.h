@@ -49,14 +49,15 @@ __device__ __forceinline__ uint32_t quant_int(float x, float s, float lo, float 
 // integer unless the product lies within 2^-18 of a half-integer; the test
 // |rem| < 1/2 - 2^-17 leaves a margin for rem's own rounding.  If any lane
 // of the wavefront fails it (or is not finite), the wavefront divides
-// instead.  Codes come from t's bits: symmetric, the two's-complement low
-// bits of n (a group's own scale keeps |n| <= qmax); affine, n + z clamped
-// to [0, qmax].  A zero scale (r = 0) gives n = 0, and its group's z is 0.
+// instead.  The codes are the low bits of t's bits (returned as `bits`):
+// symmetric, the two's-complement low bits of n (a group's own scale keeps
+// |n| <= qmax); affine, n + z clamped to [0, qmax], so the low byte is the
+// code itself.  A zero scale (r = 0) gives n = 0, and its group's z is 0.
 constexpr float kRoundAddend = 12582912.0f;  // 1.5 * 2^23
 template <int N, bool AFF>
-__device__ __forceinline__ void kivi_codes(uint32_t (&code)[N], const float (&x)[N],
+__device__ __forceinline__ void kivi_codes(uint32_t (&bits)[N], const float (&x)[N],
                                            const float (&s)[N], const float (&r)[N],
-                                           const float (&zm)[N], float qmax, uint32_t mask) {
+                                           const float (&zm)[N], float qmax) {
   constexpr float M = kRoundAddend;
   float t[N];
   bool near = false;
@@ -75,8 +76,31 @@ __device__ __forceinline__ void kivi_codes(uint32_t (&code)[N], const float (&x)
   for (int i = 0; i < N; ++i) {
     float v = t[i];
     if constexpr (AFF) v = fminf(fmaxf(v, M), M + qmax);
-    code[i] = __builtin_bit_cast(uint32_t, v) & mask;
+    bits[i] = __builtin_bit_cast(uint32_t, v);
   }
+}
+
+// Byte gathers for packing codes (byte_pair<B>: the low bytes of a and b as
+// bytes B and B + 1 of the result, zeros elsewhere; byte_spread<B>: as
+// bytes B and B + 2).
+template <int B>
+__device__ __forceinline__ uint32_t byte_pair(uint32_t a, uint32_t b) {
+  constexpr uint32_t z = 0x0C0C0C0Cu;  // selector 0x0C: a zero byte
+  constexpr uint32_t sel = (z & ~(0xFFFFu << (8 * B))) | (0x0400u << (8 * B));
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+template <int B>
+__device__ __forceinline__ uint32_t byte_spread(uint32_t a, uint32_t b) {
+  constexpr uint32_t z = 0x0C0C0C0Cu;
+  constexpr uint32_t sel = (z & ~((0xFFu << (8 * B)) | (0xFFu << (8 * B + 16)))) |
+                           (0x00u << (8 * B)) | (0x04u << (8 * B + 16));
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+// Eight 4-bit codes (low nibbles of the bytes of lo, low nibbles of the
+// bytes of hi; other bits ignored) as one dword: byte k = lo's byte k in
+// its low nibble, hi's byte k in its high nibble.
+__device__ __forceinline__ uint32_t nibbles_of(uint32_t lo, uint32_t hi) {
+  return (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u);
 }
 
 // x / s clamped to the format's finite range (448 E4M3, 57344 E5M2).

@@ -70,7 +70,8 @@ def decode_times(rows):
     dec = [i for i, r in enumerate(rows) if "paged_decode" in r["Kernel_Name"]]
     if not dec:
         return None
-    grid = min(int(rows[i]["Grid_Size_X"]) for i in dec)
+    grid = min(int(rows[i]["Grid_Size_X"]) for i in dec)   # work-items
+    wg_size = int(rows[dec[0]].get("Workgroup_Size_X") or 0)
     d_us, m_us, span = [], [], []
     for i in dec:
         r = rows[i]
@@ -90,7 +91,8 @@ def decode_times(rows):
            "merge_median_us": round(statistics.median(m_us), 3) if m_us else 0.0,
            "launch_span_us": round(statistics.mean(span), 3),
            "launch_span_median_us": round(statistics.median(span), 3),
-           "dispatches": len(d_us), "decode_grid": grid}
+           "dispatches": len(d_us), "decode_grid": grid,
+           "decode_workgroups": grid // wg_size if wg_size else None}
     return out
 
 
@@ -114,7 +116,8 @@ def stats(directory: str, command: str, out: str, workload: str | None = None,
                      f"{sum(v) / 1000:.3f} |")
     if dt is not None:
         lines += ["", "Decode launches as bench.py's roofline times them (kvq_paged_decode "
-                  f"dispatches, grid {dt['decode_grid']} workgroups, {dt['dispatches']} of "
+                  f"dispatches, grid {dt['decode_grid']} work-items = "
+                  f"{dt.get('decode_workgroups')} workgroups, {dt['dispatches']} of "
                   "them): decode kernel mean / median "
                   f"{dt['decode_us']:.2f} / {dt['decode_median_us']:.2f} us, partition "
                   f"reduce after it {dt['merge_us']:.2f} / {dt['merge_median_us']:.2f} us, "
