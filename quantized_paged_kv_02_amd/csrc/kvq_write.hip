@@ -316,6 +316,77 @@ __global__ __launch_bounds__(64) void kvq_write_f16_kernel(WriteArgs a) {
   store_v_f16(a.v_codes + chunk * 4096, pos % kBlock, lane, rv);
 }
 
+// FP16 bulk write (prefill): one 256-thread workgroup per run of
+// kWriteBlocks 16-token blocks of a row and one KV head, as the INT8/FP8
+// block write.  Thread t holds channels 8 (t % 16) .. + 7 of token slot
+// t / 16 of every block (one 16-byte load of K and one of V per block, all
+// issued first).  K: those 8 channels are one 16-byte run of the chunk,
+// stored directly when the token is new.  V: a 16-byte unit holds channels
+// m and m + 16 of the four tokens of a slot quad; each block's V goes
+// through LDS in the chunk's byte order, then every thread stores one unit
+// (by halves for units whose tokens are not all new).
+__global__ __launch_bounds__(256) void kvq_write_f16_block_kernel(WriteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[2048];  // one V chunk
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
+  const int s_new = a.seq_lens[b];
+  const int s_old = s_new - n_new;
+  const int lb0 = s_old / kBlock + (int)blockIdx.x * kWriteBlocks;  // first logical block
+  if (n_new <= 0 || lb0 * kBlock >= s_new) return;
+  const int slot = tid >> 4, k8 = tid & 15;
+  u32x4 rk[kWriteBlocks], rv[kWriteBlocks];
+  int phys[kWriteBlocks];
+#pragma unroll
+  for (int j = 0; j < kWriteBlocks; ++j) {
+    const int lb = lb0 + j;
+    const int pos = lb * kBlock + slot;
+    rk[j] = rv[j] = u32x4{0u, 0u, 0u, 0u};
+    phys[j] = 0;
+    if (lb * kBlock < s_new) {
+      phys[j] = a.block_tables[(size_t)b * a.max_blocks_per_seq + lb];
+      if (pos >= s_old && pos < s_new) {
+        const size_t src =
+            ((size_t)(c_begin + pos - s_old) * a.num_kv_heads + h) * kHeadDim + 8 * k8;
+        rk[j] = ld16(a.k_new + src);
+        rv[j] = ld16(a.v_new + src);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kWriteBlocks; ++j) {
+    const int lb = lb0 + j;
+    if (lb * kBlock >= s_new) break;  // uniform
+    const int t_lo = max(lb * kBlock, s_old), t_hi = min(lb * kBlock + kBlock, s_new);
+    const bool live = lb * kBlock + slot >= t_lo && lb * kBlock + slot < t_hi;
+    const size_t chunk = (size_t)phys[j] * a.num_kv_heads + h;
+    if (live)
+      *reinterpret_cast<u32x4 *>(a.k_codes + chunk * 4096 + k16_offset(slot, 8 * k8)) = rk[j];
+    if (j > 0) __syncthreads();  // the previous block's V units are stored
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vlds[v16_offset(slot, 8 * k8 + e) >> 1] =
+          (uint16_t)((e & 1) ? (rv[j][e >> 1] >> 16) : (rv[j][e >> 1] & 0xFFFFu));
+    __syncthreads();
+    // unit tid: channels m, m + 16 (bytes 0..7, 8..15) of slots 4q .. 4q + 3
+    const int q0 = lb * kBlock + 4 * ((tid >> 4) & 3);
+    uint8_t *dst = a.v_codes + chunk * 4096 + 16 * tid;
+    if (q0 >= t_lo && q0 + 3 < t_hi) {
+      *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(&vlds[8 * tid]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (q0 + e >= t_lo && q0 + e < t_hi) {
+          reinterpret_cast<uint16_t *>(dst)[e] = vlds[8 * tid + e];
+          reinterpret_cast<uint16_t *>(dst)[4 + e] = vlds[8 * tid + 4 + e];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // INT4 KIVI
 // ---------------------------------------------------------------------------
@@ -381,6 +452,12 @@ hipError_t launch_write_q8(const WriteArgs &a, int dtype, int batch, int max_new
 }
 
 hipError_t launch_write_f16(const WriteArgs &a, int batch, int max_new, hipStream_t stream) {
+  if (max_new > 1) {
+    const int blocks = (max_new + 14) / kBlock + 1;  // blocks a run of max_new tokens can touch
+    const dim3 grid((blocks + kWriteBlocks - 1) / kWriteBlocks, a.num_kv_heads, batch);
+    hipLaunchKernelGGL(kvq_write_f16_block_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kvq_write_f16_kernel, dim3(max_new, a.num_kv_heads, batch), dim3(64), 0,
                      stream, a);
   return hipGetLastError();
