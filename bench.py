@@ -210,7 +210,7 @@ def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
 # ---------------------------------------------------------------------------
 
 def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(128, 256, 512, 1024, 2048),
-                    threads: int = 256):
+                    threads: int = 256, orders=(0, 1)):
     """Read ``gib`` GiB (a power of two) per launch in 1 KiB chunks (one
     16-byte buffer load per lane, the decode's granule and cache policy)
     with several grid sizes, in wavefront-strided and in scattered chunk
@@ -247,6 +247,8 @@ def bandwidth_probe(gib: float = 4, reps: int = 5, grids=(128, 256, 512, 1024, 2
 
     rows = []
     for order, name in ((0, "strided"), (1, "scattered")):
+        if order not in orders:
+            continue
         for wgs in grids:
             launch(wgs, order, reps - 1)
             e0.record()
@@ -791,6 +793,13 @@ def main():
                     help="threads per workgroup of the probe (--probe)")
     ap.add_argument("--probe", action="store_true",
                     help="run only the read-bandwidth probe and print its JSON")
+    ap.add_argument("--probe-grids", default="",
+                    help="workgroup counts of the probe (--probe), comma-separated")
+    ap.add_argument("--probe-order", default="both", choices=["strided", "scattered", "both"],
+                    help="chunk order of the probe (--probe)")
+    ap.add_argument("--probe-reps", type=int, default=5,
+                    help="launches per probe configuration (--probe; at least the buffer's "
+                         "slices)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
@@ -800,7 +809,11 @@ def main():
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         raise SystemExit(2)
     if args.probe:
-        print(json.dumps(bandwidth_probe(args.probe_gib, threads=args.probe_threads)),
+        grids = tuple(int(g) for g in args.probe_grids.split(",")) if args.probe_grids else (
+            128, 256, 512, 1024, 2048)
+        orders = {"strided": (0,), "scattered": (1,), "both": (0, 1)}[args.probe_order]
+        print(json.dumps(bandwidth_probe(args.probe_gib, reps=args.probe_reps, grids=grids,
+                                         threads=args.probe_threads, orders=orders)),
               flush=True)
         return
     run(args)
