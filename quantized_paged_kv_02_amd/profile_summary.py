@@ -18,6 +18,12 @@ Two commands:
       plain device copy of known size in the same run (copyBuffer
       dispatches of the probe's grid), so the figure is in bytes.  The
       decode launch is the decode kernel plus the partition reduce kernel.
+
+  python -m quantized_paged_kv_02_amd.profile_summary crosscheck <dir> --workload NAME
+        --command CMD --out FILE
+      The launch's read traffic from L2-to-DRAM and L1-to-L2 read-request
+      counters of one ``rocprofv3 --pmc`` run, each calibrated on the run's
+      device copy: a second figure beside FETCH_SIZE's.
 """
 
 from __future__ import annotations
@@ -188,6 +194,50 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, cmd_fe
           f"(scales {rf:.3f} / {wf:.3f})")
 
 
+def crosscheck(directory: str, workload: str, copy_mib: int, command: str, out: str,
+               counters=("TCC_EA0_RDREQ_DRAM_sum", "TCP_TCC_READ_REQ_sum")) -> None:
+    """Read traffic of one decode launch from request counters of other
+    blocks than FETCH_SIZE's: L2-to-DRAM read requests and L1-to-L2 read
+    requests.  Each is turned into bytes with the bytes per request the
+    same counter shows for the run's device copy (its read side: the copy
+    reads ``copy_mib`` MiB), and compared with the launch's algorithmic
+    bytes and with the FETCH_SIZE figure in decode_traffic.json."""
+    copy_bytes = copy_mib * (1 << 20)
+    rows_all = list(csv.DictReader(open(_find(directory, "counter_collection.csv"))))
+    lines = ["# Decode read traffic from request counters", "",
+             f"Command: `{command}`", "",
+             f"Workload {workload}.  Each counter is summed over its instances per "
+             "dispatch; bytes per request come from the same counter on the run's "
+             f"{copy_mib} MiB device copy (copyBuffer; its reads only).  Per launch = decode "
+             "kernel + partition reduce, medians over dispatches.", "",
+             "| counter | per copy | bytes per request | per launch | bytes per launch |",
+             "|---|---|---|---|---|"]
+    figures = {}
+    for name in counters:
+        rows = [r for r in rows_all if r["Counter_Name"] == name]
+        if not rows:
+            continue
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(copies)
+        per_copy = statistics.median([c for c in copies if c > 0.9 * big])
+        bpr = copy_bytes / per_copy
+        dec = [float(r["Counter_Value"]) for r in rows if "paged_decode" in r["Kernel_Name"]]
+        red = [float(r["Counter_Value"]) for r in rows if "partition_reduce" in r["Kernel_Name"]]
+        n = statistics.median(dec) + (statistics.median(red) if red else 0.0)
+        figures[name] = n * bpr
+        lines.append(f"| {name} | {per_copy:.0f} | {bpr:.2f} | {n:.0f} | {n * bpr / 1e6:.2f} MB |")
+    tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile)).get(workload)
+        if t:
+            lines += ["", f"FETCH_SIZE-derived read bytes per launch (decode_traffic.json): "
+                      f"{t['read_bytes'] / 1e6:.2f} MB."]
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}: " + ", ".join(f"{k} {v / 1e6:.2f} MB" for k, v in figures.items()))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -213,7 +263,16 @@ def main(argv=None):
     t.add_argument("--split-tokens", type=int, default=None,
                    help="the partition length the profiled launches used")
     t.add_argument("--partition", default="per-row", choices=["per-row", "balanced"])
+    c = sub.add_parser("crosscheck")
+    c.add_argument("dir")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--copy-mib", type=int, default=1024)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "crosscheck":
+        crosscheck(a.dir, a.workload, a.copy_mib, a.command, a.out)
+        return 0
     if a.cmd == "stats":
         stats(a.dir, a.command, a.out, a.workload, a.times_out, a.split_tokens, a.partition)
     else:
