@@ -200,7 +200,7 @@ def cpu_baseline(w, lens, workers: int, target_cpu_s: float = 20.0):
             "sample": (f"{n} of {len(all_units)} (layer, row) units of {w.name}; each: "
                        f"quantize the new token (write), dequantize the row's cache and fp64 "
                        f"attention (attention); numpy oracle, 1 BLAS thread per process, "
-                       f"{cores} processes at once (the GPU box's CPU share is 16 of its "
+                       f"{cores} processes at once (a 16-CPU share of the host's "
                        f"{nproc} logical CPUs); {tw + ta:.1f} s of CPU work; K/V drawn on "
                        f"the CPU by the same recipe")}
 
@@ -782,7 +782,7 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a device copy of this many MiB (profiler yardstick)")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
-                    help="oracle processes (the GPU box's CPU share is 16)")
+                    help="oracle processes (default: 16, the host CPU share a GPU job gets)")
     ap.add_argument("--partition", default="auto", choices=["auto", "per-row", "balanced"],
                     help="decode partitions: the host plan's choice (auto) or a forced mode")
     ap.add_argument("--no-probe", action="store_true",
