@@ -158,10 +158,6 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-// D(16x16) += A(16x16) * B(16x16) with k-slots 4*(l/16) .. +3 per lane.
-__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
 
 // Raw buffer resource over `bytes` bytes at `base` (a wave-uniform address);
 // bytes == 0 makes every load through it return zeros without touching
