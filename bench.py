@@ -78,9 +78,10 @@ def _cpu_unit(args):
     import oracle
     w = inputs.WORKLOADS[name]
     k, v = inputs.gen_kv(w, layer, row, seq, "cpu", 0)
-    k = k.numpy()
-    v = v.numpy()
-    q = inputs.gen_q(w, layer, "cpu", 0)[row].numpy().astype(np.float64)
+    # bf16 inputs (a BF16 cache) as float32, exactly; numpy has no bf16
+    k = k.float().numpy() if k.dtype == torch.bfloat16 else k.numpy()
+    v = v.float().numpy() if v.dtype == torch.bfloat16 else v.numpy()
+    q = inputs.gen_q(w, layer, "cpu", 0)[row].float().numpy().astype(np.float64)
     scale = 1.0 / math.sqrt(inputs.HEAD_DIM)
     with threadpool_limits(limits=1):
         if w.dtype in ("int4", "int4-affine", "int2-affine"):
@@ -102,7 +103,7 @@ def _cpu_unit(args):
             k_hat, v_hat = oracle.kivi_dequantize(full)
             oracle.decode_attention(q, k_hat, v_hat, scale)
             return t1 - t0, time.perf_counter() - t1
-        if w.dtype == "fp16":
+        if w.dtype in ("fp16", "bf16"):
             # unquantized cache: the new token is stored as is
             t0 = time.perf_counter()
             oracle.decode_attention(q, k, v, scale)

@@ -147,6 +147,14 @@
  *   V: 1024*(c>>5) + 256*(s>>2) + 16*(c&15) + 8*((c>>4)&1) + 2*(s&3)
  * k_codes / v_codes point at these arrays.  There are no scales: the
  * granularity fields are ignored and k_scales / v_scales may be NULL.
+ *
+ * ---- BF16 (unquantized) layout: KVQ_FP16's with bf16 values ----
+ * The other half-precision baseline ([intelli] §5 compares INT8 with the
+ * 16-bit cache a model runs in; bf16 is the usual one for Llama-class
+ * models).  Byte offsets, chunk size and the absent scales are those of
+ * KVQ_FP16.  Every 16-bit input of the calls that take one (q, k_new, v_new)
+ * is then bf16; scores use bf16 products with fp32 sums and the softmax
+ * weights of the value product are rounded to bf16 (fp16 for KVQ_FP16).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -176,8 +184,10 @@ typedef enum kvq_dtype {
   KVQ_INT4_AFFINE = 5, /* INT4 KIVI grouping, asymmetric: codes 0..15 with a
                           zero point per group                              */
   KVQ_FP8_E5M2 = 6, /* 1 byte per value, OCP E5M2, divisor 57344            */
-  KVQ_INT2_AFFINE = 7 /* 2-bit KIVI: 0.25 byte per value, codes 0..3 with a
-                         zero point per group                               */
+  KVQ_INT2_AFFINE = 7, /* 2-bit KIVI: 0.25 byte per value, codes 0..3 with a
+                          zero point per group                              */
+  KVQ_BF16 = 8      /* 2 bytes per value, unquantized bf16 (the FP16 layout);
+                       q, k_new and v_new are bf16 for this dtype           */
 } kvq_dtype;
 
 typedef enum kvq_granularity {
@@ -254,7 +264,8 @@ size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
                                   int32_t max_seq_len);
 
 /* Quantize-on-write: append new K/V tokens to the cache.
- *   k_new, v_new : fp16 [total_new][H][128], the new tokens of all rows
+ *   k_new, v_new : fp16 [total_new][H][128] (bf16 for a BF16 cache), the
+ *                  new tokens of all rows
  *                  packed in row order.
  *   cu_new       : int32 [batch+1], row b's tokens are k_new[cu_new[b] ..
  *                  cu_new[b+1]-1]; cu_new[0] == 0, cu_new[batch] ==
@@ -265,7 +276,8 @@ size_t kvq_decode_workspace_bytes(const kvq_layout *layout, int32_t batch,
  *   max_new_per_seq: host bound on n_b.
  * INT8/FP8: writes codes (and per-token scales when the granularity is
  * KVQ_PER_TOKEN) into the block slots.  Static scales are read from the
- * cache's scale arrays.  FP16: stores the values in the block slots.
+ * cache's scale arrays.  FP16 / BF16: stores the values in the block
+ * slots.
  * INT4: first quantizes the 64-token groups nq(S_old+1) .. nq(S_new+1)-1
  * (those that leave the fp16 window up to length S_new+1, see the INT4
  * layout; read from the ring or straight from k_new/v_new) into INT4 blocks
@@ -285,8 +297,8 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache,
  *   out[b][hq][:] = sum_t softmax_t(s_t) * v_hat[t],
  *   s_t = softmax_scale * dot(q[b][hq], k_hat[t]),  t < seq_lens[b],
  * with KV head hq / (Hq/H), k_hat/v_hat the dequantized values (code*scale,
- * or fp16 for INT4 residual tokens and for an FP16 cache).
- *   q        : fp16 [batch][Hq][128]
+ * or fp16 for INT4 residual tokens and for an FP16 cache; bf16 for BF16).
+ *   q        : fp16 [batch][Hq][128] (bf16 for a BF16 cache)
  *   out      : fp32 [batch][Hq][128]; rows with seq_lens[b] == 0 get zeros.
  *   workspace: device buffer of at least kvq_decode_workspace_bytes(layout,
  *              batch, max_seq_len) bytes, 256-byte aligned (may be NULL when
@@ -310,9 +322,10 @@ kvq_status kvq_paged_decode(const kvq_layout *layout, const kvq_cache *cache,
  * [yunthe] section "PagedAttention与KV Cache量化协同工作原理").  Same cache
  * contents and the same out, bit for bit, as kvq_write with one token per
  * row followed by kvq_paged_decode with these arguments.
- *   k_new, v_new : fp16 [batch][H][128]; entry b is row b's new token, at
- *                  position seq_lens[b]-1 (seq_lens count it).  Rows with
- *                  seq_lens[b] == 0 take no token and their entry is unread.
+ *   k_new, v_new : fp16 [batch][H][128] (bf16 for a BF16 cache); entry b is
+ *                  row b's new token, at position seq_lens[b]-1 (seq_lens
+ *                  count it).  Rows with seq_lens[b] == 0 take no token and
+ *                  their entry is unread.
  *   q, block_tables, seq_lens, max_seq_len, softmax_scale, out, workspace,
  *   workspace_bytes: as for kvq_paged_decode.
  * INT8/FP8/FP16: a single launch (plus the partition merge when the launch
@@ -415,9 +428,10 @@ kvq_status kvq_check_tables(const kvq_layout *layout, const int32_t *host_block_
  * verification of draft tokens, or a chunk of prefill, over the cache; the
  * whole-history read of [oh-bug] section "为什么长上下文更需要 KV Cache
  * Quantization" shared by n_query queries):
- *   q   : fp16 [batch][n_query][Hq][128]; query j of row b sits at position
- *         seq_lens[b] - n_query + j (its K/V already written, e.g. by
- *         kvq_write) and attends to tokens 0 .. seq_lens[b] - n_query + j.
+ *   q   : fp16 [batch][n_query][Hq][128] (bf16 for a BF16 cache); query j
+ *         of row b sits at position seq_lens[b] - n_query + j (its K/V
+ *         already written, e.g. by kvq_write) and attends to tokens
+ *         0 .. seq_lens[b] - n_query + j.
  *   out : fp32 [batch][n_query][Hq][128]; a query with no visible token
  *         (seq_lens[b] - n_query + j < 0) gets zeros.
  *   workspace: kvq_paged_decode_mq_workspace_bytes(layout, n_query, batch,

@@ -39,14 +39,19 @@ int kivi_len(int s, int residual) {
   return n > 0 ? (n / kGroup) * kGroup : 0;
 }
 
+// Unquantized caches: fp16 or bf16 values, no scales, no residual ring.
+bool unquantized(const kvq_layout *L) {
+  return L->dtype == KVQ_FP16 || L->dtype == KVQ_BF16;
+}
+
 kvq_status check_layout(const kvq_layout *L) {
   if (!L) return KVQ_ERR_INVALID_ARG;
   if (L->struct_size != sizeof(kvq_layout)) return KVQ_ERR_INVALID_ARG;
   if (L->dtype != KVQ_INT8 && L->dtype != KVQ_FP8_E4M3 && L->dtype != KVQ_INT4 &&
       L->dtype != KVQ_FP16 && L->dtype != KVQ_INT4_AFFINE && L->dtype != KVQ_FP8_E5M2 &&
-      L->dtype != KVQ_INT2_AFFINE)
+      L->dtype != KVQ_INT2_AFFINE && L->dtype != KVQ_BF16)
     return KVQ_ERR_INVALID_ARG;
-  if (L->dtype != KVQ_FP16) {  // an FP16 cache has no scales
+  if (!unquantized(L)) {  // an FP16 / BF16 cache has no scales
     if (L->k_gran < KVQ_PER_TENSOR || L->k_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
     if (L->v_gran < KVQ_PER_TENSOR || L->v_gran > KVQ_PER_TOKEN) return KVQ_ERR_INVALID_ARG;
   }
@@ -80,7 +85,7 @@ kvq_status check_cache(const kvq_layout *L, const kvq_cache *C, int32_t batch) {
   if (!C) return KVQ_ERR_INVALID_ARG;
   if (!C->k_codes || !C->v_codes) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(C->k_codes) || !aligned16(C->v_codes)) return KVQ_ERR_ALIGNMENT;
-  if (L->dtype == KVQ_FP16) return KVQ_OK;  // no scales, no ring
+  if (unquantized(L)) return KVQ_OK;  // no scales, no ring
   if (!C->k_scales || !C->v_scales) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(C->k_scales) || !aligned16(C->v_scales)) return KVQ_ERR_ALIGNMENT;
   if (kivi(L)) {
@@ -120,7 +125,7 @@ int choose_part_blocks(const kvq_layout *L, int32_t batch, int max_blocks,
       kCUs * kvq::decode_wg_per_cu(L->dtype, kvq::decode_scale_kind(L->k_gran),
                                    kvq::decode_scale_kind(L->v_gran));
   const long overhead = int4                       ? kWgOverheadInt4
-                        : L->dtype == KVQ_FP16 ? kWgOverheadF16
+                        : unquantized(L) ? kWgOverheadF16
                                                : kWgOverheadQ8;
   const long top = max_blocks > quantum ? max_blocks : quantum;
   // workgroups of a launch whose partitions hold c blocks
@@ -319,8 +324,8 @@ kvq_status kvq_write(const kvq_layout *layout, const kvq_cache *cache, const uin
     // 64)) <= 64 ceil(n / 64) (less while S - n < 128), so ceil(n / 64)
     const int max_groups = (max_new_per_seq + kGroup - 1) / kGroup;
     e = kvq::launch_write_int4(a, layout->dtype, batch, max_new_per_seq, max_groups, s);
-  } else if (layout->dtype == KVQ_FP16) {
-    e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);
+  } else if (unquantized(layout)) {
+    e = kvq::launch_write_f16(a, batch, max_new_per_seq, s);  // bits copied as they are
   } else {
     e = kvq::launch_write_q8(a, layout->dtype, batch, max_new_per_seq, s);
   }

@@ -9,8 +9,11 @@
 namespace kvq {
 
 enum Dtype : int {  // kvq_dtype
-  kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5, kFp8E5M2 = 6, kInt2Affine = 7
+  kInt8 = 1, kFp8 = 2, kInt4 = 3, kFp16 = 4, kInt4Affine = 5, kFp8E5M2 = 6, kInt2Affine = 7,
+  kBf16 = 8
 };
+// Unquantized caches (fp16 or bf16 values, no scales)
+constexpr bool is_f16_cache(int dtype) { return dtype == kFp16 || dtype == kBf16; }
 // KIVI-grouped caches: INT4 symmetric or affine, 2-bit affine
 constexpr bool is_kivi(int dtype) {
   return dtype == kInt4 || dtype == kInt4Affine || dtype == kInt2Affine;
@@ -29,7 +32,7 @@ enum ScaleKind : int { kUniform = 0, kChannel = 1, kToken = 2 };
 // fits three per CU in registers and LDS, but on the KIVI shape six
 // partitions per row at three per CU ran 3 % slower than four at two.)
 constexpr int decode_wg_per_cu(int dtype, int k_kind, int v_kind) {
-  return (is_kivi(dtype) || dtype == kFp16) ? 2
+  return (is_kivi(dtype) || is_f16_cache(dtype)) ? 2
          : ((dtype == kFp8 || dtype == kFp8E5M2) && v_kind == kToken && k_kind != kUniform) ? 2
                                                                       : 3;
 }

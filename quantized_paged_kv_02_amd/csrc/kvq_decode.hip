@@ -182,6 +182,29 @@ __device__ __forceinline__ f16x8 p_operand(const f32x4 &p0, const f32x4 &p1) {
                (f16)p1[0], (f16)p1[1], (f16)p1[2], (f16)p1[3]};
 }
 
+// BF16 caches: 16-bit operands carried in f16x8 containers hold bf16 bits.
+// bf16 keeps 8 significant bits, fp16 11: the weights go to the value
+// product as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi) (p - hi is
+// exact in fp32), about 16 significant bits together, at the cost of a
+// second value MFMA per tile.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void p_operand_bf16(const f32x4 &p0, const f32x4 &p1, f16x8 &hi,
+                                               f16x8 &lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = i < 4 ? p0[i] : p1[i - 4];
+    h[i] = (__bf16)p;
+    l[i] = (__bf16)(p - (float)h[i]);
+  }
+  hi = __builtin_bit_cast(f16x8, h);
+  lo = __builtin_bit_cast(f16x8, l);
+}
+__device__ __forceinline__ f32x4 mfma32_bf16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
   return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -412,16 +435,17 @@ __device__ __forceinline__ f16x8 value_operand16(const Pair16 &t, int j) {
              u2_to_f16x4(u32x2{t.v[1][j >> 1][w], t.v[1][j >> 1][w + 1]}));
 }
 
-// valid_s, valid_v as for compute_pair8.
-template <bool TAIL>
+// valid_s, valid_v as for compute_pair8.  BF: a BF16 cache (bf16 operands).
+template <bool TAIL, bool BF>
 __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16x8 (&bq)[4],
                                                float kmul, int valid_s, int valid_v, int qd) {
+  auto mma = [](f16x8 a, f16x8 b, f32x4 c) { return BF ? mfma32_bf16(a, b, c) : mfma32(a, b, c); };
   f32x4 s[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[u] = mfma32(u4_to_f16x8(t.k[u][j]), bq[j], s[u]);
+    for (int j = 0; j < 4; ++j) s[u] = mma(u4_to_f16x8(t.k[u][j]), bq[j], s[u]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float v = s[u][r] * kmul;
@@ -430,7 +454,9 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
   }
   f32x4 p0, p1;
   softmax_update(st, s[0], s[1], p0, p1);
-  const f16x8 pb = p_operand(p0, p1);
+  f16x8 pb, pl;
+  if constexpr (BF) p_operand_bf16(p0, p1, pb, pl);
+  else pb = p_operand(p0, p1);
   if (TAIL) {
     // zero the values of unattended tokens (stale, possibly NaN): dword w
     // of a quarter holds tokens 2(w&1), 2(w&1)+1 of the lane's four
@@ -444,11 +470,16 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
       }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = mfma32(value_operand16(t, j), pb, st.o[j]);
+  for (int j = 0; j < 8; ++j) {
+    const f16x8 v = value_operand16(t, j);
+    st.o[j] = mma(v, pb, st.o[j]);
+    if constexpr (BF) st.o[j] = mma(v, pl, st.o[j]);
+  }
 }
 
 template <int DT> struct UnitOf { using T = Pair8; };
 template <> struct UnitOf<kFp16> { using T = Pair16; };
+template <> struct UnitOf<kBf16> { using T = Pair16; };
 
 // Query operand of the score product for this lane's channels 32qd..32qd+31
 // (as 4 x 8 fp16), zero for the 16 - cols padding columns.  Column n is
@@ -478,7 +509,7 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
   load_q(qr, a, b, h, n, qd);
   f16x8 bq[4], bq_lo[4];
   float kmul = a.qk_scale;
-  if constexpr (DT == kFp16) {
+  if constexpr (is_f16_cache(DT)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bq[j] = bq_lo[j] = u4_to_f16x8(qr[j]);
   } else if constexpr (KS == kChannel) {
@@ -525,7 +556,7 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
     const int cnt = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
     using Unit = typename UnitOf<DT>::T;
     auto load_unit = [&](Unit &t, int ph0, int ph1) {
-      if constexpr (DT == kFp16) {
+      if constexpr (is_f16_cache(DT)) {
         load_pair16(t, a, ph0, ph1, h, lane);
       } else {
         load_pair8<KS, VS>(t, a, ph0, ph1, h, lane, qd);
@@ -536,8 +567,8 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
       load_unit(t, uniform(sh.s.ids[j0]), uniform(sh.s.ids[j0 + 1]));
     };
     auto compute = [&](Unit &t, int) {
-      if constexpr (DT == kFp16) {
-        compute_pair16<false>(st, t, bq, kmul, 32, 32, qd);
+      if constexpr (is_f16_cache(DT)) {
+        compute_pair16<false, DT == kBf16>(st, t, bq, kmul, 32, 32, qd);
       } else {
         compute_pair8<DT, KS, VS, false>(st, t, bq, bq_lo, kmul, 32, 32, qd);
       }
@@ -558,14 +589,14 @@ __device__ void stream_q8(Softmax &st, const DecodeArgs &a, SharedLds &sh, int b
       const int ph1 = c0 + j0 + 1 < c1 ? uniform(sh.s.ids[j0 + 1]) : ph0;
       Unit t;
       load_unit(t, ph0, ph1);
-      if constexpr (DT == kFp16) {
-        compute_pair16<true>(st, t, bq, kmul, valid_s, valid_v, qd);
+      if constexpr (is_f16_cache(DT)) {
+        compute_pair16<true, DT == kBf16>(st, t, bq, kmul, valid_s, valid_v, qd);
       } else {
         compute_pair8<DT, KS, VS, true>(st, t, bq, bq_lo, kmul, valid_s, valid_v, qd);
       }
     }
   }
-  if constexpr (DT == kFp16) return;  // no scales
+  if constexpr (is_f16_cache(DT)) return;  // no scales
   // uniform and per-channel V scales multiply o once (per-token ones rode
   // on the weights, with the operand boost to remove)
   if constexpr (VS == kToken && operand_boost<DT>() != 1.0f) {
@@ -1949,7 +1980,7 @@ __device__ __forceinline__ void decode_workgroup(const DecodeArgs &a, SharedLds 
     if (a.k_new != nullptr && p == n_main - 1) {
       // this workgroup streams the row's last block: store the new token
       // first, complete (every counter drained) before any wave reads it
-      if constexpr (DT == kFp16) {
+      if constexpr (is_f16_cache(DT)) {
         append_token_f16(a, b, h, seq_len, wave, lane);
       } else {
         append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
@@ -2012,7 +2043,7 @@ __device__ void decode_balanced(const DecodeArgs &a, SharedLds &sh, int *pre) {
     softmax_init(st);
     if (a.k_new != nullptr && blk1 == nb) {
       // this segment holds the row's last block: store the new token first
-      if constexpr (DT == kFp16) {
+      if constexpr (is_f16_cache(DT)) {
         append_token_f16(a, b, h, seq_len, wave, lane);
       } else {
         append_token_q8<DT, KS, VS>(a, b, h, seq_len, wave, lane);
@@ -2198,6 +2229,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int k_kind, int v_kind,
                        0, stream, a);
   } else if (dtype == kInt4Affine) {
     hipLaunchKernelGGL((kvq_paged_decode_int4_kernel<kInt4Affine, false>), grid, dim3(kThreads),
+                       0, stream, a);
+  } else if (dtype == kBf16) {
+    hipLaunchKernelGGL((kvq_paged_decode_kernel<kBf16, kUniform, kUniform>), grid, dim3(kThreads),
                        0, stream, a);
   } else if (dtype == kFp16) {
     hipLaunchKernelGGL((kvq_paged_decode_kernel<kFp16, kUniform, kUniform>), grid, dim3(kThreads),

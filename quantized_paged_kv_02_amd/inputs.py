@@ -36,8 +36,8 @@ class Workload:
     num_kv_heads: int
     seq: int | tuple            # fixed length, or (lo, hi) uniform inclusive
     dtype: str                  # "int8" | "fp8" | "fp8e5m2" | "int4" | "int4-affine" |
-                                # "int2-affine" | "fp16"
-    k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16)
+                                # "int2-affine" | "fp16" | "bf16"
+    k_gran: str                 # "tensor" | "head" | "channel" | "token" ("none": fp16, bf16)
     v_gran: str
     table: str = "identity"     # "identity" | "shuffled"
     channel_outliers: tuple = ()    # (count, factor, tensors) e.g. (4, 10.0, "kvq")
@@ -103,6 +103,15 @@ WORKLOADS = {
     "llama3-70b-fp16": Workload(
         "llama3-70b-fp16", 80, 24, 64, 8, 16384, "fp16", "none", "none",
         description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, FP16 cache"),
+    # the same baselines for models that run in bf16: cache, queries and new
+    # tokens in bf16
+    "llama2-7b-bf16": Workload(
+        "llama2-7b-bf16", 32, 4, 32, 32, 2048, "bf16", "none", "none",
+        element_outliers=(0.01, 8.0, "kv"),
+        description="Llama-2-7B shape: 32 layers, 32/32 heads, batch 4, seq 2048, BF16 cache"),
+    "llama3-70b-bf16": Workload(
+        "llama3-70b-bf16", 80, 24, 64, 8, 16384, "bf16", "none", "none",
+        description="Llama-3-70B shape: 80 layers, 64/8 heads, batch 24, seq 16384, BF16 cache"),
 }
 
 
@@ -163,12 +172,13 @@ def _draw(w: Workload, shape, tensor: str, seed: int, layer: int, row: int, devi
         x = torch.where(u < prob, x * factor, x)
     if w.shift and tensor in w.shift[1]:
         x = x + w.shift[0]
-    return x.to(torch.float16)
+    return x.to(torch.bfloat16 if w.dtype == "bf16" else torch.float16)
 
 
 def gen_kv(w: Workload, layer: int, row: int, n_tokens: int, device="cpu", seed: int = 0,
            offset: int = 0):
-    """fp16 K and V of one row, tokens offset .. offset+n_tokens-1, shape
+    """fp16 (bf16 for a BF16 cache) K and V of one row, tokens
+    offset .. offset+n_tokens-1, shape
     [n_tokens, Hkv, 128].  Tokens are drawn per (row, layer); ``offset`` only
     selects an independent stream for tokens written later."""
     shape = (n_tokens, w.num_kv_heads, HEAD_DIM)

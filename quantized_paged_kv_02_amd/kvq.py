@@ -17,15 +17,16 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2, INT2_AFFINE = 1, 2, 3, 4, 5, 6, 7
+INT8, FP8_E4M3, INT4, FP16, INT4_AFFINE, FP8_E5M2, INT2_AFFINE, BF16 = 1, 2, 3, 4, 5, 6, 7, 8
 PER_TENSOR, PER_HEAD, PER_CHANNEL, PER_TOKEN = 0, 1, 2, 3
 PARTITION_PER_ROW, PARTITION_BALANCED = 0, 1
 PARTITIONS = {"per-row": PARTITION_PER_ROW, "balanced": PARTITION_BALANCED}
 DTYPES = {"int8": INT8, "fp8": FP8_E4M3, "int4": INT4, "fp16": FP16,
-          "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2, "int2-affine": INT2_AFFINE}
+          "int4-affine": INT4_AFFINE, "fp8e5m2": FP8_E5M2, "int2-affine": INT2_AFFINE,
+          "bf16": BF16}
 GRANS = {"tensor": PER_TENSOR, "head": PER_HEAD, "channel": PER_CHANNEL,
          "token": PER_TOKEN,
-         "none": PER_TENSOR}   # FP16 cache: no scales, the field is ignored
+         "none": PER_TENSOR}   # FP16 / BF16 cache: no scales, the field is ignored
 
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_ALIGNMENT", -4: "KVQ_ERR_WORKSPACE",
@@ -208,6 +209,12 @@ def scale_shape(layout: Layout, gran: int):
     return (layout.num_blocks, layout.num_kv_heads, layout.block_size)
 
 
+def act_dtype(layout: Layout):
+    """dtype of the 16-bit inputs (q, k_new, v_new) a layout's calls take:
+    bf16 for a BF16 cache, fp16 otherwise."""
+    return torch.bfloat16 if layout.dtype == BF16 else torch.float16
+
+
 def alloc_cache(layout: Layout, ring_rows: int = 0, device="cuda",
                 k_static=None, v_static=None) -> KVCache:
     """Allocate one layer's pool.  Static scales (per tensor/head/channel)
@@ -227,10 +234,10 @@ def alloc_cache(layout: Layout, ring_rows: int = 0, device="cuda",
         k_resid = torch.empty((ring_rows, h, ring, 128), dtype=torch.float16, device=device)
         v_resid = torch.empty((ring_rows, h, ring // 4, 128, 4), dtype=torch.float16,
                               device=device)
-    elif layout.dtype == FP16:
-        # unquantized: 4 KiB of fp16 per (block, head), no scales
-        k_codes = torch.empty((nb, h, 2048), dtype=torch.float16, device=device)
-        v_codes = torch.empty((nb, h, 2048), dtype=torch.float16, device=device)
+    elif layout.dtype in (FP16, BF16):
+        # unquantized: 4 KiB of fp16 / bf16 per (block, head), no scales
+        k_codes = torch.empty((nb, h, 2048), dtype=act_dtype(layout), device=device)
+        v_codes = torch.empty((nb, h, 2048), dtype=act_dtype(layout), device=device)
         k_scales = v_scales = k_resid = v_resid = None
     else:
         k_codes = torch.empty((nb, h, 2048), dtype=torch.uint8, device=device)
@@ -274,8 +281,8 @@ def write(cache: KVCache, k_new, v_new, cu_new, block_tables, seq_lens,
     lay = cache.layout
     batch = _tables(block_tables, seq_lens, lay)
     total_new = int(k_new.shape[0]) if isinstance(k_new, torch.Tensor) else 0
-    _arg(k_new, "k_new", torch.float16, (total_new, lay.num_kv_heads, lay.head_dim))
-    _arg(v_new, "v_new", torch.float16, (total_new, lay.num_kv_heads, lay.head_dim))
+    _arg(k_new, "k_new", act_dtype(lay), (total_new, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", act_dtype(lay), (total_new, lay.num_kv_heads, lay.head_dim))
     _arg(cu_new, "cu_new", torch.int32, (batch + 1,))
     c = cache.struct()
     st = LIB.kvq_write(ctypes.byref(cache.layout), ctypes.byref(c), _ptr(k_new), _ptr(v_new),
@@ -290,7 +297,7 @@ def paged_decode(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
     """kvq_paged_decode: one decode step of attention (see kvq.h)."""
     lay = cache.layout
     batch = _tables(block_tables, seq_lens, lay)
-    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(q, "q", act_dtype(lay), (batch, lay.num_q_heads, lay.head_dim))
     _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
     _arg(workspace, "workspace")
     c = cache.struct()
@@ -308,9 +315,9 @@ def write_decode(cache: KVCache, k_new, v_new, q, block_tables, seq_lens, max_se
     """kvq_write_decode: append one token per row, then decode (see kvq.h)."""
     lay = cache.layout
     batch = _tables(block_tables, seq_lens, lay)
-    _arg(k_new, "k_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
-    _arg(v_new, "v_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
-    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(k_new, "k_new", act_dtype(lay), (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", act_dtype(lay), (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(q, "q", act_dtype(lay), (batch, lay.num_q_heads, lay.head_dim))
     _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
     _arg(workspace, "workspace")
     c = cache.struct()
@@ -329,9 +336,9 @@ def write_decode_noalloc(cache: KVCache, k_new, v_new, q, block_tables, seq_lens
     library's per-GPU array (no workspace; see kvq.h)."""
     lay = cache.layout
     batch = _tables(block_tables, seq_lens, lay)
-    _arg(k_new, "k_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
-    _arg(v_new, "v_new", torch.float16, (batch, lay.num_kv_heads, lay.head_dim))
-    _arg(q, "q", torch.float16, (batch, lay.num_q_heads, lay.head_dim))
+    _arg(k_new, "k_new", act_dtype(lay), (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(v_new, "v_new", act_dtype(lay), (batch, lay.num_kv_heads, lay.head_dim))
+    _arg(q, "q", act_dtype(lay), (batch, lay.num_q_heads, lay.head_dim))
     _arg(out, "out", torch.float32, (batch, lay.num_q_heads, lay.head_dim))
     c = cache.struct()
     st = LIB.kvq_write_decode_noalloc(ctypes.byref(lay), ctypes.byref(c), _ptr(k_new),
@@ -383,7 +390,7 @@ def paged_decode_mq(cache: KVCache, q, block_tables, seq_lens, max_seq_len: int,
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [batch, n_query, Hq, 128] tensor")
     n_query = int(q.shape[1])
-    _arg(q, "q", torch.float16, (batch, n_query, lay.num_q_heads, lay.head_dim))
+    _arg(q, "q", act_dtype(lay), (batch, n_query, lay.num_q_heads, lay.head_dim))
     _arg(out, "out", torch.float32, (batch, n_query, lay.num_q_heads, lay.head_dim))
     _arg(workspace, "workspace")
     c = cache.struct()

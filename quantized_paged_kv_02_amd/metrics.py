@@ -35,7 +35,7 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
     """Algorithmic bytes of one layer's decode over rows of lengths ``lens``."""
     hkv, hq, d = num_kv_heads, num_q_heads, HEAD_DIM
     b = len(lens)
-    total = b * hq * d * 2 + b * hq * d * 4          # q fp16 in, out fp32
+    total = b * hq * d * 2 + b * hq * d * 4          # q fp16 (bf16) in, out fp32
     uniform_scales = 0
     for s in (int(x) for x in lens):
         if dtype in ("int4", "int4-affine", "int2-affine"):
@@ -52,7 +52,7 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
                 total += hkv * nq * 2                 # V zero points
             total += hkv * r * d * 2 * 2              # fp16 K and V residual
             total += (nq // BLOCK) * 4                # block-table entries
-        elif dtype == "fp16":
+        elif dtype in ("fp16", "bf16"):
             total += 2 * hkv * s * d * 2              # K and V values, 2 bytes
             total += ((s + BLOCK - 1) // BLOCK) * 4
         else:
@@ -61,7 +61,7 @@ def decode_bytes(dtype: str, k_gran: str, v_gran: str, lens, num_q_heads: int,
                 if gran == "token":
                     total += hkv * s * 4
             total += ((s + BLOCK - 1) // BLOCK) * 4
-    if dtype not in ("int4", "int4-affine", "int2-affine", "fp16"):
+    if dtype not in ("int4", "int4-affine", "int2-affine", "fp16", "bf16"):
         for gran in (k_gran, v_gran):
             if gran != "token":
                 uniform_scales += _scale_bytes_uniform(gran, hkv)
@@ -76,9 +76,10 @@ def decode_flops(lens, num_q_heads: int) -> int:
 
 def write_bytes(dtype: str, k_gran: str, v_gran: str, n_new: int, num_kv_heads: int) -> int:
     """Bytes of one INT8/FP8 quantize-on-write of ``n_new`` tokens: fp16 K/V
-    read, codes (and per-token scales) written.  FP16: K/V read and stored."""
+    read, codes (and per-token scales) written.  FP16 / BF16: K/V read and
+    stored."""
     hkv, d = num_kv_heads, HEAD_DIM
-    if dtype == "fp16":
+    if dtype in ("fp16", "bf16"):
         return n_new * hkv * d * 2 * 2 * 2
     total = n_new * hkv * d * 2 * 2 + n_new * hkv * d * 2
     for gran in (k_gran, v_gran):

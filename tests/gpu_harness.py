@@ -37,10 +37,17 @@ class CaseResult:
     softmax_scale: float
 
 
+def _np(t):
+    """A tensor on the host as numpy; bf16 (which numpy lacks) as float32,
+    an exact conversion."""
+    t = t.cpu()
+    return t.float().numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+
 def _static(w, gran, tensors, dtype):
     """Static scales from the rows' prefill tokens, by the oracle's
     calibration (rows folded in one at a time)."""
-    if dtype == "fp16" or gran not in ("tensor", "head", "channel"):
+    if dtype in ("fp16", "bf16") or gran not in ("tensor", "head", "channel"):
         return None
     s = None
     for t in tensors:
@@ -147,7 +154,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         kvq.paged_decode_mq(cache, q, table_t, lens_t, max_len, scale, out, ws)
     elif fused:
         # entry r is row r's decode token; rows of length 0 keep zeros (unread)
-        kn = torch.zeros((b, w.num_kv_heads, 128), dtype=torch.float16, device=device)
+        kn = torch.zeros((b, w.num_kv_heads, 128), dtype=kvq.act_dtype(layout), device=device)
         vn = torch.zeros_like(kn)
         for r in range(b):
             if lens[r] >= 1:
@@ -170,14 +177,14 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, o, ws)
         rep_outs.append(o)
     torch.cuda.synchronize()
-    pools = {name: getattr(cache, name).cpu().numpy()
+    pools = {name: _np(getattr(cache, name))
              for name in ("k_codes", "v_codes", "k_scales", "v_scales")
              if getattr(cache, name) is not None}
     if cache.k_resid is not None:
         pools["k_resid"] = cache.k_resid.cpu().numpy()
         pools["v_resid"] = cache.v_resid.cpu().numpy()
-    res = CaseResult(w, lens, table, [k.cpu().numpy() for k in ks], [v.cpu().numpy() for v in vs],
-                     q.cpu().numpy(), out.cpu().numpy(), pools, k_static, v_static, scale)
+    res = CaseResult(w, lens, table, [_np(k) for k in ks], [_np(v) for v in vs],
+                     _np(q), out.cpu().numpy(), pools, k_static, v_static, scale)
     if decode_twice:
         res.out2 = out2.cpu().numpy()
     res.repeat_outs = [o.cpu().numpy() for o in rep_outs]
@@ -229,13 +236,15 @@ def oracle_row(res: CaseResult, r: int, check_codes=True):
             assert np.array_equal(rv.view(np.uint16), kv["v_resid"].view(np.uint16)), \
                 f"row {r}: ring V"
         k_hat, v_hat = oracle.kivi_dequantize(kv)
-    elif w.dtype == "fp16":
-        # unquantized: the cache holds the inputs' fp16 bits, attended as such
+    elif w.dtype in ("fp16", "bf16"):
+        # unquantized: the cache holds the inputs' 16-bit values, attended as
+        # such (bf16 arrays arrive as float32, converted exactly)
         if check_codes:
             for which, x in (("k", kb), ("v", vb)):
-                g = lv.logical_codes(p[f"{which}_codes"], row, s, which, "fp16")
-                assert np.array_equal(g.view(np.uint16), x.view(np.uint16)), \
-                    f"row {r}: fp16 {which} values differ"
+                g = lv.logical_codes(p[f"{which}_codes"], row, s, which, w.dtype)
+                bits = np.uint32 if x.dtype == np.float32 else np.uint16
+                assert np.array_equal(g.view(bits), x.view(bits)), \
+                    f"row {r}: {w.dtype} {which} values differ"
         k_hat, v_hat = kb, vb
     else:
         out = []

@@ -83,10 +83,11 @@ def chunk4(pool_chunk, which, signed=True):
 
 def logical_codes(pool, table_row, n_tokens, which, dtype):
     """pool [NB, H, bytes] -> codes [n_tokens, H, 128] (uint8 for INT8/FP8
-    bit patterns, int8 for INT4, the fp16 values for an FP16 pool)."""
+    bit patterns, int8 for INT4, the fp16 values for an FP16 pool, the
+    float32 values of a BF16 pool read as float32)."""
     pool = np.asarray(pool)
     h = pool.shape[1]
-    kind = {"int4": np.int8, "fp16": np.float16}.get(dtype, np.uint8)
+    kind = {"int4": np.int8, "fp16": np.float16, "bf16": np.float32}.get(dtype, np.uint8)
     out = np.zeros((n_tokens, h, 128), kind)   # int4-affine: uint8 codes 0..15
     for j in range((n_tokens + 15) // 16):
         phys = int(table_row[j])
@@ -98,7 +99,7 @@ def logical_codes(pool, table_row, n_tokens, which, dtype):
                 c = chunk4(pool[phys, hh], which, signed=False)
             elif dtype == "int2-affine":
                 c = chunk2(pool[phys, hh], which)
-            elif dtype == "fp16":
+            elif dtype in ("fp16", "bf16"):
                 c = chunk16(pool[phys, hh], which)
             else:
                 c = chunk8(pool[phys, hh], which)

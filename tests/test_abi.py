@@ -194,22 +194,24 @@ def test_decode_rejects_oversized_grid():
     assert _decode(lay, c, batch=127, max_len=1 << 20) == WS
 
 
-def test_fp16_cache_rules():
-    # an FP16 cache has no scales: NULL scale pointers and any granularity
-    # field are accepted, the code arrays are still required and aligned
-    lay = _layout(dtype=4, k_gran=77, v_gran=-5)
+@pytest.mark.parametrize("dt", [4, 8])
+def test_fp16_cache_rules(dt):
+    # an FP16 or BF16 cache has no scales: NULL scale pointers and any
+    # granularity field are accepted, the code arrays are still required and
+    # aligned
+    lay = _layout(dtype=dt, k_gran=77, v_gran=-5)
     bare = _cache(k_scales=None, v_scales=None)
     assert kvq.validate(lay, bare, 2, 100) == OK
     assert kvq.validate(lay, _cache(k_codes=None, k_scales=None, v_scales=None), 2, 100) == INV
     assert kvq.validate(lay, _cache(v_codes=FAKE + 2, k_scales=None, v_scales=None), 2,
                         100) == ALN
     assert kvq.validate(_layout(dtype=6), bare, 2, 100) == INV
-    assert kvq.validate(_layout(dtype=4, split_tokens=24), bare, 2, 100) == INV
+    assert kvq.validate(_layout(dtype=dt, split_tokens=24), bare, 2, 100) == INV
     assert _decode(lay, bare, q=None) == INV
     assert _write(lay, bare, cu=FAKE + 4) == ALN
     assert _write_decode(lay, bare, vn=None) == INV
     # same partition plan rules: a split launch needs partials
-    assert kvq.decode_workspace_bytes(_layout(dtype=4, split_tokens=16), 2, 100) > 0
+    assert kvq.decode_workspace_bytes(_layout(dtype=dt, split_tokens=16), 2, 100) > 0
 
 
 def test_int4_affine_rules():
@@ -251,8 +253,8 @@ def test_calibrate_rules():
     # per-token tensors are not calibrated: their pointers may be NULL
     tok = _layout(dtype=1, k_gran=3, v_gran=3)
     assert _calibrate(tok, k=None, v=None, ks=None, vs=None) == OK
-    # no static scales: INT4, affine INT4, FP16
-    for dt, kg, vg in ((3, 2, 3), (5, 2, 3), (4, 0, 0)):
+    # no static scales: INT4, affine INT4, FP16, BF16
+    for dt, kg, vg in ((3, 2, 3), (5, 2, 3), (4, 0, 0), (8, 0, 0)):
         assert _calibrate(_layout(dtype=dt, k_gran=kg, v_gran=vg)) == UNS
     assert _calibrate(_layout(dtype=2, k_gran=0, v_gran=0, num_kv_heads=257,
                               num_q_heads=257)) == UNS

@@ -59,7 +59,7 @@ def _run_layers(w, lens, fused=False, label=None):
 @pytest.mark.parametrize("name", ["llama2-7b", "llama3-8b-gqa", "kivi-int4", "llama3-70b-int8",
                                   "llama3-70b-fp8", "llama2-7b-fp16", "llama3-70b-fp16",
                                   "kivi-int4-affine", "llama3-70b-fp8e5m2",
-                                  "kivi-int2-affine"])
+                                  "kivi-int2-affine", "llama2-7b-bf16", "llama3-70b-bf16"])
 def test_fullsize_layer(name):
     w = W[name]
     _run_layers(w, inputs.seq_lens(w))

@@ -23,6 +23,7 @@ def _w(dtype, kg, vg, hq, hkv, table="shuffled"):
 
 
 FORMATS = [("int8", "token", "token"), ("fp8", "head", "head"), ("fp16", "none", "none"),
+           ("bf16", "none", "none"),
            ("fp8e5m2", "channel", "token"), ("int4", "channel", "token"),
            ("int4-affine", "channel", "token"), ("int2-affine", "channel", "token")]
 

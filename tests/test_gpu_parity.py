@@ -128,8 +128,9 @@ def test_repeated_split_launches_on_one_workspace(dtype, kg, vg):
 @pytest.mark.parametrize("lens,split", [([1, 37, 300], 64), ([16, 17, 31, 32, 33], 0),
                                         ([0, 1, 0, 2], 0), ([777, 15, 2000], 256),
                                         ([100, 257, 31], 4096)])
-def test_fp16_cache(lens, split):
-    w = _small("fp16", "none", "none", table="shuffled",
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp16_cache(lens, split, dtype):
+    w = _small(dtype, "none", "none", table="shuffled",
                channel_outliers=(4, 10.0, "kvq"))
     res = run_case(w, lens, split_tokens=split, decode_twice=True)
     live = [r for r, s in enumerate(lens) if s > 0]
@@ -141,14 +142,24 @@ def test_fp16_cache(lens, split):
 
 
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1), (16, 2), (12, 3)])
-def test_fp16_group_sizes(hq, hkv):
-    w = _small("fp16", "none", "none", hq=hq, hkv=hkv)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp16_group_sizes(hq, hkv, dtype):
+    w = _small(dtype, "none", "none", hq=hq, hkv=hkv)
     check_rows(run_case(w, [16, 33, 129], split_tokens=32))
 
 
-def test_fp16_chunked_writes():
-    w = _small("fp16", "none", "none", table="shuffled")
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp16_chunked_writes(dtype):
+    w = _small(dtype, "none", "none", table="shuffled")
     check_rows(run_case(w, [300, 1000, 17], chunks=3, split_tokens=128))
+
+
+def test_bf16_cache_large_values():
+    """bf16 values beyond fp16's range (V ~ N(0,1) * 1e6 on four channels)
+    and below its smallest normal: the BF16 path never passes through fp16."""
+    w = _small("bf16", "none", "none", channel_outliers=(4, 1.0e6, "v"))
+    res = run_case(w, [300, 1000], split_tokens=128)
+    check_rows(res)
 
 
 # --- asymmetric (affine) INT4 KIVI groups: codes, scales and zero points bit
@@ -253,7 +264,8 @@ BAL_LENS = [1, 0, 300, 1000, 17, 64, 2000, 5]
                                                ("fp8", "head", "head", "shuffled"),
                                                ("fp8e5m2", "channel", "token", "shuffled"),
                                                ("int8", "channel", "tensor", "shuffled"),
-                                               ("fp16", "none", "none", "shuffled")])
+                                               ("fp16", "none", "none", "shuffled"),
+                                               ("bf16", "none", "none", "shuffled")])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("hkv", [2, 8])
 def test_balanced_partitions(dtype, kg, vg, table, fused, hkv):

@@ -33,6 +33,7 @@ CASES = [
     ("fp8", "channel", "token", "identity"),
     ("int4", "channel", "token", "shuffled"),
     ("fp16", "none", "none", "shuffled"),
+    ("bf16", "none", "none", "identity"),
     ("int4-affine", "channel", "token", "shuffled"),
     ("int2-affine", "channel", "token", "identity"),
     ("fp8e5m2", "channel", "token", "shuffled"),
