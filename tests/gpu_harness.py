@@ -57,7 +57,7 @@ def _static(w, gran, tensors, dtype):
 
 def fill_garbage(cache):
     """Poison every pool byte so reads of unwritten slots would show."""
-    if cache.layout.dtype == 4:        # FP16 values
+    if cache.layout.dtype in (4, 8):   # FP16 / BF16 values
         cache.k_codes.fill_(float("nan"))
         cache.v_codes.fill_(float("nan"))
         return
