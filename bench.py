@@ -342,7 +342,8 @@ def launch_floor(layer_bytes: int):
 
 class Bench:
     def __init__(self, w: inputs.Workload, device="cuda", n_query: int = 0,
-                 partition: str = "auto", with_probe: bool = True):
+                 partition: str = "auto", with_probe: bool = True, prefill_calls: int = 10,
+                 prefill_warm: int = 30):
         import torch
         from quantized_paged_kv_02_amd import kvq
         self.torch, self.kvq, self.w = torch, kvq, w
@@ -416,23 +417,37 @@ class Bench:
             kvq.write(cache, kpre, vpre, cu, self.table, n_t, int(n.max()))
             if layer == 0:
                 # time the prefill write of one layer: rewriting the same
-                # tokens stores the same codes, scales and ring values
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(3):
+                # tokens stores the same codes, scales and ring values.  Every
+                # kernel of the call is timed (a KIVI write is the flush and
+                # the fp16-window append).  The engine clock dips for a few
+                # milliseconds once back-to-back write kernels start (to ~1.6
+                # GHz around the 3rd-10th call, back above 2 GHz by the
+                # 20th), so prefill_warm untimed calls come first, then
+                # prefill_calls timed back to back, each between its own
+                # events; us is their median
+                for _ in range(prefill_warm):
                     kvq.write(cache, kpre, vpre, cu, self.table, n_t, int(n.max()))
-                e1.record()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(max(1, prefill_calls))]
+                for e0, e1 in ev:
+                    e0.record()
+                    kvq.write(cache, kpre, vpre, cu, self.table, n_t, int(n.max()))
+                    e1.record()
                 torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / 3
+                calls = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+                us = float(np.median(calls))
+                us_mean = float(np.mean(calls))
                 if w.dtype in KIVI:
                     nbytes = metrics.kivi_write_bytes(w.dtype, n, w.num_kv_heads, w.residual_len)
                 else:
                     nbytes = metrics.write_bytes(w.dtype, w.k_gran, w.v_gran, int(n.sum()),
                                                  w.num_kv_heads)
                 self.prefill_write = {
-                    "call": "kvq_write of one layer's prefill (S - 1 tokens per row)",
+                    "call": "kvq_write of one layer's prefill (S - 1 tokens per row): median "
+                            "of back-to-back calls after untimed ones",
+                    "warm_calls": prefill_warm,
                     "tokens": int(n.sum()), "bytes": nbytes, "us": round(us, 2),
+                    "us_mean": round(us_mean, 2), "calls": len(calls),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
                 if with_probe:
@@ -528,7 +543,8 @@ def run(args):
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
     bench = Bench(w, n_query=args.n_query, partition=args.partition,
-                  with_probe=not args.no_probe)
+                  with_probe=not args.no_probe, prefill_calls=args.prefill_calls,
+                  prefill_warm=args.prefill_warm)
     b = w.batch
     L = w.layers
     layer_bytes = metrics.decode_bytes(w.dtype, w.k_gran, w.v_gran, bench.lens,
@@ -780,6 +796,10 @@ def main():
     ap.add_argument("--kernel-samples", type=int, default=10,
                     help="extra synchronised replays for the per-launch timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-calls", type=int, default=10,
+                    help="back-to-back prefill writes timed for prefill_write")
+    ap.add_argument("--prefill-warm", type=int, default=30,
+                    help="untimed back-to-back prefill writes before them")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a device copy of this many MiB (profiler yardstick)")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),

@@ -24,6 +24,13 @@ Two commands:
       The launch's read traffic from L2-to-DRAM and L1-to-L2 read-request
       counters of one ``rocprofv3 --pmc`` run, each calibrated on the run's
       device copy: a second figure beside FETCH_SIZE's.
+
+  python -m quantized_paged_kv_02_amd.profile_summary clock <dir> --kernels REGEX
+        --command CMD --out FILE
+      Effective engine clock per dispatch of the kernels matching REGEX from
+      a ``rocprofv3 --pmc GRBM_GUI_ACTIVE`` run: the counter (GPU-active
+      cycles, summed over the agent's XCDs) / the XCD count / the dispatch's
+      duration, in dispatch order with the idle gap before each.
 """
 
 from __future__ import annotations
@@ -34,6 +41,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -238,6 +246,39 @@ def crosscheck(directory: str, workload: str, copy_mib: int, command: str, out: 
     print(f"wrote {out}: " + ", ".join(f"{k} {v / 1e6:.2f} MB" for k, v in figures.items()))
 
 
+def clock(directory: str, kernels: str, command: str, out: str) -> None:
+    """Per-dispatch durations and effective clocks (see the module notes)."""
+    agents = list(csv.DictReader(open(_find(directory, "agent_info.csv"))))
+    gpu = next(a for a in agents if a.get("Name", "").startswith("gfx"))
+    xcc = int(gpu["Num_Xcc"])
+    peak = float(gpu["Max_Engine_Clk_Fcompute"]) / 1e3
+    rows = [r for r in csv.DictReader(open(_find(directory, "counter_collection.csv")))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and re.search(kernels, r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# Engine clock per dispatch", "", f"Command: `{command}`", "",
+             f"Kernels matching `{kernels}`, in dispatch order.  Clock = GRBM_GUI_ACTIVE "
+             f"(summed over the {xcc} XCDs) / {xcc} / duration; the agent's maximum "
+             f"engine clock is {peak:.2f} GHz.  Gap: idle time since the previous "
+             "listed dispatch ended.", "",
+             "| # | kernel | gap us | duration us | clock GHz |", "|---|---|---|---|---|"]
+    prev = None
+    clocks, durs = [], []
+    for i, r in enumerate(rows):
+        s0, e0 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        ghz = float(r["Counter_Value"]) / xcc / (e0 - s0)
+        gap = (s0 - prev) / 1e3 if prev is not None else 0.0
+        prev = e0
+        clocks.append(ghz)
+        durs.append((e0 - s0) / 1e3)
+        lines.append(f"| {i} | `{_short(r['Kernel_Name'])}` | {gap:.1f} | "
+                     f"{(e0 - s0) / 1e3:.1f} | {ghz:.3f} |")
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}: {len(rows)} dispatches, clock {min(clocks):.2f} .. {max(clocks):.2f} "
+          f"GHz, duration {min(durs):.1f} .. {max(durs):.1f} us")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -269,7 +310,15 @@ def main(argv=None):
     c.add_argument("--copy-mib", type=int, default=1024)
     c.add_argument("--command", required=True)
     c.add_argument("--out", required=True)
+    k = sub.add_parser("clock")
+    k.add_argument("dir")
+    k.add_argument("--kernels", required=True, help="regular expression on kernel names")
+    k.add_argument("--command", required=True)
+    k.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "clock":
+        clock(a.dir, a.kernels, a.command, a.out)
+        return 0
     if a.cmd == "crosscheck":
         crosscheck(a.dir, a.workload, a.copy_mib, a.command, a.out)
         return 0
