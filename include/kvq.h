@@ -28,8 +28,8 @@
  *    ([intelli] §6 Q1; [oh-bug] section "为什么长上下文更需要 KV Cache
  *    Quantization").
  *
- *  - An unquantized FP16 cache through the same kernels, the baseline of
- *    the memory / latency comparison ([intelli] §5).
+ *  - An unquantized FP16 or BF16 cache through the same kernels, the
+ *    baseline of the memory / latency comparison ([intelli] §5).
  *  - An asymmetric INT4 KIVI cache (the affine form with integer zero
  *    points of [oh-bug] section "量化不是简单'截断精度'") and static-scale
  *    calibration from calibration tokens ([yunthe] section "配置与启动参数").
@@ -154,7 +154,9 @@
  * models).  Byte offsets, chunk size and the absent scales are those of
  * KVQ_FP16.  Every 16-bit input of the calls that take one (q, k_new, v_new)
  * is then bf16; scores use bf16 products with fp32 sums and the softmax
- * weights of the value product are rounded to bf16 (fp16 for KVQ_FP16).
+ * weights enter the value product as two bf16 terms, hi = bf16(p) and
+ * lo = bf16(p - hi), about 16 significant bits (KVQ_FP16: one fp16 term, 11
+ * bits), so both meet the same output tolerance.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -206,7 +208,7 @@ typedef enum kvq_granularity {
  *    unequal length leave no workgroup short of work ([oh-bug] section
  *    "为什么长上下文更需要 KV Cache Quantization": each step streams each
  *    row's whole history).  A range that crosses rows leaves one partial per
- *    row segment; the merge launch always runs.  INT8, FP8 and FP16 caches,
+ *    row segment; the merge launch always runs.  INT8, FP8, FP16 and BF16 caches,
  *    batch <= 256; split_tokens is unused.  Results equal the per-row
  *    partitions' up to the order of the fp32 sums. */
 typedef enum kvq_partition {
@@ -471,8 +473,9 @@ kvq_status kvq_paged_decode_mq(const kvq_layout *layout, const kvq_cache *cache,
  *   workspace    : device buffer of kvq_calibrate_workspace_bytes(layout,
  *                  n_tokens) bytes, 256-byte aligned; contents need no
  *                  initialisation.
- * Two launches on `stream`.  Errors: KVQ_ERR_UNSUPPORTED for INT4 and FP16
- * caches (no static scales) or more than 256 KV heads; KVQ_ERR_INVALID_ARG
+ * Two launches on `stream`.  Errors: KVQ_ERR_UNSUPPORTED for the KIVI
+ * (INT4, affine INT4, 2-bit), FP16 and BF16 caches (no static scales) or
+ * more than 256 KV heads; KVQ_ERR_INVALID_ARG
  * for n_tokens < 0 or a missing pointer of a calibrated tensor;
  * KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE as elsewhere.  n_tokens == 0 does
  * nothing. */
