@@ -431,5 +431,47 @@ __device__ __forceinline__ void append_token(const WriteArgs &a, int i, int h, i
   vb[4] = (uint16_t)(vp >> 16);
 }
 
+// Store the new tokens of row b, head h that stay in the fp16 window and
+// fall in its x-th position quad (positions 4q .. 4q+3, q counted from the
+// quad of the first such token; ring slots 4q % RING .. +3, contiguous as
+// RING is a multiple of 4).  One wavefront, lane l: channels 2l and 2l + 1.
+// A V ring row holds a quad's four tokens per channel, so each lane writes
+// its two channels' four tokens as one 16-byte unit, merged with the
+// slots' current contents where the quad is only partly new.  One
+// workgroup per quad: no other workgroup of the launch touches its slots.
+__device__ __forceinline__ void append_quad(const WriteArgs &a, int x, int h, int b, int lane) {
+  const int H = a.num_kv_heads;
+  int c_begin, n_new;
+  new_tokens(a, b, c_begin, n_new);
+  if (n_new <= 0) return;
+  const int s_new = a.seq_lens[b];
+  const int s_old = s_new - n_new;
+  const int lo = max(s_old, kivi_len(s_new, a.residual));  // first position kept in fp16
+  if (lo >= s_new) return;
+  const int p0 = 4 * (lo / 4 + x);
+  if (p0 >= s_new) return;
+  const size_t ring_row = (size_t)b * H + h;
+  const int slot0 = p0 % a.ring;
+  uint16_t *vq = a.v_resid + ((ring_row * (a.ring / 4) + slot0 / 4) * kHeadDim + 2 * lane) * 4;
+  // dwords: channel 2l tokens (0, 1), (2, 3); channel 2l + 1 tokens (0, 1), (2, 3)
+  u32x4 vw = {0u, 0u, 0u, 0u};
+  if (p0 < lo || p0 + 3 >= s_new) vw = ld16(vq);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pos = p0 + e;
+    if (pos < lo || pos >= s_new) continue;
+    const size_t src = ((size_t)(c_begin + pos - s_old) * H + h) * kHeadDim + 2 * lane;
+    const uint32_t kp = *reinterpret_cast<const uint32_t *>(a.k_new + src);
+    const uint32_t vp = *reinterpret_cast<const uint32_t *>(a.v_new + src);
+    *reinterpret_cast<uint32_t *>(a.k_resid + (ring_row * a.ring + slot0 + e) * kHeadDim +
+                                  2 * lane) = kp;
+    const int sh = 16 * (e & 1);
+    const uint32_t keep = ~(0xFFFFu << sh);
+    vw[e >> 1] = (vw[e >> 1] & keep) | ((vp & 0xFFFFu) << sh);
+    vw[2 + (e >> 1)] = (vw[2 + (e >> 1)] & keep) | ((vp >> 16) << sh);
+  }
+  *reinterpret_cast<u32x4 *>(vq) = vw;
+}
+
 }  // namespace
 }  // namespace kvq

@@ -397,15 +397,12 @@ __global__ __launch_bounds__(256) void kvq_int4_flush_kernel(WriteArgs a) {
   int4_flush<DT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
-// Workgroup x appends the row's new token n_new - 1 - x: a row keeps at
-// most ring - 1 tokens in fp16 (S - nq(S) < R + G), so only the last
-// min(n_new, ring) new tokens can land in the ring.
+// Workgroup x stores the row's new fp16-window tokens in the x-th position
+// quad they occupy (append_quad): a row keeps at most ring - 1 tokens in
+// fp16 (S - nq(S) < R + G), so at most min(n_new, ring - 1) new tokens, in
+// at most (min(n_new, ring) + 3) / 4 + 1 quads, land in the ring.
 __global__ __launch_bounds__(64) void kvq_int4_append_kernel(WriteArgs a) {
-  int c_begin, n_new;
-  new_tokens(a, blockIdx.z, c_begin, n_new);
-  const int i = n_new - 1 - (int)blockIdx.x;
-  if (i < 0) return;
-  append_token(a, i, blockIdx.y, blockIdx.z, threadIdx.x);
+  append_quad(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
 // Flush and append in one launch: workgroups x < 2*groups flush, the rest
@@ -492,8 +489,9 @@ hipError_t launch_write_int4(const WriteArgs &a, int dtype, int batch, int max_n
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kvq_int4_append_kernel,
-                     dim3(max_new < a.ring ? max_new : a.ring, a.num_kv_heads, batch), dim3(64),
-                     0, stream, a);
+                     dim3(((max_new < a.ring ? max_new : a.ring) + 3) / 4 + 1, a.num_kv_heads,
+                          batch),
+                     dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
