@@ -58,6 +58,15 @@
  *    tables must lie in [0, num_blocks): an id outside is an out-of-bounds
  *    access.  kvq_check_tables checks host copies of both.
  *  - Non-finite K/V inputs give unspecified codes.
+ *  - Numerics of the decode: fp16 (bf16 for a BF16 cache) matrix operands
+ *    with fp32 accumulation and an fp32 softmax.  Every finite V is safe:
+ *    the running maximum lags a score by at most log2(65504 / s) for the
+ *    largest per-token V scale s the format can hold, so weights times V
+ *    scales stay finite in fp16.  Per-channel K scales (KIVI groups, static
+ *    per-channel INT8/FP8) are folded into the query: |q_c| * s_c must stay
+ *    below 65504 (e.g. KIVI K values up to 1000 with |q_c| < 450).  The
+ *    absolute error of an output scales with the magnitude of the values it
+ *    averages (fp16 operand rounding, ~2^-11 relative).
  *
  * One kvq_cache describes ONE layer.  Shapes below use
  *   NB = num_blocks, H = num_kv_heads, Hq = num_q_heads, D = head_dim = 128,

@@ -76,6 +76,17 @@ constexpr float kNegInf = -__builtin_inff();
 // The running max is only moved when a score exceeds it by more than this
 // (log2 units), so p <= 2^8 and rescaling of o is rare.
 constexpr float kRescaleSlack = 8.0f;
+// Where the weights are multiplied by a per-token V scale sigma before the
+// fp16 operand is formed, the lag is bounded so that 2^slack * sigma stays
+// below 65504 for every scale finite fp16 values can give: INT8 per token
+// sigma <= 65504 / 127 (slack 6), INT4 <= 65504 / 7 and affine INT4
+// <= 2 * 65504 / 15 (slack 2), 2-bit <= 2 * 65504 / 3 (slack 0.5).  E4M3
+// (<= 65504 / 448) and E5M2 (times 2^7, <= 65504 / 448 as well) fit under
+// kRescaleSlack.  Measured on the KIVI shape: the 2-bit launch ~1 % slower
+// with the tight bound (more frequent rescales), INT4 within noise.
+constexpr float kSlackInt8Token = 6.0f;
+constexpr float kSlackInt4 = 2.0f;
+constexpr float kSlackInt2 = 0.5f;
 
 struct Softmax {
   float m;     // running max (log2 domain), same on the 4 lanes of a head
@@ -122,11 +133,12 @@ __device__ __forceinline__ void softmax_init(Softmax &st) {
 // Fold the scores of two blocks (4 tokens each per lane, log2 domain,
 // masked = -inf) into the running state; returns p relative to the new max.
 __device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, const f32x4 &s1,
-                                               f32x4 &p0, f32x4 &p1) {
+                                               f32x4 &p0, f32x4 &p1,
+                                               float slack = kRescaleSlack) {
   float bm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
   bm = max_over_quads(bm);
-  const bool need = bm > st.m + kRescaleSlack;
+  const bool need = bm > st.m + slack;
   if (__any(need)) {
     const float mn = need ? bm : st.m;
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
@@ -148,13 +160,14 @@ __device__ __forceinline__ void softmax_update(Softmax &st, const f32x4 &s0, con
 
 // The same for four blocks at once (one max and one rescale decision).
 __device__ __forceinline__ void softmax_update4(Softmax &st, f32x4 (&vb)[2],
-                                                const f32x4 (&s)[4], f32x4 (&p)[4]) {
+                                                const f32x4 (&s)[4], f32x4 (&p)[4],
+                                                float slack) {
   float bm = kNegInf;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     bm = fmaxf(bm, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
   bm = max_over_quads(bm);
-  const bool need = bm > st.m + kRescaleSlack;
+  const bool need = bm > st.m + slack;
   if (__any(need)) {
     const float mn = need ? bm : st.m;
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
@@ -368,7 +381,8 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
     }
   }
   f32x4 p0, p1;
-  softmax_update(st, s[0], s[1], p0, p1);
+  softmax_update(st, s[0], s[1], p0, p1,
+                 VS == kToken && DT == kInt8 ? kSlackInt8Token : kRescaleSlack);
   if constexpr (VS == kToken) {
     constexpr float boost = operand_boost<DT>();  // removed from o at the end
 #pragma unroll
@@ -906,7 +920,7 @@ __device__ __forceinline__ void compute_group4(Softmax &st, f32x4 (&vb)[2], cons
   f32x4 pg[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] *= qk_scale;
-  softmax_update4(st, vb, acc, pg);
+  softmax_update4(st, vb, acc, pg, kSlackInt4);
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
     const f32x4 &p0 = pg[2 * pr], &p1 = pg[2 * pr + 1];
@@ -1094,7 +1108,7 @@ __device__ __forceinline__ void compute_group2(Softmax &st, f32x4 (&vb)[2], cons
   f32x4 pg[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] *= qk_scale;
-  softmax_update4(st, vb, acc, pg);
+  softmax_update4(st, vb, acc, pg, kSlackInt2);
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
     const f32x4 &p0 = pg[2 * pr], &p1 = pg[2 * pr + 1];
@@ -1231,11 +1245,11 @@ __device__ __forceinline__ float all_banks(float x) {
 // score exceeds it by more than the slack; only then is the head-wide max
 // taken (over the four banks and the four row groups).
 __device__ __forceinline__ void softmax_update_c(Softmax &st, f32x4 (&vb)[4], const f32x4 &s,
-                                                 f32x4 &p) {
+                                                 f32x4 &p, float slack) {
   const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  if (__any(lm > st.m + kRescaleSlack)) {
+  if (__any(lm > st.m + slack)) {
     const float bm = max_over_quads(bank_max(lm));
-    const bool need = bm > st.m + kRescaleSlack;
+    const bool need = bm > st.m + slack;
     const float mn = need ? bm : st.m;
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
     st.l *= alpha;
@@ -1344,7 +1358,7 @@ __device__ __forceinline__ void compute_group4c(Softmax &st, f32x4 (&vb)[4], con
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
-  softmax_update_c(st, vb, s, p);
+  softmax_update_c(st, vb, s, p, kSlackInt4);
   // weights times the V scales of this lane's tokens (channel groups 0, 1)
   // tokens 2, 3 of every 4 meet value codes stored as 1152 + 16 code
   const float p2 = p[2] * 0.0625f, p3 = p[3] * 0.0625f;
@@ -1500,7 +1514,7 @@ __device__ __forceinline__ void compute_group2c(Softmax &st, f32x4 (&vb)[4], con
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = (s[i] - off) * qk_scale;
   f32x4 p;
-  softmax_update_c(st, vb, s, p);
+  softmax_update_c(st, vb, s, p, kSlackInt2);
   // weights times the V scales of this lane's tokens (channel groups 0, 1)
   const uint32_t d0[2] = {pack_rne(p[0] * t.vsa[0], p[1] * t.vsa[2]),
                           pack_rne(p[2] * t.vsb[0], p[3] * t.vsb[2])};

@@ -75,13 +75,15 @@ def fill_garbage(cache):
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
              table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
-             n_query=0, host_plan=False, partition="per-row", device="cuda"):
+             n_query=0, host_plan=False, partition="per-row", device="cuda", kv=None, q=None):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
     step instead of by kvq_write before kvq_paged_decode.  ``host_plan``:
     partition as bench.py does, from the rows' lengths on the host
-    (kvq_plan_split_tokens), instead of ``split_tokens``."""
+    (kvq_plan_split_tokens), instead of ``split_tokens``.  ``kv``: the rows'
+    (K, V) device tensors [S, H, 128] instead of the workload's draws; ``q``:
+    the queries [B, Hq, 128] likewise."""
     from quantized_paged_kv_02_amd import kvq
     lens = np.asarray(lens, np.int32)
     b = len(lens)
@@ -97,7 +99,7 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         layout.partition = kvq.plan_partition(layout, lens)
     ks, vs = [], []
     for r in range(b):
-        k, v = inputs.gen_kv(w, layer, r, int(lens[r]), device, seed)
+        k, v = kv[r] if kv is not None else inputs.gen_kv(w, layer, r, int(lens[r]), device, seed)
         ks.append(k)
         vs.append(v)
     prefill_k = [k[:max(int(s) - 1, 0)] for k, s in zip(ks, lens)]
@@ -146,7 +148,8 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         nbytes = kvq.paged_decode_mq_workspace_bytes(layout, n_query, b, max_len)
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
     else:
-        q = inputs.gen_q(w, layer, device, seed, batch=b)
+        if q is None:
+            q = inputs.gen_q(w, layer, device, seed, batch=b)
         out = torch.full((b, w.num_q_heads, 128), float("nan"), dtype=torch.float32,
                          device=device)
         ws = kvq.alloc_workspace(layout, b, max_len, device)
