@@ -64,7 +64,8 @@
  *    largest per-token V scale s the format can hold, so weights times V
  *    scales stay finite in fp16.  Per-channel K scales (KIVI groups, static
  *    per-channel INT8/FP8) are folded into the query: |q_c| * s_c must stay
- *    below 65504 (e.g. KIVI K values up to 1000 with |q_c| < 450).  The
+ *    below 65504 (e.g. K values within +-1000 and |q_c| < 450 for
+ *    symmetric INT4, |q_c| < 98 for 2-bit affine groups).  The
  *    absolute error of an output scales with the magnitude of the values it
  *    averages (fp16 operand rounding, ~2^-11 relative).
  *
