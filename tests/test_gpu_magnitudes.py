@@ -14,6 +14,9 @@ weight times the scale), so the absolute error scales with the values: the
 pages' atol 2e-3 is taken relative to max |v| of the row (2e-3 * max|v|),
 with the same rtol 1e-2.  At these magnitudes the fp16 rounding of the
 inputs themselves (a spacing of 32 near 60000) is far coarser.
+
+test_degenerate_rows: a zero query, an all-zero row (zero scales and
+codes) and V constant over the tokens, per format, split and unsplit.
 """
 
 import math
@@ -87,3 +90,66 @@ def test_large_values_after_score_jump(dtype, kg, vg, hq):
         assert (err <= bound).all(), (f"row {r}: max abs err {err.max():.3e} "
                                       f"(max |v| {vmax:.0f}), ratio {(err / bound).max():.3f}")
     print(f"{w.name}: max err / tolerance {ratio:.3f}", flush=True)
+
+
+# --- degenerate inputs with closed forms
+
+DEGENERATE = [("int8", "token", "token", 8), ("int8", "channel", "head", 8),
+              ("fp8", "token", "token", 8), ("fp8e5m2", "tensor", "token", 8),
+              ("int4", "channel", "token", 8), ("int4", "channel", "token", 16),
+              ("int4-affine", "channel", "token", 8), ("int2-affine", "channel", "token", 8),
+              ("int2-affine", "channel", "token", 16), ("fp16", "none", "none", 8),
+              ("bf16", "none", "none", 8)]
+
+
+def _degenerate_rows(w, lens, seed):
+    """Row 0: zero query (every score 0: the output is the mean of the
+    dequantized values).  Row 1: K and V all zero (zero scales and codes:
+    output 0).  Row 2: V the same vector at every token (output that vector
+    as dequantized).  Other entries N(0, 1)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(inputs.derive_seed(seed, "degenerate"))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    h = w.num_kv_heads
+    rows = []
+    for r, s in enumerate(lens):
+        k = torch.randn((s, h, 128), generator=g)
+        v = torch.randn((s, h, 128), generator=g)
+        if r == 1:
+            k.zero_()
+            v.zero_()
+        if r == 2:
+            v[:] = torch.randn((1, h, 128), generator=g)
+        rows.append((k.to(dt).cuda(), v.to(dt).cuda()))
+    q = torch.randn((len(lens), w.num_q_heads, 128), generator=g)
+    q[0] = 0.0
+    return rows, q.to(dt).cuda()
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("dtype,kg,vg,hq", DEGENERATE)
+def test_degenerate_rows(dtype, kg, vg, hq, split):
+    w = inputs.scaled_down(W["tiny"], name=f"deg-{dtype}-{kg}-{vg}-{hq}", batch=3,
+                           num_q_heads=hq, num_kv_heads=2, dtype=dtype, k_gran=kg, v_gran=vg,
+                           channel_outliers=())
+    lens = [600, 400, 333]
+    kv, q = _degenerate_rows(w, lens, seed=5)
+    res = run_case(w, lens, split_tokens=split, kv=kv, q=q, decode_twice=True)
+    assert np.all(np.isfinite(res.out)), "non-finite outputs"
+    assert np.array_equal(res.out, res.out2), "decode is not bitwise reproducible"
+    for r in range(len(lens)):
+        want = oracle_row(res, r)
+        err = np.abs(res.out[r].astype(np.float64) - want)
+        assert np.all(err <= 2e-3 + 1e-2 * np.abs(want)), f"row {r}: max abs err {err.max():.3e}"
+    # closed forms, independent of the oracle's attention: an all-zero row
+    # gives exactly zero; for the 16-bit caches (values stored as given) a
+    # zero query averages V uniformly and a V constant over tokens is the
+    # output itself
+    assert np.all(res.out[1] == 0.0), "row 1 (all zero): output not exactly zero"
+    if dtype in ("fp16", "bf16"):
+        g = hq // w.num_kv_heads
+        for hh in range(hq):
+            v0 = res.v[0][:, hh // g, :].astype(np.float64)
+            assert np.allclose(res.out[0][hh], v0.mean(axis=0), atol=2e-3, rtol=1e-2), hh
+            v2 = res.v[2][0, hh // g, :].astype(np.float64)
+            assert np.allclose(res.out[2][hh], v2, atol=2e-3, rtol=1e-2), hh
