@@ -65,9 +65,13 @@
  *    scales stay finite in fp16.  Per-channel K scales (KIVI groups, static
  *    per-channel INT8/FP8) are folded into the query: |q_c| * s_c must stay
  *    below 65504 (e.g. K values within +-1000 and |q_c| < 450 for
- *    symmetric INT4, |q_c| < 98 for 2-bit affine groups).  The
- *    absolute error of an output scales with the magnitude of the values it
- *    averages (fp16 operand rounding, ~2^-11 relative).
+ *    symmetric INT4, |q_c| < 98 for 2-bit affine groups).  The softmax
+ *    weights (times per-token V scales) enter the value product as a pair
+ *    of fp16 terms, hi and the rounded remainder (~22 significant bits), for
+ *    the FP16 cache and the INT8/FP8 per-token V scales, and as one fp16
+ *    term (11 bits) for static V scales and the KIVI formats.  The absolute
+ *    error of an output scales with the magnitude of the values it
+ *    averages.
  *
  * One kvq_cache describes ONE layer.  Shapes below use
  *   NB = num_blocks, H = num_kv_heads, Hq = num_q_heads, D = head_dim = 128,
@@ -165,8 +169,8 @@
  * KVQ_FP16.  Every 16-bit input of the calls that take one (q, k_new, v_new)
  * is then bf16; scores use bf16 products with fp32 sums and the softmax
  * weights enter the value product as two bf16 terms, hi = bf16(p) and
- * lo = bf16(p - hi), about 16 significant bits (KVQ_FP16: one fp16 term, 11
- * bits), so both meet the same output tolerance.
+ * lo = bf16(p - hi), about 16 significant bits (KVQ_FP16: two fp16 terms,
+ * about 22 bits), so both meet the same output tolerance.
  */
 #ifndef KVQ_H
 #define KVQ_H

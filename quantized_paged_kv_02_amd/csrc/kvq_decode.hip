@@ -195,6 +195,19 @@ __device__ __forceinline__ f16x8 p_operand(const f32x4 &p0, const f32x4 &p1) {
                (f16)p1[0], (f16)p1[1], (f16)p1[2], (f16)p1[3]};
 }
 
+// The same weights as two fp16 terms, hi = fp16(p) and lo = fp16(p - hi)
+// (p - hi is exact in fp32): about 22 significant bits where one term keeps
+// 11, for a second value product per tile.
+__device__ __forceinline__ void p_operand_hilo(const f32x4 &p0, const f32x4 &p1, f16x8 &hi,
+                                               f16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = i < 4 ? p0[i] : p1[i - 4];
+    hi[i] = (f16)p;
+    lo[i] = (f16)(p - (float)hi[i]);
+  }
+}
+
 // BF16 caches: 16-bit operands carried in f16x8 containers hold bf16 bits.
 // bf16 keeps 8 significant bits, fp16 11: the weights go to the value
 // product as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi) (p - hi is
@@ -393,7 +406,11 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
       if (TAIL && 16 + 4 * qd + r >= valid_s) p1[r] = 0.0f;
     }
   }
-  const f16x8 pb = p_operand(p0, p1);
+  // per-token V scales: the weights as a hi + lo pair (a second value
+  // product per tile); otherwise one fp16 term
+  f16x8 pb, pl;
+  if constexpr (VS == kToken) p_operand_hilo(p0, p1, pb, pl);
+  else pb = p_operand(p0, p1);
   if (TAIL) {
     // zero the codes of tokens past the end (their bytes may be stale or NaN)
     const int v0 = valid_v - 4 * qd, v1 = valid_v - 16 - 4 * qd;
@@ -410,6 +427,7 @@ __device__ __forceinline__ void compute_pair8(Softmax &st, Pair8 &t, const f16x8
     const f16x8 av = cat(codes4_to_f16<DT>(t.v[0][j >> 2][j & 3]),
                          codes4_to_f16<DT>(t.v[1][j >> 2][j & 3]));
     st.o[j] = mfma32(av, pb, st.o[j]);
+    if constexpr (VS == kToken) st.o[j] = mfma32(av, pl, st.o[j]);
   }
 }
 
@@ -470,7 +488,7 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
   softmax_update(st, s[0], s[1], p0, p1);
   f16x8 pb, pl;
   if constexpr (BF) p_operand_bf16(p0, p1, pb, pl);
-  else pb = p_operand(p0, p1);
+  else p_operand_hilo(p0, p1, pb, pl);
   if (TAIL) {
     // zero the values of unattended tokens (stale, possibly NaN): dword w
     // of a quarter holds tokens 2(w&1), 2(w&1)+1 of the lane's four
@@ -487,7 +505,7 @@ __device__ __forceinline__ void compute_pair16(Softmax &st, Pair16 &t, const f16
   for (int j = 0; j < 8; ++j) {
     const f16x8 v = value_operand16(t, j);
     st.o[j] = mma(v, pb, st.o[j]);
-    if constexpr (BF) st.o[j] = mma(v, pl, st.o[j]);
+    st.o[j] = mma(v, pl, st.o[j]);
   }
 }
 

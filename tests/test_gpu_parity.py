@@ -280,7 +280,7 @@ def test_balanced_partitions(dtype, kg, vg, table, fused, hkv):
 
 def test_balanced_matches_per_row_closely():
     # the same attention; the partitions' running maxima differ, so the
-    # softmax weights round to fp16 differently (2^-11 relative each)
+    # weights' fp16 operands round differently
     w = _small("int8", "token", "token", hq=16, hkv=4, table="shuffled")
     a = run_case(w, BAL_LENS, partition="balanced", split_tokens=0)
     b = run_case(w, BAL_LENS, partition="per-row", split_tokens=64)
