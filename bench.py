@@ -734,7 +734,8 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        # the matrix products' operand type (fp32 accumulation and softmax)
+        "dtype": "bf16" if w.dtype == "bf16" else "f16",
         "data": "synthetic",
         "tokens_per_s": round(b * max(args.n_query, 1) / (ms * 1e-3), 2),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
