@@ -75,7 +75,8 @@ def fill_garbage(cache):
 
 def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=None,
              table=None, garbage=True, decode_twice=False, fused=False, repeats=0,
-             n_query=0, host_plan=False, partition="per-row", device="cuda", kv=None, q=None):
+             n_query=0, host_plan=False, partition="per-row", device="cuda", kv=None, q=None,
+             compact_pools=False):
     """Write rows of lengths ``lens`` (prefill of S-1 tokens in ``chunks``
     calls, then one decode token) and run one decode step.  ``fused``: the
     decode token is written by kvq_write_decode together with the decode
@@ -83,7 +84,9 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
     partition as bench.py does, from the rows' lengths on the host
     (kvq_plan_split_tokens), instead of ``split_tokens``.  ``kv``: the rows'
     (K, V) device tensors [S, H, 128] instead of the workload's draws; ``q``:
-    the queries [B, Hq, 128] likewise."""
+    the queries [B, Hq, 128] likewise.  ``compact_pools``: copy to the host
+    only the blocks the table names (gathered on the device, the table
+    renumbered to match), for pools too large to copy whole."""
     from quantized_paged_kv_02_amd import kvq
     lens = np.asarray(lens, np.int32)
     b = len(lens)
@@ -180,9 +183,21 @@ def run_case(w: inputs.Workload, lens, seed=0, layer=0, split_tokens=0, chunks=N
         kvq.paged_decode(cache, q, table_t, lens_t, max_len, scale, o, ws)
         rep_outs.append(o)
     torch.cuda.synchronize()
-    pools = {name: _np(getattr(cache, name))
-             for name in ("k_codes", "v_codes", "k_scales", "v_scales")
-             if getattr(cache, name) is not None}
+    if compact_pools:
+        # block-major arrays: codes always, scales when per token or KIVI
+        used = np.unique(table)
+        idx = torch.as_tensor(used.astype(np.int64), device=device)
+        major = {"k_codes": True, "v_codes": True,
+                 "k_scales": w.dtype in KIVI or w.k_gran == "token",
+                 "v_scales": w.dtype in KIVI or w.v_gran == "token"}
+        pools = {name: _np(getattr(cache, name).index_select(0, idx) if bm
+                           else getattr(cache, name))
+                 for name, bm in major.items() if getattr(cache, name) is not None}
+        table = np.searchsorted(used, table).astype(np.int32)
+    else:
+        pools = {name: _np(getattr(cache, name))
+                 for name in ("k_codes", "v_codes", "k_scales", "v_scales")
+                 if getattr(cache, name) is not None}
     if cache.k_resid is not None:
         pools["k_resid"] = cache.k_resid.cpu().numpy()
         pools["v_resid"] = cache.v_resid.cpu().numpy()
