@@ -47,6 +47,9 @@
  *    returns KVQ_ERR_HIP (the HIP error state is cleared before launching).
  *  - Device pointers must be 16-byte aligned; fp16 data is IEEE binary16
  *    passed as uint16_t; fp32 is IEEE binary32.
+ *  - Pool arrays may be of any size the device holds (byte offsets are
+ *    formed in 64 bits; a layer's code arrays may pass 4 GiB); block ids
+ *    and num_blocks are int32.
  *  - Host integers (batch, total_new, max_new_per_seq, max_seq_len) size the
  *    grids, because seq_lens lives on the device; they must bound the device
  *    values: seq_lens[b] <= max_seq_len for every row b of a decode
