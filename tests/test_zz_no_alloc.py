@@ -6,8 +6,9 @@ It must give what kvq_write_decode gives on the same inputs, bit for bit
 device, the second smaller than the first (fewer rows, shorter rows,
 another format), so the second runs over the partials the first left in
 the shared array.  Both calls are split into several partitions per row,
-so the partials are really used.  A call whose partials would not fit is
-rejected on the host.
+so the partials are really used.  Three more calls in a row cover the
+2-bit KIVI, BF16 and FP8 E5M2 paths.  A call whose partials would not fit
+is rejected on the host.
 """
 
 import math
@@ -100,6 +101,22 @@ def test_noalloc_matches_write_decode_twice():
                             num_kv_heads=2, dtype="int4", k_gran="channel", v_gran="token",
                             channel_outliers=(8, 10.0, "k"))
     _both(w2, [500, 383, 300], 64)
+
+
+def test_noalloc_other_formats_in_a_row():
+    # 2-bit KIVI (compact layout), then a BF16 cache, then FP8 E5M2 per
+    # token, each smaller than the one before and each over the partials the
+    # previous call left in the array
+    w3 = inputs.scaled_down(W["tiny"], name="noalloc-int2", batch=4, num_q_heads=8,
+                            num_kv_heads=2, dtype="int2-affine", k_gran="channel",
+                            v_gran="token")
+    _both(w3, [900, 450, 700, 333], 128)
+    w4 = inputs.scaled_down(W["tiny"], name="noalloc-bf16", batch=3, num_q_heads=16,
+                            num_kv_heads=2, dtype="bf16", k_gran="none", v_gran="none")
+    _both(w4, [800, 500, 257], 64)
+    w5 = inputs.scaled_down(W["tiny"], name="noalloc-e5m2", batch=2, num_q_heads=8,
+                            num_kv_heads=2, dtype="fp8e5m2", k_gran="token", v_gran="token")
+    _both(w5, [400, 130], 32)
 
 
 def test_noalloc_rejects_partials_beyond_the_array():
