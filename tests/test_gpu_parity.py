@@ -292,3 +292,25 @@ def test_balanced_multi_query(n_query):
     w = _small("int8", "token", "token", hq=8, hkv=2, table="shuffled")
     res = run_case(w, [3, 1000, 40, 1], partition="balanced", n_query=n_query)
     check_rows(res)
+
+
+# Query groups that are not powers of two: the score tiles carry g live
+# columns of 16 (8-bit and 16-bit caches, generic INT4 layout) or of 4
+# (compact INT4 layout, g = 3), the rest zero queries whose outputs are
+# never written.
+ODD_GROUP_FORMATS = [("int8", "token", "token"), ("fp8", "head", "head"),
+                     ("fp8e5m2", "tensor", "token"), ("int8", "channel", "tensor"),
+                     ("fp16", "none", "none"), ("bf16", "none", "none"),
+                     ("int4", "channel", "token"), ("int4-affine", "channel", "token"),
+                     ("int2-affine", "channel", "token")]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("g", [3, 5, 6, 7])
+@pytest.mark.parametrize("dtype,kg,vg", ODD_GROUP_FORMATS)
+def test_odd_query_groups(dtype, kg, vg, g, fused):
+    w = _small(dtype, kg, vg, hq=2 * g, hkv=2, table="shuffled",
+               channel_outliers=(8, 10.0, "k"))
+    res = run_case(w, [300, 700, 65], split_tokens=128, fused=fused, decode_twice=True)
+    check_rows(res)
+    assert np.array_equal(res.out, res.out2)
