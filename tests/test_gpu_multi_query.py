@@ -51,3 +51,21 @@ def test_single_query_equals_decode(dtype, kg, vg):
     one = run_case(w, lens, split_tokens=64, n_query=1)
     dec = run_case(w, lens, split_tokens=64)
     assert np.array_equal(one.out[:, 0].view(np.uint32), dec.out.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype,kg,vg", FORMATS)
+@pytest.mark.parametrize("n_query,hq,hkv", [(3, 3, 1), (5, 6, 2), (7, 4, 2), (3, 5, 5),
+                                            (2, 14, 2), (5, 3, 3)])
+@pytest.mark.parametrize("split", [0, 64])
+def test_multi_query_odd_columns(dtype, kg, vg, n_query, hq, hkv, split):
+    # n_query x g score columns that are not powers of two (9, 15, 14, 3,
+    # 14, 5): column c is query token c / g of head c % g, each with its own
+    # causal mask
+    lens = [1, 4, 17, 31, 33, 300, 1000, 0]
+    res = run_case(_w(dtype, kg, vg, hq, hkv), lens, split_tokens=split, n_query=n_query)
+    assert res.out.shape == (len(lens), n_query, hq, 128)
+    check_rows(res, rows=[r for r, s in enumerate(lens) if s > 0])
+    for r, s in enumerate(lens):
+        for j in range(n_query):
+            if s - n_query + j < 0:
+                assert np.all(res.out[r, j] == 0), (r, j)
