@@ -294,6 +294,25 @@ def test_balanced_multi_query(n_query):
     check_rows(res)
 
 
+@pytest.mark.parametrize("dtype,kg,vg", [("int8", "token", "token"), ("fp8", "head", "head"),
+                                         ("fp8e5m2", "tensor", "token"),
+                                         ("fp16", "none", "none"), ("bf16", "none", "none")])
+@pytest.mark.parametrize("g,n_query", [(3, 1), (5, 1), (3, 3), (1, 5), (7, 2)])
+def test_balanced_odd_columns(dtype, kg, vg, g, n_query):
+    # balanced ranges with query groups and column counts (g x queries: 3,
+    # 5, 9, 5, 14) that are not powers of two
+    w = _small(dtype, kg, vg, hq=2 * g, hkv=2, table="shuffled")
+    res = run_case(w, BAL_LENS, partition="balanced", n_query=n_query if n_query > 1 else 0)
+    check_rows(res, rows=[r for r, s in enumerate(BAL_LENS) if s > 0])
+    if n_query > 1:
+        for r, s in enumerate(BAL_LENS):
+            for j in range(n_query):
+                if s - n_query + j < 0:
+                    assert np.all(res.out[r, j] == 0), (r, j)
+    else:
+        assert np.all(res.out[1] == 0)
+
+
 # Query groups that are not powers of two: the score tiles carry g live
 # columns of 16 (8-bit and 16-bit caches, generic INT4 layout) or of 4
 # (compact INT4 layout, g = 3), the rest zero queries whose outputs are
