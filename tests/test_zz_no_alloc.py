@@ -6,9 +6,9 @@ It must give what kvq_write_decode gives on the same inputs, bit for bit
 device, the second smaller than the first (fewer rows, shorter rows,
 another format), so the second runs over the partials the first left in
 the shared array.  Both calls are split into several partitions per row,
-so the partials are really used.  Three more calls in a row cover the
-2-bit KIVI, BF16 and FP8 E5M2 paths.  A call whose partials would not fit
-is rejected on the host.
+so the partials are really used.  Four more calls in a row cover the
+2-bit KIVI, BF16 and FP8 E5M2 paths and balanced partitions.  A call
+whose partials would not fit is rejected on the host.
 """
 
 import math
@@ -24,14 +24,14 @@ pytestmark = pytest.mark.gpu
 W = inputs.WORKLOADS
 
 
-def _prefilled(w, lens, split, layer=0):
+def _prefilled(w, lens, split, layer=0, partition="per-row"):
     """A cache holding the prefill (S-1 tokens) of rows ``lens`` plus the
     decode-step inputs."""
     from quantized_paged_kv_02_amd import kvq
     lens = np.asarray(lens, np.int32)
     table, nb = inputs.block_tables(w, lens)
     lay = kvq.make_layout(w.dtype, w.k_gran, w.v_gran, w.num_q_heads, w.num_kv_heads, nb,
-                          table.shape[1], split, w.residual_len)
+                          table.shape[1], split, w.residual_len, partition=partition)
     static = ("tensor", "head", "channel")
     ks = np.full(kvq.scale_shape(lay, lay.k_gran), 0.05, np.float32) \
         if w.k_gran in static and w.dtype not in ("int4", "fp16") else None
@@ -70,11 +70,11 @@ def _same_cache(a, b):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"cache.{name} differs"
 
 
-def _both(w, lens, split):
+def _both(w, lens, split, partition="per-row"):
     """kvq_write_decode and kvq_write_decode_noalloc from one prefilled
     cache; compares outputs and caches bit for bit."""
     from quantized_paged_kv_02_amd import kvq
-    lay, cache, step = _prefilled(w, lens, split)
+    lay, cache, step = _prefilled(w, lens, split, partition=partition)
     assert kvq.decode_workspace_bytes(lay, len(lens), step["max_seq_len"]) > 0, \
         "the case must use partials"
     other = _clone(cache)
@@ -117,6 +117,10 @@ def test_noalloc_other_formats_in_a_row():
     w5 = inputs.scaled_down(W["tiny"], name="noalloc-e5m2", batch=2, num_q_heads=8,
                             num_kv_heads=2, dtype="fp8e5m2", k_gran="token", v_gran="token")
     _both(w5, [400, 130], 32)
+    # balanced ranges (partials per row segment), over what the calls above left
+    w6 = inputs.scaled_down(W["tiny"], name="noalloc-balanced", batch=5, num_q_heads=6,
+                            num_kv_heads=2, table="shuffled")
+    _both(w6, [1, 900, 40, 333, 17], 0, partition="balanced")
 
 
 def test_noalloc_rejects_partials_beyond_the_array():
