@@ -102,6 +102,20 @@ def test_int4_residual_64_shuffled():
     check_rows(run_case(w, [63, 64, 65, 500], split_tokens=64))
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype", ["int4", "int4-affine", "int2-affine"])
+@pytest.mark.parametrize("residual", [256, 512])
+def test_kivi_long_residual_windows(residual, dtype, fused):
+    # fp16 windows of 256 and 512 tokens (rings of 320 and 576 slots): rows
+    # inside the window, one group past it, at the next group's first token
+    # and far past it, written in three chunks so the ring wraps between
+    # writes
+    w = _small(dtype, "channel", "token", residual_len=residual, table="shuffled",
+               channel_outliers=(8, 10.0, "k"))
+    lens = [residual - 1, residual + 64, residual + 65, 2000]
+    check_rows(run_case(w, lens, chunks=3, split_tokens=128, fused=fused))
+
+
 @pytest.mark.parametrize("chunks", [2, 5])
 def test_int8_chunked_writes(chunks):
     w = _small("int8", "token", "channel")
