@@ -1,5 +1,7 @@
 """Host-side measurement logic: the algorithmic byte model every roofline
-fraction divides by, and the rocprofv3 summaries (no GPU).
+fraction divides by, and the rocprofv3 summaries (decode durations from a
+kernel trace, HBM bytes from counters scaled on a copy, engine clocks) on
+synthetic traces (no GPU).
 
 The byte counts are written out here from the cache layouts (codes, scales,
 fp16 residual tokens, the fp16 queries read, the fp32 outputs written and
@@ -106,3 +108,61 @@ def test_clock_summary(tmp_path):
     assert cells[1][3:6] == ["100.0", "550.0", "2.000"]   # 100 us idle before it
     assert "2.40 GHz" in text and "8 XCDs" in text
     assert os.path.exists(out)
+
+
+def _trace_row(name, start_ns, dur_ns, grid, wg=256):
+    return {"Kernel_Name": name, "Start_Timestamp": str(start_ns),
+            "End_Timestamp": str(start_ns + dur_ns), "Grid_Size_X": str(grid),
+            "Workgroup_Size_X": str(wg)}
+
+
+def test_decode_times_from_a_trace():
+    """Decode dispatches with the launch's own grid, each followed by its
+    merge; a decode step's launch with extra flush workgroups (a larger
+    grid) and other kernels are left out."""
+    rows, t = [], 1_000_000
+    for dec_us, red_us in ((100.0, 5.0), (102.0, 4.0), (98.0, 6.0)):
+        rows.append(_trace_row("kvq::kvq_paged_decode_int4_kernel<3, true>", t, int(dec_us * 1e3),
+                               256 * 256))
+        t += int(dec_us * 1e3) + 2_000          # 2 us between decode and merge
+        rows.append(_trace_row("kvq::kvq_partition_reduce_kernel", t, int(red_us * 1e3), 16384))
+        t += int(red_us * 1e3) + 50_000
+    rows.append(_trace_row("kvq::kvq_paged_decode_int4_kernel<3, true>", t, 400_000,
+                           300 * 256))                       # flushing step: excluded
+    rows.append(_trace_row("at::native::fill", t + 500_000, 3_000, 1024))
+    got = profile_summary.decode_times(rows[::-1])           # order by start time
+    assert got["dispatches"] == 3 and got["decode_workgroups"] == 256
+    assert got["decode_us"] == pytest.approx(100.0)
+    assert got["merge_us"] == pytest.approx(5.0)
+    assert got["launch_span_us"] == pytest.approx(100.0 + 2.0 + 5.0)
+    assert got["decode_median_us"] == pytest.approx(100.0)
+
+
+def test_traffic_scaled_by_the_copy(tmp_path):
+    """Bytes per launch = (median decode + median merge counter, KiB) x
+    1024 x (copy size / what the counter reads for the copy)."""
+    copy_mib = 1024
+    for counter, copy_reads, dec, red in (("FETCH_SIZE", 512 * 1024, [300_000, 310_000, 305_000],
+                                           [100, 120]),
+                                          ("WRITE_SIZE", 1024 * 1024, [60, 62, 64], [10, 10])):
+        d = tmp_path / counter
+        d.mkdir()
+        rows = [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": counter,
+                 "Counter_Value": str(v)} for v in (copy_reads, copy_reads, 3.0)]
+        rows += [{"Kernel_Name": "kvq_paged_decode_int4_kernel", "Counter_Name": counter,
+                  "Counter_Value": str(v)} for v in dec]
+        rows += [{"Kernel_Name": "kvq_partition_reduce_kernel", "Counter_Name": counter,
+                  "Counter_Value": str(v)} for v in red]
+        _write_csv(d / "run_counter_collection.csv", rows)
+    out = tmp_path / "traffic.json"
+    profile_summary.traffic(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"),
+                            "kivi-int4", copy_mib, "f", "w", str(out), split_tokens=16384)
+    import json
+    t = json.load(open(out))
+    e = t["kivi-int4"]
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["read_bytes"] == int((305_000 + 110) * 1024 * 2.0)
+    assert e["write_bytes"] == int((62 + 10) * 1024 * 1.0)
+    assert e["bytes_per_launch"] == e["read_bytes"] + e["write_bytes"]
+    assert t["kernel_source_hash"] == profile_summary.kernel_source_hash()
+    assert e["dispatches"] == [3, 3] and e["split_tokens"] == 16384
