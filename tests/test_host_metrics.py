@@ -166,3 +166,30 @@ def test_traffic_scaled_by_the_copy(tmp_path):
     assert e["bytes_per_launch"] == e["read_bytes"] + e["write_bytes"]
     assert t["kernel_source_hash"] == profile_summary.kernel_source_hash()
     assert e["dispatches"] == [3, 3] and e["split_tokens"] == 16384
+
+
+def test_crosscheck_bytes_per_request_from_the_copy(tmp_path):
+    """Each request counter becomes bytes with the bytes per request the
+    copy shows (copy bytes / its requests): a 64-byte-request counter and a
+    128-byte one give the same launch bytes for the same traffic."""
+    copy_mib = 256
+    copy_bytes = copy_mib << 20
+    launch_bytes = 610_000_000          # decode + merge read traffic
+    rows = []
+    for name, req in (("TCC_EA0_RDREQ_DRAM_sum", 64), ("TCP_TCC_READ_REQ_sum", 128)):
+        rows += [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": name,
+                  "Counter_Value": str(copy_bytes // req)} for _ in range(2)]
+        dec = (launch_bytes - 128 * 1024) // req
+        rows += [{"Kernel_Name": "kvq_paged_decode_int4_kernel", "Counter_Name": name,
+                  "Counter_Value": str(v)} for v in (dec - 10, dec, dec + 10)]
+        rows += [{"Kernel_Name": "kvq_partition_reduce_kernel", "Counter_Name": name,
+                  "Counter_Value": str(128 * 1024 // req)}]
+    _write_csv(tmp_path / "run_counter_collection.csv", rows)
+    out = tmp_path / "x.md"
+    profile_summary.crosscheck(str(tmp_path), "kivi-int4", copy_mib, "cmd", str(out))
+    text = out.read_text()
+    for name, req in (("TCC_EA0_RDREQ_DRAM_sum", 64), ("TCP_TCC_READ_REQ_sum", 128)):
+        line = next(ln for ln in text.splitlines() if ln.startswith(f"| {name} |"))
+        cells = [c.strip() for c in line.split("|")]
+        assert cells[3] == f"{req:.2f}"
+        assert cells[5] == f"{launch_bytes / 1e6:.2f} MB"
